@@ -1,0 +1,144 @@
+"""Python front of the fp64 selective-scan oracle (``sscan_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg use this module; the HIP path never does.
+
+``build()`` compiles the C source with gcc (-O2, no fast-math).  ``sscan_fwd`` and
+``sscan_bidir`` take float64 numpy arrays in the layouts of the C file and return
+the gated output in float64 (never rounded to a storage dtype).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "sscan_oracle.c")
+LIB = os.path.join(HERE, "liboracle_sscan.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into ``liboracle_sscan.so`` next to its source."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
+                               "-o", tmp, SRC, "-lm", "-lpthread"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build(force=True)
+        lib = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        INT = ctypes.c_int
+        lib.oracle_sscan_fwd.argtypes = [P, P, P, INT, P, P, P, P, P, P, I64, I64, I64, I64, INT, P, P, INT]
+        lib.oracle_sscan_fwd.restype = INT
+        lib.oracle_sscan_bidir.argtypes = [P, P, P] + [P] * 12 + [INT, I64, I64, I64, I64, INT]
+        lib.oracle_sscan_bidir.restype = INT
+        lib.oracle_softplus_f64.argtypes = [ctypes.c_double]
+        lib.oracle_softplus_f64.restype = ctypes.c_double
+        lib.oracle_silu_f64.argtypes = [ctypes.c_double]
+        lib.oracle_silu_f64.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def sscan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, reverse=False,
+              h0=None, return_last_state=False, nthreads: int = 1):
+    """One direction; returns out [b, d, L] (and h_last [b, d, N] if asked)."""
+    u = _c64(u)
+    b, d, L = u.shape
+    A = _c64(A)
+    N = A.shape[1]
+    delta = _c64(delta, (b, d, L))
+    B = _c64(B, (b, N, L))
+    C = _c64(C, (b, N, L))
+    D = _c64(D, (d,))
+    z = _c64(z, (b, d, L))
+    bias = _c64(delta_bias, (d,))
+    h0 = _c64(h0, (b, d, N))
+    out = np.empty((b, d, L), dtype=np.float64)
+    hl = np.empty((b, d, N), dtype=np.float64) if return_last_state else None
+    st = _load().oracle_sscan_fwd(_p(u), _p(delta), _p(bias), int(bool(softplus)), _p(A), _p(B), _p(C),
+                                  _p(D), _p(z), _p(out), b, d, L, N, int(bool(reverse)), _p(h0), _p(hl),
+                                  int(nthreads))
+    if st != 0:
+        raise RuntimeError(f"oracle_sscan_fwd failed with status {st}")
+    return (out, hl) if return_last_state else out
+
+
+def sscan_bidir(u, z, fwd: dict, rev: dict, softplus=True, nthreads: int = 1):
+    """Both directions (separate parameter dicts with keys delta, A, B, C and
+    optional D, delta_bias), summed and gated once."""
+    u = _c64(u)
+    b, d, L = u.shape
+    z = _c64(z, (b, d, L))
+    out = np.empty((b, d, L), dtype=np.float64)
+    args = []
+    keep = []
+    for p in (fwd, rev):
+        A = _c64(p["A"])
+        N = A.shape[1]
+        arrs = [_c64(p["delta"], (b, d, L)), _c64(p.get("delta_bias"), (d,)), A,
+                _c64(p["B"], (b, N, L)), _c64(p["C"], (b, N, L)), _c64(p.get("D"), (d,))]
+        keep.extend(arrs)
+        args.extend(_p(a) for a in arrs)
+    N = keep[2].shape[1]
+    if keep[8].shape[1] != N:
+        raise ValueError("both directions need the same dstate")
+    st = _load().oracle_sscan_bidir(_p(u), _p(z), _p(out), *args, int(bool(softplus)), b, d, L, N, int(nthreads))
+    if st != 0:
+        raise RuntimeError(f"oracle_sscan_bidir failed with status {st}")
+    return out
+
+
+def softplus(x: float) -> float:
+    return _load().oracle_softplus_f64(float(x))
+
+
+def silu(x: float) -> float:
+    return _load().oracle_silu_f64(float(x))
+
+
+def run_inputs(x64: dict, softplus=True, nthreads: int = 1, reverse=False, gate=True):
+    """Oracle on a dict from ``inputs.as_f64_dict`` (one or two directions)."""
+    z = x64["z"] if gate else None
+    dirs = x64["dirs"]
+    if len(dirs) == 1:
+        p = dirs[0]
+        return sscan_fwd(x64["u"], x64["delta"], p["A"], p["B"], p["C"], p["D"], z, p["delta_bias"],
+                         softplus=softplus, reverse=reverse, nthreads=nthreads)
+    f, r = dirs
+    return sscan_bidir(x64["u"], z, dict(f, delta=x64["delta"]), dict(r, delta=x64["delta"]),
+                       softplus=softplus, nthreads=nthreads)
