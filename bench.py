@@ -1,0 +1,168 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X selective scan (Mamba S6) on one GPU.
+
+Workload: the long-sequence single-direction scan (batch 1, d_inner 1536,
+len 262144, dstate 16, bf16 u/delta/z/y, f32 B/C, seeded synthetic inputs already
+resident in HBM).  One step = one sscan_fwd call (all its kernels).  Prints ONE
+JSON line on stdout.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan Melem/s (batch·dim·len) + achieved HBM GB/s vs MI355X peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9  # CUs x SIMDs x lanes x clock: non-packed fp32 lane-instructions/s
+EXP_SLOTS = 2.0                 # v_exp_f32 issue cost in VALU slots (measured: half the FMA rate)
+FLOPS_PER_ELEM_STATE = 6.0      # dt*A (1) + dt*u*B (1) + state FMA (2) + readout FMA (2)
+SLOTS_PER_ELEM_STATE = 4.0 + EXP_SLOTS  # the same four VALU ops plus one exp
+ALU_PEAK_TFLOPS = VALU_LANE_OPS / SLOTS_PER_ELEM_STATE * FLOPS_PER_ELEM_STATE / 1e12
+
+
+def alg_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one call: u, delta, z read once, y written once,
+    B and C read once per direction, A/D/bias per direction."""
+    io = 2 if cfg.io_dtype == "bf16" else 4
+    bc = 2 if cfg.bc_dtype == "bf16" else 4
+    per_dir = 2 * cfg.batch * cfg.dstate * cfg.len * bc + cfg.dim * (cfg.dstate + 2) * 4
+    return 4 * cfg.elems * io + cfg.ndir * per_dir
+
+
+def cpu_baseline(x, y_gpu, cfg, target_s: float = 8.0):
+    """The fp64 oracle, as it stands, on whole sampled rows of the same inputs,
+    using every host core available to this process."""
+    import numpy as np
+
+    from oracle import oracle
+    from selective_state_space_sscan_amd import inputs as I
+
+    cores = oracle.default_threads()
+
+    def run_rows(rows):
+        out = []
+        for b, d in rows:
+            sl = lambda t: I.f64(t[b:b + 1, d:d + 1])
+            u, z, delta = sl(x.u), sl(x.z), sl(x.delta)
+            ps = [dict(delta=delta, A=I.f64(p.A[d:d + 1]), B=I.f64(p.B[b:b + 1]), C=I.f64(p.C[b:b + 1]),
+                       D=I.f64(p.D[d:d + 1]), delta_bias=I.f64(p.delta_bias[d:d + 1])) for p in x.dirs]
+            if len(ps) == 1:
+                p = ps[0]
+                out.append(oracle.sscan_fwd(u, delta, p["A"], p["B"], p["C"], p["D"], z, p["delta_bias"], nthreads=1))
+            else:
+                out.append(oracle.sscan_bidir(u, z, ps[0], ps[1], nthreads=1))
+        return out
+
+    # rows are independent: run them on all cores with a thread pool (the C oracle
+    # releases the GIL inside ctypes calls)
+    from concurrent.futures import ThreadPoolExecutor
+
+    rng = np.random.default_rng(1234)
+    all_rows = [(b, d) for b in range(cfg.batch) for d in range(cfg.dim)]
+    order = [all_rows[i] for i in rng.permutation(len(all_rows))]
+    # calibrate on one row per core, then size the sample to about target_s
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(lambda r: run_rows([r]), order[:cores]))
+    t_cal = time.perf_counter() - t0
+    n_rows = int(min(len(order), max(cores, cores * target_s / max(t_cal, 1e-6))))
+    sample = order[:n_rows]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        refs = list(ex.map(lambda r: run_rows([r])[0], sample))
+    dt = time.perf_counter() - t0
+    elems = n_rows * cfg.len
+    # parity of the GPU output on the same sampled rows (the oracle output is at hand)
+    got = np.concatenate([I.f64(y_gpu[b:b + 1, d:d + 1].cpu()) for b, d in sample[:64]], 1)
+    ref = np.concatenate(refs[:64], 1)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = float(np.max(np.abs(got - ref) / (np.abs(ref) + rms)))
+    return {
+        "value": elems / dt / 1e6, "unit": "Melem/s", "cores": cores, "kind": "oracle",
+        "sample": f"{n_rows} whole rows of {cfg.len} tokens ({elems} elements, {cfg.ndir} direction(s)) "
+                  f"of the same seeded inputs, fp64 sequential per row, {cores} threads, {dt:.1f} s",
+        "seconds": dt, "gpu_parity_on_sample": {"floored_max_err": err, "rows_compared": min(64, n_rows)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long-seq-fwd")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.exit("bench.py measures one GPU only: this build has no multi-GPU path "
+                 "(run with --gpus 1)")
+
+    import torch
+
+    from selective_state_space_sscan_amd import inputs as I
+    from selective_state_space_sscan_amd import sscan
+
+    sscan.load_library()
+    names = [c.name for c in I.CONFIGS]
+    ci = names.index(args.workload)
+    cfg = I.CONFIGS[ci]
+    dev = torch.device("cuda:0")
+    x = I.config_inputs(ci, 0)
+    xd = x.to(dev)
+    ws_bytes = sscan.workspace_bytes(cfg.batch, cfg.dim, cfg.len, cfg.dstate, cfg.bidir)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(xd.u)
+
+    def step():
+        sscan.run_inputs(xd, out=y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        step()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms = total_ms / args.steps
+    value = cfg.elems / (ms * 1e-3) / 1e6
+
+    nbytes = alg_bytes(cfg)
+    flops = FLOPS_PER_ELEM_STATE * cfg.dstate * cfg.elems * cfg.ndir
+    achieved_tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": value, "unit": "Melem/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded numpy PCG64, shapes of the pages' workloads)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "dim": cfg.dim, "len": cfg.len, "dstate": cfg.dstate,
+                   "directions": cfg.ndir, "io_dtype": cfg.io_dtype, "bc_dtype": cfg.bc_dtype},
+        "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / ALU_PEAK_TFLOPS, "traffic": None},
+        "hbm": {"achieved_GBs": gbs, "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
+                "algorithmic_bytes_per_step": nbytes},
+        "step_ms_p10_p50_p90": [float(sorted(per_step_ms)[int(q * (len(per_step_ms) - 1))]) for q in (0.1, 0.5, 0.9)],
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x, y, cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

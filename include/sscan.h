@@ -1,0 +1,125 @@
+/*
+ * sscan.h -- C ABI of the MI355X (gfx950) selective scan (Mamba S6).
+ *
+ * Operation (Hand-written simplified Mamba2 page, sections 2.2, 4.2-4.4;
+ * Reproducing Vision Mamba page, section 3.2 for the bidirectional sum):
+ *
+ *   dt_t = softplus(delta_t + delta_bias_d)   (or delta_t + delta_bias_d if softplus == 0)
+ *   h_n  = 0 at the first processed token
+ *   h_n <- exp(dt_t * A[d,n]) * h_n + dt_t * B[b,n,t] * u_t      (zero-order hold for A,
+ *                                                                  first-order Bbar = dt*B)
+ *   y_t  = sum_n C[b,n,t] * h_n + D_d * u_t
+ *   out_t = y_t * silu(z_t),  silu(x) = x / (1 + exp(-x))          (z == NULL: out = y)
+ *
+ * sscan_fwd runs one direction: t ascending, or t descending when reverse != 0
+ * (a forward scan of the time-flipped sequence, flipped back).  sscan_bidir runs
+ * both directions, each with its own delta/bias/A/B/C/D, adds the two y and gates
+ * the sum once.  The state is carried across the whole sequence (it is never reset
+ * between internal chunks) and is never written to memory as a sequence.
+ *
+ * Layouts (all row-major and contiguous, element strides implied by the sizes):
+ *   u, delta, z, y : [batch, dim, len]     dtype io_dtype  (SSCAN_F32 or SSCAN_BF16)
+ *   B, C           : [batch, dstate, len]  dtype bc_dtype  (shared by all channels)
+ *   A              : [dim, dstate]         float32 (diagonal state matrix per channel)
+ *   D, delta_bias  : [dim]                 float32
+ * Arithmetic and the state are float32; bf16 inputs widen exactly, bf16 outputs
+ * round to nearest even.  dstate must be 16.
+ *
+ * Ownership: every data pointer is a DEVICE pointer owned by the caller.  The
+ * library allocates no memory on these calls and keeps no state after return.
+ * Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ * call returns; y is valid once the stream reaches that point, and inputs must stay
+ * alive until then.  y must not overlap any input.  Long sequences need a
+ * caller-provided device workspace of sscan_workspace_bytes(...) bytes (NULL is
+ * allowed when that size is 0); its contents on entry do not matter.
+ *
+ * Errors: every argument is checked before any HIP call; on error nothing is
+ * enqueued and a negative status is returned (see sscan_strerror).  A failure
+ * reported by the HIP runtime at launch is returned as SSCAN_ERR_HIP.  No
+ * exception crosses this interface.  Calls are thread-safe (no global mutable
+ * state); calls that share a workspace must be ordered on one stream.
+ */
+#ifndef SSCAN_H_
+#define SSCAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define SSCAN_API __attribute__((visibility("default")))
+#else
+#define SSCAN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sscan_status {
+  SSCAN_OK = 0,
+  SSCAN_ERR_NULL = -1,        /* a required pointer is NULL */
+  SSCAN_ERR_SHAPE = -2,       /* batch, dim or len < 0, or a size product overflows */
+  SSCAN_ERR_UNSUPPORTED = -3, /* dstate != 16 or unknown dtype code */
+  SSCAN_ERR_ALIGN = -4,       /* a pointer is not aligned to its element size */
+  SSCAN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than sscan_workspace_bytes */
+  SSCAN_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
+  SSCAN_ERR_ALIAS = -7        /* y overlaps an input */
+};
+
+enum sscan_dtype { SSCAN_F32 = 0, SSCAN_BF16 = 1 };
+
+/* Parameters of one scan direction (all device pointers). */
+typedef struct sscan_dir_params {
+  const void* delta;        /* [batch, dim, len] io_dtype, required (may alias the other direction's) */
+  const float* delta_bias;  /* [dim], optional (NULL = 0) */
+  const float* A;           /* [dim, dstate], required */
+  const void* B;            /* [batch, dstate, len] bc_dtype, required */
+  const void* C;            /* [batch, dstate, len] bc_dtype, required */
+  const float* D;           /* [dim], optional (NULL = 0) */
+} sscan_dir_params;
+
+/* One direction.  Required: u, delta, A, B, C, y.  Optional: delta_bias, D, z.
+ * A size of 0 in batch, dim or len is a valid empty call (nothing is enqueued). */
+SSCAN_API int sscan_fwd(const void* u, const void* delta, const float* delta_bias, int softplus,
+              const float* A, const void* B, const void* C, const float* D,
+              const void* z, void* y,
+              int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+              int reverse, void* stream,
+              int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+
+/* Both directions summed, gated once.  Required: u, y, fwd, rev and inside each
+ * direction delta, A, B, C.  Optional: z and each direction's delta_bias and D. */
+SSCAN_API int sscan_bidir(const void* u, const void* z, void* y,
+                const sscan_dir_params* fwd, const sscan_dir_params* rev, int softplus,
+                int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+
+/* Same checks as sscan_fwd / sscan_bidir without touching the GPU: returns the
+ * status the call would return before any launch.  workspace is only compared with
+ * the required size (it is never dereferenced). */
+SSCAN_API int sscan_validate_fwd(const void* u, const void* delta, const float* delta_bias, int softplus,
+                       const float* A, const void* B, const void* C, const float* D,
+                       const void* z, const void* y,
+                       int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                       int reverse, int io_dtype, int bc_dtype,
+                       const void* workspace, size_t workspace_bytes);
+SSCAN_API int sscan_validate_bidir(const void* u, const void* z, const void* y,
+                         const sscan_dir_params* fwd, const sscan_dir_params* rev, int softplus,
+                         int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                         int io_dtype, int bc_dtype, const void* workspace, size_t workspace_bytes);
+
+/* Bytes of device workspace a call with these sizes needs (0 if none); bidir != 0
+ * for sscan_bidir.  Returns 0 for invalid sizes (the call itself reports them). */
+SSCAN_API size_t sscan_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir);
+
+/* Static description of a status code; never NULL. */
+SSCAN_API const char* sscan_strerror(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+SSCAN_API int sscan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSCAN_H_ */

@@ -1,0 +1,65 @@
+// sscan_internal.h -- launch interface between the C ABI (sscan_capi.cpp) and the
+// gfx950 kernels (sscan_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace sscan {
+
+constexpr int kDState = 16;        // states per channel held in registers
+constexpr int kLanes = 64;         // channels per wavefront (lane = channel)
+
+constexpr int kTile = 16;          // tokens per per-lane register tile
+
+// Sequences longer than kShortMax are split into segments scanned in parallel;
+// the state entering each segment is produced by the aggregate and carry kernels.
+constexpr int64_t kShortMax = 256;
+constexpr int64_t kMaxBidirSegment = 256;  // LDS meeting buffer: seg_len * 64 * 4 B
+constexpr int64_t kSegAlign = 64;          // segment lengths are multiples of this
+
+struct DirArgs {
+  const void* delta;
+  const float* delta_bias;  // nullable
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;           // nullable
+};
+
+struct ScanArgs {
+  const void* u;
+  const void* z;            // nullable
+  void* y;
+  DirArgs dir[2];
+  int ndir;                 // 1 or 2
+  int reverse;              // single direction only
+  int softplus;
+  int io_bf16;              // u, delta, z, y are bf16 (else f32)
+  int bc_bf16;              // B, C are bf16 (else f32)
+  int64_t batch, dim, len;
+};
+
+// How a call is split along the sequence, and the workspace it needs (floats,
+// in this order):
+//   bc   [ndir][batch][len][32]        B_t (16 states) then C_t (16), fp32, token-major
+//   agg  [ndir][batch][nseg][17][dim]  segment end states (from zero) + sum of dt
+//   hin  [ndir][batch][nseg][16][dim]  state entering every segment
+// agg and hin exist only when nseg > 1.
+struct Plan {
+  int64_t seg_len;          // tokens per segment
+  int64_t nseg;             // segments per row (1: no aggregate/carry kernels)
+  size_t bc_floats;
+  size_t agg_floats;
+  size_t hin_floats;
+  size_t workspace_bytes;
+};
+
+Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir);
+
+// Enqueues the whole call on `stream`; returns the first HIP error (hipSuccess if none).
+hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* workspace, hipStream_t stream);
+
+}  // namespace sscan

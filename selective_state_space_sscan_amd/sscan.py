@@ -1,0 +1,194 @@
+"""Thin ctypes binding of ``libsscan.so`` (the C ABI in include/sscan.h).
+
+Argument marshalling only: every step of the scan runs in the library's HIP
+kernels.  PyTorch supplies device memory (inputs, outputs, the workspace) and the
+current stream.  If the library is missing this module raises; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsscan.so")
+
+SSCAN_F32 = 0
+SSCAN_BF16 = 1
+DSTATE = 16
+
+_DT_CODE = {torch.float32: SSCAN_F32, torch.bfloat16: SSCAN_BF16}
+
+
+class SScanError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({strerror(status)})")
+        self.status = status
+
+
+class DirParams(ctypes.Structure):
+    _fields_ = [("delta", ctypes.c_void_p), ("delta_bias", ctypes.c_void_p), ("A", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads (once) and returns the shared library; raises if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m selective_state_space_sscan_amd.build`")
+    lib = ctypes.CDLL(p)
+    V, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    DP = ctypes.POINTER(DirParams)
+    lib.sscan_fwd.argtypes = [V, V, V, I, V, V, V, V, V, V, I64, I64, I64, I64, I, V, I, I, V, SZ]
+    lib.sscan_fwd.restype = I
+    lib.sscan_bidir.argtypes = [V, V, V, DP, DP, I, I64, I64, I64, I64, V, I, I, V, SZ]
+    lib.sscan_bidir.restype = I
+    lib.sscan_validate_fwd.argtypes = [V, V, V, I, V, V, V, V, V, V, I64, I64, I64, I64, I, I, I, V, SZ]
+    lib.sscan_validate_fwd.restype = I
+    lib.sscan_validate_bidir.argtypes = [V, V, V, DP, DP, I, I64, I64, I64, I64, I, I, V, SZ]
+    lib.sscan_validate_bidir.restype = I
+    lib.sscan_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.sscan_workspace_bytes.restype = SZ
+    lib.sscan_strerror.argtypes = [I]
+    lib.sscan_strerror.restype = ctypes.c_char_p
+    lib.sscan_version.argtypes = []
+    lib.sscan_version.restype = I
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().sscan_strerror(int(status)).decode()
+
+
+def workspace_bytes(batch: int, dim: int, length: int, dstate: int = DSTATE, bidir: bool = False) -> int:
+    return int(load_library().sscan_workspace_bytes(batch, dim, length, dstate, int(bool(bidir))))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: Optional[torch.Tensor], name: str, device, dtype=None, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _check(workspace, "workspace", device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, reverse: bool = False,
+        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One-direction scan (``sscan_fwd``).  u, delta, z: [batch, dim, len] f32/bf16;
+    B, C: [batch, 16, len] f32/bf16; A: [dim, 16] f32; D, delta_bias: [dim] f32.
+    Returns the gated output, same dtype as u, enqueued on the current stream."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.fwd needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or B.dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = u.shape
+    _check(u, "u", dev)
+    _check(delta, "delta", dev, u.dtype, u.shape)
+    _check(z, "z", dev, u.dtype, u.shape)
+    _check(A, "A", dev, torch.float32, (d, DSTATE))
+    _check(B, "B", dev, None, (b, DSTATE, L))
+    _check(C, "C", dev, B.dtype, (b, DSTATE, L))
+    _check(D, "D", dev, torch.float32, (d,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (d,))
+    if out is None:
+        out = torch.empty_like(u)
+    _check(out, "out", dev, u.dtype, u.shape)
+    if u.numel() == 0:
+        return out
+    ws, ws_bytes = _workspace(workspace_bytes(b, d, L, DSTATE, False), dev, workspace)
+    st = lib.sscan_fwd(_ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C),
+                       _ptr(D), _ptr(z), _ptr(out), b, d, L, DSTATE, int(bool(reverse)), _stream(dev),
+                       _DT_CODE[u.dtype], _DT_CODE[B.dtype], _ptr(ws), ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_fwd")
+    return out
+
+
+def _dir(p: dict, name: str, dev, u, bdtype):
+    b, d, L = u.shape
+    _check(p["delta"], f"{name}.delta", dev, u.dtype, u.shape)
+    _check(p["A"], f"{name}.A", dev, torch.float32, (d, DSTATE))
+    _check(p["B"], f"{name}.B", dev, bdtype, (b, DSTATE, L))
+    _check(p["C"], f"{name}.C", dev, bdtype, (b, DSTATE, L))
+    _check(p.get("D"), f"{name}.D", dev, torch.float32, (d,))
+    _check(p.get("delta_bias"), f"{name}.delta_bias", dev, torch.float32, (d,))
+    return DirParams(p["delta"].data_ptr(), p["delta_bias"].data_ptr() if p.get("delta_bias") is not None else None,
+                     p["A"].data_ptr(), p["B"].data_ptr(), p["C"].data_ptr(),
+                     p["D"].data_ptr() if p.get("D") is not None else None)
+
+
+def bidir(u, z, fwd: dict, rev: dict, softplus: bool = True, out: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Bidirectional scan (``sscan_bidir``): ``fwd`` and ``rev`` are dicts with
+    delta, A, B, C and optional D, delta_bias.  Returns (y_fwd + y_rev) * silu(z)."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.bidir needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or fwd["B"].dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = u.shape
+    _check(u, "u", dev)
+    _check(z, "z", dev, u.dtype, u.shape)
+    pf = _dir(fwd, "fwd", dev, u, fwd["B"].dtype)
+    pr = _dir(rev, "rev", dev, u, fwd["B"].dtype)
+    if out is None:
+        out = torch.empty_like(u)
+    _check(out, "out", dev, u.dtype, u.shape)
+    if u.numel() == 0:
+        return out
+    ws, ws_bytes = _workspace(workspace_bytes(b, d, L, DSTATE, True), dev, workspace)
+    st = lib.sscan_bidir(_ptr(u), _ptr(z), _ptr(out), ctypes.byref(pf), ctypes.byref(pr), int(bool(softplus)),
+                         b, d, L, DSTATE, _stream(dev), _DT_CODE[u.dtype], _DT_CODE[fwd["B"].dtype], _ptr(ws),
+                         ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_bidir")
+    return out
+
+
+def run_inputs(x, softplus: bool = True, out=None, workspace=None) -> torch.Tensor:
+    """Runs the scan on a ``ScanInputs`` already on the device (one or two directions)."""
+    if len(x.dirs) == 1:
+        p = x.dirs[0]
+        return fwd(x.u, x.delta, p.A, p.B, p.C, p.D, x.z, p.delta_bias, softplus=softplus, out=out,
+                   workspace=workspace)
+    f, r = x.dirs
+    mk = lambda p: dict(delta=x.delta, delta_bias=p.delta_bias, A=p.A, B=p.B, C=p.C, D=p.D)
+    return bidir(x.u, x.z, mk(f), mk(r), softplus=softplus, out=out, workspace=workspace)

@@ -1,0 +1,174 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call.
+
+Pointers passed here are fake, never dereferenced: validation only looks at
+NULL-ness, alignment, overlap and sizes.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_sscan_amd import sscan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sscan.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, EALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sscan.LIB_PATH):
+        from selective_state_space_sscan_amd import build
+        build.build()
+    return sscan.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SSCAN_API\s+[\w\s\*]*?\b(sscan_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert {"sscan_fwd", "sscan_bidir", "sscan_workspace_bytes", "sscan_strerror"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_version(lib):
+    for st in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, EALIAS, 123):
+        assert isinstance(sscan.strerror(st), str) and sscan.strerror(st)
+    assert sscan.strerror(123) == "unknown status"
+    assert lib.sscan_version() >= 100
+
+
+class Fake:
+    """Disjoint fake device addresses, 256-byte aligned."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes):
+        p = self.next
+        self.next += (nbytes + 4096) // 256 * 256 + 256
+        return p
+
+
+def fwd_args(b, d, L, io=0, bc=0, **over):
+    f = Fake()
+    ie = 2 if io == 1 else 4
+    be = 2 if bc == 1 else 4
+    a = dict(u=f(b * d * L * ie), delta=f(b * d * L * ie), bias=f(d * 4), softplus=1, A=f(d * 64), B=f(b * 16 * L * be),
+             C=f(b * 16 * L * be), D=f(d * 4), z=f(b * d * L * ie), y=f(b * d * L * ie), b=b, d=d, L=L, N=16,
+             reverse=0, io=io, bc=bc, ws=f(1 << 33), ws_bytes=1 << 33)
+    a.update(over)
+    return a
+
+
+def call_validate_fwd(lib, a):
+    return lib.sscan_validate_fwd(a["u"], a["delta"], a["bias"], a["softplus"], a["A"], a["B"], a["C"], a["D"],
+                                  a["z"], a["y"], a["b"], a["d"], a["L"], a["N"], a["reverse"], a["io"], a["bc"],
+                                  a["ws"], a["ws_bytes"])
+
+
+def test_validate_fwd_accepts_good_arguments(lib):
+    for io, bc in ((0, 0), (1, 1), (1, 0)):
+        assert call_validate_fwd(lib, fwd_args(2, 64, 32, io, bc)) == OK
+        assert call_validate_fwd(lib, fwd_args(1, 1536, 262144, io, bc)) == OK
+    assert call_validate_fwd(lib, fwd_args(2, 64, 32, D=None, bias=None, z=None)) == OK
+
+
+@pytest.mark.parametrize("name", ["u", "delta", "A", "B", "C", "y"])
+def test_validate_fwd_null_required(lib, name):
+    assert call_validate_fwd(lib, fwd_args(2, 64, 32, **{name: None})) == ENULL
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(b=-1), ESHAPE), (dict(d=-5), ESHAPE), (dict(L=-1), ESHAPE),
+    (dict(b=1 << 40, d=1 << 20, L=1 << 20), ESHAPE),
+    (dict(N=8), EUNSUP), (dict(N=32), EUNSUP), (dict(io=2), EUNSUP), (dict(bc=-1), EUNSUP),
+])
+def test_validate_fwd_bad_sizes_and_codes(lib, over, status):
+    assert call_validate_fwd(lib, dict(fwd_args(2, 64, 32), **over)) == status
+
+
+def test_validate_fwd_alignment(lib):
+    a = fwd_args(2, 64, 32)
+    assert call_validate_fwd(lib, dict(a, u=a["u"] + 2)) == EALIGN
+    assert call_validate_fwd(lib, dict(a, A=a["A"] + 1)) == EALIGN
+    assert call_validate_fwd(lib, dict(a, B=a["B"] + 2)) == EALIGN
+    bf = fwd_args(2, 64, 32, io=1, bc=1)
+    assert call_validate_fwd(lib, dict(bf, u=bf["u"] + 2, y=bf["y"] + 2)) == OK  # bf16: 2-byte alignment suffices
+    assert call_validate_fwd(lib, dict(bf, y=bf["y"] + 1)) == EALIGN
+
+
+def test_validate_fwd_aliasing(lib):
+    a = fwd_args(2, 64, 32)
+    assert call_validate_fwd(lib, dict(a, y=a["u"])) == EALIAS
+    assert call_validate_fwd(lib, dict(a, y=a["z"] + 64)) == EALIAS
+    assert call_validate_fwd(lib, dict(a, y=a["B"])) == EALIAS
+
+
+def test_empty_call_is_ok_even_without_pointers(lib):
+    a = fwd_args(0, 64, 32, u=None, y=None, delta=None)
+    assert call_validate_fwd(lib, a) == OK
+    assert call_validate_fwd(lib, fwd_args(2, 64, 0)) == OK
+
+
+def staging_bytes(ndir, b, L):
+    # B and C re-laid token-major in fp32: 32 floats per token and direction
+    return (ndir * b * L * 32 + 63) // 64 * 64 * 4
+
+
+def test_workspace_rules(lib):
+    short = lib.sscan_workspace_bytes(64, 384, 197, 16, 1)
+    assert short == staging_bytes(2, 64, 197)  # unsplit sequence: B/C staging only
+    assert lib.sscan_workspace_bytes(2, 64, 32, 16, 0) == staging_bytes(1, 2, 32)
+    assert call_validate_fwd(lib, fwd_args(2, 64, 32, ws=None, ws_bytes=0)) == EWS
+    long_f = lib.sscan_workspace_bytes(1, 1536, 262144, 16, 0)
+    long_b = lib.sscan_workspace_bytes(8, 192, 16384, 16, 1)
+    assert long_f > 0 and long_b > 0
+    # staging plus per-segment aggregates: a few percent of the inputs at most
+    assert staging_bytes(1, 1, 262144) < long_f < 0.05 * (1536 * 262144 * 2 * 4)
+    assert call_validate_fwd(lib, fwd_args(1, 1536, 262144, ws=None, ws_bytes=0)) == EWS
+    assert call_validate_fwd(lib, fwd_args(1, 1536, 262144, ws_bytes=long_f - 1)) == EWS
+    a = fwd_args(1, 1536, 262144, ws_bytes=long_f)
+    assert call_validate_fwd(lib, a) == OK
+    assert call_validate_fwd(lib, dict(a, ws=a["ws"] + 4)) == EALIGN
+    assert lib.sscan_workspace_bytes(1, 1536, 262144, 8, 0) == 0  # unsupported dstate: reported by the call
+
+
+def test_validate_bidir(lib):
+    f = Fake()
+    b, d, L = 8, 192, 16384
+    n_io, n_bc = b * d * L * 2, b * 16 * L * 2
+    u, z, y, delta = f(n_io), f(n_io), f(n_io), f(n_io)
+    mk = lambda: sscan.DirParams(delta, f(d * 4), f(d * 64), f(n_bc), f(n_bc), f(d * 4))
+    pf, pr = mk(), mk()
+    ws = lib.sscan_workspace_bytes(b, d, L, 16, 1)
+    wsp = f(ws)
+    V = lambda *a: lib.sscan_validate_bidir(*a)
+    assert V(u, z, y, ctypes.byref(pf), ctypes.byref(pr), 1, b, d, L, 16, 1, 1, wsp, ws) == OK
+    assert V(u, z, y, None, ctypes.byref(pr), 1, b, d, L, 16, 1, 1, wsp, ws) == ENULL
+    bad = sscan.DirParams(delta, None, None, pf.B, pf.C, None)
+    assert V(u, z, y, ctypes.byref(pf), ctypes.byref(bad), 1, b, d, L, 16, 1, 1, wsp, ws) == ENULL
+    assert V(u, z, y, ctypes.byref(pf), ctypes.byref(pr), 1, b, d, L, 16, 1, 1, None, 0) == EWS
+    assert V(u, z, pf.B, ctypes.byref(pf), ctypes.byref(pr), 1, b, d, L, 16, 1, 1, wsp, ws) == EALIAS
+    assert V(u, z, y, ctypes.byref(pf), ctypes.byref(pr), 1, b, d, L, 16, 1, 1, y + 128, ws) == EALIAS
+
+
+def test_run_entry_points_reject_before_any_hip_call(lib):
+    """The run entry points return validation errors without touching HIP (no GPU here)."""
+    a = fwd_args(2, 64, 32, u=None)
+    st = lib.sscan_fwd(a["u"], a["delta"], a["bias"], 1, a["A"], a["B"], a["C"], a["D"], a["z"], a["y"],
+                       2, 64, 32, 16, 0, None, 0, 0, None, 0)
+    assert st == ENULL
+    st = lib.sscan_fwd(1 << 40, a["delta"], a["bias"], 1, a["A"], a["B"], a["C"], a["D"], a["z"], a["y"],
+                       2, 64, 32, 12, 0, None, 0, 0, None, 0)
+    assert st == EUNSUP
+    st = lib.sscan_bidir(None, None, None, None, None, 1, 2, 64, 32, 16, None, 0, 0, None, 0)
+    assert st == ENULL

@@ -1,0 +1,162 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case draws seeded inputs, runs ``libsscan.so`` on cuda:0 and compares with
+the oracle on the same (exactly widened) values using the floored relative error
+of tests/parity.py: <= 1e-4 for float32 I/O, <= 2e-2 for bfloat16 I/O.
+Configs 0-3 are compared in full; the long-sequence config 4 in the launch
+configuration the benchmark times, on whole sampled rows.
+"""
+import os
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from parity import TOL, metrics
+from selective_state_space_sscan_amd import inputs as I
+from selective_state_space_sscan_amd import sscan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+NTHREADS = min(16, oracle.default_threads())
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    sscan.load_library()  # raises if the extension is missing: no fallback
+    if not os.path.exists(oracle.LIB):
+        oracle.build(force=True)
+
+
+def gpu_run(x, softplus=True, gate=True, reverse=False):
+    xd = x.to(DEV)
+    z = xd.z if gate else None
+    if len(xd.dirs) == 1:
+        p = xd.dirs[0]
+        y = sscan.fwd(xd.u, xd.delta, p.A, p.B, p.C, p.D, z, p.delta_bias, softplus=softplus, reverse=reverse)
+    else:
+        mk = lambda p: dict(delta=xd.delta, delta_bias=p.delta_bias, A=p.A, B=p.B, C=p.C, D=p.D)
+        y = sscan.bidir(xd.u, z, mk(xd.dirs[0]), mk(xd.dirs[1]), softplus=softplus)
+    torch.cuda.synchronize()
+    return y
+
+
+def oracle_run(x, softplus=True, gate=True, reverse=False):
+    return oracle.run_inputs(I.as_f64_dict(x), softplus=softplus, nthreads=NTHREADS, reverse=reverse, gate=gate)
+
+
+def check(got, ref, io_dtype, what):
+    if isinstance(got, torch.Tensor):
+        got = I.f64(got.cpu())
+    m = metrics(got, ref)
+    print(f"{what}: {m}", flush=True)
+    assert m["floored_max"] <= TOL[io_dtype], (what, m)
+    return m
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_config_full_parity(cfg):
+    x = I.config_inputs(cfg, 0)
+    got = gpu_run(x)
+    ref = oracle_run(x)
+    check(got, ref, x.io_dtype, f"config {cfg} ({I.CONFIGS[cfg].name})")
+
+
+@pytest.mark.parametrize("cfg,k", [(0, 1), (0, 2), (1, 1), (1, 2)])
+def test_small_configs_more_seeds(cfg, k):
+    x = I.config_inputs(cfg, k)
+    check(gpu_run(x), oracle_run(x), x.io_dtype, f"config {cfg} seed {k}")
+
+
+def test_config4_long_sequence_sampled_rows():
+    """The benchmark's workload and launch configuration; whole rows (all 262144
+    tokens, so every segment boundary and carry) compared for sampled channels."""
+    x = I.config_inputs(4, 0)
+    got = gpu_run(x).cpu()
+    rows = sorted(set([0, 1, 63, 64, 65, 767, 768, 1535] + list(np.random.default_rng(4).choice(1536, 16, replace=False))))
+    x64 = I.as_f64_dict(x)
+    p = x64["dirs"][0]
+    refs, gots = [], []
+    for d in rows:
+        ref = oracle.sscan_fwd(x64["u"][:, d:d + 1], x64["delta"][:, d:d + 1], p["A"][d:d + 1], p["B"], p["C"],
+                               p["D"][d:d + 1], x64["z"][:, d:d + 1], p["delta_bias"][d:d + 1], nthreads=1)
+        refs.append(ref)
+        gots.append(I.f64(got[:, d:d + 1]))
+    check(np.concatenate(gots, 1), np.concatenate(refs, 1), "bf16", f"config 4 rows {rows}")
+
+
+EDGE = [
+    # name, batch, dim, len, bidir, io, bc, kwargs
+    ("len1-fwd", 2, 64, 1, False, "f32", "f32", {}),
+    ("len1-bidir", 2, 64, 1, True, "f32", "f32", {}),
+    ("len2-bidir", 1, 64, 2, True, "f32", "f32", {}),
+    ("dim-tail-fwd", 2, 70, 45, False, "f32", "f32", {}),
+    ("dim-tail-bidir", 3, 130, 33, True, "bf16", "bf16", {}),
+    ("dim1", 1, 1, 100, True, "f32", "f32", {}),
+    ("short-max", 2, 64, 256, True, "f32", "f32", {}),
+    ("short-max+1", 2, 64, 257, True, "f32", "f32", {}),
+    ("long-ragged-fwd", 2, 96, 1000, False, "f32", "f32", {}),
+    ("long-ragged-rev", 2, 96, 1000, False, "f32", "f32", dict(reverse=True)),
+    ("long-ragged-bidir", 2, 96, 1003, True, "f32", "f32", {}),
+    ("long-bf16-f32bc", 1, 128, 5000, False, "bf16", "f32", {}),
+    ("long-bf16-bidir", 1, 64, 4099, True, "bf16", "bf16", {}),
+    ("no-gate", 2, 64, 300, True, "f32", "f32", dict(gate=False)),
+    ("no-softplus", 2, 64, 50, False, "f32", "f32", dict(softplus=False)),
+    ("rev-short", 2, 64, 50, False, "bf16", "bf16", dict(reverse=True)),
+]
+
+
+@pytest.mark.parametrize("name,b,d,L,bidir,io,bc,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(name, b, d, L, bidir, io, bc, kw):
+    x = I.make_inputs(b, d, L, bidir=bidir, io_dtype=io, bc_dtype=bc, seed=zlib.crc32(name.encode()) % 10000)
+    if not kw.get("softplus", True):
+        # without softplus the step is delta + bias itself: keep it positive
+        x.delta.abs_().add_(0.01)
+        for p in x.dirs:
+            p.delta_bias.zero_()
+    got = gpu_run(x, **kw)
+    ref = oracle_run(x, **kw)
+    check(got, ref, io, name)
+
+
+def test_optional_D_and_bias_absent():
+    x = I.make_inputs(2, 64, 300, seed=5)
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    y = sscan.fwd(xd.u, xd.delta, p.A, p.B, p.C, None, xd.z, None)
+    torch.cuda.synchronize()
+    x64 = I.as_f64_dict(x)
+    q = x64["dirs"][0]
+    ref = oracle.sscan_fwd(x64["u"], x64["delta"], q["A"], q["B"], q["C"], None, x64["z"], None)
+    check(y, ref, "f32", "no D, no bias")
+
+
+def test_deterministic_reruns():
+    x = I.config_inputs(3, 1).to(DEV)
+    a = sscan.run_inputs(x)
+    b = sscan.run_inputs(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_nan_propagates_like_the_oracle():
+    for bidir in (False, True):
+        x = I.make_inputs(2, 64, 600, bidir=bidir, seed=9)
+        x.u[1, 5, 333] = float("nan")
+        got = I.f64(gpu_run(x).cpu())
+        ref = oracle_run(x)
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), bidir
+        fin = ~np.isnan(ref)
+        m = metrics(got[fin], ref[fin])
+        assert m["floored_max"] <= TOL["f32"]
+
+
+def test_empty_input_returns_empty():
+    u = torch.empty(2, 0, 5, device=DEV)
+    A = torch.empty(0, 16, device=DEV)
+    B = torch.randn(2, 16, 5, device=DEV)
+    y = sscan.fwd(u, u, A, B, B)
+    assert y.shape == (2, 0, 5)
