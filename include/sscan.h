@@ -94,6 +94,28 @@ SSCAN_API int sscan_bidir(const void* u, const void* z, void* y,
                 int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
                 int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
 
+/* Profiling variants (for timing the internal steps of a call, not needed for
+ * results): the same work as sscan_fwd / sscan_bidir, and on the same stream
+ * events[0] is recorded before the first kernel and events[k] after step k of
+ * the call: 1 = B/C staging, 2 = segment aggregates, 3 = carry chain between
+ * segments, 4 = output pass.  Steps a call does not need (an unsplit sequence has
+ * no aggregate or carry step) get zero-length intervals.  events holds
+ * SSCAN_PROFILE_EVENTS hipEvent_t handles created by the caller (NULL entries are
+ * skipped; events itself may be NULL). */
+#define SSCAN_PROFILE_EVENTS 5
+SSCAN_API int sscan_fwd_profiled(const void* u, const void* delta, const float* delta_bias, int softplus,
+                       const float* A, const void* B, const void* C, const float* D,
+                       const void* z, void* y,
+                       int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                       int reverse, void* stream,
+                       int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes,
+                       void* const* events);
+SSCAN_API int sscan_bidir_profiled(const void* u, const void* z, void* y,
+                         const sscan_dir_params* fwd, const sscan_dir_params* rev, int softplus,
+                         int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                         int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes,
+                         void* const* events);
+
 /* Same checks as sscan_fwd / sscan_bidir without touching the GPU: returns the
  * status the call would return before any launch.  workspace is only compared with
  * the required size (it is never dereferenced). */

@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
+static_assert(SSCAN_PROFILE_EVENTS == sscan::kProfileEvents, "event count mismatch");
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -127,14 +128,18 @@ sscan::ScanArgs make_args(const void* u, const void* z, void* y, const DirView* 
 
 int run(const void* u, const void* z, void* y, const DirView* dirs, int ndir, int reverse, int softplus,
         int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream, int io_dtype, int bc_dtype,
-        void* workspace, size_t workspace_bytes) {
+        void* workspace, size_t workspace_bytes, void* const* events = nullptr) {
   sscan::Plan plan{};
   bool empty = false;
   const int st = validate(u, z, y, dirs, ndir, batch, dim, len, dstate, io_dtype, bc_dtype, workspace,
                           workspace_bytes, &plan, &empty);
   if (st != SSCAN_OK || empty) return st;
   const sscan::ScanArgs a = make_args(u, z, y, dirs, ndir, reverse, softplus, batch, dim, len, io_dtype, bc_dtype);
-  const hipError_t e = sscan::launch_scan(a, plan, static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+  hipEvent_t ev[sscan::kProfileEvents] = {};
+  if (events)
+    for (int i = 0; i < sscan::kProfileEvents; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+  const hipError_t e = sscan::launch_scan(a, plan, static_cast<float*>(workspace), static_cast<hipStream_t>(stream),
+                                          events ? ev : nullptr);
   return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
 }
 
@@ -162,6 +167,25 @@ int sscan_bidir(const void* u, const void* z, void* y, const sscan_dir_params* f
   const DirView d[2] = {view_of(fwd), view_of(rev)};
   return run(u, z, y, d, 2, 0, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype, workspace,
              workspace_bytes);
+}
+
+int sscan_fwd_profiled(const void* u, const void* delta, const float* delta_bias, int softplus, const float* A,
+                       const void* B, const void* C, const float* D, const void* z, void* y, int64_t batch,
+                       int64_t dim, int64_t len, int64_t dstate, int reverse, void* stream, int io_dtype,
+                       int bc_dtype, void* workspace, size_t workspace_bytes, void* const* events) {
+  const DirView d{delta, delta_bias, A, B, C, D};
+  return run(u, z, y, &d, 1, reverse, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype, workspace,
+             workspace_bytes, events);
+}
+
+int sscan_bidir_profiled(const void* u, const void* z, void* y, const sscan_dir_params* fwd,
+                         const sscan_dir_params* rev, int softplus, int64_t batch, int64_t dim, int64_t len,
+                         int64_t dstate, void* stream, int io_dtype, int bc_dtype, void* workspace,
+                         size_t workspace_bytes, void* const* events) {
+  if (!fwd || !rev) return SSCAN_ERR_NULL;
+  const DirView d[2] = {view_of(fwd), view_of(rev)};
+  return run(u, z, y, d, 2, 0, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype, workspace,
+             workspace_bytes, events);
 }
 
 int sscan_validate_fwd(const void* u, const void* delta, const float* delta_bias, int softplus, const float* A,

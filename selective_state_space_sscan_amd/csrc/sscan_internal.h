@@ -12,12 +12,11 @@ namespace sscan {
 constexpr int kDState = 16;        // states per channel held in registers
 constexpr int kLanes = 64;         // channels per wavefront (lane = channel)
 
-constexpr int kTile = 16;          // tokens per per-lane register tile
+constexpr int kTile = 32;          // tile alignment unit (tokens; a multiple of every tile size)
 
 // Sequences longer than kShortMax are split into segments scanned in parallel;
 // the state entering each segment is produced by the aggregate and carry kernels.
 constexpr int64_t kShortMax = 256;
-constexpr int64_t kMaxBidirSegment = 256;  // LDS meeting buffer: seg_len * 64 * 4 B
 constexpr int64_t kSegAlign = 64;          // segment lengths are multiples of this
 
 struct DirArgs {
@@ -59,7 +58,14 @@ struct Plan {
 
 Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir);
 
+// Boundaries of the steps of one call: before staging, after staging, after the
+// segment aggregates, after the carry chain, after the output pass.
+constexpr int kProfileEvents = 5;
+
 // Enqueues the whole call on `stream`; returns the first HIP error (hipSuccess if none).
-hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* workspace, hipStream_t stream);
+// With `events` (kProfileEvents entries, NULL entries skipped) each step boundary is
+// also recorded on the stream.
+hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* workspace, hipStream_t stream,
+                       hipEvent_t const* events = nullptr);
 
 }  // namespace sscan

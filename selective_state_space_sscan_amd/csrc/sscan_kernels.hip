@@ -40,10 +40,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBC = 2 * kDState;  // floats per token in the staged B/C buffer
 
-// Scan kernels keep about 100 live VGPRs per lane (16 states, 16 scaled A, the
-// token tiles); capping them at 128 lets four waves share each SIMD and stops the
-// scheduler from hoisting many tokens' exponentials ahead at the cost of occupancy.
-#define SSCAN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(4, 8)))
+// Scan kernels keep about 150 live VGPRs per lane (16 states, 16 scaled A, the
+// current and next token tiles); capping them at 168 lets three waves share each
+// SIMD and stops the scheduler from hoisting many tokens' exponentials ahead at the
+// cost of occupancy.
+#define SSCAN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3, 8)))
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
@@ -52,14 +53,16 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(x) = max(x, 0) + log1p(exp(-|x|)).  log1p(w) is taken as
-// log(1 + w) * w / ((1 + w) - 1): the quotient cancels the rounding of 1 + w, so
-// the result keeps full relative accuracy for small w (step sizes near 1e-4).
+// softplus(x) = max(x, 0) + log1p(w), w = exp(-|x|) in (0, 1].  log1p(w) is
+// log(s) for s = 1 + w rounded, plus the rounding error c = w - (s - 1) scaled by
+// 1/s ~ 1 - w: log(s + c) = log(s) + c/s + O(c^2), and c (below 2^-24) times
+// the dropped w^2 term is far below the result's last bit (log1p(w) ~ w).  This
+// keeps full relative accuracy for small step sizes (1e-4 and below).
 __device__ __forceinline__ float softplus_f32(float x) {
   const float w = exp2_hw(-fabsf(x) * kLog2e);
   const float s = 1.0f + w;
-  const float d = s - 1.0f;
-  const float lp = (d == 0.0f) ? w : (log2_hw(s) * kLn2) * (w * rcp_hw(d));
+  const float c = w - (s - 1.0f);
+  const float lp = fmaf(log2_hw(s), kLn2, c * (1.0f - w));
   return fmaxf(x, 0.0f) + lp;
 }
 
@@ -76,38 +79,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
-// Storage-type access.  A tile holds kTile consecutive tokens of one row as
-// 32-bit words (two bf16 per word, low half = earlier token).
+// Storage-type access.  A tile holds kTok consecutive tokens of one row as sixteen
+// 32-bit words (32 bf16 tokens, two per word with the earlier token in the low
+// half, or 16 f32 tokens): four 16-byte vector loads per tensor, half a 128-byte
+// L2 line.  Narrower tiles touch each line more times, far enough apart that the
+// line has left L2 in between and is fetched again.
+constexpr int kWords = 16;
+
 template <bool BF16>
 struct Io;
 template <>
 struct Io<false> {
   using T = float;
-  static constexpr int kWords = kTile;
+  static constexpr int kTok = 16;
   static __device__ __forceinline__ float load(const T* p, int64_t i) { return p[i]; }
   static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = v; }
   static __device__ __forceinline__ float get(const uint32_t (&w)[kWords], int j) { return __uint_as_float(w[j]); }
   static __device__ __forceinline__ void load_elems(uint32_t (&w)[kWords], const T* row, int64_t t) {
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) w[j] = __float_as_uint(row[t + j]);
+    for (int j = 0; j < kTok; ++j) w[j] = __float_as_uint(row[t + j]);
   }
-  static __device__ __forceinline__ void store_tile(T* row, int64_t t, const float (&y)[kTile], bool vec) {
-    if (vec) {
-      uint4* p = reinterpret_cast<uint4*>(row + t);
+  static __device__ __forceinline__ void pack(uint32_t (&w)[kWords], const float (&y)[kTok]) {
 #pragma unroll
-      for (int i = 0; i < kTile / 4; ++i)
-        p[i] = make_uint4(__float_as_uint(y[4 * i]), __float_as_uint(y[4 * i + 1]), __float_as_uint(y[4 * i + 2]),
-                          __float_as_uint(y[4 * i + 3]));
-    } else {
+    for (int j = 0; j < kTok; ++j) w[j] = __float_as_uint(y[j]);
+  }
+  static __device__ __forceinline__ void store_elems(T* row, int64_t t, const uint32_t (&w)[kWords]) {
 #pragma unroll
-      for (int j = 0; j < kTile; ++j) row[t + j] = y[j];
-    }
+    for (int j = 0; j < kTok; ++j) row[t + j] = __uint_as_float(w[j]);
   }
 };
 template <>
 struct Io<true> {
   using T = uint16_t;
-  static constexpr int kWords = kTile / 2;
+  static constexpr int kTok = 32;
   static __device__ __forceinline__ float load(const T* p, int64_t i) { return __uint_as_float(uint32_t(p[i]) << 16); }
   static __device__ __forceinline__ void store(T* p, int64_t i, float v) {
     p[i] = uint16_t(pack_bf16x2(v, 0.0f) & 0xffffu);
@@ -119,31 +123,28 @@ struct Io<true> {
 #pragma unroll
     for (int i = 0; i < kWords; ++i) w[i] = uint32_t(row[t + 2 * i]) | (uint32_t(row[t + 2 * i + 1]) << 16);
   }
-  static __device__ __forceinline__ void store_tile(T* row, int64_t t, const float (&y)[kTile], bool vec) {
-    uint32_t w[kWords];
+  static __device__ __forceinline__ void pack(uint32_t (&w)[kWords], const float (&y)[kTok]) {
 #pragma unroll
     for (int i = 0; i < kWords; ++i) w[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
-    if (vec) {
-      uint4* p = reinterpret_cast<uint4*>(row + t);
+  }
+  static __device__ __forceinline__ void store_elems(T* row, int64_t t, const uint32_t (&w)[kWords]) {
 #pragma unroll
-      for (int i = 0; i < kWords / 4; ++i) p[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kWords; ++i) {
-        row[t + 2 * i] = uint16_t(w[i] & 0xffffu);
-        row[t + 2 * i + 1] = uint16_t(w[i] >> 16);
-      }
+    for (int i = 0; i < kWords; ++i) {
+      row[t + 2 * i] = uint16_t(w[i] & 0xffffu);
+      row[t + 2 * i + 1] = uint16_t(w[i] >> 16);
     }
   }
 };
 
+// Tiles start at multiples of kTok, so with 16-byte aligned rows ("vec") each tile
+// is two aligned 16-byte words per lane.
 template <bool BF16>
-__device__ __forceinline__ void load_tile(uint32_t (&w)[Io<BF16>::kWords], const typename Io<BF16>::T* row,
-                                          int64_t t, bool vec) {
+__device__ __forceinline__ void load_tile(uint32_t (&w)[kWords], const typename Io<BF16>::T* row, int64_t t,
+                                          bool vec) {
   if (vec) {
     const uint4* p = reinterpret_cast<const uint4*>(row + t);
 #pragma unroll
-    for (int i = 0; i < Io<BF16>::kWords / 4; ++i) {
+    for (int i = 0; i < kWords / 4; ++i) {
       const uint4 v = p[i];
       w[4 * i] = v.x;
       w[4 * i + 1] = v.y;
@@ -152,6 +153,20 @@ __device__ __forceinline__ void load_tile(uint32_t (&w)[Io<BF16>::kWords], const
     }
   } else {
     Io<BF16>::load_elems(w, row, t);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_tile(typename Io<BF16>::T* row, int64_t t, const float (&y)[Io<BF16>::kTok],
+                                           bool vec) {
+  uint32_t w[kWords];
+  Io<BF16>::pack(w, y);
+  if (vec) {
+    uint4* p = reinterpret_cast<uint4*>(row + t);
+#pragma unroll
+    for (int i = 0; i < kWords / 4; ++i) p[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  } else {
+    Io<BF16>::store_elems(row, t, w);
   }
 }
 
@@ -171,6 +186,7 @@ template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
 struct Lane {
   using IO = Io<IO_BF16>;
   using T = typename IO::T;
+  static constexpr int kTok = IO::kTok;
   const T* u;
   const T* delta;
   const T* z;     // nullable
@@ -191,86 +207,129 @@ struct Lane {
     return SOFTPLUS ? softplus_f32(x) : x;
   }
 
+  // The staged B/C of token t (wave-uniform: scalar loads into SGPRs).
+  struct BC {
+    float v[kBC];
+  };
+  template <int MODE>
+  __device__ __forceinline__ void load_bc(BC& r, int64_t t) const {
+    const float* p = bc + t * kBC;
+    constexpr int kCount = MODE == kAggregate ? kDState : kBC;  // the aggregate needs no C
+#pragma unroll
+    for (int i = 0; i < kCount; ++i) r.v[i] = p[i];
+  }
+
   // Advances the state by one token; returns y (before the gate) for the output
   // modes, nothing useful for kAggregate.
   template <int MODE>
-  __device__ __forceinline__ float token(float uu, float draw, int64_t t) {
-    const float* bct = bc + t * kBC;
+  __device__ __forceinline__ float token(float uu, float draw, const BC& bct) {
     const float dt = step_size(draw);
     const float dtu = dt * uu;
     if (MODE == kAggregate) {
       sum_dt += dt;
 #pragma unroll
-      for (int n = 0; n < kDState; ++n) h[n] = fmaf(exp2_hw(dt * A2[n]), h[n], dtu * bct[n]);
+      for (int n = 0; n < kDState; ++n) h[n] = fmaf(exp2_hw(dt * A2[n]), h[n], dtu * bct.v[n]);
       return 0.0f;
     }
     float s = 0.0f;
 #pragma unroll
     for (int n = 0; n < kDState; ++n) {
-      h[n] = fmaf(exp2_hw(dt * A2[n]), h[n], dtu * bct[n]);
-      s = fmaf(bct[kDState + n], h[n], s);
+      h[n] = fmaf(exp2_hw(dt * A2[n]), h[n], dtu * bct.v[n]);
+      s = fmaf(bct.v[kDState + n], h[n], s);
     }
     return fmaf(Dd, uu, s);
   }
 
   __device__ __forceinline__ float gate(float yv, float zv) const { return HAS_Z ? yv * silu_f32(zv) : yv; }
 
-  // Tokens [ta, tb) in scan order (descending when REV).  ta/tb are multiples of
-  // kTile except at the end of the sequence.
+  // Tokens [ta, tb) in scan order (descending when REV).  ta is a multiple of
+  // kTok; tb too unless it is the end of the sequence, so only the top tile can be
+  // partial.  Full tiles are software-pipelined: the next tile's u and delta are
+  // loaded while the current one is scanned.
   template <bool REV, int MODE>
   __device__ void scan(int64_t ta, int64_t tb) {
     if (tb <= ta) return;
-    const int64_t k_first = ta / kTile, k_last = (tb - 1) / kTile;
-    for (int64_t kk = 0; kk <= k_last - k_first; ++kk) {
-      const int64_t k = REV ? k_last - kk : k_first + kk;
-      const int64_t tlo = max64(ta, k * kTile), thi = min64(tb, (k + 1) * kTile);
-      if (thi - tlo == kTile) {
-        full_tile<REV, MODE>(tlo);
-      } else {
-        for (int64_t i = 0; i < thi - tlo; ++i) partial_token<MODE>(REV ? thi - 1 - i : tlo + i);
-      }
+    const int64_t tfull = ta + (tb - ta) / kTok * kTok;
+    if (REV) {
+      for (int64_t t = tb - 1; t >= tfull; --t) partial_token<MODE>(t);
+      full_tiles<REV, MODE>(ta, tfull);
+    } else {
+      full_tiles<REV, MODE>(ta, tfull);
+      for (int64_t t = tfull; t < tb; ++t) partial_token<MODE>(t);
     }
   }
 
   template <bool REV, int MODE>
-  __device__ __forceinline__ void full_tile(int64_t t) {
-    constexpr bool kNeedZ = HAS_Z && (MODE == kStore || MODE == kMeet);
-    uint32_t wu[IO::kWords], wd[IO::kWords], wz[IO::kWords];
-    load_tile<IO_BF16>(wu, u, t, vec);
-    load_tile<IO_BF16>(wd, delta, t, vec);
-    if (kNeedZ) {
-      load_tile<IO_BF16>(wz, z, t, vec);
-    } else {
-#pragma unroll
-      for (int i = 0; i < IO::kWords; ++i) wz[i] = 0;
-    }
-    float yt[kTile];
-#pragma unroll
-    for (int jj = 0; jj < kTile; ++jj) {
-      const int j = REV ? kTile - 1 - jj : jj;
-      float yv = token<MODE>(IO::get(wu, j), IO::get(wd, j), t + j);
-      // materialise this token's readout now: otherwise it is sunk towards the
-      // tile's store and all 16 tokens' states stay live
-      if (MODE != kAggregate) asm volatile("" : "+v"(yv));
-      if (MODE == kStore) {
-        yt[j] = gate(yv, IO::get(wz, j));
-      } else if (MODE == kPark) {
-        part[(t + j - t0) * kLanes + lane] = yv;
-      } else if (MODE == kMeet) {
-        yt[j] = gate(yv + part[(t + j - t0) * kLanes + lane], IO::get(wz, j));
+  __device__ __forceinline__ void full_tiles(int64_t ta, int64_t tb) {
+    const int64_t ntiles = (tb - ta) / kTok;
+    if (ntiles <= 0) return;
+    uint32_t cu[kWords], cd[kWords], nu[kWords], nd[kWords];
+    int64_t t = REV ? tb - kTok : ta;
+    load_tile<IO_BF16>(cu, u, t, vec);
+    load_tile<IO_BF16>(cd, delta, t, vec);
+    for (int64_t i = 0; i < ntiles; ++i) {
+      const int64_t tn = REV ? t - kTok : t + kTok;
+      if (i + 1 < ntiles) {
+        load_tile<IO_BF16>(nu, u, tn, vec);
+        load_tile<IO_BF16>(nd, delta, tn, vec);
       }
+      tile<REV, MODE>(t, cu, cd);
+#pragma unroll
+      for (int w = 0; w < kWords; ++w) {
+        cu[w] = nu[w];
+        cd[w] = nd[w];
+      }
+      t = tn;
+    }
+  }
+
+  template <bool REV, int MODE>
+  __device__ __forceinline__ void tile(int64_t t, const uint32_t (&wu)[kWords], const uint32_t (&wd)[kWords]) {
+    constexpr bool kOut = (MODE == kStore || MODE == kMeet);
+    uint32_t wz[kWords];
+    // z is needed only for the gate at the end of the tile: its load latency hides
+    // behind the tile's tokens
+    if (kOut && HAS_Z) load_tile<IO_BF16>(wz, z, t, vec);
+    float yt[kTok];
+    BC cur, nxt;
+    load_bc<MODE>(cur, t + (REV ? kTok - 1 : 0));
+#pragma unroll
+    for (int jj = 0; jj < kTok; ++jj) {
+      const int j = REV ? kTok - 1 - jj : jj;
+      // prefetch the next token's B/C: its scalar-load latency hides behind this token
+      if (jj + 1 < kTok) load_bc<MODE>(nxt, t + (REV ? j - 1 : j + 1));
+      float yv = token<MODE>(IO::get(wu, j), IO::get(wd, j), cur);
+      // materialise this token's readout now: otherwise it is sunk towards the
+      // tile's store and all tokens' states stay live
+      if (MODE != kAggregate) asm volatile("" : "+v"(yv));
+      if (MODE == kPark) {
+        part[(t + j - t0) * kLanes + lane] = yv;
+      } else if (kOut) {
+        yt[j] = yv;
+      }
+      cur = nxt;
       // keep each token's work together: the 16 state chains of one token give
       // enough independent instructions, and hoisting later tokens' exponentials
       // ahead only raises register pressure
       __builtin_amdgcn_sched_barrier(0);
     }
-    if ((MODE == kStore || MODE == kMeet) && active) IO::store_tile(y, t, yt, vec);
+    if (kOut) {
+#pragma unroll
+      for (int j = 0; j < kTok; ++j) {
+        float v = yt[j];
+        if (MODE == kMeet) v += part[(t + j - t0) * kLanes + lane];
+        yt[j] = gate(v, HAS_Z ? IO::get(wz, j) : 0.0f);
+      }
+      if (active) store_tile<IO_BF16>(y, t, yt, vec);
+    }
   }
 
   template <int MODE>
   __device__ __forceinline__ void partial_token(int64_t t) {
     const float uu = IO::load(u, t);
-    const float yv = token<MODE>(uu, IO::load(delta, t), t);
+    BC cur;
+    load_bc<MODE>(cur, t);
+    const float yv = token<MODE>(uu, IO::load(delta, t), cur);
     if (MODE == kPark) {
       part[(t - t0) * kLanes + lane] = yv;
     } else if (MODE == kStore || MODE == kMeet) {
@@ -477,7 +536,7 @@ __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_
   load_entry(L, a, dir, s.b, s.seg, s.g, nseg, hin);
   const int64_t t0 = s.seg * seg_len;
   const int64_t t1 = min64(a.len, t0 + seg_len);
-  const int64_t mid = t0 + ((t1 - t0) / 2) / kTile * kTile;
+  const int64_t mid = t0 + ((t1 - t0) / 2) / kTile * kTile;  // a multiple of both tile sizes
   L.part = (lds_float*)part;
   L.t0 = t0;
   if (dir == 0) {
@@ -496,7 +555,10 @@ __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
-hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream) {
+hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
+  auto mark = [&](int i) {
+    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
+  };
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const int64_t nblocks = a.batch * p.nseg * ngroups;
   const size_t esz = IO_BF16 ? 2 : 4;
@@ -507,18 +569,23 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   float* hin = p.nseg > 1 ? agg + p.agg_floats : nullptr;
 
   const int64_t bc_blocks = int64_t(a.ndir) * a.batch * ((a.len + 63) / 64);
+  mark(0);
   if (a.bc_bf16) {
     hipLaunchKernelGGL(stage_bc_kernel<true>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, a, bc);
   } else {
     hipLaunchKernelGGL(stage_bc_kernel<false>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, a, bc);
   }
+  mark(1);
   if (p.nseg > 1) {
     hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS>), dim3(unsigned(nblocks), unsigned(a.ndir)),
                        dim3(kLanes), 0, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), agg, int(vec));
+    mark(2);
     const int64_t threads = int64_t(a.ndir) * a.batch * kDState * a.dim;
     hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, a, p.nseg,
                        static_cast<const float*>(agg), hin);
   }
+  if (p.nseg <= 1) mark(2);
+  mark(3);
   if (a.ndir == 1) {
     hipLaunchKernelGGL((scan_output_dir_kernel<IO_BF16, SOFTPLUS, HAS_Z>), dim3(unsigned(nblocks)), dim3(kLanes), 0,
                        stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), static_cast<const float*>(hin),
@@ -529,19 +596,33 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
                        dim3(2 * kLanes), lds, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc),
                        static_cast<const float*>(hin), int(vec));
   }
+  mark(4);
   return hipGetLastError();
 }
 
 template <bool IO_BF16>
-hipError_t launch_io(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream) {
+hipError_t launch_io(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
   if (a.softplus) {
-    return a.z ? launch_typed<IO_BF16, true, true>(a, p, w, stream) : launch_typed<IO_BF16, true, false>(a, p, w, stream);
+    return a.z ? launch_typed<IO_BF16, true, true>(a, p, w, stream, ev) : launch_typed<IO_BF16, true, false>(a, p, w, stream, ev);
   }
-  return a.z ? launch_typed<IO_BF16, false, true>(a, p, w, stream) : launch_typed<IO_BF16, false, false>(a, p, w, stream);
+  return a.z ? launch_typed<IO_BF16, false, true>(a, p, w, stream, ev) : launch_typed<IO_BF16, false, false>(a, p, w, stream, ev);
 }
 
 }  // namespace
 
+// Resident wave slots of the scan kernels on MI355X: 256 CUs x 4 SIMDs x 3 waves
+// (the scan kernels are held to <= 168 VGPRs).
+constexpr int64_t kWaveSlots = 256 * 4 * 3;
+// Bidirectional segments: the LDS meeting buffer (seg_len x 64 lanes x 4 B) must
+// leave room for eight two-wave blocks per CU.
+constexpr int64_t kBidirSegment = 64;
+
+// Splitting along the sequence.  Sequences up to kShortMax tokens are scanned whole.
+// Longer ones are cut into equal segments (multiples of kTile tokens) so that the
+// output step has about two rounds of resident waves: enough waves to cover load
+// latency and even out per-wave speed, without the long carry chain and large
+// aggregate buffers of many short segments (measured on the long-sequence and
+// Mamba-YOLO workloads).
 Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   Plan p{};
   const int64_t ngroups = (dim + kLanes - 1) / kLanes;
@@ -549,20 +630,19 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   p.seg_len = std::max<int64_t>(len, 1);
   p.nseg = 1;
   if (len > kShortMax) {
-    // Aim for about 8 wavefronts per SIMD (256 CUs x 4 SIMDs) over the output step.
-    const int64_t target_waves = 8192;
-    const int64_t waves_per_seg = groups * ndir;
-    int64_t nseg = std::max<int64_t>(2, (target_waves + waves_per_seg - 1) / waves_per_seg);
-    int64_t seg_len = (len + nseg - 1) / nseg;
-    seg_len = std::max<int64_t>(kSegAlign, (seg_len + kSegAlign - 1) / kSegAlign * kSegAlign);
-    if (ndir == 2) seg_len = std::min<int64_t>(seg_len, kMaxBidirSegment);
-    nseg = (len + seg_len - 1) / seg_len;
-    while (nseg > 1 && batch * nseg * ngroups > (int64_t(1) << 30)) {  // keep the block count within a 1-D grid
-      seg_len *= 2;
-      nseg = (len + seg_len - 1) / seg_len;
+    int64_t seg_len;
+    if (ndir == 2) {
+      seg_len = kBidirSegment;
+    } else {
+      const int64_t target_segs = std::max<int64_t>(2, 2 * kWaveSlots / groups);
+      seg_len = (len + target_segs - 1) / target_segs;
+      seg_len = std::max<int64_t>(kSegAlign, (seg_len + kTile - 1) / kTile * kTile);
     }
+    // keep the block count within a 1-D grid
+    while ((len + seg_len - 1) / seg_len > 1 && batch * ((len + seg_len - 1) / seg_len) * ngroups > (int64_t(1) << 30))
+      seg_len *= 2;
     p.seg_len = seg_len;
-    p.nseg = nseg;
+    p.nseg = (len + seg_len - 1) / seg_len;
   }
   p.bc_floats = size_t(ndir) * batch * len * kBC;
   // keep the sections 256-byte aligned
@@ -575,8 +655,8 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   return p;
 }
 
-hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* ws, hipStream_t stream) {
-  return a.io_bf16 ? launch_io<true>(a, p, ws, stream) : launch_io<false>(a, p, ws, stream);
+hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* ws, hipStream_t stream, hipEvent_t const* events) {
+  return a.io_bf16 ? launch_io<true>(a, p, ws, stream, events) : launch_io<false>(a, p, ws, stream, events);
 }
 
 }  // namespace sscan

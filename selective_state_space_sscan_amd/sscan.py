@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libsscan.so")
 SSCAN_F32 = 0
 SSCAN_BF16 = 1
 DSTATE = 16
+PROFILE_EVENTS = 5  # step boundaries: start, staged B/C, aggregates, carry, output
+PROFILE_STEPS = ("stage_bc", "aggregate", "carry", "output")
 
 _DT_CODE = {torch.float32: SSCAN_F32, torch.bfloat16: SSCAN_BF16}
 
@@ -52,6 +54,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_fwd.restype = I
     lib.sscan_bidir.argtypes = [V, V, V, DP, DP, I, I64, I64, I64, I64, V, I, I, V, SZ]
     lib.sscan_bidir.restype = I
+    lib.sscan_fwd_profiled.argtypes = lib.sscan_fwd.argtypes + [V]
+    lib.sscan_fwd_profiled.restype = I
+    lib.sscan_bidir_profiled.argtypes = lib.sscan_bidir.argtypes + [V]
+    lib.sscan_bidir_profiled.restype = I
     lib.sscan_validate_fwd.argtypes = [V, V, V, I, V, V, V, V, V, V, I64, I64, I64, I64, I, I, I, V, SZ]
     lib.sscan_validate_fwd.restype = I
     lib.sscan_validate_bidir.argtypes = [V, V, V, DP, DP, I, I64, I64, I64, I64, I, I, V, SZ]
@@ -65,6 +71,51 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     if path is None:
         _lib = lib
     return lib
+
+
+class HipEvents:
+    """PROFILE_EVENTS timing events of the HIP runtime the library runs on, for the
+    profiled entry points (one set per call in flight)."""
+
+    _hip = None
+
+    def __init__(self):
+        if HipEvents._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime already mapped by torch and libsscan
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvents._hip = hip
+        self._ev = (ctypes.c_void_p * PROFILE_EVENTS)()
+        for i in range(PROFILE_EVENTS):
+            h = ctypes.c_void_p()
+            if HipEvents._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self._ev[i] = h
+
+    @property
+    def handles(self):
+        return self._ev
+
+    def step_ms(self):
+        """Milliseconds of each step (dict keyed by PROFILE_STEPS); waits for the last event."""
+        hip = HipEvents._hip
+        hip.hipEventSynchronize(self._ev[PROFILE_EVENTS - 1])
+        out = {}
+        for i, name in enumerate(PROFILE_STEPS):
+            ms = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(ms), self._ev[i], self._ev[i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out[name] = float(ms.value)
+        return out
+
+    def __del__(self):
+        hip = HipEvents._hip
+        if hip is not None:
+            for h in self._ev:
+                if h:
+                    hip.hipEventDestroy(h)
 
 
 def strerror(status: int) -> str:
@@ -108,10 +159,12 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, reverse: bool = False,
-        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+        events: Optional[HipEvents] = None) -> torch.Tensor:
     """One-direction scan (``sscan_fwd``).  u, delta, z: [batch, dim, len] f32/bf16;
     B, C: [batch, 16, len] f32/bf16; A: [dim, 16] f32; D, delta_bias: [dim] f32.
-    Returns the gated output, same dtype as u, enqueued on the current stream."""
+    Returns the gated output, same dtype as u, enqueued on the current stream.
+    With ``events`` the profiled entry point also records the step boundaries."""
     lib = load_library()
     dev = u.device
     if dev.type != "cuda":
@@ -133,9 +186,13 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = Tru
     if u.numel() == 0:
         return out
     ws, ws_bytes = _workspace(workspace_bytes(b, d, L, DSTATE, False), dev, workspace)
-    st = lib.sscan_fwd(_ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C),
-                       _ptr(D), _ptr(z), _ptr(out), b, d, L, DSTATE, int(bool(reverse)), _stream(dev),
-                       _DT_CODE[u.dtype], _DT_CODE[B.dtype], _ptr(ws), ws_bytes)
+    args = [_ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(out), b, d, L, DSTATE, int(bool(reverse)), _stream(dev), _DT_CODE[u.dtype], _DT_CODE[B.dtype],
+            _ptr(ws), ws_bytes]
+    if events is None:
+        st = lib.sscan_fwd(*args)
+    else:
+        st = lib.sscan_fwd_profiled(*args, ctypes.cast(events.handles, ctypes.c_void_p))
     if st != 0:
         raise SScanError(st, "sscan_fwd")
     return out
@@ -155,7 +212,7 @@ def _dir(p: dict, name: str, dev, u, bdtype):
 
 
 def bidir(u, z, fwd: dict, rev: dict, softplus: bool = True, out: Optional[torch.Tensor] = None,
-          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+          workspace: Optional[torch.Tensor] = None, events: Optional[HipEvents] = None) -> torch.Tensor:
     """Bidirectional scan (``sscan_bidir``): ``fwd`` and ``rev`` are dicts with
     delta, A, B, C and optional D, delta_bias.  Returns (y_fwd + y_rev) * silu(z)."""
     lib = load_library()
@@ -175,20 +232,23 @@ def bidir(u, z, fwd: dict, rev: dict, softplus: bool = True, out: Optional[torch
     if u.numel() == 0:
         return out
     ws, ws_bytes = _workspace(workspace_bytes(b, d, L, DSTATE, True), dev, workspace)
-    st = lib.sscan_bidir(_ptr(u), _ptr(z), _ptr(out), ctypes.byref(pf), ctypes.byref(pr), int(bool(softplus)),
-                         b, d, L, DSTATE, _stream(dev), _DT_CODE[u.dtype], _DT_CODE[fwd["B"].dtype], _ptr(ws),
-                         ws_bytes)
+    args = [_ptr(u), _ptr(z), _ptr(out), ctypes.byref(pf), ctypes.byref(pr), int(bool(softplus)), b, d, L, DSTATE,
+            _stream(dev), _DT_CODE[u.dtype], _DT_CODE[fwd["B"].dtype], _ptr(ws), ws_bytes]
+    if events is None:
+        st = lib.sscan_bidir(*args)
+    else:
+        st = lib.sscan_bidir_profiled(*args, ctypes.cast(events.handles, ctypes.c_void_p))
     if st != 0:
         raise SScanError(st, "sscan_bidir")
     return out
 
 
-def run_inputs(x, softplus: bool = True, out=None, workspace=None) -> torch.Tensor:
+def run_inputs(x, softplus: bool = True, out=None, workspace=None, events: Optional[HipEvents] = None) -> torch.Tensor:
     """Runs the scan on a ``ScanInputs`` already on the device (one or two directions)."""
     if len(x.dirs) == 1:
         p = x.dirs[0]
         return fwd(x.u, x.delta, p.A, p.B, p.C, p.D, x.z, p.delta_bias, softplus=softplus, out=out,
-                   workspace=workspace)
+                   workspace=workspace, events=events)
     f, r = x.dirs
     mk = lambda p: dict(delta=x.delta, delta_bias=p.delta_bias, A=p.A, B=p.B, C=p.C, D=p.D)
-    return bidir(x.u, x.z, mk(f), mk(r), softplus=softplus, out=out, workspace=workspace)
+    return bidir(x.u, x.z, mk(f), mk(r), softplus=softplus, out=out, workspace=workspace, events=events)

@@ -160,3 +160,24 @@ def test_empty_input_returns_empty():
     B = torch.randn(2, 16, 5, device=DEV)
     y = sscan.fwd(u, u, A, B, B)
     assert y.shape == (2, 0, 5)
+
+
+def test_step_size_softplus_accuracy():
+    """With len 1, B = C = 1/4 (sum_n C_n B_n = 1), no D and no gate, the output is
+    the step size softplus(delta + bias) itself, so this pins the kernel's softplus
+    (exp and log included) elementwise, including the small steps (down to about
+    1e-13) that the long-memory workloads use."""
+    d = 4096
+    x = np.concatenate([np.linspace(-30.0, 30.0, d - 64), [0.0, 1e-7, -1e-7, 20.0, -20.0] + [-9.2] * 59])
+    u = torch.ones(1, d, 1)
+    delta = torch.tensor(x, dtype=torch.float32).view(1, d, 1)
+    A = -torch.ones(d, 16)
+    B = torch.full((1, 16, 1), 0.25)
+    dev = lambda t: t.to(DEV).contiguous()
+    y = sscan.fwd(dev(u), dev(delta), dev(A), dev(B), dev(B))
+    torch.cuda.synchronize()
+    got = I.f64(y.cpu()).ravel()
+    ref = oracle.sscan_fwd(I.f64(u), I.f64(delta), I.f64(A), I.f64(B), I.f64(B)).ravel()
+    rel = np.abs(got - ref) / np.abs(ref)
+    print(f"softplus max rel err {rel.max():.3e} at x={x[np.argmax(rel)]:.4g}", flush=True)
+    assert rel.max() <= 2e-6
