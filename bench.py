@@ -7,6 +7,17 @@ resident in HBM).  One step = one sscan_fwd call (all its kernels).  Prints ONE
 JSON line on stdout.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+                 [--copy-calibration]
+
+Timing: K plain calls between two HIP events give ms_per_step; K more calls of the
+profiled entry point (events recorded between the call's kernels on the same
+stream) give each kernel's average duration, and the dominant kernel's roofline.
+--copy-calibration ends with a plain streaming kernel (negation of 512 MiB: 512 MiB
+read, 512 MiB written), the known-size
+reference that scales the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc
+run of this command (selective_state_space_sscan_amd/profiling.py turns such runs
+into profiles/traffic_<workload>.json, which fills "traffic" while the kernel
+source is unchanged).
 """
 from __future__ import annotations
 
@@ -101,6 +112,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long-seq-fwd")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="finish with a 512 MiB negation kernel (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         sys.exit("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -129,25 +142,36 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    # per-kernel timing: the profiled entry point records HIP events between the
-    # call's kernels on the same stream (one event set per step)
-    evsets = [sscan.HipEvents() for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
-    for k in range(args.steps):
-        step(evsets[k])
+    for _ in range(args.steps):
+        step()
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / args.steps
     value = cfg.elems / (ms * 1e-3) / 1e6
+    # per-kernel timing: the profiled entry point records HIP events between the
+    # call's kernels on the same stream (one event set per call)
+    evsets = [sscan.HipEvents() for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evsets[k])
+    torch.cuda.synchronize()
     per_kernel = {name: [] for name in sscan.PROFILE_STEPS}
     for ev in evsets:
         for name, v in ev.step_ms().items():
             per_kernel[name].append(v)
     kernel_ms = {name: sum(v) / len(v) for name, v in per_kernel.items()}
     dominant = max(kernel_ms, key=kernel_ms.get)
+    if args.copy_calibration:
+        # a plain streaming kernel of known traffic: reads 512 MiB, writes 512 MiB
+        src = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     nbytes = alg_bytes(cfg)
     # algorithmic work of the output kernel: the full recurrence and readout of
@@ -161,7 +185,7 @@ def main():
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded numpy PCG64, shapes of the pages' workloads)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "dim": cfg.dim, "len": cfg.len, "dstate": cfg.dstate,
                    "directions": cfg.ndir, "io_dtype": cfg.io_dtype, "bc_dtype": cfg.bc_dtype},
-        "roofline": {"bound": "alu", "kernel": "scan_output", "achieved": achieved_tflops, "peak": ALU_PEAK_TFLOPS,
+        "roofline": {"bound": "alu", "kernel": dominant, "achieved": achieved_tflops, "peak": ALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / ALU_PEAK_TFLOPS, "traffic": None},
         "kernels_ms": kernel_ms,
         "step_alu": {"achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
@@ -172,6 +196,11 @@ def main():
     }
     if dominant != "output":
         out["roofline"]["kernel"] = dominant
+    from selective_state_space_sscan_amd import profiling
+
+    traffic = profiling.load_traffic(os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json"))
+    if traffic and dominant in traffic["per_launch"]:
+        out["roofline"]["traffic"] = traffic["per_launch"][dominant]["bytes"]
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x, y, cfg)
     print(json.dumps(out), flush=True)

@@ -460,41 +460,80 @@ __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_aggregate_kernel(
   agg[agg_index(dir, s.b, s.seg, kDState, d, a.batch, a.dim, nseg)] = L.sum_dt;
 }
 
-// Step 2: one thread per (direction, batch, state, channel) chains the segment
-// aggregates in scan order and writes the state entering every segment.  The
-// aggregate loads do not depend on the chain, so they are issued in batches.
-__global__ __launch_bounds__(256) void scan_carry_kernel(ScanArgs a, int64_t nseg, const float* __restrict__ agg,
-                                                         float* __restrict__ hin) {
-  constexpr int kBatch = 32;
-  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = int64_t(a.ndir) * a.batch * kDState * a.dim;
-  if (idx >= total) return;
-  const int64_t d = idx % a.dim;
-  const int n = int((idx / a.dim) % kDState);
-  const int64_t rest = idx / (a.dim * kDState);
-  const int64_t b = rest % a.batch;
-  const int dir = int(rest / a.batch);
+// Step 2: the chain of segment aggregates in scan order,
+//   h_in[k+1] = exp(A sum_dt[k]) h_in[k] + H[k],   h_in[0] = 0,
+// for every (direction, batch, state, channel).  The combine is associative, so
+// each chain is split into kCarryParts runs of consecutive segments: each run is
+// first reduced on its own (its decay exponent is the sum of its sum_dt), the runs'
+// totals are chained through LDS, and each run is walked again from its entry
+// state writing h_in.  A block holds 64 channels (coalesced along d) x the parts.
+constexpr int kCarryParts = 16;
+
+__global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanArgs a, int64_t nseg,
+                                                                       const float* __restrict__ agg,
+                                                                       float* __restrict__ hin) {
+  __shared__ float sh_s[kCarryParts][kLanes];
+  __shared__ float sh_h[kCarryParts][kLanes];
+  const int lane = threadIdx.x % kLanes;
+  const int part = threadIdx.x / kLanes;
+  const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
+  int64_t r = blockIdx.x;
+  const int64_t g = r % ngroups;
+  r /= ngroups;
+  const int n = int(r % kDState);
+  r /= kDState;
+  const int64_t b = r % a.batch;
+  const int dir = int(r / a.batch);
   const int reverse = a.ndir == 2 ? dir : a.reverse;
+  const int64_t d_raw = g * kLanes + lane;
+  const bool active = d_raw < a.dim;
+  const int64_t d = active ? d_raw : a.dim - 1;
   const float* Adir = dir ? a.dir[1].A : a.dir[0].A;
   const float A2 = Adir[d * kDState + n] * kLog2e;
-  float h = 0.0f;
-  for (int64_t k0 = 0; k0 < nseg; k0 += kBatch) {
-    float H[kBatch], S[kBatch];
+  const int64_t chunk = (nseg + kCarryParts - 1) / kCarryParts;
+  const int64_t k0 = min64(nseg, part * chunk), k1 = min64(nseg, k0 + chunk);
+  auto seg_of = [&](int64_t k) { return reverse ? nseg - 1 - k : k; };
+  // the last segment in scan order has no aggregate (nothing follows it)
+  const int64_t kagg = min64(k1, nseg - 1);
+  // a run's aggregates are loaded kBatch at a time, all loads in flight together
+  // (they do not depend on the chain); runs of up to kBatch segments are loaded once
+  constexpr int kBatch = 32;
+  float hb[kBatch], sb[kBatch];
+  auto load_batch = [&](int64_t kb) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int64_t k = k0 + i;
-      const int64_t seg = reverse ? nseg - 1 - k : k;
-      const bool has = k + 1 < nseg;
-      H[i] = has ? agg[agg_index(dir, b, seg, n, d, a.batch, a.dim, nseg)] : 0.0f;
-      S[i] = has ? agg[agg_index(dir, b, seg, kDState, d, a.batch, a.dim, nseg)] : 0.0f;
+      const int64_t k = kb + i;
+      const bool has = k < kagg;
+      const int64_t seg = seg_of(has ? k : 0);  // a valid segment even when the run is empty
+      hb[i] = has ? agg[agg_index(dir, b, seg, n, d, a.batch, a.dim, nseg)] : 0.0f;
+      sb[i] = has ? agg[agg_index(dir, b, seg, kDState, d, a.batch, a.dim, nseg)] : 0.0f;
     }
+  };
+  float S = 0.0f, H = 0.0f;
+  for (int64_t kb = k0; kb < kagg; kb += kBatch) {
+    load_batch(kb);
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int64_t k = k0 + i;
-      if (k < nseg) {
-        const int64_t seg = reverse ? nseg - 1 - k : k;
-        hin[hin_index(dir, b, seg, n, d, a.batch, a.dim, nseg)] = h;
-        h = fmaf(exp2_hw(A2 * S[i]), h, H[i]);
+      if (kb + i < kagg) {
+        H = fmaf(exp2_hw(A2 * sb[i]), H, hb[i]);
+        S += sb[i];
+      }
+    }
+  }
+  sh_s[part][lane] = S;
+  sh_h[part][lane] = H;
+  __syncthreads();
+  float h = 0.0f;
+  for (int q = 0; q < part; ++q) h = fmaf(exp2_hw(A2 * sh_s[q][lane]), h, sh_h[q][lane]);
+  const bool reuse = kagg - k0 <= kBatch;  // the run's aggregates are still in registers
+  for (int64_t kb = k0; kb < k1; kb += kBatch) {
+    if (!reuse) load_batch(kb);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t k = kb + i;
+      if (k < k1) {
+        if (active) hin[hin_index(dir, b, seg_of(k), n, d, a.batch, a.dim, nseg)] = h;
+        if (k < kagg) h = fmaf(exp2_hw(A2 * sb[i]), h, hb[i]);
       }
     }
   }
@@ -580,9 +619,9 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
     hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS>), dim3(unsigned(nblocks), unsigned(a.ndir)),
                        dim3(kLanes), 0, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), agg, int(vec));
     mark(2);
-    const int64_t threads = int64_t(a.ndir) * a.batch * kDState * a.dim;
-    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, a, p.nseg,
-                       static_cast<const float*>(agg), hin);
+    const int64_t carry_blocks = int64_t(a.ndir) * a.batch * kDState * ngroups;
+    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), dim3(kLanes * kCarryParts), 0, stream, a,
+                       p.nseg, static_cast<const float*>(agg), hin);
   }
   if (p.nseg <= 1) mark(2);
   mark(3);

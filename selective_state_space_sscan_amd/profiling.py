@@ -1,0 +1,91 @@
+"""HBM traffic of the scan kernels from rocprofv3 counter collections.
+
+``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` report, per dispatch, the
+KiB the L2 read from / wrote to memory.  Both are scaled by what the same counter
+reads for a plain streaming kernel of known traffic (bench.py --copy-calibration
+negates 512 MiB: 512 MiB read, 512 MiB written): the factor is known bytes /
+counted bytes.  The summary is keyed by the
+SHA-256 of the kernel source, so a summary taken before the kernels changed is
+recognisably stale.
+
+  python -m selective_state_space_sscan_amd.profiling FETCH_DIR WRITE_DIR OUT.json
+
+FETCH_DIR / WRITE_DIR are the rocprofv3 output directories (containing
+*counter_collection.csv) of ``bench.py --copy-calibration`` runs.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(PKG, "csrc", "sscan_kernels.hip")
+COPY_BYTES = 512 << 20
+COPY_KERNEL = "neg_kernel"  # the calibration kernel (torch.neg), unique in the run
+KERNELS = {"stage_bc_kernel": "stage_bc", "scan_aggregate_kernel": "aggregate", "scan_carry_kernel": "carry",
+           "scan_output_dir_kernel": "output", "scan_output_bidir_kernel": "output"}
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def _per_dispatch(directory: str, counter: str):
+    """{step name or 'copy': mean counter value (KiB) per dispatch}."""
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    total = collections.defaultdict(float)
+    dispatches = collections.defaultdict(set)
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = "copy" if COPY_KERNEL in name else next((v for k, v in KERNELS.items() if k in name), None)
+            if key is None:
+                continue
+            total[key] += float(r["Counter_Value"])
+            dispatches[key].add((f, r["Dispatch_Id"]))
+    return {k: total[k] / len(dispatches[k]) for k in total}
+
+
+def summarize(fetch_dir: str, write_dir: str) -> dict:
+    fetch = _per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _per_dispatch(write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy"] * 1024.0)
+    steps = {}
+    for k in fetch:
+        if k == "copy":
+            continue
+        rd = fetch[k] * 1024.0 * f_scale
+        wr = write.get(k, 0.0) * 1024.0 * w_scale
+        steps[k] = {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
+    return {"kernel_source_sha256": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+            "copy_bytes": COPY_BYTES, "per_launch": steps}
+
+
+def load_traffic(path: str):
+    """The per-launch traffic summary if it matches the current kernel source, else None."""
+    if not os.path.exists(path):
+        return None
+    doc = json.load(open(path))
+    if doc.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return doc
+
+
+if __name__ == "__main__":
+    if len(sys.argv) != 4:
+        sys.exit(__doc__)
+    doc = summarize(sys.argv[1], sys.argv[2])
+    with open(sys.argv[3], "w") as fh:
+        json.dump(doc, fh, indent=1)
+    print(json.dumps(doc, indent=1))
