@@ -29,8 +29,13 @@ def _dt_numpy(delta, bias, softplus):
     return np.logaddexp(0.0, x) if softplus else x
 
 
-def brute_dir(u, delta, A, B, C, D=None, delta_bias=None, softplus=True, reverse=False):
-    """Ungated output of one direction (float64 numpy), O(b*d*L^2*N)."""
+def brute_dir(u, delta, A, B, C, D=None, delta_bias=None, softplus=True, reverse=False, h0=None):
+    """Ungated output of one direction (float64 numpy), O(b*d*L^2*N).
+
+    With an entry state h0 [b, d, N] (the state before the first scanned token),
+    every output also reads that state decayed over all tokens scanned so far:
+    y_t += sum_n C[n,t] exp(A_n E_t) h0_n, E_t = sum_{r<=t} dt_r forward,
+    sum_{r>=t} dt_r reverse."""
     u = np.asarray(u, np.float64)
     b, d, L = u.shape
     N = A.shape[1]
@@ -56,7 +61,28 @@ def brute_dir(u, delta, A, B, C, D=None, delta_bias=None, softplus=True, reverse
             K = np.einsum("nt,nts,ns->ts", C[bi], E, B[bi]) * dt[bi, di][None, :]
             K = np.where(mask, K, 0.0)
             y[bi, di] = K @ u[bi, di] + (0.0 if D is None else D[di]) * u[bi, di]
+            if h0 is not None:
+                E = St if not reverse else St[-1] - St + dt[bi, di]
+                y[bi, di] += np.einsum("nt,nt,n->t", C[bi], np.exp(A[di][:, None] * E[None, :]), h0[bi, di])
     return y
+
+
+def brute_last_state(u, delta, A, B, delta_bias=None, softplus=True, reverse=False, h0=None):
+    """State after the last scanned token, [b, d, N], as one weighted sum:
+    h_n = exp(A_n sum_all dt) h0_n + sum_s exp(A_n W_s) dt_s B[n,s] u_s with
+    W_s = sum of the step sizes scanned after token s (r > s forward, r < s reverse)."""
+    u = np.asarray(u, np.float64)
+    b, d, L = u.shape
+    N = A.shape[1]
+    dt = _dt_numpy(np.asarray(delta, np.float64), delta_bias, softplus)
+    total = dt.sum(-1)  # [b, d]
+    incl = np.cumsum(dt, -1)
+    W = (total[..., None] - incl) if not reverse else (incl - dt)
+    h = np.einsum("dn,bdns,bds,bns,bds->bdn", np.ones((d, N)), np.exp(A[None, :, :, None] * W[:, :, None, :]),
+                  dt, B, u)
+    if h0 is not None:
+        h = h + np.exp(A[None] * total[..., None]) * h0
+    return h
 
 
 def silu_numpy(x):

@@ -325,6 +325,42 @@ def test_p11_chunk_carry_invariance(oracle_lib, reverse):
     assert np.abs(reset - full).max() > 1e-3 * np.abs(full).max()
 
 
+# --- P12: entry state and final state (Mamba2 page, section 5.2: recurrent inference carries
+#          the fixed-size state from one call to the next; YOLO26 page section 5.1) -------------
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_p12_entry_and_last_state_match_materialised_form(oracle_lib, reverse):
+    """Outputs with an entry state h0 and the returned last state against the
+    weighted-sum forms of ``brute`` (no recurrence).  Catches h0 read in the wrong
+    layout ([b, d, N] with N fastest), decayed by the wrong prefix, or a last
+    state taken one token early."""
+    rng = np.random.default_rng(121)
+    b, d, L, N = 2, 3, 23, 16
+    u, z, p = _case(rng, b, d, L, N)
+    h0 = rng.normal(size=(b, d, N))
+    out, hl = _fwd(oracle_lib, u, p, z=z, reverse=reverse, h0=h0, return_last_state=True)
+    ref = brute.brute_dir(u, reverse=reverse, h0=h0, **p) * _silu_lib(z)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+    ref_h = brute.brute_last_state(u, p["delta"], p["A"], p["B"], p["delta_bias"], reverse=reverse, h0=h0)
+    np.testing.assert_allclose(hl, ref_h, rtol=1e-11, atol=1e-12 * np.abs(ref_h).max())
+
+
+def test_p12_len1_step_closed_form(oracle_lib):
+    """One token from state h0 (the single-step decode): h_n = exp(dt A_n) h0_n +
+    dt B_n u, out = (sum_n C_n h_n + D u) silu(z).  Catches A transposed, the
+    decay applied to the input term, or the old state read out."""
+    rng = np.random.default_rng(122)
+    b, d, N = 3, 4, 16
+    u, z, p = _case(rng, b, d, 1, N)
+    h0 = rng.normal(size=(b, d, N))
+    out, hl = _fwd(oracle_lib, u, p, z=z, h0=h0, return_last_state=True)
+    dt = _softplus_lib(p["delta"][:, :, 0] + p["delta_bias"][None, :])  # [b, d]
+    h = np.exp(dt[..., None] * p["A"][None]) * h0 + dt[..., None] * p["B"][:, None, :, 0] * u[:, :, :1]
+    ref = (np.einsum("bn,bdn->bd", p["C"][:, :, 0], h) + p["D"][None] * u[:, :, 0]) * _silu_lib(z[:, :, 0])
+    np.testing.assert_allclose(hl, h, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(out[:, :, 0], ref, rtol=1e-13, atol=1e-14)
+
+
 # --- scalar helpers and special values ------------------------------------------------------------
 
 @pytest.mark.parametrize("x", [-700.0, -60.0, -20.0, -9.2, -3.0, -1e-8, 0.0, 1e-8, 2.5, 20.0, 60.0, 700.0])
