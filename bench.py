@@ -9,9 +9,12 @@ JSON line on stdout.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
                  [--copy-calibration]
 
-Timing: K plain calls between two HIP events give ms_per_step; K more calls of the
-profiled entry point (events recorded between the call's kernels on the same
-stream) give each kernel's average duration, and the dominant kernel's roofline.
+Timing: K plain calls between two HIP events give ms_per_step (for a workload
+whose data fits the 256 MB Infinity Cache, rotating over copies of the inputs so
+the number is a cold-HBM one; the warm figure is reported beside it); K more calls
+of the profiled entry point (events recorded between the call's kernels on the
+same stream) give each kernel's average duration, the dominant kernel's roofline,
+and the median / p10 / p90 of single calls.
 --copy-calibration ends with a plain streaming kernel (negation of 512 MiB: 512 MiB
 read, 512 MiB written), the known-size
 reference that scales the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc
@@ -47,6 +50,35 @@ def alg_bytes(cfg) -> int:
     bc = 2 if cfg.bc_dtype == "bf16" else 4
     per_dir = 2 * cfg.batch * cfg.dstate * cfg.len * bc + cfg.dim * (cfg.dstate + 2) * 4
     return 4 * cfg.elems * io + cfg.ndir * per_dir
+
+
+COLD_BYTES = 1 << 30            # rotate inputs until the touched footprint exceeds this (> 256 MB MALL)
+
+
+def percentile(v, q):
+    v = sorted(v)
+    i = (len(v) - 1) * q / 100.0
+    lo = int(i)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (i - lo)
+
+
+def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Achievable HBM bandwidth: a plain device-to-device copy of 1 GiB
+    (read + written bytes / time)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(x, y_gpu, cfg, target_s: float = 8.0):
@@ -92,6 +124,11 @@ def cpu_baseline(x, y_gpu, cfg, target_s: float = 8.0):
         refs = list(ex.map(lambda r: run_rows([r])[0], sample))
     dt = time.perf_counter() - t0
     elems = n_rows * cfg.len
+    # the same oracle on one core, on a smaller sample of the same rows
+    n1 = max(1, min(n_rows, int(target_s / 4 / max(t_cal, 1e-6))))
+    t1 = time.perf_counter()
+    run_rows(sample[:n1])
+    dt1 = time.perf_counter() - t1
     # parity of the GPU output on the same sampled rows (the oracle output is at hand)
     got = np.concatenate([I.f64(y_gpu[b:b + 1, d:d + 1].cpu()) for b, d in sample[:64]], 1)
     ref = np.concatenate(refs[:64], 1)
@@ -101,8 +138,103 @@ def cpu_baseline(x, y_gpu, cfg, target_s: float = 8.0):
         "value": elems / dt / 1e6, "unit": "Melem/s", "cores": cores, "kind": "oracle",
         "sample": f"{n_rows} whole rows of {cfg.len} tokens ({elems} elements, {cfg.ndir} direction(s)) "
                   f"of the same seeded inputs, fp64 sequential per row, {cores} threads, {dt:.1f} s",
-        "seconds": dt, "gpu_parity_on_sample": {"floored_max_err": err, "rows_compared": min(64, n_rows)},
+        "seconds": dt, "cpu_model": cpu_model(),
+        "one_core": {"value": n1 * cfg.len / dt1 / 1e6, "unit": "Melem/s", "rows": n1, "seconds": dt1},
+        "gpu_parity_on_sample": {"floored_max_err": err, "rows_compared": min(64, n_rows)},
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Single-token decode (sscan_step): batch streams of the long-sequence workload's
+# 1536 channels, bf16 u/delta/z/y, f32 B/C and f32 state.
+DECODE = dict(name="decode-step", batch=256, dim=1536, io_dtype="bf16", bc_dtype="f32")
+
+
+def decode_alg_bytes(b, d, io, bc) -> int:
+    """Algorithmic bytes of one step: the state read and written (2 x 64 B per
+    channel), u/delta/z read and y written, A/D/bias per channel, B/C per batch row."""
+    return b * d * (2 * 64 + 4 * io) + d * (64 + 8) + b * 2 * 16 * bc
+
+
+def bench_decode(args, torch, I, sscan):
+    import numpy as np
+
+    c = DECODE
+    b, d = c["batch"], c["dim"]
+    dev = torch.device("cuda:0")
+    x = I.make_inputs(b, d, 1, io_dtype=c["io_dtype"], bc_dtype=c["bc_dtype"], seed=9000, dt_range=(1e-4, 1e-2))
+    h0 = torch.from_numpy(np.random.default_rng(9001).normal(0.0, 1.0, (b, d, 16))).float()
+    xd = x.to(dev)
+    p = xd.dirs[0]
+    col = lambda t: t[..., 0].contiguous()
+    u, delta, z, B, C = col(xd.u), col(xd.delta), col(xd.z), col(p.B), col(p.C)
+    y = torch.empty_like(u)
+    io = 2 if c["io_dtype"] == "bf16" else 4
+    bc = 2 if c["bc_dtype"] == "bf16" else 4
+    nbytes = decode_alg_bytes(b, d, io, bc)
+    # cold: rotate over enough state buffers (with their own inputs) to exceed the cache
+    nsets = -(-COLD_BYTES // nbytes)
+    sets = [(h0.to(dev), u.clone(), delta.clone(), z.clone(), torch.empty_like(y)) for _ in range(nsets)]
+
+    def call(k):
+        st, uu, dd, zz, yy = sets[k % nsets]
+        sscan.step(st, uu, dd, p.A, B, C, p.D, zz, p.delta_bias, out=yy)
+
+    for k in range(max(args.warmup, nsets)):
+        call(k)
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        call(k)
+    ev[1].record(stream)
+    # warm: the same buffers every step
+    for _ in range(args.steps):
+        call(0)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    warm_ms = ev[1].elapsed_time(ev[2]) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    copy_gbs = copy_bandwidth(torch, dev)
+    out = {
+        "metric": METRIC, "value": b * d / (ms * 1e-3) / 1e6, "unit": "Melem/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": c["name"], "batch": b, "dim": d, "len": 1, "dstate": 16, "io_dtype": c["io_dtype"],
+                   "bc_dtype": c["bc_dtype"], "state_dtype": "f32"},
+        # one kernel per step: the events around K back-to-back launches time it
+        "roofline": {"bound": "hbm", "kernel": "step", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "cache": f"cold: rotating over {nsets} state buffers; warm (one buffer, {nbytes / 1e6:.1f} MB) "
+                 f"{warm_ms * 1e3:.2f} us = {nbytes / (warm_ms * 1e-3) / 1e9:.0f} GB/s",
+        "hbm": {"algorithmic_bytes_per_step": nbytes, "achievable_copy_GBs": copy_gbs},
+    }
+    if not args.no_cpu:
+        from oracle import oracle
+
+        x64 = I.as_f64_dict(x)
+        q = x64["dirs"][0]
+        cores = oracle.default_threads()
+        t0 = time.perf_counter()
+        oracle.sscan_fwd(x64["u"], x64["delta"], q["A"], q["B"], q["C"], q["D"], x64["z"], q["delta_bias"],
+                         h0=h0.double().numpy(), return_last_state=True, nthreads=cores)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": b * d / dt / 1e6, "unit": "Melem/s", "cores": cores, "kind": "oracle",
+                               "sample": f"the whole step ({b * d} channels, one token) from the same state, "
+                                         f"fp64, {cores} threads, {dt:.2f} s", "cpu_model": cpu_model()}
+    return out
 
 
 def main():
@@ -110,7 +242,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="long-seq-fwd")
+    ap.add_argument("--workload", default="long-seq-fwd",
+                    help="a scan workload of selective_state_space_sscan_amd.inputs.CONFIGS, or decode-step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with a 512 MiB negation kernel (counter calibration for rocprofv3 --pmc runs)")
@@ -125,6 +258,9 @@ def main():
     from selective_state_space_sscan_amd import sscan
 
     sscan.load_library()
+    if args.workload == DECODE["name"]:
+        print(json.dumps(bench_decode(args, torch, I, sscan)), flush=True)
+        return
     names = [c.name for c in I.CONFIGS]
     ci = names.index(args.workload)
     cfg = I.CONFIGS[ci]
@@ -159,11 +295,32 @@ def main():
         step(evsets[k])
     torch.cuda.synchronize()
     per_kernel = {name: [] for name in sscan.PROFILE_STEPS}
+    per_call = []
     for ev in evsets:
         for name, v in ev.step_ms().items():
             per_kernel[name].append(v)
+        per_call.append(ev.total_ms())
     kernel_ms = {name: sum(v) / len(v) for name, v in per_kernel.items()}
     dominant = max(kernel_ms, key=kernel_ms.get)
+    footprint = ws_bytes + sum(t.numel() * t.element_size() for t in xd.tensors()) + y.numel() * y.element_size()
+    warm = None
+    if footprint < COLD_BYTES:
+        # the call's data fits the 256 MB Infinity Cache: time it again rotating
+        # among enough copies of the inputs to exceed it (cold), keep the first as warm
+        sets = [(xd.clone(), torch.empty_like(y)) for _ in range(-(-COLD_BYTES // footprint))]
+        for xs, ys in sets:
+            sscan.run_inputs(xs, out=ys, workspace=ws)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(args.steps):
+            xs, ys = sets[k % len(sets)]
+            sscan.run_inputs(xs, out=ys, workspace=ws)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        warm, ms = ms, start.elapsed_time(stop) / args.steps
+        value = cfg.elems / (ms * 1e-3) / 1e6
+        del sets
+    copy_gbs = copy_bandwidth(torch, dev)
     if args.copy_calibration:
         # a plain streaming kernel of known traffic: reads 512 MiB, writes 512 MiB
         src = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
@@ -188,10 +345,16 @@ def main():
         "roofline": {"bound": "alu", "kernel": dominant, "achieved": achieved_tflops, "peak": ALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / ALU_PEAK_TFLOPS, "traffic": None},
         "kernels_ms": kernel_ms,
+        "call_ms": {"median": percentile(per_call, 50), "p10": percentile(per_call, 10),
+                    "p90": percentile(per_call, 90), "calls": len(per_call)},
+        "per_direction_Melem_s": value * cfg.ndir,
+        "cache": ("cold: footprint %.0f MB per call, above the 256 MB Infinity Cache" % (footprint / 1e6))
+        if warm is None else ("cold: rotating over copies of the inputs; warm (one set) %.4f ms" % warm),
         "step_alu": {"achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
                      "frac": flops / (ms * 1e-3) / 1e12 / ALU_PEAK_TFLOPS},
         "hbm": {"achieved_GBs": nbytes / (ms * 1e-3) / 1e9, "peak_GBs": HBM_PEAK_GBS,
-                "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes_per_step": nbytes},
+                "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes_per_step": nbytes,
+                "achievable_copy_GBs": copy_gbs},
         "wall_s_timed": wall,
     }
     if dominant != "output":

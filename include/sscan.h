@@ -63,7 +63,7 @@ enum sscan_status {
   SSCAN_ERR_ALIGN = -4,       /* a pointer is not aligned to its element size */
   SSCAN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than sscan_workspace_bytes */
   SSCAN_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
-  SSCAN_ERR_ALIAS = -7        /* y overlaps an input */
+  SSCAN_ERR_ALIAS = -7        /* an output overlaps an input, another output or the workspace */
 };
 
 enum sscan_dtype { SSCAN_F32 = 0, SSCAN_BF16 = 1 };
@@ -93,6 +93,43 @@ SSCAN_API int sscan_bidir(const void* u, const void* z, void* y,
                 const sscan_dir_params* fwd, const sscan_dir_params* rev, int softplus,
                 int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
                 int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+
+/* One direction with state I/O, for recurrent inference over a stream cut into
+ * pieces (Hand-written simplified Mamba2 page, section 5.2: the fixed-size state is
+ * all that carries from one step to the next; Mamba in the YOLO26 backbone page,
+ * section 5.1: segments hand their hidden state on).  The same as sscan_fwd, and
+ *   h0     [batch, dim, dstate] float32, optional: the state before the first scanned
+ *          token (NULL = 0); with reverse != 0 the first scanned token is t = len-1;
+ *   h_last [batch, dim, dstate] float32, optional: receives the state after the last
+ *          scanned token (t = len-1 forward, t = 0 reverse).  With len == 0 it
+ *          receives h0 (or zeros).
+ * Calling this on consecutive pieces of a sequence, each h_last passed as the next
+ * h0, gives the outputs of one call on the whole sequence (up to rounding).  Both
+ * pointers must be 16-byte aligned.  h_last may be the same pointer as h0 (the
+ * state is updated in place) but must not otherwise overlap h0, any input, y or
+ * the workspace; y must not overlap h0.  Workspace: sscan_workspace_bytes(..., 0). */
+SSCAN_API int sscan_fwd_state(const void* u, const void* delta, const float* delta_bias, int softplus,
+                    const float* A, const void* B, const void* C, const float* D,
+                    const void* z, void* y, const float* h0, float* h_last,
+                    int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                    int reverse, void* stream,
+                    int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+
+/* One token of the recurrence from a stored state (single-step decode, same
+ * passages as sscan_fwd_state): for every (b, d)
+ *   h[b,d,:] <- exp(dt A[d,:]) * h[b,d,:] + dt * B[b,:] * u[b,d]
+ *   y[b,d]    = (sum_n C[b,n] h[b,d,n] + D_d u[b,d]) * silu(z[b,d])
+ * with dt as in sscan_fwd.  Layouts: state [batch, dim, dstate] float32 (read and
+ * updated in place); u, delta, z, y [batch, dim] io_dtype; B, C [batch, dstate]
+ * bc_dtype; A [dim, dstate], D and delta_bias [dim] float32.  state and A must be
+ * 16-byte aligned, B and C aligned to four elements (16 bytes f32, 8 bytes bf16).
+ * Required: state, u, delta, A, B, C, y; optional: delta_bias, D, z.  No
+ * workspace.  state and y must not overlap each other or any input.  Equal to
+ * sscan_fwd_state with len = 1 and h0 = h_last = state. */
+SSCAN_API int sscan_step(float* state, const void* u, const void* delta, const float* delta_bias, int softplus,
+               const float* A, const void* B, const void* C, const float* D,
+               const void* z, void* y, int64_t batch, int64_t dim, int64_t dstate, void* stream,
+               int io_dtype, int bc_dtype);
 
 /* Profiling variants (for timing the internal steps of a call, not needed for
  * results): the same work as sscan_fwd / sscan_bidir, and on the same stream
@@ -129,6 +166,17 @@ SSCAN_API int sscan_validate_bidir(const void* u, const void* z, const void* y,
                          const sscan_dir_params* fwd, const sscan_dir_params* rev, int softplus,
                          int64_t batch, int64_t dim, int64_t len, int64_t dstate,
                          int io_dtype, int bc_dtype, const void* workspace, size_t workspace_bytes);
+
+SSCAN_API int sscan_validate_fwd_state(const void* u, const void* delta, const float* delta_bias, int softplus,
+                             const float* A, const void* B, const void* C, const float* D,
+                             const void* z, const void* y, const float* h0, const float* h_last,
+                             int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                             int reverse, int io_dtype, int bc_dtype,
+                             const void* workspace, size_t workspace_bytes);
+SSCAN_API int sscan_validate_step(const float* state, const void* u, const void* delta, const float* delta_bias,
+                        int softplus, const float* A, const void* B, const void* C, const float* D,
+                        const void* z, const void* y, int64_t batch, int64_t dim, int64_t dstate,
+                        int io_dtype, int bc_dtype);
 
 /* Bytes of device workspace a call with these sizes needs (0 if none); bidir != 0
  * for sscan_bidir.  Returns 0 for invalid sizes (the call itself reports them). */

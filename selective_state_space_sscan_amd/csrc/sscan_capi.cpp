@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 static_assert(SSCAN_PROFILE_EVENTS == sscan::kProfileEvents, "event count mismatch");
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -106,6 +106,32 @@ int validate(const void* u, const void* z, const void* y, const DirView* dirs, i
   return SSCAN_OK;
 }
 
+// Entry and final state of a single-direction call: 16-byte aligned [batch][dim][16]
+// fp32; h_last may be h0 itself but must not overlap anything else the call reads
+// or writes, and y must not overlap h0.
+int check_state(const float* h0, float* h_last, const void* u, const void* z, const void* y, const DirView& p,
+                int64_t batch, int64_t dim, int64_t len, int io_dtype, int bc_dtype, const void* workspace,
+                size_t workspace_bytes) {
+  if (!aligned(h0, 16) || !aligned(h_last, 16)) return SSCAN_ERR_ALIGN;
+  Sizes sz{};
+  const int st = check_sizes(batch, dim, len, sscan::kDState, io_dtype, bc_dtype, &sz);
+  if (st != SSCAN_OK) return st;
+  const size_t sbytes = size_t(batch) * size_t(dim) * sscan::kDState * 4;
+  const Range h0r = h0 ? range_of(h0, sbytes) : Range{0, 0};
+  const Range hlr = h_last ? range_of(h_last, sbytes) : Range{0, 0};
+  const size_t io = sz.io_elems * sz.io_esz, bcb = sz.bc_elems * sz.bc_esz, vec = size_t(dim) * 4;
+  const Range others[] = {range_of(u, io),       range_of(z, z ? io : 0),       range_of(y, io),
+                          range_of(p.delta, io), range_of(p.B, bcb),            range_of(p.C, bcb),
+                          range_of(p.A, vec * sscan::kDState), range_of(p.delta_bias, p.delta_bias ? vec : 0),
+                          range_of(p.D, p.D ? vec : 0), range_of(workspace, workspace ? workspace_bytes : 0)};
+  for (const Range& r : others)
+    if (overlap(hlr, r)) return SSCAN_ERR_ALIAS;
+  if (overlap(h0r, range_of(y, io)) || overlap(h0r, range_of(workspace, workspace ? workspace_bytes : 0)))
+    return SSCAN_ERR_ALIAS;
+  if (h0 && h_last && overlap(h0r, hlr) && h0r.lo != hlr.lo) return SSCAN_ERR_ALIAS;
+  return SSCAN_OK;
+}
+
 sscan::ScanArgs make_args(const void* u, const void* z, void* y, const DirView* dirs, int ndir, int reverse,
                           int softplus, int64_t batch, int64_t dim, int64_t len, int io_dtype, int bc_dtype) {
   sscan::ScanArgs a;
@@ -126,15 +152,40 @@ sscan::ScanArgs make_args(const void* u, const void* z, void* y, const DirView* 
   return a;
 }
 
+int validate_state_call(const void* u, const void* z, const void* y, const DirView& d, const float* h0,
+                        float* h_last, int64_t batch, int64_t dim, int64_t len, int64_t dstate, int io_dtype,
+                        int bc_dtype, const void* workspace, size_t workspace_bytes, sscan::Plan* plan,
+                        bool* empty) {
+  int st = validate(u, z, y, &d, 1, batch, dim, len, dstate, io_dtype, bc_dtype, workspace, workspace_bytes, plan,
+                    empty);
+  if (st != SSCAN_OK) return st;
+  if (batch == 0 || dim == 0) return SSCAN_OK;  // no state at all
+  return check_state(h0, h_last, u, z, y, d, batch, dim, len, io_dtype, bc_dtype, workspace, workspace_bytes);
+}
+
 int run(const void* u, const void* z, void* y, const DirView* dirs, int ndir, int reverse, int softplus,
         int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream, int io_dtype, int bc_dtype,
-        void* workspace, size_t workspace_bytes, void* const* events = nullptr) {
+        void* workspace, size_t workspace_bytes, void* const* events = nullptr, const float* h0 = nullptr,
+        float* h_last = nullptr) {
   sscan::Plan plan{};
   bool empty = false;
-  const int st = validate(u, z, y, dirs, ndir, batch, dim, len, dstate, io_dtype, bc_dtype, workspace,
-                          workspace_bytes, &plan, &empty);
-  if (st != SSCAN_OK || empty) return st;
-  const sscan::ScanArgs a = make_args(u, z, y, dirs, ndir, reverse, softplus, batch, dim, len, io_dtype, bc_dtype);
+  const bool state = h0 || h_last;
+  const int st = state ? validate_state_call(u, z, y, dirs[0], h0, h_last, batch, dim, len, dstate, io_dtype,
+                                             bc_dtype, workspace, workspace_bytes, &plan, &empty)
+                       : validate(u, z, y, dirs, ndir, batch, dim, len, dstate, io_dtype, bc_dtype, workspace,
+                                  workspace_bytes, &plan, &empty);
+  if (st != SSCAN_OK) return st;
+  sscan::ScanArgs a = make_args(u, z, y, dirs, ndir, reverse, softplus, batch, dim, len, io_dtype, bc_dtype);
+  a.h0 = h0;
+  a.h_last = h_last;
+  if (empty) {
+    // no tokens: the final state is the entry state
+    if (len == 0 && h_last && h_last != h0 && batch > 0 && dim > 0) {
+      const hipError_t e = sscan::launch_state_passthrough(a, static_cast<hipStream_t>(stream));
+      return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+    }
+    return SSCAN_OK;
+  }
   hipEvent_t ev[sscan::kProfileEvents] = {};
   if (events)
     for (int i = 0; i < sscan::kProfileEvents; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
@@ -213,6 +264,71 @@ int sscan_validate_bidir(const void* u, const void* z, const void* y, const ssca
                   &empty);
 }
 
+int sscan_fwd_state(const void* u, const void* delta, const float* delta_bias, int softplus, const float* A,
+                    const void* B, const void* C, const float* D, const void* z, void* y, const float* h0,
+                    float* h_last, int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse,
+                    void* stream, int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes) {
+  const DirView d{delta, delta_bias, A, B, C, D};
+  if (!h0 && !h_last)
+    return run(u, z, y, &d, 1, reverse, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype, workspace,
+               workspace_bytes);
+  return run(u, z, y, &d, 1, reverse, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype, workspace,
+             workspace_bytes, nullptr, h0, h_last);
+}
+
+int sscan_validate_fwd_state(const void* u, const void* delta, const float* delta_bias, int softplus,
+                             const float* A, const void* B, const void* C, const float* D, const void* z,
+                             const void* y, const float* h0, const float* h_last, int64_t batch, int64_t dim,
+                             int64_t len, int64_t dstate, int reverse, int io_dtype, int bc_dtype,
+                             const void* workspace, size_t workspace_bytes) {
+  (void)softplus;
+  (void)reverse;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  sscan::Plan plan{};
+  bool empty = false;
+  return validate_state_call(u, z, y, d, h0, const_cast<float*>(h_last), batch, dim, len, dstate, io_dtype,
+                             bc_dtype, workspace, workspace_bytes, &plan, &empty);
+}
+
+int sscan_validate_step(const float* state, const void* u, const void* delta, const float* delta_bias,
+                        int softplus, const float* A, const void* B, const void* C, const float* D, const void* z,
+                        const void* y, int64_t batch, int64_t dim, int64_t dstate, int io_dtype, int bc_dtype) {
+  (void)softplus;
+  Sizes sz{};
+  // one token: the sequence checks with len = 1 cover sizes and dtypes
+  int st = check_sizes(batch, dim, 1, dstate, io_dtype, bc_dtype, &sz);
+  if (st != SSCAN_OK) return st;
+  if (batch == 0 || dim == 0) return SSCAN_OK;
+  if (!state || !u || !delta || !A || !B || !C || !y) return SSCAN_ERR_NULL;
+  // state and A are read as 16-byte pieces, B and C as 4 states at a time
+  const size_t bc_align = 4 * sz.bc_esz;
+  if (!aligned(state, 16) || !aligned(u, sz.io_esz) || !aligned(delta, sz.io_esz) || !aligned(z, sz.io_esz) ||
+      !aligned(y, sz.io_esz) || !aligned(B, bc_align) || !aligned(C, bc_align) || !aligned(A, 16) ||
+      !aligned(D, 4) || !aligned(delta_bias, 4))
+    return SSCAN_ERR_ALIGN;
+  const size_t io = sz.io_elems * sz.io_esz, bcb = sz.bc_elems * sz.bc_esz, vec = size_t(dim) * 4;
+  const Range sr = range_of(state, sz.io_elems * sscan::kDState * 4), yr = range_of(y, io);
+  const Range ins[] = {range_of(u, io), range_of(delta, io), range_of(z, z ? io : 0), range_of(B, bcb),
+                       range_of(C, bcb), range_of(A, vec * sscan::kDState),
+                       range_of(delta_bias, delta_bias ? vec : 0), range_of(D, D ? vec : 0)};
+  if (overlap(sr, yr)) return SSCAN_ERR_ALIAS;
+  for (const Range& r : ins)
+    if (overlap(sr, r) || overlap(yr, r)) return SSCAN_ERR_ALIAS;
+  return SSCAN_OK;
+}
+
+int sscan_step(float* state, const void* u, const void* delta, const float* delta_bias, int softplus,
+               const float* A, const void* B, const void* C, const float* D, const void* z, void* y, int64_t batch,
+               int64_t dim, int64_t dstate, void* stream, int io_dtype, int bc_dtype) {
+  const int st = sscan_validate_step(state, u, delta, delta_bias, softplus, A, B, C, D, z, y, batch, dim, dstate,
+                                     io_dtype, bc_dtype);
+  if (st != SSCAN_OK || batch == 0 || dim == 0) return st;
+  sscan::StepArgs a{state, u, delta, z, y, delta_bias, A, B, C, D, softplus ? 1 : 0, io_dtype == SSCAN_BF16,
+                    bc_dtype == SSCAN_BF16, batch, dim};
+  const hipError_t e = sscan::launch_step(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+}
+
 size_t sscan_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir) {
   Sizes sz{};
   if (check_sizes(batch, dim, len, dstate, SSCAN_F32, SSCAN_F32, &sz) != SSCAN_OK) return 0;
@@ -229,7 +345,7 @@ const char* sscan_strerror(int status) {
     case SSCAN_ERR_ALIGN: return "a pointer is not aligned to its element size (workspace: 16 bytes)";
     case SSCAN_ERR_WORKSPACE: return "workspace missing or smaller than sscan_workspace_bytes()";
     case SSCAN_ERR_HIP: return "HIP runtime error at launch";
-    case SSCAN_ERR_ALIAS: return "the output overlaps an input or the workspace";
+    case SSCAN_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
     default: return "unknown status";
   }
 }

@@ -39,6 +39,24 @@ struct ScanArgs {
   int io_bf16;              // u, delta, z, y are bf16 (else f32)
   int bc_bf16;              // B, C are bf16 (else f32)
   int64_t batch, dim, len;
+  const float* h0;          // nullable: state before the first scanned token, [batch][dim][16]
+  float* h_last;            // nullable: receives the state after the last scanned token (may equal h0)
+};
+
+// One token of the recurrence from a stored state (single-step decode).
+struct StepArgs {
+  float* state;             // [batch][dim][16], read and updated in place
+  const void* u;            // [batch][dim] io dtype
+  const void* delta;
+  const void* z;            // nullable
+  void* y;
+  const float* delta_bias;  // nullable, [dim]
+  const float* A;           // [dim][16]
+  const void* B;            // [batch][16] bc dtype
+  const void* C;
+  const float* D;           // nullable, [dim]
+  int softplus, io_bf16, bc_bf16;
+  int64_t batch, dim;
 };
 
 // How a call is split along the sequence, and the workspace it needs (floats,
@@ -67,5 +85,10 @@ constexpr int kProfileEvents = 5;
 // also recorded on the stream.
 hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* workspace, hipStream_t stream,
                        hipEvent_t const* events = nullptr);
+
+// A call with len == 0 and a final state requested: h_last = h0 (or 0).
+hipError_t launch_state_passthrough(const ScanArgs& a, hipStream_t stream);
+
+hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 
 }  // namespace sscan

@@ -392,11 +392,35 @@ __device__ __forceinline__ void init_lane(LaneT& L, const ScanArgs& a, int dir, 
   for (int n = 0; n < kDState; ++n) L.h[n] = 0.0f;
 }
 
+// A lane's 16 states in the caller's [batch][dim][16] layout (64 contiguous bytes).
+__device__ __forceinline__ void load_state16(float (&h)[kDState], const float* p) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < kDState / 4; ++i) {
+    const float4 v = q[i];
+    h[4 * i] = v.x;
+    h[4 * i + 1] = v.y;
+    h[4 * i + 2] = v.z;
+    h[4 * i + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ void store_state16(float* p, const float (&h)[kDState]) {
+  float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+  for (int i = 0; i < kDState / 4; ++i) q[i] = make_float4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+}
+
+// State entering a segment: from the carry chain when the sequence is split, else
+// the caller's entry state (or zero).
 template <class LaneT>
 __device__ __forceinline__ void load_entry(LaneT& L, const ScanArgs& a, int dir, int64_t b, int64_t seg,
                                            int64_t g, int64_t nseg, const float* hin) {
-  if (nseg <= 1) return;
   const int64_t d = min64(g * kLanes + threadIdx.x % kLanes, a.dim - 1);
+  if (nseg <= 1) {
+    if (a.h0) load_state16(L.h, a.h0 + (b * a.dim + d) * kDState);
+    return;
+  }
 #pragma unroll
   for (int n = 0; n < kDState; ++n) L.h[n] = hin[hin_index(dir, b, seg, n, d, a.batch, a.dim, nseg)];
 }
@@ -461,7 +485,7 @@ __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_aggregate_kernel(
 }
 
 // Step 2: the chain of segment aggregates in scan order,
-//   h_in[k+1] = exp(A sum_dt[k]) h_in[k] + H[k],   h_in[0] = 0,
+//   h_in[k+1] = exp(A sum_dt[k]) h_in[k] + H[k],   h_in[0] = h0 (or 0),
 // for every (direction, batch, state, channel).  The combine is associative, so
 // each chain is split into kCarryParts runs of consecutive segments: each run is
 // first reduced on its own (its decay exponent is the sum of its sum_dt), the runs'
@@ -523,7 +547,7 @@ __global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanAr
   sh_s[part][lane] = S;
   sh_h[part][lane] = H;
   __syncthreads();
-  float h = 0.0f;
+  float h = a.h0 ? a.h0[(b * a.dim + d) * kDState + n] : 0.0f;  // entry state of the first segment
   for (int q = 0; q < part; ++q) h = fmaf(exp2_hw(A2 * sh_s[q][lane]), h, sh_h[q][lane]);
   const bool reuse = kagg - k0 <= kBatch;  // the run's aggregates are still in registers
   for (int64_t kb = k0; kb < k1; kb += kBatch) {
@@ -556,6 +580,78 @@ __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_output_dir_kernel
     L.template scan<true, kStore>(t0, t1);
   } else {
     L.template scan<false, kStore>(t0, t1);
+  }
+  // the segment scanned last holds the final state
+  if (a.h_last && L.active && (a.reverse ? s.seg == 0 : s.seg == nseg - 1))
+    store_state16(a.h_last + (s.b * a.dim + s.g * kLanes + threadIdx.x) * kDState, L.h);
+}
+
+// len == 0 with a final state requested: the state passes through unchanged.
+__global__ __launch_bounds__(256) void state_passthrough_kernel(const float* h0, float* h_last, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) h_last[i] = h0 ? h0[i] : 0.0f;
+}
+
+// One token from a stored state.  Four consecutive lanes share a channel and
+// each owns four of its states, so the state and A are read and written as
+// contiguous 16-byte pieces (a wave covers 16 channels = 1 KiB of state):
+//   h_n <- exp(dt A_n) h_n + dt B_n u,  out = (sum_n C_n h_n + D u) silu(z).
+// The four partial readouts are summed across the lane quad with DPP.  Grid:
+// x over channels (64 per block), y = batch row, so B and C are block-uniform.
+// The per-state arithmetic is the same as one token of the sequence kernels.
+constexpr int kStepThreads = 256;
+constexpr int kStepChannels = kStepThreads / 4;
+
+__device__ __forceinline__ float quad_sum(float v) {
+  // xor 1 then xor 2 within each group of four lanes (DPP quad permutations)
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  return v;
+}
+
+template <bool IO_BF16, bool BC_BF16, bool SOFTPLUS>
+__global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t b0) {
+  using IO = Io<IO_BF16>;
+  using T = typename IO::T;
+  const int64_t b = b0 + blockIdx.y;
+  const int q = threadIdx.x & 3;  // which four states
+  const int64_t d_raw = int64_t(blockIdx.x) * kStepChannels + (threadIdx.x >> 2);
+  const bool active = d_raw < a.dim;
+  const int64_t d = active ? d_raw : a.dim - 1;  // idle lanes shadow a valid channel and store nothing
+  const int64_t i = b * a.dim + d;
+  const float4 hv = reinterpret_cast<const float4*>(a.state + i * kDState)[q];
+  const float4 av = reinterpret_cast<const float4*>(a.A + d * kDState)[q];
+  float h[4] = {hv.x, hv.y, hv.z, hv.w};
+  const float A2[4] = {av.x * kLog2e, av.y * kLog2e, av.z * kLog2e, av.w * kLog2e};
+  float Bv[4], Cv[4];
+  if (BC_BF16) {
+    const uint2 bw = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.B) + b * kDState)[q];
+    const uint2 cw = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.C) + b * kDState)[q];
+    Bv[0] = bf16_lo(bw.x), Bv[1] = bf16_hi(bw.x), Bv[2] = bf16_lo(bw.y), Bv[3] = bf16_hi(bw.y);
+    Cv[0] = bf16_lo(cw.x), Cv[1] = bf16_hi(cw.x), Cv[2] = bf16_lo(cw.y), Cv[3] = bf16_hi(cw.y);
+  } else {
+    const float4 bv = reinterpret_cast<const float4*>(static_cast<const float*>(a.B) + b * kDState)[q];
+    const float4 cv = reinterpret_cast<const float4*>(static_cast<const float*>(a.C) + b * kDState)[q];
+    Bv[0] = bv.x, Bv[1] = bv.y, Bv[2] = bv.z, Bv[3] = bv.w;
+    Cv[0] = cv.x, Cv[1] = cv.y, Cv[2] = cv.z, Cv[3] = cv.w;
+  }
+  const float uu = IO::load(static_cast<const T*>(a.u), i);
+  const float x = IO::load(static_cast<const T*>(a.delta), i) + (a.delta_bias ? a.delta_bias[d] : 0.0f);
+  const float dt = SOFTPLUS ? softplus_f32(x) : x;
+  const float dtu = dt * uu;
+  float s = 0.0f;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    h[n] = fmaf(exp2_hw(dt * A2[n]), h[n], dtu * Bv[n]);
+    s = fmaf(Cv[n], h[n], s);
+  }
+  s = quad_sum(s);
+  if (!active) return;
+  reinterpret_cast<float4*>(a.state + i * kDState)[q] = make_float4(h[0], h[1], h[2], h[3]);
+  if (q == 0) {
+    float yv = fmaf(a.D ? a.D[d] : 0.0f, uu, s);
+    if (a.z) yv *= silu_f32(IO::load(static_cast<const T*>(a.z), i));
+    IO::store(static_cast<T*>(a.y), i, yv);
   }
 }
 
@@ -696,6 +792,33 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
 
 hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* ws, hipStream_t stream, hipEvent_t const* events) {
   return a.io_bf16 ? launch_io<true>(a, p, ws, stream, events) : launch_io<false>(a, p, ws, stream, events);
+}
+
+hipError_t launch_state_passthrough(const ScanArgs& a, hipStream_t stream) {
+  const int64_t n = a.batch * a.dim * kDState;
+  hipLaunchKernelGGL(state_passthrough_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, a.h0, a.h_last,
+                     n);
+  return hipGetLastError();
+}
+
+hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
+  constexpr int64_t kMaxRows = 65535;  // grid y limit: batch rows per launch
+  const int key = (a.io_bf16 ? 4 : 0) | (a.bc_bf16 ? 2 : 0) | (a.softplus ? 1 : 0);
+  for (int64_t b0 = 0; b0 < a.batch; b0 += kMaxRows) {
+    const dim3 grid(unsigned((a.dim + kStepChannels - 1) / kStepChannels), unsigned(std::min(kMaxRows, a.batch - b0)));
+    const dim3 block(kStepThreads);
+    switch (key) {
+      case 0: hipLaunchKernelGGL((step_kernel<false, false, false>), grid, block, 0, stream, a, b0); break;
+      case 1: hipLaunchKernelGGL((step_kernel<false, false, true>), grid, block, 0, stream, a, b0); break;
+      case 2: hipLaunchKernelGGL((step_kernel<false, true, false>), grid, block, 0, stream, a, b0); break;
+      case 3: hipLaunchKernelGGL((step_kernel<false, true, true>), grid, block, 0, stream, a, b0); break;
+      case 4: hipLaunchKernelGGL((step_kernel<true, false, false>), grid, block, 0, stream, a, b0); break;
+      case 5: hipLaunchKernelGGL((step_kernel<true, false, true>), grid, block, 0, stream, a, b0); break;
+      case 6: hipLaunchKernelGGL((step_kernel<true, true, false>), grid, block, 0, stream, a, b0); break;
+      default: hipLaunchKernelGGL((step_kernel<true, true, true>), grid, block, 0, stream, a, b0); break;
+    }
+  }
+  return hipGetLastError();
 }
 
 }  // namespace sscan

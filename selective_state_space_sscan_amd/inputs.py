@@ -109,6 +109,20 @@ class ScanInputs:
     def dstate(self) -> int:
         return self.dirs[0].A.shape[1]
 
+    def tensors(self) -> List[torch.Tensor]:
+        """Every distinct input tensor (each direction's parameters included)."""
+        ts = [self.u, self.delta, self.z]
+        for p in self.dirs:
+            ts += [p.delta_bias, p.A, p.B, p.C, p.D]
+        return ts
+
+    def clone(self) -> "ScanInputs":
+        """The same values in new storage (on the same device)."""
+        return ScanInputs(
+            self.u.clone(), self.delta.clone(), self.z.clone(),
+            [DirParams(p.delta_bias.clone(), p.A.clone(), p.B.clone(), p.C.clone(), p.D.clone()) for p in self.dirs],
+            self.io_dtype, self.bc_dtype)
+
     def to(self, device) -> "ScanInputs":
         mv = lambda t: t.to(device, non_blocking=False).contiguous()
         return ScanInputs(

@@ -62,6 +62,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_validate_fwd.restype = I
     lib.sscan_validate_bidir.argtypes = [V, V, V, DP, DP, I, I64, I64, I64, I64, I, I, V, SZ]
     lib.sscan_validate_bidir.restype = I
+    lib.sscan_fwd_state.argtypes = [V, V, V, I, V, V, V, V, V, V, V, V, I64, I64, I64, I64, I, V, I, I, V, SZ]
+    lib.sscan_fwd_state.restype = I
+    lib.sscan_validate_fwd_state.argtypes = [V, V, V, I, V, V, V, V, V, V, V, V, I64, I64, I64, I64, I, I, I, V, SZ]
+    lib.sscan_validate_fwd_state.restype = I
+    lib.sscan_step.argtypes = [V, V, V, V, I, V, V, V, V, V, V, I64, I64, I64, V, I, I]
+    lib.sscan_step.restype = I
+    lib.sscan_validate_step.argtypes = [V, V, V, V, I, V, V, V, V, V, V, I64, I64, I64, I, I]
+    lib.sscan_validate_step.restype = I
     lib.sscan_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.sscan_workspace_bytes.restype = SZ
     lib.sscan_strerror.argtypes = [I]
@@ -109,6 +117,15 @@ class HipEvents:
                 raise RuntimeError("hipEventElapsedTime failed")
             out[name] = float(ms.value)
         return out
+
+    def total_ms(self) -> float:
+        """Milliseconds from the first to the last event (the whole call)."""
+        hip = HipEvents._hip
+        hip.hipEventSynchronize(self._ev[PROFILE_EVENTS - 1])
+        ms = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(ms), self._ev[0], self._ev[PROFILE_EVENTS - 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
 
     def __del__(self):
         hip = HipEvents._hip
@@ -195,6 +212,81 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = Tru
         st = lib.sscan_fwd_profiled(*args, ctypes.cast(events.handles, ctypes.c_void_p))
     if st != 0:
         raise SScanError(st, "sscan_fwd")
+    return out
+
+
+def fwd_state(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0: Optional[torch.Tensor] = None,
+              h_last: Optional[torch.Tensor] = None, softplus: bool = True, reverse: bool = False,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """One-direction scan with state I/O (``sscan_fwd_state``).  h0 (optional) is
+    the state before the first scanned token, [batch, dim, 16] f32; the state after
+    the last scanned token is written to ``h_last`` (allocated if None, may be h0
+    itself).  Returns (out, h_last)."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.fwd_state needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or B.dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = u.shape
+    _check(u, "u", dev)
+    _check(delta, "delta", dev, u.dtype, u.shape)
+    _check(z, "z", dev, u.dtype, u.shape)
+    _check(A, "A", dev, torch.float32, (d, DSTATE))
+    _check(B, "B", dev, None, (b, DSTATE, L))
+    _check(C, "C", dev, B.dtype, (b, DSTATE, L))
+    _check(D, "D", dev, torch.float32, (d,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (d,))
+    _check(h0, "h0", dev, torch.float32, (b, d, DSTATE))
+    if h_last is None:
+        h_last = torch.empty((b, d, DSTATE), dtype=torch.float32, device=dev)
+    _check(h_last, "h_last", dev, torch.float32, (b, d, DSTATE))
+    if out is None:
+        out = torch.empty_like(u)
+    _check(out, "out", dev, u.dtype, u.shape)
+    if b * d == 0:
+        return out, h_last
+    ws, ws_bytes = _workspace(workspace_bytes(b, d, L, DSTATE, False), dev, workspace)
+    st = lib.sscan_fwd_state(_ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C),
+                             _ptr(D), _ptr(z), _ptr(out), _ptr(h0), _ptr(h_last), b, d, L, DSTATE,
+                             int(bool(reverse)), _stream(dev), _DT_CODE[u.dtype], _DT_CODE[B.dtype], _ptr(ws),
+                             ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_fwd_state")
+    return out, h_last
+
+
+def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token from a stored state (``sscan_step``), updating ``state``
+    [batch, dim, 16] f32 in place.  u, delta, z: [batch, dim]; B, C: [batch, 16].
+    Returns y [batch, dim] in u's dtype."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.step needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or B.dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d = u.shape
+    _check(state, "state", dev, torch.float32, (b, d, DSTATE))
+    _check(u, "u", dev)
+    _check(delta, "delta", dev, u.dtype, u.shape)
+    _check(z, "z", dev, u.dtype, u.shape)
+    _check(A, "A", dev, torch.float32, (d, DSTATE))
+    _check(B, "B", dev, None, (b, DSTATE))
+    _check(C, "C", dev, B.dtype, (b, DSTATE))
+    _check(D, "D", dev, torch.float32, (d,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (d,))
+    if out is None:
+        out = torch.empty_like(u)
+    _check(out, "out", dev, u.dtype, u.shape)
+    if u.numel() == 0:
+        return out
+    st = lib.sscan_step(_ptr(state), _ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B),
+                        _ptr(C), _ptr(D), _ptr(z), _ptr(out), b, d, DSTATE, _stream(dev), _DT_CODE[u.dtype],
+                        _DT_CODE[B.dtype])
+    if st != 0:
+        raise SScanError(st, "sscan_step")
     return out
 
 

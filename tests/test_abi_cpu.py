@@ -172,3 +172,72 @@ def test_run_entry_points_reject_before_any_hip_call(lib):
     assert st == EUNSUP
     st = lib.sscan_bidir(None, None, None, None, None, 1, 2, 64, 32, 16, None, 0, 0, None, 0)
     assert st == ENULL
+
+
+# --- state I/O and single-step decode ------------------------------------------------------------
+
+def call_validate_state(lib, a, h0, hl):
+    return lib.sscan_validate_fwd_state(a["u"], a["delta"], a["bias"], a["softplus"], a["A"], a["B"], a["C"], a["D"],
+                                        a["z"], a["y"], h0, hl, a["b"], a["d"], a["L"], a["N"], a["reverse"], a["io"],
+                                        a["bc"], a["ws"], a["ws_bytes"])
+
+
+def test_validate_fwd_state(lib):
+    f = Fake()
+    f.next = 1 << 46  # clear of the addresses fwd_args hands out
+    a = fwd_args(2, 64, 300, io=1)
+    sb = 2 * 64 * 16 * 4
+    h0, hl = f(sb), f(sb)
+    assert call_validate_state(lib, a, h0, hl) == OK
+    assert call_validate_state(lib, a, None, hl) == OK
+    assert call_validate_state(lib, a, h0, None) == OK
+    assert call_validate_state(lib, a, h0, h0) == OK            # the state updated in place
+    assert call_validate_state(lib, a, h0, h0 + 64) == EALIAS   # partial overlap
+    assert call_validate_state(lib, a, h0, h0 + 4) == EALIGN    # state buffers need 16 bytes
+    assert call_validate_state(lib, a, h0, a["u"]) == EALIAS
+    assert call_validate_state(lib, a, h0, a["A"]) == EALIAS
+    assert call_validate_state(lib, a, h0, a["ws"] + 256) == EALIAS
+    assert call_validate_state(lib, dict(a, y=h0), h0, hl) == EALIAS
+    assert call_validate_state(lib, dict(a, u=None), h0, hl) == ENULL
+    # an empty sequence with a final state is a valid call (the state passes through)
+    assert call_validate_state(lib, fwd_args(2, 64, 0), h0, hl) == OK
+
+
+def step_args(b, d, io=0, bc=0, **over):
+    f = Fake()
+    ie = 2 if io == 1 else 4
+    be = 2 if bc == 1 else 4
+    a = dict(state=f(b * d * 64), u=f(b * d * ie), delta=f(b * d * ie), bias=f(d * 4), softplus=1, A=f(d * 64),
+             B=f(b * 16 * be), C=f(b * 16 * be), D=f(d * 4), z=f(b * d * ie), y=f(b * d * ie), b=b, d=d, N=16,
+             io=io, bc=bc)
+    a.update(over)
+    return a
+
+
+def call_validate_step(lib, a):
+    return lib.sscan_validate_step(a["state"], a["u"], a["delta"], a["bias"], a["softplus"], a["A"], a["B"], a["C"],
+                                   a["D"], a["z"], a["y"], a["b"], a["d"], a["N"], a["io"], a["bc"])
+
+
+def test_validate_step(lib):
+    for io, bc in ((0, 0), (1, 1), (1, 0)):
+        assert call_validate_step(lib, step_args(4, 1536, io, bc)) == OK
+    assert call_validate_step(lib, step_args(4, 100, D=None, bias=None, z=None)) == OK
+    for name in ("state", "u", "delta", "A", "B", "C", "y"):
+        assert call_validate_step(lib, step_args(4, 100, **{name: None})) == ENULL, name
+    a = step_args(4, 100)
+    assert call_validate_step(lib, dict(a, N=8)) == EUNSUP
+    assert call_validate_step(lib, dict(a, b=-1)) == ESHAPE
+    assert call_validate_step(lib, dict(a, state=a["state"] + 4)) == EALIGN
+    assert call_validate_step(lib, dict(a, A=a["A"] + 4)) == EALIGN
+    assert call_validate_step(lib, dict(a, B=a["B"] + 8)) == EALIGN
+    ab = step_args(4, 100, io=1, bc=1)
+    assert call_validate_step(lib, dict(ab, B=ab["B"] + 8, C=ab["C"] + 8)) == OK  # bf16: 8 bytes suffice
+    assert call_validate_step(lib, dict(ab, C=ab["C"] + 4)) == EALIGN
+    assert call_validate_step(lib, dict(a, y=a["state"])) == EALIAS
+    assert call_validate_step(lib, dict(a, y=a["u"])) == EALIAS
+    assert call_validate_step(lib, dict(a, state=a["B"])) == EALIAS
+    assert call_validate_step(lib, step_args(0, 100, state=None, u=None)) == OK  # empty
+    st = lib.sscan_step(None, a["u"], a["delta"], a["bias"], 1, a["A"], a["B"], a["C"], a["D"], a["z"], a["y"],
+                        4, 100, 16, None, 0, 0)
+    assert st == ENULL

@@ -1,0 +1,172 @@
+"""GPU parity of the state I/O entry points (``sscan_fwd_state``, ``sscan_step``)
+against the fp64 oracle.
+
+The oracle's entry-state / final-state path is pinned in test_oracle_pins.py
+(P11, P12).  Outputs use the floored relative error of tests/parity.py; final
+states are float32 on both the GPU and in the comparison, so they are held to the
+float32 bound (1e-4) whatever the I/O dtype.
+"""
+import os
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from parity import TOL, metrics
+from selective_state_space_sscan_amd import inputs as I
+from selective_state_space_sscan_amd import sscan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+NTHREADS = min(16, oracle.default_threads())
+STATE_TOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    sscan.load_library()  # raises if the extension is missing: no fallback
+    if not os.path.exists(oracle.LIB):
+        oracle.build(force=True)
+
+
+def check(got, ref, tol, what):
+    if isinstance(got, torch.Tensor):
+        got = I.f64(got.cpu())
+    m = metrics(got, ref)
+    print(f"{what}: {m}", flush=True)
+    assert m["floored_max"] <= tol, (what, m)
+
+
+def draw(name, b, d, L, io, bc, **kw):
+    x = I.make_inputs(b, d, L, io_dtype=io, bc_dtype=bc, seed=zlib.crc32(name.encode()) % 10000, **kw)
+    rng = np.random.default_rng(zlib.crc32(name.encode()) % 1000 + 7)
+    h0 = torch.from_numpy(rng.normal(0.0, 1.0, (b, d, 16))).float()
+    return x, h0
+
+
+def oracle_state(x, h0, reverse=False, gate=True, softplus=True):
+    x64 = I.as_f64_dict(x)
+    p = x64["dirs"][0]
+    return oracle.sscan_fwd(x64["u"], x64["delta"], p["A"], p["B"], p["C"], p["D"], x64["z"] if gate else None,
+                            p["delta_bias"], softplus=softplus, reverse=reverse,
+                            h0=None if h0 is None else h0.double().numpy(), return_last_state=True,
+                            nthreads=NTHREADS)
+
+
+STATE_CASES = [
+    # name, batch, dim, len, io, bc, reverse, with h0
+    ("short-fwd", 2, 64, 100, "f32", "f32", False, True),
+    ("short-rev", 2, 70, 77, "f32", "f32", True, True),
+    ("short-no-h0", 2, 64, 40, "f32", "f32", False, False),
+    ("long-fwd", 2, 96, 3000, "f32", "f32", False, True),
+    ("long-rev", 1, 130, 2500, "f32", "f32", True, True),
+    ("long-bf16", 1, 128, 5000, "bf16", "f32", False, True),
+    ("len1", 3, 64, 1, "bf16", "bf16", False, True),
+]
+
+
+@pytest.mark.parametrize("name,b,d,L,io,bc,reverse,with_h0", STATE_CASES, ids=[c[0] for c in STATE_CASES])
+def test_fwd_state_parity(name, b, d, L, io, bc, reverse, with_h0):
+    x, h0 = draw(name, b, d, L, io, bc)
+    if not with_h0:
+        h0 = None
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    y, hl = sscan.fwd_state(xd.u, xd.delta, p.A, p.B, p.C, p.D, xd.z, p.delta_bias,
+                            h0=None if h0 is None else h0.to(DEV), reverse=reverse)
+    torch.cuda.synchronize()
+    ref_y, ref_h = oracle_state(x, h0, reverse=reverse)
+    check(y, ref_y, TOL[io], f"{name} y")
+    check(hl, ref_h, STATE_TOL, f"{name} h_last")
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_streaming_pieces_equal_one_call(reverse):
+    """A sequence fed in pieces of uneven length (short and segmented ones), the
+    state kept in one buffer updated in place, matches the oracle on the whole."""
+    b, d, L = 2, 96, 2900
+    x, _ = draw(f"stream-{reverse}", b, d, L, "f32", "f32")
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    cuts = [0, 1, 130, 257, 1500, 1501, L]
+    pieces = list(zip(cuts[:-1], cuts[1:]))
+    if reverse:
+        pieces = pieces[::-1]
+    h = torch.zeros(b, d, 16, device=DEV)
+    y = torch.empty_like(xd.u)
+    for s, e in pieces:
+        sl = lambda t: t[:, :, s:e].contiguous()
+        ys, _ = sscan.fwd_state(sl(xd.u), sl(xd.delta), p.A, sl(p.B), sl(p.C), p.D, sl(xd.z), p.delta_bias,
+                                h0=h, h_last=h, reverse=reverse)
+        y[:, :, s:e] = ys
+    torch.cuda.synchronize()
+    ref_y, ref_h = oracle_state(x, None, reverse=reverse)
+    check(y, ref_y, TOL["f32"], f"stream reverse={reverse} y")
+    check(h, ref_h, STATE_TOL, f"stream reverse={reverse} h")
+
+
+def test_empty_sequence_passes_state_through():
+    b, d = 2, 70
+    x, h0 = draw("empty", b, d, 0, "f32", "f32")
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    h0d = h0.to(DEV)
+    _, hl = sscan.fwd_state(xd.u, xd.delta, p.A, p.B, p.C, p.D, xd.z, p.delta_bias, h0=h0d)
+    _, hz = sscan.fwd_state(xd.u, xd.delta, p.A, p.B, p.C, p.D, xd.z, p.delta_bias,
+                            h_last=torch.full((b, d, 16), 7.0, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(hl.cpu(), h0)
+    assert torch.count_nonzero(hz).item() == 0
+
+
+STEP_CASES = [
+    # name, batch, dim, io, bc, gate, softplus
+    ("f32", 4, 100, "f32", "f32", True, True),
+    ("bf16", 3, 1536, "bf16", "bf16", True, True),
+    ("bf16-f32bc", 2, 64, "bf16", "f32", True, True),
+    ("no-gate", 2, 130, "f32", "f32", False, True),
+    ("no-softplus", 2, 64, "f32", "f32", True, False),
+]
+
+
+@pytest.mark.parametrize("name,b,d,io,bc,gate,softplus", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_step_decode_loop(name, b, d, io, bc, gate, softplus):
+    """T single-token steps from a random state reproduce the oracle's output
+    sequence and final state for the same T tokens."""
+    T = 24
+    x, h0 = draw("step-" + name, b, d, T, io, bc)
+    if not softplus:
+        x.delta.abs_().add_(0.01)
+        x.dirs[0].delta_bias.zero_()
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    state = h0.to(DEV).clone()
+    ys = []
+    for t in range(T):
+        col = lambda v: v[:, :, t].contiguous()
+        ys.append(sscan.step(state, col(xd.u), col(xd.delta), p.A, col(p.B), col(p.C), p.D,
+                             col(xd.z) if gate else None, p.delta_bias, softplus=softplus))
+    y = torch.stack(ys, -1)
+    torch.cuda.synchronize()
+    ref_y, ref_h = oracle_state(x, h0, gate=gate, softplus=softplus)
+    check(y, ref_y, TOL[io], f"step {name} y")
+    check(state, ref_h, STATE_TOL, f"step {name} state")
+
+
+def test_step_matches_one_token_sequence_call():
+    """sscan_step and sscan_fwd_state with len = 1 compute the same token."""
+    b, d = 2, 200
+    x, h0 = draw("step-vs-seq", b, d, 1, "f32", "f32")
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    y_seq, h_seq = sscan.fwd_state(xd.u, xd.delta, p.A, p.B, p.C, p.D, xd.z, p.delta_bias, h0=h0.to(DEV))
+    state = h0.to(DEV).clone()
+    y_step = sscan.step(state, xd.u[:, :, 0].contiguous(), xd.delta[:, :, 0].contiguous(), p.A,
+                        p.B[:, :, 0].contiguous(), p.C[:, :, 0].contiguous(), p.D, xd.z[:, :, 0].contiguous(),
+                        p.delta_bias)
+    torch.cuda.synchronize()
+    check(y_step, I.f64(y_seq[:, :, 0].cpu()), 1e-6, "step vs len-1 call y")
+    check(state, I.f64(h_seq.cpu()), 1e-6, "step vs len-1 call state")
