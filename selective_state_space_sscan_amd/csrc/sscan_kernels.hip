@@ -487,17 +487,26 @@ __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_aggregate_kernel(
 // Step 2: the chain of segment aggregates in scan order,
 //   h_in[k+1] = exp(A sum_dt[k]) h_in[k] + H[k],   h_in[0] = h0 (or 0),
 // for every (direction, batch, state, channel).  The combine is associative, so
-// each chain is split into kCarryParts runs of consecutive segments: each run is
-// first reduced on its own (its decay exponent is the sum of its sum_dt), the runs'
-// totals are chained through LDS, and each run is walked again from its entry
-// state writing h_in.  A block holds 64 channels (coalesced along d) x the parts.
+// each chain is split into runs of consecutive segments, one wave per run (up to
+// kCarryParts, each run at least kCarryMinRun segments): each run is first reduced
+// on its own (its decay exponent is the sum of its sum_dt), the runs' totals are
+// chained through LDS, and each run is walked again from its entry state writing
+// h_in.  A block holds 64 channels (coalesced along d) x the runs.
 constexpr int kCarryParts = 16;
+constexpr int64_t kCarryMinRun = 8;
+
+int carry_parts(int64_t nseg) {
+  int p = 1;
+  while (p < kCarryParts && nseg / (2 * p) >= kCarryMinRun) p *= 2;
+  return p;
+}
 
 __global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanArgs a, int64_t nseg,
                                                                        const float* __restrict__ agg,
                                                                        float* __restrict__ hin) {
   __shared__ float sh_s[kCarryParts][kLanes];
   __shared__ float sh_h[kCarryParts][kLanes];
+  const int nparts = int(blockDim.x) / kLanes;
   const int lane = threadIdx.x % kLanes;
   const int part = threadIdx.x / kLanes;
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
@@ -514,7 +523,7 @@ __global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanAr
   const int64_t d = active ? d_raw : a.dim - 1;
   const float* Adir = dir ? a.dir[1].A : a.dir[0].A;
   const float A2 = Adir[d * kDState + n] * kLog2e;
-  const int64_t chunk = (nseg + kCarryParts - 1) / kCarryParts;
+  const int64_t chunk = (nseg + nparts - 1) / nparts;
   const int64_t k0 = min64(nseg, part * chunk), k1 = min64(nseg, k0 + chunk);
   auto seg_of = [&](int64_t k) { return reverse ? nseg - 1 - k : k; };
   // the last segment in scan order has no aggregate (nothing follows it)
@@ -716,8 +725,8 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
                        dim3(kLanes), 0, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), agg, int(vec));
     mark(2);
     const int64_t carry_blocks = int64_t(a.ndir) * a.batch * kDState * ngroups;
-    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), dim3(kLanes * kCarryParts), 0, stream, a,
-                       p.nseg, static_cast<const float*>(agg), hin);
+    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), dim3(kLanes * carry_parts(p.nseg)), 0, stream,
+                       a, p.nseg, static_cast<const float*>(agg), hin);
   }
   if (p.nseg <= 1) mark(2);
   mark(3);

@@ -98,6 +98,8 @@ EDGE = [
     ("dim1", 1, 1, 100, True, "f32", "f32", {}),
     ("short-max", 2, 64, 256, True, "f32", "f32", {}),
     ("short-max+1", 2, 64, 257, True, "f32", "f32", {}),
+    ("split-few-segments", 1, 64, 300, False, "f32", "f32", {}),
+    ("split-few-segments-bidir", 1, 64, 300, True, "f32", "f32", {}),
     ("long-ragged-fwd", 2, 96, 1000, False, "f32", "f32", {}),
     ("long-ragged-rev", 2, 96, 1000, False, "f32", "f32", dict(reverse=True)),
     ("long-ragged-bidir", 2, 96, 1003, True, "f32", "f32", {}),
