@@ -18,6 +18,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "sscan_oracle.c")
+SRC_BWD = os.path.join(HERE, "sscan_oracle_bwd.c")
 LIB = os.path.join(HERE, "liboracle_sscan.so")
 
 _lib = None
@@ -28,7 +29,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(LIB):
         tmp = LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
-                               "-o", tmp, SRC, "-lm", "-lpthread"])
+                               "-o", tmp, SRC, SRC_BWD, "-lm", "-lpthread"])
         os.replace(tmp, LIB)
     return LIB
 
@@ -46,6 +47,8 @@ def _load():
         lib.oracle_sscan_fwd.restype = INT
         lib.oracle_sscan_bidir.argtypes = [P, P, P] + [P] * 12 + [INT, I64, I64, I64, I64, INT]
         lib.oracle_sscan_bidir.restype = INT
+        lib.oracle_sscan_bwd.argtypes = [P, P, P, P, P, INT, P, P, P, INT, I64, I64, I64, I64, INT]
+        lib.oracle_sscan_bwd.restype = INT
         lib.oracle_softplus_f64.argtypes = [ctypes.c_double]
         lib.oracle_softplus_f64.restype = ctypes.c_double
         lib.oracle_silu_f64.argtypes = [ctypes.c_double]
@@ -121,6 +124,48 @@ def sscan_bidir(u, z, fwd: dict, rev: dict, softplus=True, nthreads: int = 1):
     if st != 0:
         raise RuntimeError(f"oracle_sscan_bidir failed with status {st}")
     return out
+
+
+GRAD_NAMES = ("ddelta", "ddelta_bias", "dA", "dB", "dC", "dD")
+
+
+def sscan_bwd(u, z, g, dirs, softplus=True, reverse=False, nthreads: int = 1):
+    """Gradients of sum(g * out) for one direction (``dirs`` = [params], scanned
+    in reverse if ``reverse``) or two (``dirs`` = [forward, reverse]).  Each params
+    dict has delta, A, B, C and optional D, delta_bias.  Returns
+    {"du", "dz" (None without z), "dirs": [{ddelta, ddelta_bias, dA, dB, dC, dD}]}
+    in float64; a gradient of an absent optional input is None."""
+    u = _c64(u)
+    b, d, L = u.shape
+    z = _c64(z, (b, d, L))
+    g = _c64(g, (b, d, L))
+    ndir = len(dirs)
+    if ndir not in (1, 2):
+        raise ValueError("one or two directions")
+    N = np.asarray(dirs[0]["A"]).shape[1]
+    keep, ins, outs, res = [], [], [], []
+    for p in dirs:
+        arrs = [_c64(p["delta"], (b, d, L)), _c64(p.get("delta_bias"), (d,)), _c64(p["A"], (d, N)),
+                _c64(p["B"], (b, N, L)), _c64(p["C"], (b, N, L)), _c64(p.get("D"), (d,))]
+        keep.extend(arrs)
+        ins.extend(_p(a) for a in arrs)
+        gr = {"ddelta": np.empty((b, d, L)), "ddelta_bias": np.empty(d) if p.get("delta_bias") is not None else None,
+              "dA": np.empty((d, N)), "dB": np.empty((b, N, L)), "dC": np.empty((b, N, L)),
+              "dD": np.empty(d) if p.get("D") is not None else None}
+        res.append(gr)
+        outs.extend(_p(gr[k]) for k in GRAD_NAMES)
+    du = np.empty((b, d, L))
+    dz = np.empty((b, d, L)) if z is not None else None
+    rev = [int(bool(reverse))] if ndir == 1 else [0, 1]
+    P = ctypes.c_void_p
+    ins_a = (P * len(ins))(*[x.value if x is not None else None for x in ins])
+    outs_a = (P * len(outs))(*[x.value if x is not None else None for x in outs])
+    rev_a = (ctypes.c_int * ndir)(*rev)
+    st = _load().oracle_sscan_bwd(_p(u), _p(z), _p(g), _p(du), _p(dz), ndir, ins_a, rev_a, outs_a,
+                                  int(bool(softplus)), b, d, L, N, int(nthreads))
+    if st != 0:
+        raise RuntimeError(f"oracle_sscan_bwd failed with status {st}")
+    return {"du": du, "dz": dz, "dirs": res}
 
 
 def softplus(x: float) -> float:

@@ -1,0 +1,177 @@
+"""Pins of the fp64 backward oracle (oracle/sscan_oracle_bwd.c).
+
+The gradients are checked against two things the derivation in that file does not
+share: central finite differences of the forward oracle (itself pinned in
+test_oracle_pins.py), and PyTorch's reverse-mode differentiation (a library
+routine) through a plain fp64 token-by-token recurrence.  No HIP code is involved.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+
+NAMES = ("ddelta", "ddelta_bias", "dA", "dB", "dC", "dD")
+
+
+def _case(rng, b, d, L, N=16, dt_scale=1.0):
+    p = dict(
+        delta=rng.normal(0.0, 0.5, (b, d, L)),
+        A=-np.exp(rng.uniform(-1.0, 1.5, (d, N))),
+        B=rng.normal(size=(b, N, L)),
+        C=rng.normal(size=(b, N, L)),
+        D=rng.normal(size=d),
+        delta_bias=rng.uniform(-3.0, 0.5, d) + np.log(dt_scale),
+    )
+    return p
+
+
+def _inputs(seed, b, d, L, ndir):
+    rng = np.random.default_rng(seed)
+    u = rng.normal(size=(b, d, L))
+    z = rng.normal(size=(b, d, L))
+    g = rng.normal(size=(b, d, L))
+    dirs = [_case(rng, b, d, L) for _ in range(ndir)]
+    return u, z, g, dirs
+
+
+def _fwd(u, z, dirs, softplus=True, reverse=False):
+    if len(dirs) == 1:
+        p = dirs[0]
+        return oracle.sscan_fwd(u, p["delta"], p["A"], p["B"], p["C"], p.get("D"), z, p.get("delta_bias"),
+                                softplus=softplus, reverse=reverse)
+    return oracle.sscan_bidir(u, z, dirs[0], dirs[1], softplus=softplus)
+
+
+def _loss(u, z, g, dirs, softplus, reverse):
+    return float(np.sum(g * _fwd(u, z, dirs, softplus, reverse)))
+
+
+# --- G1: central finite differences of the forward oracle --------------------------------------
+
+@pytest.mark.parametrize("ndir,reverse,softplus,gate", [
+    (1, False, True, True), (1, True, True, True), (1, False, False, False), (2, False, True, True)])
+def test_g1_gradients_match_central_differences(ndir, reverse, softplus, gate):
+    """Each gradient entry against (L(x + h) - L(x - h)) / 2h of the forward oracle.
+    Catches any wrong term, sign or index in the derivation (a dropped decay of the
+    adjoint, softplus' missing, h_t used where h_{t-1} belongs, ...)."""
+    b, d, L = 2, 3, 9
+    u, z, g, dirs = _inputs(300 + 10 * ndir + reverse + 2 * softplus, b, d, L, ndir)
+    if not softplus:
+        for p in dirs:
+            p["delta"] = np.abs(p["delta"]) + 0.05
+            p["delta_bias"] = np.zeros(d)
+    if not gate:
+        z = None
+    got = oracle.sscan_bwd(u, z, g, dirs, softplus=softplus, reverse=reverse)
+    rng = np.random.default_rng(7)
+    h = 1e-5
+
+    def fd(mutate):
+        plus, minus = mutate(h), mutate(-h)
+        return (_loss(*plus, softplus, reverse) - _loss(*minus, softplus, reverse)) / (2 * h)
+
+    def pick(shape, k=6):
+        return [tuple(int(rng.integers(0, s)) for s in shape) for _ in range(k)]
+
+    checks = []
+    for idx in pick(u.shape):
+        def mu(e, idx=idx):
+            uu = u.copy()
+            uu[idx] += e
+            return uu, z, g, dirs
+        checks.append(("du", idx, got["du"][idx], fd(mu)))
+    if z is not None:
+        for idx in pick(z.shape):
+            def mz(e, idx=idx):
+                zz = z.copy()
+                zz[idx] += e
+                return u, zz, g, dirs
+            checks.append(("dz", idx, got["dz"][idx], fd(mz)))
+    keys = {"ddelta": "delta", "ddelta_bias": "delta_bias", "dA": "A", "dB": "B", "dC": "C", "dD": "D"}
+    for k in range(ndir):
+        for gname, pname in keys.items():
+            for idx in pick(dirs[k][pname].shape, 4):
+                def mp(e, k=k, pname=pname, idx=idx):
+                    nd = [dict(p) for p in dirs]
+                    arr = nd[k][pname].copy()
+                    arr[idx] += e
+                    nd[k][pname] = arr
+                    return u, z, g, nd
+                checks.append((f"dir{k}.{gname}", idx, got["dirs"][k][gname][idx], fd(mp)))
+    for name, idx, val, ref in checks:
+        assert abs(val - ref) <= 1e-6 * (1.0 + abs(ref)), (name, idx, val, ref)
+
+
+# --- G2: reverse-mode differentiation by PyTorch through a plain recurrence ---------------------
+
+def _torch_forward(u, z, dirs, softplus, reverse_single):
+    """Token-by-token fp64 recurrence in torch ops (the forward definition)."""
+    b, d, L = u.shape
+    y = torch.zeros_like(u)
+    for k, p in enumerate(dirs):
+        rev = reverse_single if len(dirs) == 1 else (k == 1)
+        x = p["delta"] + p["delta_bias"][None, :, None]
+        dt = torch.nn.functional.softplus(x) if softplus else x
+        h = torch.zeros(b, d, p["A"].shape[1], dtype=torch.float64)
+        ys = [None] * L
+        for s in range(L):
+            t = L - 1 - s if rev else s
+            a = torch.exp(dt[:, :, t, None] * p["A"][None])
+            h = a * h + (dt[:, :, t] * u[:, :, t])[..., None] * p["B"][:, None, :, t]
+            ys[t] = (h * p["C"][:, None, :, t]).sum(-1) + p["D"][None] * u[:, :, t]
+        y = y + torch.stack(ys, -1)
+    return y * torch.nn.functional.silu(z) if z is not None else y
+
+
+@pytest.mark.parametrize("ndir,reverse", [(1, False), (1, True), (2, False)])
+def test_g2_gradients_match_autograd(ndir, reverse):
+    b, d, L = 2, 4, 13
+    u, z, g, dirs = _inputs(400 + 10 * ndir + reverse, b, d, L, ndir)
+    got = oracle.sscan_bwd(u, z, g, dirs, reverse=reverse)
+    T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    ut, zt = T(u), T(z)
+    dts = [{k: T(v) for k, v in p.items()} for p in dirs]
+    out = _torch_forward(ut, zt, dts, True, reverse)
+    (out * torch.tensor(g)).sum().backward()
+    np.testing.assert_allclose(got["du"], ut.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["dz"], zt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    keys = {"ddelta": "delta", "ddelta_bias": "delta_bias", "dA": "A", "dB": "B", "dC": "C", "dD": "D"}
+    for k in range(ndir):
+        for gname, pname in keys.items():
+            ref = dts[k][pname].grad.numpy()
+            np.testing.assert_allclose(got["dirs"][k][gname], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max(),
+                                       err_msg=f"dir{k}.{gname}")
+
+
+# --- G3: reverse direction = flip of the forward direction (Reproducing Vision Mamba page,
+#         section 3.2) --------------------------------------------------------------------------
+
+def test_g3_reverse_gradients_are_flipped_forward_gradients():
+    b, d, L = 2, 3, 11
+    u, z, g, dirs = _inputs(500, b, d, L, 1)
+    p = dirs[0]
+    rev = oracle.sscan_bwd(u, z, g, [p], reverse=True)
+    fl = lambda a: np.ascontiguousarray(a[..., ::-1])
+    pf = dict(p, delta=fl(p["delta"]), B=fl(p["B"]), C=fl(p["C"]))
+    fwd = oracle.sscan_bwd(fl(u), fl(z), fl(g), [pf])
+    np.testing.assert_allclose(rev["du"], fl(fwd["du"]), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(rev["dz"], fl(fwd["dz"]), rtol=1e-12, atol=1e-13)
+    for name in ("ddelta", "dB", "dC"):
+        np.testing.assert_allclose(rev["dirs"][0][name], fl(fwd["dirs"][0][name]), rtol=1e-12, atol=1e-13)
+    for name in ("ddelta_bias", "dA", "dD"):
+        np.testing.assert_allclose(rev["dirs"][0][name], fwd["dirs"][0][name], rtol=1e-12, atol=1e-13)
+
+
+def test_optional_inputs_absent_and_thread_invariance():
+    b, d, L = 3, 5, 7
+    u, z, g, dirs = _inputs(600, b, d, L, 1)
+    p = dict(dirs[0])
+    p.pop("D")
+    p.pop("delta_bias")
+    one = oracle.sscan_bwd(u, None, g, [p], nthreads=1)
+    many = oracle.sscan_bwd(u, None, g, [p], nthreads=4)
+    assert one["dz"] is None and one["dirs"][0]["dD"] is None and one["dirs"][0]["ddelta_bias"] is None
+    for k in ("ddelta", "dA", "dB", "dC"):
+        np.testing.assert_allclose(one["dirs"][0][k], many["dirs"][0][k], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(one["du"], many["du"], rtol=1e-13, atol=1e-14)
