@@ -131,6 +131,51 @@ SSCAN_API int sscan_step(float* state, const void* u, const void* delta, const f
                const void* z, void* y, int64_t batch, int64_t dim, int64_t dstate, void* stream,
                int io_dtype, int bc_dtype);
 
+/* Gradients of one direction's parameters (all device pointers, written by the
+ * backward entry points). */
+typedef struct sscan_dir_grads {
+  void* ddelta;         /* [batch, dim, len] io_dtype, required (when it has elements) */
+  float* ddelta_bias;   /* [dim], optional (NULL = not computed) */
+  float* dA;            /* [dim, dstate], required (when it has elements) */
+  void* dB;             /* [batch, dstate, len] bc_dtype, required (when it has elements) */
+  void* dC;             /* [batch, dstate, len] bc_dtype, required (when it has elements) */
+  float* dD;            /* [dim], optional (NULL = not computed) */
+} sscan_dir_grads;
+
+/* Backward pass of sscan_fwd (training: Reproducing Vision Mamba page, section 1.3,
+ * hand-written gradients of the scan; Hand-written simplified Mamba2 page, section
+ * 5.1, a custom backward that recomputes the forward states instead of storing
+ * them).  Given dout = dLoss/dout [batch, dim, len] io_dtype for the output of
+ * sscan_fwd with the same inputs, writes
+ *   du [batch, dim, len] io_dtype (required), dz (required when z is given, else
+ *   ignored), and grads->ddelta, ddelta_bias, dA, dB, dC, dD,
+ * the exact gradients of sum(dout * out) up to float32 rounding (bf16 outputs
+ * round to nearest even).  The forward states are recomputed in 32-token windows;
+ * nothing from the forward call is needed.  Results are bitwise reproducible (no
+ * atomics: every sum runs in a fixed order).  Workspace: sscan_bwd_workspace_bytes
+ * (..., 0) bytes, 16-byte aligned (a few bytes per element: window entry states,
+ * adjoints and partial sums).  Outputs must not overlap each other, any input or
+ * the workspace; inputs may overlap each other.  An empty call (batch, dim or len
+ * 0) writes zeros to the parameter gradients that have elements. */
+SSCAN_API int sscan_bwd(const void* u, const void* delta, const float* delta_bias, int softplus,
+              const float* A, const void* B, const void* C, const float* D,
+              const void* z, const void* dout, void* du, void* dz, const sscan_dir_grads* grads,
+              int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse, void* stream,
+              int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+
+/* Backward pass of sscan_bidir: du and dz of the shared u and z, and each
+ * direction's parameter gradients in its own sscan_dir_grads (when both directions
+ * read one delta tensor, its gradient is gfwd->ddelta + grev->ddelta).
+ * Workspace: sscan_bwd_workspace_bytes(..., 1). */
+SSCAN_API int sscan_bidir_bwd(const void* u, const void* z, const void* dout, void* du, void* dz,
+                    const sscan_dir_params* fwd, const sscan_dir_params* rev,
+                    const sscan_dir_grads* gfwd, const sscan_dir_grads* grev, int softplus,
+                    int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                    int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+
+/* Bytes of device workspace a backward call needs (0 if none or invalid sizes). */
+SSCAN_API size_t sscan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir);
+
 /* Profiling variants (for timing the internal steps of a call, not needed for
  * results): the same work as sscan_fwd / sscan_bidir, and on the same stream
  * events[0] is recorded before the first kernel and events[k] after step k of
@@ -177,6 +222,18 @@ SSCAN_API int sscan_validate_step(const float* state, const void* u, const void*
                         int softplus, const float* A, const void* B, const void* C, const float* D,
                         const void* z, const void* y, int64_t batch, int64_t dim, int64_t dstate,
                         int io_dtype, int bc_dtype);
+
+SSCAN_API int sscan_validate_bwd(const void* u, const void* delta, const float* delta_bias, int softplus,
+                       const float* A, const void* B, const void* C, const float* D,
+                       const void* z, const void* dout, const void* du, const void* dz,
+                       const sscan_dir_grads* grads, int64_t batch, int64_t dim, int64_t len,
+                       int64_t dstate, int reverse, int io_dtype, int bc_dtype,
+                       const void* workspace, size_t workspace_bytes);
+SSCAN_API int sscan_validate_bidir_bwd(const void* u, const void* z, const void* dout, const void* du,
+                             const void* dz, const sscan_dir_params* fwd, const sscan_dir_params* rev,
+                             const sscan_dir_grads* gfwd, const sscan_dir_grads* grev, int softplus,
+                             int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                             int io_dtype, int bc_dtype, const void* workspace, size_t workspace_bytes);
 
 /* Bytes of device workspace a call with these sizes needs (0 if none); bidir != 0
  * for sscan_bidir.  Returns 0 for invalid sizes (the call itself reports them). */

@@ -1,0 +1,533 @@
+// sscan_bwd.hip -- gfx950 kernels of the selective scan's backward pass.
+//
+// Gradients of sum(dout * out) for out = (sum over directions of the scan + D u) *
+// silu(z), with respect to u, z and each direction's delta, delta_bias, A, B, C, D.
+// Training differentiates the scan by hand and recomputes the forward states
+// rather than storing them (Reproducing Vision Mamba page, section 1.3; Hand-written
+// simplified Mamba2 page, section 5.1).  Reverse-mode differentiation of
+//   h_t = a_t h_{t-1} + dt_t B_t u_t,  a_t = exp(dt_t A),  y_t = C_t h_t + D u_t
+// gives, with the adjoint lambda_t = dLoss/dh_t travelling against the scan,
+//   lambda_t = C_t dy_t + mu_t,  mu_{t-1} = a_t lambda_t,  dy_t = dout_t silu(z_t),
+// dC_t += dy_t h_t, dB_t += lambda_t dt_t u_t, du_t += D dy_t + sum_n lambda dt B,
+// d(dt_t) = sum_n lambda (B u_t + A a_t h_{t-1}), dA += lambda dt a_t h_{t-1},
+// ddelta = d(dt) softplus'(delta + bias), dz = dout y silu'(z).
+//
+// Work is cut into 32-token windows.  The state entering every window comes from
+// the forward segment aggregates and carry chain (the forward pass's kernels with
+// 32-token segments); the adjoint entering every window from the other side comes
+// from the same two steps run against the scan order (adjoint aggregates: mu from
+// zero across each window, then the carry chain flipped).  The window pass then
+// needs, for every token, the state before it while the adjoint walks backwards:
+// one lane per (channel, state) -- four channels x 16 states per wavefront -- keeps
+// the window's 32 states of its (channel, state) in registers, recomputed forward
+// from the window's entry state, and walks back through them.  Sums over the 16
+// states of a channel use DPP within a 16-lane row.  A wavefront holds one
+// (batch, window) and loops over channel groups, so the sums over channels that dB
+// and dC need stay in registers (a sum per token and state, no atomics); sums over
+// tokens and batch rows (dA, dD, delta_bias) go through per-window partials and a
+// fixed-order reduction, so results are bitwise reproducible.
+#include "sscan_device.h"
+
+namespace sscan {
+namespace {
+
+constexpr int kWin = 32;           // tokens per backward window
+constexpr int kGroup = 4;          // channels per wavefront in the window pass
+constexpr int kPartRows = kDState + 2;  // per-window partials: dA[16], dD, delta_bias
+
+// per-token, per-channel values shared through LDS in the window pass
+enum TokQ : int { QDT, QDTU, QDY, QU, QSIG, QDZ, QDUSKIP, QYSKIP, kTokQ };
+enum OutQ : int { ODU, ODDT, OY, kOutQ };
+
+// Output handling of the window pass.
+enum BwdOut : int {
+  kSingle = 0,  // one direction: du, dz final
+  kFirst = 1,   // first of two directions: du and y kept in fp32 scratch
+  kSecond = 2,  // second of two: adds the first direction's du and y, writes du, dz
+};
+
+__device__ __forceinline__ float sigmoid_f32(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
+
+// Sum over the 16 lanes of a DPP row (quad xor 1, quad xor 2, row rotate 4, 8);
+// every lane of the row receives the sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x124>(v);  // row_ror:4
+  v += dpp_mov<0x128>(v);  // row_ror:8
+  return v;
+}
+
+__device__ __forceinline__ size_t part_index(int dir, int64_t b, int64_t k, int r, int64_t d, int64_t batch,
+                                             int64_t dim, int64_t nwin) {
+  return ((((size_t)dir * batch + b) * nwin + k) * kPartRows + r) * dim + d;
+}
+
+__device__ __forceinline__ size_t pbc_index(int j, int dir, int64_t b, int which, int n, int64_t t, int ndir,
+                                            int64_t batch, int64_t len) {
+  return (((((size_t)j * ndir + dir) * batch + b) * 2 + which) * kDState + n) * len + t;
+}
+
+// Adjoint aggregates: for every window except the last one the adjoint reaches,
+// mu from zero carried across the window against the scan order (H), and the sum
+// of its step sizes (S).  Same layout as the forward aggregates.  a.u is dout.
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
+__global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void bwd_adjoint_aggregate_kernel(
+    ScanArgs a, int64_t seg_len, int64_t nseg, const float* __restrict__ bc, float* __restrict__ agg, int vec) {
+  const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
+  const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
+  const int dir = blockIdx.y;
+  const int reverse = a.ndir == 2 ? dir : a.reverse;
+  if (reverse ? s.seg == nseg - 1 : s.seg == 0) return;
+  Lane<IO_BF16, SOFTPLUS, HAS_Z> L;
+  init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
+  const int64_t t0 = s.seg * seg_len;
+  const int64_t t1 = min64(a.len, t0 + seg_len);
+  if (reverse) {
+    L.template scan<false, kAdjoint>(t0, t1);
+  } else {
+    L.template scan<true, kAdjoint>(t0, t1);
+  }
+  if (!L.active) return;
+  const int64_t d = s.g * kLanes + threadIdx.x;
+#pragma unroll
+  for (int n = 0; n < kDState; ++n) agg[agg_index(dir, s.b, s.seg, n, d, a.batch, a.dim, nseg)] = L.h[n];
+  agg[agg_index(dir, s.b, s.seg, kDState, d, a.batch, a.dim, nseg)] = L.sum_dt;
+}
+
+// One channel group's per-token inputs for one lane: two consecutive tokens of one
+// channel (lane >> 4) in the window.
+template <bool IO_BF16, bool HAS_Z>
+struct TokIn {
+  float u[2], draw[2], z[2], g[2];
+  float bias, D;
+};
+
+template <bool IO_BF16, bool HAS_Z>
+__device__ __forceinline__ void load_tok(TokIn<IO_BF16, HAS_Z>& r, const BwdArgs& a, const DirArgs& pd, int64_t b,
+                                         int64_t g, int64_t t0, int wl) {
+  using IO = Io<IO_BF16>;
+  using T = typename IO::T;
+  const int cc = threadIdx.x >> 4, i0 = (threadIdx.x & 15) * 2;
+  const int64_t d = min64(g * kGroup + cc, a.fwd.dim - 1);
+  const int64_t row = (b * a.fwd.dim + d) * a.fwd.len + t0;
+  r.bias = pd.delta_bias ? pd.delta_bias[d] : 0.0f;
+  r.D = pd.D ? pd.D[d] : 0.0f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = i0 + e < wl ? i0 + e : wl - 1;  // a valid token for the ragged tail
+    r.u[e] = IO::load(static_cast<const T*>(a.fwd.u), row + i);
+    r.draw[e] = IO::load(static_cast<const T*>(pd.delta), row + i);
+    r.g[e] = IO::load(static_cast<const T*>(a.dout), row + i);
+    r.z[e] = HAS_Z ? IO::load(static_cast<const T*>(a.fwd.z), row + i) : 0.0f;
+  }
+}
+
+// The window pass for one direction.  Grid: batch * nwin * csplit one-wave blocks;
+// block j of a window covers channel groups [j*gps, (j+1)*gps).
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, bool REV, int OUT>
+__global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, int64_t nwin, int csplit, int64_t gps,
+                                                           const float* __restrict__ bc,
+                                                           const float* __restrict__ hin,
+                                                           const float* __restrict__ muin,
+                                                           float* __restrict__ part, float* __restrict__ pbc,
+                                                           float* __restrict__ acc_du, float* __restrict__ acc_y) {
+  using IO = Io<IO_BF16>;
+  using T = typename IO::T;
+  __shared__ float sBC[kWin][kBC];
+  __shared__ float sTok[kTokQ][kWin][kGroup];
+  __shared__ float sOut[kOutQ][kWin][kGroup];
+  const ScanArgs& f = a.fwd;
+  const int lane = threadIdx.x;
+  const int c = lane >> 4, n = lane & 15;
+  int64_t blk = blockIdx.x;
+  const int j = int(blk % csplit);
+  blk /= csplit;
+  const int64_t k = blk % nwin;
+  const int64_t b = blk / nwin;
+  const int64_t t0 = k * kWin;
+  const int wl = int(min64(kWin, f.len - t0));
+  const DirArgs pd = dir ? f.dir[1] : f.dir[0];
+  const DirGrads gd = dir ? a.grads[1] : a.grads[0];
+  const int64_t ngroups = (f.dim + kGroup - 1) / kGroup;
+  const int64_t g_begin = j * gps, g_end = min64(ngroups, g_begin + gps);
+
+  const float* bcw = bc + (((size_t)dir * f.batch + b) * f.len + t0) * kBC;
+  for (int e = lane; e < wl * kBC; e += kLanes) sBC[e / kBC][e % kBC] = bcw[e];
+
+  float accB[kWin], accC[kWin];
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) accB[i] = accC[i] = 0.0f;
+
+  // software pipeline: the next group's inputs are in flight while this one runs
+  TokIn<IO_BF16, HAS_Z> nx;
+  float nx_A = 0.0f, nx_h = 0.0f, nx_mu = 0.0f;
+  auto prefetch = [&](int64_t g) {
+    load_tok(nx, a, pd, b, g, t0, wl);
+    const int64_t d = min64(g * kGroup + c, f.dim - 1);
+    nx_A = pd.A[d * kDState + n];
+    if (nwin > 1) {
+      nx_h = hin[hin_index(dir, b, k, n, d, f.batch, f.dim, nwin)];
+      nx_mu = muin[hin_index(dir, b, k, n, d, f.batch, f.dim, nwin)];
+    }
+  };
+  if (g_begin < g_end) prefetch(g_begin);
+
+  for (int64_t g = g_begin; g < g_end; ++g) {
+    const TokIn<IO_BF16, HAS_Z> cur = nx;
+    const float A = nx_A, h_in = nx_h, mu_in = nx_mu;
+    __syncthreads();  // the previous group is done with the LDS buffers (and sBC is written)
+    if (g + 1 < g_end) prefetch(g + 1);
+
+    // 1. per-token values of the four channels (two tokens per lane)
+    float dD_row;
+    {
+      const int cc = lane >> 4, i0 = (lane & 15) * 2;
+      const bool act = g * kGroup + cc < f.dim;
+      float dDp = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = i0 + e;
+        const float uu = act ? cur.u[e] : 0.0f;
+        const float x = cur.draw[e] + cur.bias;
+        const float dt = SOFTPLUS ? softplus_f32(x) : x;
+        const float sig = SOFTPLUS ? sigmoid_f32(x) : 1.0f;
+        float dy = cur.g[e], qz = 0.0f;
+        if (HAS_Z) {
+          const float zv = cur.z[e];
+          const float sz = sigmoid_f32(zv);
+          dy = cur.g[e] * (zv * sz);
+          qz = cur.g[e] * (sz * fmaf(zv, 1.0f - sz, 1.0f));
+        }
+        if (!act) dy = 0.0f;
+        if (i < wl) {
+          sTok[QDT][i][cc] = dt;
+          sTok[QDTU][i][cc] = dt * uu;
+          sTok[QDY][i][cc] = dy;
+          sTok[QU][i][cc] = uu;
+          sTok[QSIG][i][cc] = sig;
+          sTok[QDZ][i][cc] = qz;
+          sTok[QDUSKIP][i][cc] = cur.D * dy;
+          sTok[QYSKIP][i][cc] = cur.D * uu;
+          dDp = fmaf(dy, uu, dDp);
+        }
+      }
+      dD_row = row_sum16(dDp);
+    }
+    __syncthreads();
+
+    // 2. forward sweep over the window from its entry state, keeping every state
+    const float A2 = A * kLog2e;
+    float hist[kWin];
+    float h = h_in;
+#pragma unroll
+    for (int s = 0; s < kWin; ++s) {
+      const int i = REV ? kWin - 1 - s : s;
+      if (i < wl) {
+        h = fmaf(exp2_hw(sTok[QDT][i][c] * A2), h, sTok[QDTU][i][c] * sBC[i][n]);
+        hist[i] = h;
+        if (HAS_Z) {
+          const float yp = row_sum16(sBC[i][kDState + n] * h);
+          if (n == 0) sOut[OY][i][c] = yp + sTok[QYSKIP][i][c];
+        }
+      }
+    }
+
+    // 3. reverse sweep: the adjoint and the gradient terms of every token
+    float mu = mu_in, dA_acc = 0.0f;
+#pragma unroll
+    for (int s = kWin - 1; s >= 0; --s) {
+      const int i = REV ? kWin - 1 - s : s;
+      if (i < wl) {
+        const float dt = sTok[QDT][i][c];
+        const float dy = sTok[QDY][i][c];
+        const float Bn = sBC[i][n];
+        const float lam = fmaf(sBC[i][kDState + n], dy, mu);
+        const float at = exp2_hw(dt * A2);
+        // the state before token i in scan order (the entry state for the first)
+        float hprev;
+        if (!REV) {
+          hprev = i == 0 ? h_in : hist[i > 0 ? i - 1 : 0];
+        } else {
+          hprev = i == wl - 1 ? h_in : hist[i + 1 < kWin ? i + 1 : kWin - 1];
+        }
+        const float w = lam * at * hprev;
+        dA_acc = fmaf(w, dt, dA_acc);
+        accB[i] = fmaf(lam, sTok[QDTU][i][c], accB[i]);
+        accC[i] = fmaf(dy, hist[i], accC[i]);
+        const float lB = lam * Bn;
+        const float pdu = row_sum16(lB * dt);
+        const float pddt = row_sum16(fmaf(lB, sTok[QU][i][c], A * w));
+        if (n == 0) {
+          sOut[ODU][i][c] = pdu;
+          sOut[ODDT][i][c] = pddt;
+        }
+        mu = at * lam;
+      }
+    }
+    {
+      const int64_t d = g * kGroup + c;
+      if (d < f.dim) part[part_index(dir, b, k, n, d, f.batch, f.dim, nwin)] = dA_acc;
+    }
+    __syncthreads();
+
+    // 4. per-token outputs (same two tokens per lane as step 1)
+    {
+      const int cc = lane >> 4, i0 = (lane & 15) * 2;
+      const int64_t d = g * kGroup + cc;
+      const bool act = d < f.dim;
+      const int64_t row = (b * f.dim + (act ? d : 0)) * f.len + t0;
+      float dbp = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = i0 + e;
+        if (i < wl) {
+          const float du = sOut[ODU][i][cc] + sTok[QDUSKIP][i][cc];
+          const float ddl = sOut[ODDT][i][cc] * sTok[QSIG][i][cc];
+          dbp += ddl;
+          if (act) {
+            IO::store(static_cast<T*>(gd.ddelta), row + i, ddl);
+            if (OUT == kSingle) {
+              IO::store(static_cast<T*>(a.du), row + i, du);
+              if (HAS_Z) IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * sOut[OY][i][cc]);
+            } else if (OUT == kFirst) {
+              acc_du[row + i] = du;
+              if (HAS_Z) acc_y[row + i] = sOut[OY][i][cc];
+            } else {
+              IO::store(static_cast<T*>(a.du), row + i, du + acc_du[row + i]);
+              if (HAS_Z)
+                IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (sOut[OY][i][cc] + acc_y[row + i]));
+            }
+          }
+        }
+      }
+      dbp = row_sum16(dbp);
+      if ((lane & 15) == 0 && act) {
+        part[part_index(dir, b, k, kDState, d, f.batch, f.dim, nwin)] = dD_row;
+        part[part_index(dir, b, k, kDState + 1, d, f.batch, f.dim, nwin)] = dbp;
+      }
+    }
+  }
+
+  // dB and dC of this window over this block's channels: sum the four channel rows
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {
+    accB[i] += __shfl_xor(accB[i], 16);
+    accB[i] += __shfl_xor(accB[i], 32);
+    accC[i] += __shfl_xor(accC[i], 16);
+    accC[i] += __shfl_xor(accC[i], 32);
+  }
+  if (c == 0) {
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) {
+      if (i < wl) {
+        pbc[pbc_index(j, dir, b, 0, n, t0 + i, f.ndir, f.batch, f.len)] = accB[i];
+        pbc[pbc_index(j, dir, b, 1, n, t0 + i, f.ndir, f.batch, f.len)] = accC[i];
+      }
+    }
+  }
+}
+
+// dA, dD and delta_bias: per-window partials summed in window order.
+__global__ __launch_bounds__(256) void bwd_reduce_params_kernel(BwdArgs a, int64_t nwin,
+                                                                const float* __restrict__ part) {
+  const ScanArgs& f = a.fwd;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(f.ndir) * kPartRows * f.dim) return;
+  const int64_t d = i % f.dim;
+  const int r = int((i / f.dim) % kPartRows);
+  const int dir = int(i / (f.dim * kPartRows));
+  // thousands of window partials: accumulate in double so the sum adds no error of
+  // its own (the partials carry float32 rounding only)
+  double s = 0.0;
+  for (int64_t b = 0; b < f.batch; ++b)
+    for (int64_t k = 0; k < nwin; ++k) s += part[part_index(dir, b, k, r, d, f.batch, f.dim, nwin)];
+  const DirGrads gd = dir ? a.grads[1] : a.grads[0];
+  if (r < kDState) {
+    gd.dA[d * kDState + r] = float(s);
+  } else if (r == kDState) {
+    if (gd.dD) gd.dD[d] = float(s);
+  } else if (gd.ddelta_bias) {
+    gd.ddelta_bias[d] = float(s);
+  }
+}
+
+// dB and dC: the channel splits' partials summed in split order, stored in B/C's dtype.
+template <bool BC_BF16>
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdArgs a, int csplit, const float* __restrict__ pbc) {
+  const ScanArgs& f = a.fwd;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(f.ndir) * f.batch * 2 * kDState * f.len) return;
+  const int64_t t = i % f.len;
+  int64_t r = i / f.len;
+  const int n = int(r % kDState);
+  r /= kDState;
+  const int which = int(r % 2);
+  r /= 2;
+  const int64_t b = r % f.batch;
+  const int dir = int(r / f.batch);
+  double s = 0.0;
+  for (int j = 0; j < csplit; ++j) s += pbc[pbc_index(j, dir, b, which, n, t, f.ndir, f.batch, f.len)];
+  const DirGrads gd = dir ? a.grads[1] : a.grads[0];
+  void* out = which ? gd.dC : gd.dB;
+  Io<BC_BF16>::store(static_cast<typename Io<BC_BF16>::T*>(out), (b * kDState + n) * f.len + t, float(s));
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(void* p, int64_t bytes) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < bytes) static_cast<unsigned char*>(p)[i] = 0;
+}
+
+bool aligned16_b(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
+hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStream_t stream) {
+  const ScanArgs& f = a.fwd;
+  const int64_t ngroups = (f.dim + kLanes - 1) / kLanes;
+  float* bc = w + p.off_bc;
+  float* agg = w + p.off_agg;
+  float* hin = w + p.off_hin;
+  float* agga = w + p.off_agga;
+  float* muin = w + p.off_muin;
+  float* part = w + p.off_part;
+  float* pbc = w + p.off_pbc;
+  float* acc_du = w + p.off_acc;
+  float* acc_y = acc_du + (p.off_acc ? size_t(f.batch) * f.dim * f.len : 0);
+
+  const int64_t bc_blocks = int64_t(f.ndir) * f.batch * ((f.len + 63) / 64);
+  if (f.bc_bf16) {
+    hipLaunchKernelGGL(stage_bc_kernel<true>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, f, bc);
+  } else {
+    hipLaunchKernelGGL(stage_bc_kernel<false>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, f, bc);
+  }
+  if (p.nwin > 1) {
+    const size_t esz = IO_BF16 ? 2 : 4;
+    bool vec = (size_t(f.len) * esz) % 16 == 0 && aligned16_b(f.u) && aligned16_b(a.dout) &&
+               (!f.z || aligned16_b(f.z));
+    for (int k = 0; k < f.ndir; ++k) vec = vec && aligned16_b(f.dir[k].delta);
+    const int64_t nblocks = f.batch * p.nwin * ngroups;
+    const int64_t carry_blocks = int64_t(f.ndir) * f.batch * kDState * ngroups;
+    const dim3 carry_block(kLanes * carry_parts(p.nwin));
+    // states entering every window
+    hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS>), dim3(unsigned(nblocks), unsigned(f.ndir)),
+                       dim3(kLanes), 0, stream, f, int64_t(kWin), p.nwin, static_cast<const float*>(bc), agg,
+                       int(vec));
+    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nwin,
+                       static_cast<const float*>(agg), hin, 0);
+    // adjoints entering every window from the other side
+    ScanArgs adj = f;
+    adj.u = a.dout;
+    hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<IO_BF16, SOFTPLUS, HAS_Z>),
+                       dim3(unsigned(nblocks), unsigned(f.ndir)), dim3(kLanes), 0, stream, adj, int64_t(kWin),
+                       p.nwin, static_cast<const float*>(bc), agga, int(vec));
+    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nwin,
+                       static_cast<const float*>(agga), muin, 1);
+  }
+  const dim3 wgrid(unsigned(f.batch * p.nwin * p.csplit));
+  const int64_t nw = p.nwin;
+  if (f.ndir == 1) {
+    if (f.reverse) {
+      hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSingle>), wgrid, dim3(kLanes), 0, stream,
+                         a, 0, nw, p.csplit, p.gps, bc, hin, muin, part, pbc, acc_du, acc_y);
+    } else {
+      hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, false, kSingle>), wgrid, dim3(kLanes), 0,
+                         stream, a, 0, nw, p.csplit, p.gps, bc, hin, muin, part, pbc, acc_du, acc_y);
+    }
+  } else {
+    hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, false, kFirst>), wgrid, dim3(kLanes), 0, stream, a,
+                       0, nw, p.csplit, p.gps, bc, hin, muin, part, pbc, acc_du, acc_y);
+    hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSecond>), wgrid, dim3(kLanes), 0, stream,
+                       a, 1, nw, p.csplit, p.gps, bc, hin, muin, part, pbc, acc_du, acc_y);
+  }
+  const int64_t np = int64_t(f.ndir) * kPartRows * f.dim;
+  hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned((np + 255) / 256)), dim3(256), 0, stream, a, p.nwin,
+                     static_cast<const float*>(part));
+  const int64_t nb = int64_t(f.ndir) * f.batch * 2 * kDState * f.len;
+  if (f.bc_bf16) {
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel<true>, dim3(unsigned((nb + 255) / 256)), dim3(256), 0, stream, a,
+                       p.csplit, static_cast<const float*>(pbc));
+  } else {
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel<false>, dim3(unsigned((nb + 255) / 256)), dim3(256), 0, stream, a,
+                       p.csplit, static_cast<const float*>(pbc));
+  }
+  return hipGetLastError();
+}
+
+template <bool IO_BF16>
+hipError_t launch_bwd_io(const BwdArgs& a, const BwdPlan& p, float* w, hipStream_t stream) {
+  const bool z = a.fwd.z != nullptr;
+  if (a.fwd.softplus) {
+    return z ? launch_bwd_typed<IO_BF16, true, true>(a, p, w, stream)
+             : launch_bwd_typed<IO_BF16, true, false>(a, p, w, stream);
+  }
+  return z ? launch_bwd_typed<IO_BF16, false, true>(a, p, w, stream)
+           : launch_bwd_typed<IO_BF16, false, false>(a, p, w, stream);
+}
+
+}  // namespace
+
+// Resident window-pass waves the plan aims for (about four per SIMD).
+constexpr int64_t kBwdWaveTarget = 256 * 4 * 4;
+
+BwdPlan make_bwd_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
+  BwdPlan p{};
+  p.nwin = std::max<int64_t>(1, (len + kWin - 1) / kWin);
+  const int64_t ngroups = std::max<int64_t>(1, (dim + kGroup - 1) / kGroup);
+  const int64_t base = std::max<int64_t>(1, int64_t(ndir) * batch * p.nwin);
+  int64_t split = std::min<int64_t>(ngroups, std::max<int64_t>(1, (kBwdWaveTarget + base - 1) / base));
+  p.gps = (ngroups + split - 1) / split;
+  p.csplit = int((ngroups + p.gps - 1) / p.gps);
+  auto up = [](size_t n) { return (n + 63) / 64 * 64; };
+  size_t off = 0;
+  p.off_bc = off;
+  off += up(size_t(ndir) * batch * len * kBC);
+  const size_t seg_agg = p.nwin > 1 ? up(size_t(ndir) * batch * p.nwin * (kDState + 1) * dim) : 0;
+  const size_t seg_in = p.nwin > 1 ? up(size_t(ndir) * batch * p.nwin * kDState * dim) : 0;
+  p.off_agg = off;
+  off += seg_agg;
+  p.off_hin = off;
+  off += seg_in;
+  p.off_agga = off;
+  off += seg_agg;
+  p.off_muin = off;
+  off += seg_in;
+  p.off_part = off;
+  off += up(size_t(ndir) * batch * p.nwin * kPartRows * dim);
+  p.off_pbc = off;
+  off += up(size_t(p.csplit) * ndir * batch * 2 * kDState * len);
+  p.off_acc = ndir == 2 ? off : 0;
+  if (ndir == 2) off += up(2 * size_t(batch) * dim * len);
+  p.workspace_bytes = off * sizeof(float);
+  return p;
+}
+
+hipError_t launch_bwd_zero(const BwdArgs& a, hipStream_t stream) {
+  const ScanArgs& f = a.fwd;
+  const int64_t bc_esz = f.bc_bf16 ? 2 : 4;
+  for (int k = 0; k < f.ndir; ++k) {
+    const DirGrads& g = a.grads[k];
+    const struct {
+      void* p;
+      int64_t bytes;
+    } bufs[] = {{g.dA, f.dim * kDState * 4},
+                {g.dD, g.dD ? f.dim * 4 : 0},
+                {g.ddelta_bias, g.ddelta_bias ? f.dim * 4 : 0},
+                {g.dB, f.batch * kDState * f.len * bc_esz},
+                {g.dC, f.batch * kDState * f.len * bc_esz}};
+    for (const auto& bf : bufs)
+      if (bf.p && bf.bytes > 0)
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3(unsigned((bf.bytes + 255) / 256)), dim3(256), 0, stream, bf.p,
+                           bf.bytes);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, float* workspace, hipStream_t stream) {
+  return a.fwd.io_bf16 ? launch_bwd_io<true>(a, p, workspace, stream) : launch_bwd_io<false>(a, p, workspace, stream);
+}
+
+}  // namespace sscan

@@ -198,6 +198,108 @@ DirView view_of(const sscan_dir_params* p) {
   return DirView{p->delta, p->delta_bias, p->A, p->B, p->C, p->D};
 }
 
+// ---- backward ----------------------------------------------------------------------
+
+constexpr int kMaxRanges = 32;
+
+struct RangeSet {
+  Range r[kMaxRanges];
+  int n = 0;
+  void add(const void* p, size_t bytes) {
+    if (p && bytes) r[n++] = range_of(p, bytes);
+  }
+};
+
+// Checks a backward call; on success fills *plan and *empty.
+int validate_bwd(const void* u, const void* z, const void* dout, const void* du, const void* dz, const DirView* dirs,
+                 const sscan_dir_grads* grads, int ndir, int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                 int io_dtype, int bc_dtype, const void* workspace, size_t workspace_bytes, sscan::BwdPlan* plan,
+                 bool* empty) {
+  Sizes sz{};
+  int st = check_sizes(batch, dim, len, dstate, io_dtype, bc_dtype, &sz);
+  if (st != SSCAN_OK) return st;
+  // a gradient buffer is required whenever it has elements
+  for (int k = 0; k < ndir; ++k)
+    if ((dim > 0 && !grads[k].dA) || (sz.bc_elems > 0 && (!grads[k].dB || !grads[k].dC))) return SSCAN_ERR_NULL;
+  *empty = (batch == 0 || dim == 0 || len == 0);
+  const size_t io = sz.io_elems * sz.io_esz, bcb = sz.bc_elems * sz.bc_esz, vec = size_t(dim) * 4;
+  RangeSet in, out;
+  if (!*empty) {
+    if (!u || !dout || !du || (z && !dz)) return SSCAN_ERR_NULL;
+    for (int k = 0; k < ndir; ++k)
+      if (!dirs[k].delta || !dirs[k].A || !dirs[k].B || !dirs[k].C || !grads[k].ddelta) return SSCAN_ERR_NULL;
+    const void* io_ptrs[] = {u, z, dout, du, dz};
+    for (const void* q : io_ptrs)
+      if (!aligned(q, sz.io_esz)) return SSCAN_ERR_ALIGN;
+    in.add(u, io);
+    in.add(z, io);
+    in.add(dout, io);
+    out.add(du, io);
+    if (z) out.add(dz, io);
+  }
+  for (int k = 0; k < ndir; ++k) {
+    const DirView& p = dirs[k];
+    const sscan_dir_grads& g = grads[k];
+    if (!aligned(p.A, 4) || !aligned(p.delta_bias, 4) || !aligned(p.D, 4) || !aligned(g.dA, 4) ||
+        !aligned(g.ddelta_bias, 4) || !aligned(g.dD, 4) || !aligned(g.dB, sz.bc_esz) || !aligned(g.dC, sz.bc_esz))
+      return SSCAN_ERR_ALIGN;
+    out.add(g.dA, vec * sscan::kDState);
+    out.add(g.ddelta_bias, vec);
+    out.add(g.dD, vec);
+    out.add(g.dB, bcb);
+    out.add(g.dC, bcb);
+    if (!*empty) {
+      if (!aligned(p.delta, sz.io_esz) || !aligned(p.B, sz.bc_esz) || !aligned(p.C, sz.bc_esz) ||
+          !aligned(g.ddelta, sz.io_esz))
+        return SSCAN_ERR_ALIGN;
+      in.add(p.delta, io);
+      in.add(p.B, bcb);
+      in.add(p.C, bcb);
+      in.add(p.A, vec * sscan::kDState);
+      in.add(p.delta_bias, vec);
+      in.add(p.D, vec);
+      out.add(g.ddelta, io);
+    }
+  }
+  if (!*empty) {
+    *plan = sscan::make_bwd_plan(batch, dim, len, ndir);
+    if (!workspace || workspace_bytes < plan->workspace_bytes) return SSCAN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return SSCAN_ERR_ALIGN;
+    out.add(workspace, plan->workspace_bytes);
+  }
+  for (int i = 0; i < out.n; ++i) {
+    for (int j = 0; j < in.n; ++j)
+      if (overlap(out.r[i], in.r[j])) return SSCAN_ERR_ALIAS;
+    for (int j = i + 1; j < out.n; ++j)
+      if (overlap(out.r[i], out.r[j])) return SSCAN_ERR_ALIAS;
+  }
+  return SSCAN_OK;
+}
+
+int run_bwd(const void* u, const void* z, const void* dout, void* du, void* dz, const DirView* dirs,
+            const sscan_dir_grads* grads, int ndir, int reverse, int softplus, int64_t batch, int64_t dim,
+            int64_t len, int64_t dstate, void* stream, int io_dtype, int bc_dtype, void* workspace,
+            size_t workspace_bytes) {
+  sscan::BwdPlan plan{};
+  bool empty = false;
+  const int st = validate_bwd(u, z, dout, du, dz, dirs, grads, ndir, batch, dim, len, dstate, io_dtype, bc_dtype,
+                              workspace, workspace_bytes, &plan, &empty);
+  if (st != SSCAN_OK) return st;
+  sscan::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.fwd = make_args(u, z, nullptr, dirs, ndir, reverse, softplus, batch, dim, len, io_dtype, bc_dtype);
+  a.dout = dout;
+  a.du = du;
+  a.dz = dz;
+  for (int k = 0; k < ndir; ++k)
+    a.grads[k] = sscan::DirGrads{grads[k].ddelta, grads[k].ddelta_bias, grads[k].dA, grads[k].dB, grads[k].dC,
+                                 grads[k].dD};
+  const hipError_t e = empty ? sscan::launch_bwd_zero(a, static_cast<hipStream_t>(stream))
+                             : sscan::launch_bwd(a, plan, static_cast<float*>(workspace),
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,6 +429,64 @@ int sscan_step(float* state, const void* u, const void* delta, const float* delt
                     bc_dtype == SSCAN_BF16, batch, dim};
   const hipError_t e = sscan::launch_step(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+}
+
+int sscan_bwd(const void* u, const void* delta, const float* delta_bias, int softplus, const float* A, const void* B,
+              const void* C, const float* D, const void* z, const void* dout, void* du, void* dz,
+              const sscan_dir_grads* grads, int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse,
+              void* stream, int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes) {
+  if (!grads) return SSCAN_ERR_NULL;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  return run_bwd(u, z, dout, du, dz, &d, grads, 1, reverse, softplus, batch, dim, len, dstate, stream, io_dtype,
+                 bc_dtype, workspace, workspace_bytes);
+}
+
+int sscan_bidir_bwd(const void* u, const void* z, const void* dout, void* du, void* dz, const sscan_dir_params* fwd,
+                    const sscan_dir_params* rev, const sscan_dir_grads* gfwd, const sscan_dir_grads* grev,
+                    int softplus, int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                    int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes) {
+  if (!fwd || !rev || !gfwd || !grev) return SSCAN_ERR_NULL;
+  const DirView d[2] = {view_of(fwd), view_of(rev)};
+  const sscan_dir_grads g[2] = {*gfwd, *grev};
+  return run_bwd(u, z, dout, du, dz, d, g, 2, 0, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype,
+                 workspace, workspace_bytes);
+}
+
+int sscan_validate_bwd(const void* u, const void* delta, const float* delta_bias, int softplus, const float* A,
+                       const void* B, const void* C, const float* D, const void* z, const void* dout,
+                       const void* du, const void* dz, const sscan_dir_grads* grads, int64_t batch, int64_t dim,
+                       int64_t len, int64_t dstate, int reverse, int io_dtype, int bc_dtype, const void* workspace,
+                       size_t workspace_bytes) {
+  (void)softplus;
+  (void)reverse;
+  if (!grads) return SSCAN_ERR_NULL;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  sscan::BwdPlan plan{};
+  bool empty = false;
+  return validate_bwd(u, z, dout, du, dz, &d, grads, 1, batch, dim, len, dstate, io_dtype, bc_dtype, workspace,
+                      workspace_bytes, &plan, &empty);
+}
+
+int sscan_validate_bidir_bwd(const void* u, const void* z, const void* dout, const void* du, const void* dz,
+                             const sscan_dir_params* fwd, const sscan_dir_params* rev, const sscan_dir_grads* gfwd,
+                             const sscan_dir_grads* grev, int softplus, int64_t batch, int64_t dim, int64_t len,
+                             int64_t dstate, int io_dtype, int bc_dtype, const void* workspace,
+                             size_t workspace_bytes) {
+  (void)softplus;
+  if (!fwd || !rev || !gfwd || !grev) return SSCAN_ERR_NULL;
+  const DirView d[2] = {view_of(fwd), view_of(rev)};
+  const sscan_dir_grads g[2] = {*gfwd, *grev};
+  sscan::BwdPlan plan{};
+  bool empty = false;
+  return validate_bwd(u, z, dout, du, dz, d, g, 2, batch, dim, len, dstate, io_dtype, bc_dtype, workspace,
+                      workspace_bytes, &plan, &empty);
+}
+
+size_t sscan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir) {
+  Sizes sz{};
+  if (check_sizes(batch, dim, len, dstate, SSCAN_F32, SSCAN_F32, &sz) != SSCAN_OK) return 0;
+  if (batch == 0 || dim == 0 || len == 0) return 0;
+  return sscan::make_bwd_plan(batch, dim, len, bidir ? 2 : 1).workspace_bytes;
 }
 
 size_t sscan_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir) {

@@ -1,0 +1,568 @@
+// sscan_device.h -- device-side building blocks shared by the forward and backward
+// gfx950 kernels of the selective scan: storage-type tiles, the per-lane scan of one
+// channel (lane = channel, 16 fp32 states in registers), the B/C staging kernel,
+// the segment-aggregate kernel and the carry chain between segments.  Included by
+// sscan_kernels.hip and sscan_bwd.hip (everything here has internal linkage).
+#pragma once
+
+#include "sscan_internal.h"
+
+#include <algorithm>
+
+namespace sscan {
+namespace {
+
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBC = 2 * kDState;  // floats per token in the staged B/C buffer
+
+// Scan kernels keep about 150 live VGPRs per lane (16 states, 16 scaled A, the
+// current and next token tiles); capping them at 168 lets three waves share each
+// SIMD and stops the scheduler from hoisting many tokens' exponentials ahead at the
+// cost of occupancy.
+#define SSCAN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3, 8)))
+
+__device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = max(x, 0) + log1p(w), w = exp(-|x|) in (0, 1].  log1p(w) is
+// log(s) for s = 1 + w rounded, plus the rounding error c = w - (s - 1) scaled by
+// 1/s ~ 1 - w: log(s + c) = log(s) + c/s + O(c^2), and c (below 2^-24) times
+// the dropped w^2 term is far below the result's last bit (log1p(w) ~ w).  This
+// keeps full relative accuracy for small step sizes (1e-4 and below).
+__device__ __forceinline__ float softplus_f32(float x) {
+  const float w = exp2_hw(-fabsf(x) * kLog2e);
+  const float s = 1.0f + w;
+  const float c = w - (s - 1.0f);
+  const float lp = fmaf(log2_hw(s), kLn2, c * (1.0f - w));
+  return fmaxf(x, 0.0f) + lp;
+}
+
+__device__ __forceinline__ float silu_f32(float x) { return x * rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats to two bf16 (round to nearest even, NaN kept), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const f2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
+// Storage-type access.  A tile holds kTok consecutive tokens of one row as sixteen
+// 32-bit words (32 bf16 tokens, two per word with the earlier token in the low
+// half, or 16 f32 tokens): four 16-byte vector loads per tensor, half a 128-byte
+// L2 line.  Narrower tiles touch each line more times, far enough apart that the
+// line has left L2 in between and is fetched again.
+constexpr int kWords = 16;
+
+template <bool BF16>
+struct Io;
+template <>
+struct Io<false> {
+  using T = float;
+  static constexpr int kTok = 16;
+  static __device__ __forceinline__ float load(const T* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = v; }
+  static __device__ __forceinline__ float get(const uint32_t (&w)[kWords], int j) { return __uint_as_float(w[j]); }
+  static __device__ __forceinline__ void load_elems(uint32_t (&w)[kWords], const T* row, int64_t t) {
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) w[j] = __float_as_uint(row[t + j]);
+  }
+  static __device__ __forceinline__ void pack(uint32_t (&w)[kWords], const float (&y)[kTok]) {
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) w[j] = __float_as_uint(y[j]);
+  }
+  static __device__ __forceinline__ void store_elems(T* row, int64_t t, const uint32_t (&w)[kWords]) {
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) row[t + j] = __uint_as_float(w[j]);
+  }
+};
+template <>
+struct Io<true> {
+  using T = uint16_t;
+  static constexpr int kTok = 32;
+  static __device__ __forceinline__ float load(const T* p, int64_t i) { return __uint_as_float(uint32_t(p[i]) << 16); }
+  static __device__ __forceinline__ void store(T* p, int64_t i, float v) {
+    p[i] = uint16_t(pack_bf16x2(v, 0.0f) & 0xffffu);
+  }
+  static __device__ __forceinline__ float get(const uint32_t (&w)[kWords], int j) {
+    return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+  }
+  static __device__ __forceinline__ void load_elems(uint32_t (&w)[kWords], const T* row, int64_t t) {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = uint32_t(row[t + 2 * i]) | (uint32_t(row[t + 2 * i + 1]) << 16);
+  }
+  static __device__ __forceinline__ void pack(uint32_t (&w)[kWords], const float (&y)[kTok]) {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+  }
+  static __device__ __forceinline__ void store_elems(T* row, int64_t t, const uint32_t (&w)[kWords]) {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) {
+      row[t + 2 * i] = uint16_t(w[i] & 0xffffu);
+      row[t + 2 * i + 1] = uint16_t(w[i] >> 16);
+    }
+  }
+};
+
+// Tiles start at multiples of kTok, so with 16-byte aligned rows ("vec") each tile
+// is two aligned 16-byte words per lane.
+template <bool BF16>
+__device__ __forceinline__ void load_tile(uint32_t (&w)[kWords], const typename Io<BF16>::T* row, int64_t t,
+                                          bool vec) {
+  if (vec) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + t);
+#pragma unroll
+    for (int i = 0; i < kWords / 4; ++i) {
+      const uint4 v = p[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  } else {
+    Io<BF16>::load_elems(w, row, t);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_tile(typename Io<BF16>::T* row, int64_t t, const float (&y)[Io<BF16>::kTok],
+                                           bool vec) {
+  uint32_t w[kWords];
+  Io<BF16>::pack(w, y);
+  if (vec) {
+    uint4* p = reinterpret_cast<uint4*>(row + t);
+#pragma unroll
+    for (int i = 0; i < kWords / 4; ++i) p[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  } else {
+    Io<BF16>::store_elems(row, t, w);
+  }
+}
+
+typedef __attribute__((address_space(3))) float lds_float;
+
+// What a scan pass does with each token's output.
+enum Mode : int {
+  kAggregate = 0,  // no readout: advance the state, sum the step sizes
+  kStore = 1,      // gate and store y
+  kPark = 2,       // park y (ungated, one direction) in the LDS meeting buffer
+  kMeet = 3,       // add the partner direction's parked y, gate, store
+  kAdjoint = 4,    // adjoint recurrence (backward pass): u holds dLoss/dout, the lane's
+                   // h holds mu and runs opposite to the direction's scan order
+};
+
+// One lane's view of one direction of one (batch, channel) row.  SOFTPLUS and
+// HAS_Z are compile-time so that a tile's 16 tokens form one straight-line block.
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
+struct Lane {
+  using IO = Io<IO_BF16>;
+  using T = typename IO::T;
+  static constexpr int kTok = IO::kTok;
+  const T* u;
+  const T* delta;
+  const T* z;     // nullable
+  T* y;
+  const float* __restrict__ bc;  // staged B/C of this (direction, batch): bc[t * 32 + ...]
+  lds_float* part;  // LDS meeting buffer (bidirectional kernel), [t - t0][64]
+  int64_t t0;     // first token of the segment (LDS buffer origin)
+  float A2[kDState];  // A * log2(e)
+  float h[kDState];
+  float bias, Dd;
+  float sum_dt;
+  int lane;
+  bool vec;       // 16-byte vector access is valid for full tiles
+  bool active;    // lane maps to a real channel (stores enabled)
+
+  __device__ __forceinline__ float step_size(float draw) const {
+    const float x = draw + bias;
+    return SOFTPLUS ? softplus_f32(x) : x;
+  }
+
+  // The staged B/C of token t (wave-uniform: scalar loads into SGPRs).
+  struct BC {
+    float v[kBC];
+  };
+  template <int MODE>
+  __device__ __forceinline__ void load_bc(BC& r, int64_t t) const {
+    const float* p = bc + t * kBC;
+    // the aggregate needs only B, the adjoint only C
+    constexpr int kFirst = MODE == kAdjoint ? kDState : 0;
+    constexpr int kEnd = MODE == kAggregate ? kDState : kBC;
+#pragma unroll
+    for (int i = kFirst; i < kEnd; ++i) r.v[i] = p[i];
+  }
+
+  // Advances the state by one token; returns y (before the gate) for the output
+  // modes, nothing useful for kAggregate.
+  template <int MODE>
+  __device__ __forceinline__ float token(float uu, float draw, const BC& bct, float zv = 0.0f) {
+    const float dt = step_size(draw);
+    if (MODE == kAdjoint) {
+      // lambda = C dy + mu;  mu <- exp(dt A) lambda   (dy = dout * silu(z))
+      sum_dt += dt;
+      const float dy = HAS_Z ? uu * silu_f32(zv) : uu;
+#pragma unroll
+      for (int n = 0; n < kDState; ++n) h[n] = exp2_hw(dt * A2[n]) * fmaf(bct.v[kDState + n], dy, h[n]);
+      return 0.0f;
+    }
+    const float dtu = dt * uu;
+    if (MODE == kAggregate) {
+      sum_dt += dt;
+#pragma unroll
+      for (int n = 0; n < kDState; ++n) h[n] = fmaf(exp2_hw(dt * A2[n]), h[n], dtu * bct.v[n]);
+      return 0.0f;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int n = 0; n < kDState; ++n) {
+      h[n] = fmaf(exp2_hw(dt * A2[n]), h[n], dtu * bct.v[n]);
+      s = fmaf(bct.v[kDState + n], h[n], s);
+    }
+    return fmaf(Dd, uu, s);
+  }
+
+  __device__ __forceinline__ float gate(float yv, float zv) const { return HAS_Z ? yv * silu_f32(zv) : yv; }
+
+  // Tokens [ta, tb) in scan order (descending when REV).  ta is a multiple of
+  // kTok; tb too unless it is the end of the sequence, so only the top tile can be
+  // partial.  Full tiles are software-pipelined: the next tile's u and delta are
+  // loaded while the current one is scanned.
+  template <bool REV, int MODE>
+  __device__ void scan(int64_t ta, int64_t tb) {
+    if (tb <= ta) return;
+    const int64_t tfull = ta + (tb - ta) / kTok * kTok;
+    if (REV) {
+      for (int64_t t = tb - 1; t >= tfull; --t) partial_token<MODE>(t);
+      full_tiles<REV, MODE>(ta, tfull);
+    } else {
+      full_tiles<REV, MODE>(ta, tfull);
+      for (int64_t t = tfull; t < tb; ++t) partial_token<MODE>(t);
+    }
+  }
+
+  template <bool REV, int MODE>
+  __device__ __forceinline__ void full_tiles(int64_t ta, int64_t tb) {
+    const int64_t ntiles = (tb - ta) / kTok;
+    if (ntiles <= 0) return;
+    uint32_t cu[kWords], cd[kWords], nu[kWords], nd[kWords];
+    int64_t t = REV ? tb - kTok : ta;
+    load_tile<IO_BF16>(cu, u, t, vec);
+    load_tile<IO_BF16>(cd, delta, t, vec);
+    for (int64_t i = 0; i < ntiles; ++i) {
+      const int64_t tn = REV ? t - kTok : t + kTok;
+      if (i + 1 < ntiles) {
+        load_tile<IO_BF16>(nu, u, tn, vec);
+        load_tile<IO_BF16>(nd, delta, tn, vec);
+      }
+      tile<REV, MODE>(t, cu, cd);
+#pragma unroll
+      for (int w = 0; w < kWords; ++w) {
+        cu[w] = nu[w];
+        cd[w] = nd[w];
+      }
+      t = tn;
+    }
+  }
+
+  template <bool REV, int MODE>
+  __device__ __forceinline__ void tile(int64_t t, const uint32_t (&wu)[kWords], const uint32_t (&wd)[kWords]) {
+    constexpr bool kOut = (MODE == kStore || MODE == kMeet);
+    uint32_t wz[kWords];
+    // z is needed only for the gate at the end of the tile: its load latency hides
+    // behind the tile's tokens (the adjoint reads it at every token)
+    if ((kOut || MODE == kAdjoint) && HAS_Z) load_tile<IO_BF16>(wz, z, t, vec);
+    float yt[kTok];
+    BC cur, nxt;
+    load_bc<MODE>(cur, t + (REV ? kTok - 1 : 0));
+#pragma unroll
+    for (int jj = 0; jj < kTok; ++jj) {
+      const int j = REV ? kTok - 1 - jj : jj;
+      // prefetch the next token's B/C: its scalar-load latency hides behind this token
+      if (jj + 1 < kTok) load_bc<MODE>(nxt, t + (REV ? j - 1 : j + 1));
+      float yv = token<MODE>(IO::get(wu, j), IO::get(wd, j), cur,
+                             (MODE == kAdjoint && HAS_Z) ? IO::get(wz, j) : 0.0f);
+      // materialise this token's readout now: otherwise it is sunk towards the
+      // tile's store and all tokens' states stay live
+      if (MODE != kAggregate && MODE != kAdjoint) asm volatile("" : "+v"(yv));
+      if (MODE == kPark) {
+        part[(t + j - t0) * kLanes + lane] = yv;
+      } else if (kOut) {
+        yt[j] = yv;
+      }
+      cur = nxt;
+      // keep each token's work together: the 16 state chains of one token give
+      // enough independent instructions, and hoisting later tokens' exponentials
+      // ahead only raises register pressure
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kOut) {
+#pragma unroll
+      for (int j = 0; j < kTok; ++j) {
+        float v = yt[j];
+        if (MODE == kMeet) v += part[(t + j - t0) * kLanes + lane];
+        yt[j] = gate(v, HAS_Z ? IO::get(wz, j) : 0.0f);
+      }
+      if (active) store_tile<IO_BF16>(y, t, yt, vec);
+    }
+  }
+
+  template <int MODE>
+  __device__ __forceinline__ void partial_token(int64_t t) {
+    const float uu = IO::load(u, t);
+    BC cur;
+    load_bc<MODE>(cur, t);
+    const float yv = token<MODE>(uu, IO::load(delta, t), cur, (MODE == kAdjoint && HAS_Z) ? IO::load(z, t) : 0.0f);
+    if (MODE == kPark) {
+      part[(t - t0) * kLanes + lane] = yv;
+    } else if (MODE == kStore || MODE == kMeet) {
+      float v = (MODE == kMeet) ? yv + part[(t - t0) * kLanes + lane] : yv;
+      if (HAS_Z) v *= silu_f32(IO::load(z, t));
+      if (active) IO::store(y, t, v);
+    }
+  }
+};
+
+struct SegIndex {
+  int64_t g, seg, b;  // channel group, segment, batch
+};
+
+__device__ __forceinline__ SegIndex decode_block(int64_t blk, int64_t ngroups, int64_t nseg) {
+  SegIndex s;
+  s.g = blk % ngroups;
+  const int64_t r = blk / ngroups;
+  s.seg = r % nseg;
+  s.b = r / nseg;
+  return s;
+}
+
+__device__ __forceinline__ size_t agg_index(int dir, int64_t b, int64_t seg, int n, int64_t d, int64_t batch,
+                                            int64_t dim, int64_t nseg) {
+  return ((((size_t)dir * batch + b) * nseg + seg) * (kDState + 1) + n) * dim + d;
+}
+
+__device__ __forceinline__ size_t hin_index(int dir, int64_t b, int64_t seg, int n, int64_t d, int64_t batch,
+                                            int64_t dim, int64_t nseg) {
+  return ((((size_t)dir * batch + b) * nseg + seg) * kDState + n) * dim + d;
+}
+
+// Sets up a lane for direction `dir` of batch b, channel group g.
+template <class LaneT>
+__device__ __forceinline__ void init_lane(LaneT& L, const ScanArgs& a, int dir, int64_t b, int64_t g,
+                                          const float* bc, bool vec) {
+  using T = typename LaneT::T;
+  const int lane = threadIdx.x % kLanes;
+  const int64_t d_raw = g * kLanes + lane;
+  L.active = d_raw < a.dim;
+  const int64_t d = L.active ? d_raw : a.dim - 1;  // idle lanes shadow a valid row and store nothing
+  const DirArgs p = dir ? a.dir[1] : a.dir[0];
+  const int64_t row = (b * a.dim + d) * a.len;
+  L.u = static_cast<const T*>(a.u) + row;
+  L.delta = static_cast<const T*>(p.delta) + row;
+  L.z = a.z ? static_cast<const T*>(a.z) + row : nullptr;
+  L.y = static_cast<T*>(a.y) + row;
+  L.bc = bc + ((size_t)dir * a.batch + b) * a.len * kBC;
+  L.part = nullptr;
+  L.t0 = 0;
+#pragma unroll
+  for (int n = 0; n < kDState; ++n) L.A2[n] = p.A[d * kDState + n] * kLog2e;
+  L.bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
+  L.Dd = p.D ? p.D[d] : 0.0f;
+  L.sum_dt = 0.0f;
+  L.lane = lane;
+  L.vec = vec;
+#pragma unroll
+  for (int n = 0; n < kDState; ++n) L.h[n] = 0.0f;
+}
+
+// A lane's 16 states in the caller's [batch][dim][16] layout (64 contiguous bytes).
+__device__ __forceinline__ void load_state16(float (&h)[kDState], const float* p) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < kDState / 4; ++i) {
+    const float4 v = q[i];
+    h[4 * i] = v.x;
+    h[4 * i + 1] = v.y;
+    h[4 * i + 2] = v.z;
+    h[4 * i + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ void store_state16(float* p, const float (&h)[kDState]) {
+  float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+  for (int i = 0; i < kDState / 4; ++i) q[i] = make_float4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+}
+
+// State entering a segment: from the carry chain when the sequence is split, else
+// the caller's entry state (or zero).
+template <class LaneT>
+__device__ __forceinline__ void load_entry(LaneT& L, const ScanArgs& a, int dir, int64_t b, int64_t seg,
+                                           int64_t g, int64_t nseg, const float* hin) {
+  const int64_t d = min64(g * kLanes + threadIdx.x % kLanes, a.dim - 1);
+  if (nseg <= 1) {
+    if (a.h0) load_state16(L.h, a.h0 + (b * a.dim + d) * kDState);
+    return;
+  }
+#pragma unroll
+  for (int n = 0; n < kDState; ++n) L.h[n] = hin[hin_index(dir, b, seg, n, d, a.batch, a.dim, nseg)];
+}
+
+// Stage B and C token-major in fp32: bc[dir][b][t][0..15] = B[b][:, t],
+// bc[dir][b][t][16..31] = C[b][:, t].  One block per (direction, batch, 64 tokens).
+template <bool BC_BF16>
+__global__ __launch_bounds__(256) void stage_bc_kernel(ScanArgs a, float* __restrict__ bc) {
+  __shared__ float tile[kBC][65];
+  const int64_t ntiles = (a.len + 63) / 64;
+  const int64_t tt = blockIdx.x % ntiles;
+  const int64_t db = blockIdx.x / ntiles;  // dir * batch + b
+  const int dir = int(db / a.batch);
+  const int64_t b = db % a.batch;
+  const DirArgs p = dir ? a.dir[1] : a.dir[0];
+  const int64_t t0 = tt * 64;
+  for (int i = threadIdx.x; i < kBC * 64; i += 256) {
+    const int r = i / 64, c = i % 64;
+    const int64_t t = t0 + c;
+    float v = 0.0f;
+    if (t < a.len) {
+      const size_t idx = ((size_t)b * kDState + (r % kDState)) * a.len + t;
+      const void* src = r < kDState ? p.B : p.C;
+      v = BC_BF16 ? Io<true>::load(static_cast<const uint16_t*>(src), idx) : static_cast<const float*>(src)[idx];
+    }
+    tile[r][c] = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * kBC; i += 256) {
+    const int c = i / kBC, r = i % kBC;
+    const int64_t t = t0 + c;
+    if (t < a.len) bc[((size_t)db * a.len + t) * kBC + r] = tile[r][c];
+  }
+}
+
+// Step 1: end state (from zero) and sum of step sizes of every segment except the
+// last one in scan order.  Grid: batch * nseg * ngroups one-wave blocks;
+// blockIdx.y selects the direction.
+template <bool IO_BF16, bool SOFTPLUS>
+__global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_aggregate_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
+                                                                const float* __restrict__ bc,
+                                                                float* __restrict__ agg, int vec) {
+  const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
+  const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
+  const int dir = blockIdx.y;
+  const int reverse = a.ndir == 2 ? dir : a.reverse;
+  if (reverse ? s.seg == 0 : s.seg == nseg - 1) return;
+  Lane<IO_BF16, SOFTPLUS, false> L;
+  init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
+  const int64_t t0 = s.seg * seg_len;
+  const int64_t t1 = min64(a.len, t0 + seg_len);
+  if (reverse) {
+    L.template scan<true, kAggregate>(t0, t1);
+  } else {
+    L.template scan<false, kAggregate>(t0, t1);
+  }
+  if (!L.active) return;
+  const int64_t d = s.g * kLanes + threadIdx.x;
+#pragma unroll
+  for (int n = 0; n < kDState; ++n) agg[agg_index(dir, s.b, s.seg, n, d, a.batch, a.dim, nseg)] = L.h[n];
+  agg[agg_index(dir, s.b, s.seg, kDState, d, a.batch, a.dim, nseg)] = L.sum_dt;
+}
+
+// Step 2: the chain of segment aggregates in scan order,
+//   h_in[k+1] = exp(A sum_dt[k]) h_in[k] + H[k],   h_in[0] = h0 (or 0),
+// for every (direction, batch, state, channel).  The combine is associative, so
+// each chain is split into runs of consecutive segments, one wave per run (up to
+// kCarryParts, each run at least kCarryMinRun segments): each run is first reduced
+// on its own (its decay exponent is the sum of its sum_dt), the runs' totals are
+// chained through LDS, and each run is walked again from its entry state writing
+// h_in.  A block holds 64 channels (coalesced along d) x the runs.
+constexpr int kCarryParts = 16;
+constexpr int64_t kCarryMinRun = 8;
+
+int carry_parts(int64_t nseg) {
+  int p = 1;
+  while (p < kCarryParts && nseg / (2 * p) >= kCarryMinRun) p *= 2;
+  return p;
+}
+
+__global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanArgs a, int64_t nseg,
+                                                                       const float* __restrict__ agg,
+                                                                       float* __restrict__ hin, int flip) {
+  __shared__ float sh_s[kCarryParts][kLanes];
+  __shared__ float sh_h[kCarryParts][kLanes];
+  const int nparts = int(blockDim.x) / kLanes;
+  const int lane = threadIdx.x % kLanes;
+  const int part = threadIdx.x / kLanes;
+  const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
+  int64_t r = blockIdx.x;
+  const int64_t g = r % ngroups;
+  r /= ngroups;
+  const int n = int(r % kDState);
+  r /= kDState;
+  const int64_t b = r % a.batch;
+  const int dir = int(r / a.batch);
+  // chain order: the direction's scan order, or the opposite one (flip: the
+  // adjoint of the backward pass travels against the scan)
+  const int reverse = (a.ndir == 2 ? dir : a.reverse) ^ flip;
+  const int64_t d_raw = g * kLanes + lane;
+  const bool active = d_raw < a.dim;
+  const int64_t d = active ? d_raw : a.dim - 1;
+  const float* Adir = dir ? a.dir[1].A : a.dir[0].A;
+  const float A2 = Adir[d * kDState + n] * kLog2e;
+  const int64_t chunk = (nseg + nparts - 1) / nparts;
+  const int64_t k0 = min64(nseg, part * chunk), k1 = min64(nseg, k0 + chunk);
+  auto seg_of = [&](int64_t k) { return reverse ? nseg - 1 - k : k; };
+  // the last segment in scan order has no aggregate (nothing follows it)
+  const int64_t kagg = min64(k1, nseg - 1);
+  // a run's aggregates are loaded kBatch at a time, all loads in flight together
+  // (they do not depend on the chain); runs of up to kBatch segments are loaded once
+  constexpr int kBatch = 32;
+  float hb[kBatch], sb[kBatch];
+  auto load_batch = [&](int64_t kb) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t k = kb + i;
+      const bool has = k < kagg;
+      const int64_t seg = seg_of(has ? k : 0);  // a valid segment even when the run is empty
+      hb[i] = has ? agg[agg_index(dir, b, seg, n, d, a.batch, a.dim, nseg)] : 0.0f;
+      sb[i] = has ? agg[agg_index(dir, b, seg, kDState, d, a.batch, a.dim, nseg)] : 0.0f;
+    }
+  };
+  float S = 0.0f, H = 0.0f;
+  for (int64_t kb = k0; kb < kagg; kb += kBatch) {
+    load_batch(kb);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (kb + i < kagg) {
+        H = fmaf(exp2_hw(A2 * sb[i]), H, hb[i]);
+        S += sb[i];
+      }
+    }
+  }
+  sh_s[part][lane] = S;
+  sh_h[part][lane] = H;
+  __syncthreads();
+  float h = a.h0 ? a.h0[(b * a.dim + d) * kDState + n] : 0.0f;  // entry state of the first segment
+  for (int q = 0; q < part; ++q) h = fmaf(exp2_hw(A2 * sh_s[q][lane]), h, sh_h[q][lane]);
+  const bool reuse = kagg - k0 <= kBatch;  // the run's aggregates are still in registers
+  for (int64_t kb = k0; kb < k1; kb += kBatch) {
+    if (!reuse) load_batch(kb);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t k = kb + i;
+      if (k < k1) {
+        if (active) hin[hin_index(dir, b, seg_of(k), n, d, a.batch, a.dim, nseg)] = h;
+        if (k < kagg) h = fmaf(exp2_hw(A2 * sb[i]), h, hb[i]);
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace sscan

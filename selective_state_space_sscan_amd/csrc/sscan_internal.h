@@ -59,6 +59,46 @@ struct StepArgs {
   int64_t batch, dim;
 };
 
+// Gradients of one direction (backward pass); nullable members are not computed.
+struct DirGrads {
+  void* ddelta;             // [batch][dim][len] io dtype
+  float* ddelta_bias;       // nullable, [dim]
+  float* dA;                // [dim][16]
+  void* dB;                 // [batch][16][len] bc dtype
+  void* dC;
+  float* dD;                // nullable, [dim]
+};
+
+struct BwdArgs {
+  ScanArgs fwd;             // the forward call's inputs (y, h0 and h_last unused)
+  const void* dout;         // dLoss/dout, [batch][dim][len] io dtype
+  void* du;
+  void* dz;                 // written when fwd.z is set
+  DirGrads grads[2];
+};
+
+// Backward split into 32-token windows, and its workspace (float offsets):
+//   bc   [ndir][batch][len][32]           staged B/C
+//   agg, hin [ndir][batch][nwin][17|16][dim]  forward window aggregates / entry states
+//   agga, muin                            the same for the adjoint (nwin > 1 only)
+//   part [ndir][batch][nwin][18][dim]      per-window dA[16], dD, delta_bias
+//   pbc  [csplit][ndir][batch][2][16][len] dB, dC per channel split
+//   acc  [2][batch][dim][len]              first direction's du and y (two directions)
+struct BwdPlan {
+  int64_t nwin;             // windows per row
+  int csplit;               // channel splits per window (blocks per window)
+  int64_t gps;              // 4-channel groups per split
+  size_t off_bc, off_agg, off_hin, off_agga, off_muin, off_part, off_pbc, off_acc;
+  size_t workspace_bytes;
+};
+
+BwdPlan make_bwd_plan(int64_t batch, int64_t dim, int64_t len, int ndir);
+hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, float* workspace, hipStream_t stream);
+
+// Gradients of an empty call: the parameter gradients (dA, dD, delta_bias, dB, dC)
+// that have elements are zero.
+hipError_t launch_bwd_zero(const BwdArgs& a, hipStream_t stream);
+
 // How a call is split along the sequence, and the workspace it needs (floats,
 // in this order):
 //   bc   [ndir][batch][len][32]        B_t (16 states) then C_t (16), fp32, token-major

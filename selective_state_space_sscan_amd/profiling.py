@@ -5,7 +5,7 @@ KiB the L2 read from / wrote to memory.  Both are scaled by what the same counte
 reads for a plain streaming kernel of known traffic (bench.py --copy-calibration
 negates 512 MiB: 512 MiB read, 512 MiB written): the factor is known bytes /
 counted bytes.  The summary is keyed by the
-SHA-256 of the kernel source, so a summary taken before the kernels changed is
+SHA-256 of the kernel sources, so a summary taken before the kernels changed is
 recognisably stale.
 
   python -m selective_state_space_sscan_amd.profiling FETCH_DIR WRITE_DIR OUT.json
@@ -24,7 +24,7 @@ import os
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(PKG, "csrc", "sscan_kernels.hip")
+CSRC = os.path.join(PKG, "csrc")
 COPY_BYTES = 512 << 20
 COPY_KERNEL = "neg_kernel"  # the calibration kernel (torch.neg), unique in the run
 KERNELS = {"stage_bc_kernel": "stage_bc", "scan_aggregate_kernel": "aggregate", "scan_carry_kernel": "carry",
@@ -32,8 +32,14 @@ KERNELS = {"stage_bc_kernel": "stage_bc", "scan_aggregate_kernel": "aggregate", 
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+    """SHA-256 over every kernel source file (name and contents, sorted by name)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
 
 
 def _per_dispatch(directory: str, counter: str):

@@ -36,6 +36,11 @@ class DirParams(ctypes.Structure):
                 ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p)]
 
 
+class DirGrads(ctypes.Structure):
+    _fields_ = [("ddelta", ctypes.c_void_p), ("ddelta_bias", ctypes.c_void_p), ("dA", ctypes.c_void_p),
+                ("dB", ctypes.c_void_p), ("dC", ctypes.c_void_p), ("dD", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -70,6 +75,17 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_step.restype = I
     lib.sscan_validate_step.argtypes = [V, V, V, V, I, V, V, V, V, V, V, I64, I64, I64, I, I]
     lib.sscan_validate_step.restype = I
+    DG = ctypes.POINTER(DirGrads)
+    lib.sscan_bwd.argtypes = [V, V, V, I, V, V, V, V, V, V, V, V, DG, I64, I64, I64, I64, I, V, I, I, V, SZ]
+    lib.sscan_bwd.restype = I
+    lib.sscan_bidir_bwd.argtypes = [V, V, V, V, V, DP, DP, DG, DG, I, I64, I64, I64, I64, V, I, I, V, SZ]
+    lib.sscan_bidir_bwd.restype = I
+    lib.sscan_validate_bwd.argtypes = [V, V, V, I, V, V, V, V, V, V, V, V, DG, I64, I64, I64, I64, I, I, I, V, SZ]
+    lib.sscan_validate_bwd.restype = I
+    lib.sscan_validate_bidir_bwd.argtypes = [V, V, V, V, V, DP, DP, DG, DG, I, I64, I64, I64, I64, I, I, V, SZ]
+    lib.sscan_validate_bidir_bwd.restype = I
+    lib.sscan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.sscan_bwd_workspace_bytes.restype = SZ
     lib.sscan_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.sscan_workspace_bytes.restype = SZ
     lib.sscan_strerror.argtypes = [I]
@@ -333,6 +349,87 @@ def bidir(u, z, fwd: dict, rev: dict, softplus: bool = True, out: Optional[torch
     if st != 0:
         raise SScanError(st, "sscan_bidir")
     return out
+
+
+def bwd_workspace_bytes(batch: int, dim: int, length: int, dstate: int = DSTATE, bidir: bool = False) -> int:
+    return int(load_library().sscan_bwd_workspace_bytes(batch, dim, length, dstate, int(bool(bidir))))
+
+
+def _grads_for(p: dict, u):
+    """Output tensors for one direction's gradients (shapes and dtypes of its inputs)."""
+    d = u.shape[1]
+    dev = u.device
+    g = {"ddelta": torch.empty_like(p["delta"]), "dA": torch.empty_like(p["A"]),
+         "dB": torch.empty_like(p["B"]), "dC": torch.empty_like(p["C"]),
+         "ddelta_bias": torch.empty(d, dtype=torch.float32, device=dev) if p.get("delta_bias") is not None else None,
+         "dD": torch.empty(d, dtype=torch.float32, device=dev) if p.get("D") is not None else None}
+    st = DirGrads(g["ddelta"].data_ptr(), g["ddelta_bias"].data_ptr() if g["ddelta_bias"] is not None else None,
+                  g["dA"].data_ptr(), g["dB"].data_ptr(), g["dC"].data_ptr(),
+                  g["dD"].data_ptr() if g["dD"] is not None else None)
+    return g, st
+
+
+def bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, softplus: bool = True, reverse: bool = False,
+        workspace: Optional[torch.Tensor] = None) -> dict:
+    """Backward pass of ``fwd`` (``sscan_bwd``): gradients of sum(dout * out).
+    Returns a dict with du, dz (None without z), ddelta, ddelta_bias, dA, dB, dC, dD
+    (None for an absent optional input), in the dtypes of the matching inputs."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.bwd needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or B.dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = u.shape
+    _check(u, "u", dev)
+    _check(delta, "delta", dev, u.dtype, u.shape)
+    _check(z, "z", dev, u.dtype, u.shape)
+    _check(dout, "dout", dev, u.dtype, u.shape)
+    _check(A, "A", dev, torch.float32, (d, DSTATE))
+    _check(B, "B", dev, None, (b, DSTATE, L))
+    _check(C, "C", dev, B.dtype, (b, DSTATE, L))
+    _check(D, "D", dev, torch.float32, (d,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (d,))
+    p = dict(delta=delta, A=A, B=B, C=C, D=D, delta_bias=delta_bias)
+    g, gst = _grads_for(p, u)
+    du = torch.empty_like(u)
+    dz = torch.empty_like(u) if z is not None else None
+    ws, ws_bytes = _workspace(bwd_workspace_bytes(b, d, L, DSTATE, False), dev, workspace)
+    st = lib.sscan_bwd(_ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                       _ptr(z), _ptr(dout), _ptr(du), _ptr(dz), ctypes.byref(gst), b, d, L, DSTATE, int(bool(reverse)),
+                       _stream(dev), _DT_CODE[u.dtype], _DT_CODE[B.dtype], _ptr(ws), ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_bwd")
+    return dict(g, du=du, dz=dz)
+
+
+def bidir_bwd(u, z, dout, fwd: dict, rev: dict, softplus: bool = True,
+              workspace: Optional[torch.Tensor] = None) -> dict:
+    """Backward pass of ``bidir`` (``sscan_bidir_bwd``).  Returns {"du", "dz",
+    "fwd": {...}, "rev": {...}} with each direction's gradients as in ``bwd``."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.bidir_bwd needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or fwd["B"].dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = u.shape
+    _check(u, "u", dev)
+    _check(z, "z", dev, u.dtype, u.shape)
+    _check(dout, "dout", dev, u.dtype, u.shape)
+    pf = _dir(fwd, "fwd", dev, u, fwd["B"].dtype)
+    pr = _dir(rev, "rev", dev, u, fwd["B"].dtype)
+    gf, gfs = _grads_for(fwd, u)
+    gr, grs = _grads_for(rev, u)
+    du = torch.empty_like(u)
+    dz = torch.empty_like(u) if z is not None else None
+    ws, ws_bytes = _workspace(bwd_workspace_bytes(b, d, L, DSTATE, True), dev, workspace)
+    st = lib.sscan_bidir_bwd(_ptr(u), _ptr(z), _ptr(dout), _ptr(du), _ptr(dz), ctypes.byref(pf), ctypes.byref(pr),
+                             ctypes.byref(gfs), ctypes.byref(grs), int(bool(softplus)), b, d, L, DSTATE, _stream(dev),
+                             _DT_CODE[u.dtype], _DT_CODE[fwd["B"].dtype], _ptr(ws), ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_bidir_bwd")
+    return {"du": du, "dz": dz, "fwd": gf, "rev": gr}
 
 
 def run_inputs(x, softplus: bool = True, out=None, workspace=None, events: Optional[HipEvents] = None) -> torch.Tensor:

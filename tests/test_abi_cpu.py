@@ -241,3 +241,41 @@ def test_validate_step(lib):
     st = lib.sscan_step(None, a["u"], a["delta"], a["bias"], 1, a["A"], a["B"], a["C"], a["D"], a["z"], a["y"],
                         4, 100, 16, None, 0, 0)
     assert st == ENULL
+
+
+# --- backward -------------------------------------------------------------------------------
+
+def bwd_call(lib, a, g, dout, du, dz):
+    gs = sscan.DirGrads(*g)
+    return lib.sscan_validate_bwd(a["u"], a["delta"], a["bias"], 1, a["A"], a["B"], a["C"], a["D"], a["z"], dout,
+                                  du, dz, ctypes.byref(gs), a["b"], a["d"], a["L"], 16, 0, a["io"], a["bc"], a["ws"],
+                                  a["ws_bytes"])
+
+
+def test_validate_bwd(lib):
+    f = Fake()
+    f.next = 1 << 46
+    b, d, L = 2, 64, 300
+    a = fwd_args(b, d, L)
+    io, bc = b * d * L * 4, b * 16 * L * 4
+    dout, du, dz = f(io), f(io), f(io)
+    g = [f(io), f(d * 4), f(d * 64), f(bc), f(bc), f(d * 4)]
+    ws = lib.sscan_bwd_workspace_bytes(b, d, L, 16, 0)
+    assert ws > lib.sscan_workspace_bytes(b, d, L, 16, 0)
+    a = dict(a, ws=f(ws), ws_bytes=ws)
+    assert bwd_call(lib, a, g, dout, du, dz) == OK
+    assert bwd_call(lib, a, g, dout, du, None) == ENULL            # z given: dz required
+    assert bwd_call(lib, dict(a, z=None), g, dout, du, None) == OK
+    assert bwd_call(lib, a, g, None, du, dz) == ENULL
+    assert bwd_call(lib, a, [None] + g[1:], dout, du, dz) == ENULL  # ddelta
+    assert bwd_call(lib, a, g[:2] + [None] + g[3:], dout, du, dz) == ENULL  # dA
+    assert bwd_call(lib, a, g[:1] + [None] + g[2:5] + [None], dout, du, dz) == OK  # optional grads
+    assert bwd_call(lib, a, g, dout, a["u"], dz) == EALIAS          # output over an input
+    assert bwd_call(lib, a, g, dout, du, du) == EALIAS              # two outputs
+    assert bwd_call(lib, a, g[:3] + [a["ws"] + 256] + g[4:], dout, du, dz) == EALIAS  # over the workspace
+    assert bwd_call(lib, dict(a, ws_bytes=ws - 1), g, dout, du, dz) == EWS
+    assert bwd_call(lib, a, g, dout + 2, du, dz) == EALIGN
+    # empty sequence: only the gradients with elements are needed
+    e = fwd_args(b, d, 0, u=None, delta=None, y=None)
+    assert bwd_call(lib, dict(e, ws=None, ws_bytes=0), [None, g[1], g[2], None, None, g[5]], None, None, None) == OK
+    assert bwd_call(lib, dict(e, ws=None, ws_bytes=0), [None, g[1], None, None, None, g[5]], None, None, None) == ENULL
