@@ -6,8 +6,8 @@ len 262144, dstate 16, bf16 u/delta/z/y, f32 B/C, seeded synthetic inputs alread
 resident in HBM).  One step = one sscan_fwd call (all its kernels).  Prints ONE
 JSON line on stdout.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
-                 [--copy-calibration]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
+                 [--no-cpu] [--copy-calibration]
 
 Timing: K plain calls between two HIP events give ms_per_step (for a workload
 whose data fits the 256 MB Infinity Cache, rotating over copies of the inputs so
@@ -155,6 +155,121 @@ def cpu_model() -> str:
     return "unknown"
 
 
+# Backward: per (element, state, direction) the algorithm recomputes the state (dt*A,
+# dt*u*B, state FMA: 4 flops, 1 exp), reads it out for dz (1), and walks the adjoint
+# back: lambda FMA (2), lambda*a*h_prev (2), dA FMA (2), dB FMA (2), dC FMA (2),
+# lambda*B (1), du term (1), A*w (1), d(dt) FMA (2), mu = a*lambda (1), one exp, and
+# the three sums over states for du, d(dt), y (3): 25 flops and 2 exps in
+# 21 + 2 * EXP_SLOTS = 25 VALU slots.
+BWD_FLOPS_PER_ELEM_STATE = 25.0
+BWD_SLOTS_PER_ELEM_STATE = 21.0 + 2 * EXP_SLOTS
+BWD_ALU_PEAK_TFLOPS = VALU_LANE_OPS / BWD_SLOTS_PER_ELEM_STATE * BWD_FLOPS_PER_ELEM_STATE / 1e12
+
+
+def bwd_alg_bytes(cfg) -> int:
+    """Algorithmic bytes of one backward call: u, z, dout and delta read, du, dz and
+    ddelta written, B and C read and dB, dC written per direction, A/D/bias read and
+    their gradients written per direction."""
+    io = 2 if cfg.io_dtype == "bf16" else 4
+    bc = 2 if cfg.bc_dtype == "bf16" else 4
+    per_dir = 4 * cfg.batch * cfg.dstate * cfg.len * bc + 2 * cfg.dim * (cfg.dstate + 2) * 4
+    return (4 + 3) * cfg.elems * io + cfg.ndir * per_dir
+
+
+def bench_bwd(args, torch, I, sscan, cfg, ci):
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    x = I.config_inputs(ci, 0)
+    xd = x.to(dev)
+    g = torch.from_numpy(np.random.default_rng(4242).standard_normal(tuple(x.u.shape), dtype=np.float32))
+    g = g.to(x.u.dtype).to(dev)
+    ws = torch.empty(max(1, sscan.bwd_workspace_bytes(cfg.batch, cfg.dim, cfg.len, cfg.dstate, cfg.bidir)),
+                     dtype=torch.uint8, device=dev)
+    mk = lambda p: dict(delta=xd.delta, delta_bias=p.delta_bias, A=p.A, B=p.B, C=p.C, D=p.D)
+
+    def step(events=None):
+        if cfg.ndir == 1:
+            p = xd.dirs[0]
+            return sscan.bwd(xd.u, xd.delta, p.A, p.B, p.C, g, D=p.D, z=xd.z, delta_bias=p.delta_bias,
+                             workspace=ws, events=events)
+        return sscan.bidir_bwd(xd.u, xd.z, g, mk(xd.dirs[0]), mk(xd.dirs[1]), workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    evsets = [sscan.HipEvents(sscan.BWD_PROFILE_STEPS) for _ in range(args.steps)]
+    for ev in evsets:
+        step(ev)
+    torch.cuda.synchronize()
+    kernel_ms = {k: sum(ev.step_ms()[k] for ev in evsets) / args.steps for k in sscan.BWD_PROFILE_STEPS}
+    per_call = [ev.total_ms() for ev in evsets]
+    t_win = kernel_ms["window_pass"] * 1e-3
+    flops = BWD_FLOPS_PER_ELEM_STATE * cfg.dstate * cfg.elems * cfg.ndir
+    achieved = flops / t_win / 1e12
+    nbytes = bwd_alg_bytes(cfg)
+    out = {
+        "metric": METRIC, "value": cfg.elems / (ms * 1e-3) / 1e6, "unit": "Melem/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded numpy PCG64, shapes of the pages' workloads)",
+        "config": {"workload": cfg.name, "pass": "bwd", "batch": cfg.batch, "dim": cfg.dim, "len": cfg.len,
+                   "dstate": cfg.dstate, "directions": cfg.ndir, "io_dtype": cfg.io_dtype, "bc_dtype": cfg.bc_dtype},
+        "roofline": {"bound": "alu", "kernel": "window_pass", "achieved": achieved, "peak": BWD_ALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BWD_ALU_PEAK_TFLOPS, "traffic": None},
+        "kernels_ms": kernel_ms,
+        "call_ms": {"median": percentile(per_call, 50), "p10": percentile(per_call, 10),
+                    "p90": percentile(per_call, 90), "calls": len(per_call)},
+        "hbm": {"achieved_GBs": nbytes / (ms * 1e-3) / 1e9, "peak_GBs": HBM_PEAK_GBS,
+                "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes_per_step": nbytes,
+                "workspace_bytes": ws.numel()},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_bwd(x, g.cpu(), cfg)
+    return out
+
+
+def cpu_baseline_bwd(x, g, cfg, target_s: float = 8.0):
+    """The fp64 backward oracle, as it stands, on whole sampled rows (each row's
+    forward and adjoint sweeps; the per-channel sums over rows are left out)."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle
+    from selective_state_space_sscan_amd import inputs as I
+
+    cores = oracle.default_threads()
+
+    def run_row(bd):
+        b, d = bd
+        sl = lambda t: I.f64(t[b:b + 1, d:d + 1])
+        dirs = [dict(delta=sl(x.delta), A=I.f64(p.A[d:d + 1]), B=I.f64(p.B[b:b + 1]), C=I.f64(p.C[b:b + 1]),
+                     D=I.f64(p.D[d:d + 1]), delta_bias=I.f64(p.delta_bias[d:d + 1])) for p in x.dirs]
+        oracle.sscan_bwd(sl(x.u), sl(x.z), sl(g), dirs, nthreads=1)
+
+    rng = np.random.default_rng(4321)
+    rows = [(int(b), int(d)) for b, d in zip(rng.integers(0, cfg.batch, 100000), rng.integers(0, cfg.dim, 100000))]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(run_row, rows[:cores]))
+    t_cal = time.perf_counter() - t0
+    n = int(max(cores, min(len(rows), cores * target_s / max(t_cal, 1e-6))))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(run_row, rows[:n]))
+    dt = time.perf_counter() - t0
+    return {"value": n * cfg.len / dt / 1e6, "unit": "Melem/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} whole rows of {cfg.len} tokens ({cfg.ndir} direction(s)) of the same seeded inputs, "
+                      f"fp64 backward per row, {cores} threads, {dt:.1f} s", "seconds": dt, "cpu_model": cpu_model()}
+
+
 # Single-token decode (sscan_step): batch streams of the long-sequence workload's
 # 1536 channels, bf16 u/delta/z/y, f32 B/C and f32 state.
 DECODE = dict(name="decode-step", batch=256, dim=1536, io_dtype="bf16", bc_dtype="f32")
@@ -244,6 +359,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long-seq-fwd",
                     help="a scan workload of selective_state_space_sscan_amd.inputs.CONFIGS, or decode-step")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward call (default) or its backward pass")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with a 512 MiB negation kernel (counter calibration for rocprofv3 --pmc runs)")
@@ -264,6 +381,9 @@ def main():
     names = [c.name for c in I.CONFIGS]
     ci = names.index(args.workload)
     cfg = I.CONFIGS[ci]
+    if args.pass_ == "bwd":
+        print(json.dumps(bench_bwd(args, torch, I, sscan, cfg, ci)), flush=True)
+        return
     dev = torch.device("cuda:0")
     x = I.config_inputs(ci, 0)
     xd = x.to(dev)

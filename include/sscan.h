@@ -198,6 +198,26 @@ SSCAN_API int sscan_bidir_profiled(const void* u, const void* z, void* y,
                          int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes,
                          void* const* events);
 
+/* Profiling variants of the backward entry points: the same work, and events[0]
+ * is recorded before the first kernel and events[k] after step k: 1 = B/C staging,
+ * 2 = states entering every window (segment aggregates and carry chain), 3 = the
+ * adjoints entering every window from the other side, 4 = the window pass(es),
+ * 5 = the sums of the parameter gradients.  events holds SSCAN_BWD_PROFILE_EVENTS
+ * hipEvent_t handles (NULL entries skipped; events may be NULL). */
+#define SSCAN_BWD_PROFILE_EVENTS 6
+SSCAN_API int sscan_bwd_profiled(const void* u, const void* delta, const float* delta_bias, int softplus,
+                       const float* A, const void* B, const void* C, const float* D,
+                       const void* z, const void* dout, void* du, void* dz, const sscan_dir_grads* grads,
+                       int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse, void* stream,
+                       int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes,
+                       void* const* events);
+SSCAN_API int sscan_bidir_bwd_profiled(const void* u, const void* z, const void* dout, void* du, void* dz,
+                             const sscan_dir_params* fwd, const sscan_dir_params* rev,
+                             const sscan_dir_grads* gfwd, const sscan_dir_grads* grev, int softplus,
+                             int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                             int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes,
+                             void* const* events);
+
 /* Same checks as sscan_fwd / sscan_bidir without touching the GPU: returns the
  * status the call would return before any launch.  workspace is only compared with
  * the required size (it is never dereferenced). */

@@ -28,16 +28,25 @@
 // fixed-order reduction, so results are bitwise reproducible.
 #include "sscan_device.h"
 
+#include <type_traits>
+
 namespace sscan {
 namespace {
 
 constexpr int kWin = 32;           // tokens per backward window
 constexpr int kGroup = 4;          // channels per wavefront in the window pass
 constexpr int kPartRows = kDState + 2;  // per-window partials: dA[16], dD, delta_bias
+#ifndef SSCAN_BWD_SCHED_TOKENS
+#define SSCAN_BWD_SCHED_TOKENS 4
+#endif
+// The window sweeps let the scheduler interleave this many consecutive tokens: one
+// token at a time leaves the single state chain of a lane exposed, unbounded
+// interleaving hoists so much that registers spill.
+constexpr int kSchedTokens = SSCAN_BWD_SCHED_TOKENS;
 
 // per-token, per-channel values shared through LDS in the window pass
 enum TokQ : int { QDT, QDTU, QDY, QU, QSIG, QDZ, QDUSKIP, QYSKIP, kTokQ };
-enum OutQ : int { ODU, ODDT, OY, kOutQ };
+enum OutQ : int { OP, OQ, OY, kOutQ };  // sum_n lambda B, sum_n A w, y
 
 // Output handling of the window pass.
 enum BwdOut : int {
@@ -50,9 +59,11 @@ __device__ __forceinline__ float sigmoid_f32(float x) { return rcp_hw(1.0f + exp
 
 // Sum over the 16 lanes of a DPP row (quad xor 1, quad xor 2, row rotate 4, 8);
 // every lane of the row receives the sum.
+// Every source lane of these patterns is inside the row, so bound_ctrl never takes
+// effect; with it (and a zero old value) the move folds into the add as one DPP add.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
@@ -140,7 +151,8 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
   using T = typename IO::T;
   __shared__ float sBC[kWin][kBC];
   __shared__ float sTok[kTokQ][kWin][kGroup];
-  __shared__ float sOut[kOutQ][kWin][kGroup];
+  __shared__ float sOutF[kOutQ * kWin * kGroup];  // [q][i][c]
+  auto sOut = [&](int q, int i, int cc) -> float { return sOutF[(q * kWin + i) * kGroup + cc]; };
   const ScanArgs& f = a.fwd;
   const int lane = threadIdx.x;
   const int c = lane >> 4, n = lane & 15;
@@ -220,54 +232,64 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
     }
     __syncthreads();
 
-    // 2. forward sweep over the window from its entry state, keeping every state
+    // 2-3. forward sweep over the window from its entry state, keeping every state,
+    // then the reverse sweep: the adjoint and the gradient terms of every token.
+    // Full windows take a copy without per-token conditions, so the unrolled tokens
+    // form one block the scheduler can interleave (each lane carries one state, one
+    // dependency chain); the per-token sums over states are written to LDS by every
+    // lane of a row (the same value to the same word).
     const float A2 = A * kLog2e;
     float hist[kWin];
-    float h = h_in;
+    float dA_acc = 0.0f;
+    auto sweeps = [&](auto full_tag) {
+      constexpr bool kFull = decltype(full_tag)::value;
+      // every lane of a row holds the row's sum: all of them store it to the same word
+      auto out_slot = [&](int q, int i) { return (q * kWin + i) * kGroup + c; };
+      float h = h_in;
 #pragma unroll
-    for (int s = 0; s < kWin; ++s) {
-      const int i = REV ? kWin - 1 - s : s;
-      if (i < wl) {
-        h = fmaf(exp2_hw(sTok[QDT][i][c] * A2), h, sTok[QDTU][i][c] * sBC[i][n]);
-        hist[i] = h;
-        if (HAS_Z) {
-          const float yp = row_sum16(sBC[i][kDState + n] * h);
-          if (n == 0) sOut[OY][i][c] = yp + sTok[QYSKIP][i][c];
+      for (int s = 0; s < kWin; ++s) {
+        const int i = REV ? kWin - 1 - s : s;
+        if (kFull || i < wl) {
+          h = fmaf(exp2_hw(sTok[QDT][i][c] * A2), h, sTok[QDTU][i][c] * sBC[i][n]);
+          hist[i] = h;
+          if (HAS_Z) sOutF[out_slot(OY, i)] = row_sum16(sBC[i][kDState + n] * h) + sTok[QYSKIP][i][c];
         }
+        if (s % kSchedTokens == kSchedTokens - 1) __builtin_amdgcn_sched_barrier(0);
       }
-    }
-
-    // 3. reverse sweep: the adjoint and the gradient terms of every token
-    float mu = mu_in, dA_acc = 0.0f;
+      float mu = mu_in;
 #pragma unroll
-    for (int s = kWin - 1; s >= 0; --s) {
-      const int i = REV ? kWin - 1 - s : s;
-      if (i < wl) {
-        const float dt = sTok[QDT][i][c];
-        const float dy = sTok[QDY][i][c];
-        const float Bn = sBC[i][n];
-        const float lam = fmaf(sBC[i][kDState + n], dy, mu);
-        const float at = exp2_hw(dt * A2);
-        // the state before token i in scan order (the entry state for the first)
-        float hprev;
-        if (!REV) {
-          hprev = i == 0 ? h_in : hist[i > 0 ? i - 1 : 0];
-        } else {
-          hprev = i == wl - 1 ? h_in : hist[i + 1 < kWin ? i + 1 : kWin - 1];
+      for (int s = kWin - 1; s >= 0; --s) {
+        const int i = REV ? kWin - 1 - s : s;
+        if (kFull || i < wl) {
+          const float dt = sTok[QDT][i][c];
+          const float dy = sTok[QDY][i][c];
+          const float lam = fmaf(sBC[i][kDState + n], dy, mu);
+          const float at = exp2_hw(dt * A2);
+          // the state before token i in scan order (the entry state for the first)
+          float hprev;
+          if (!REV) {
+            hprev = i == 0 ? h_in : hist[i > 0 ? i - 1 : 0];
+          } else if (kFull) {
+            hprev = i == kWin - 1 ? h_in : hist[i + 1 < kWin ? i + 1 : kWin - 1];
+          } else {
+            hprev = i == wl - 1 ? h_in : hist[i + 1 < kWin ? i + 1 : kWin - 1];
+          }
+          const float w = lam * at * hprev;
+          dA_acc = fmaf(w, dt, dA_acc);
+          accB[i] = fmaf(lam, sTok[QDTU][i][c], accB[i]);
+          accC[i] = fmaf(dy, hist[i], accC[i]);
+          // du = dt * P + D dy and d(dt) = u * P + Q with P = sum_n lambda B, Q = sum_n A w
+          sOutF[out_slot(OP, i)] = row_sum16(lam * sBC[i][n]);
+          sOutF[out_slot(OQ, i)] = row_sum16(A * w);
+          mu = at * lam;
         }
-        const float w = lam * at * hprev;
-        dA_acc = fmaf(w, dt, dA_acc);
-        accB[i] = fmaf(lam, sTok[QDTU][i][c], accB[i]);
-        accC[i] = fmaf(dy, hist[i], accC[i]);
-        const float lB = lam * Bn;
-        const float pdu = row_sum16(lB * dt);
-        const float pddt = row_sum16(fmaf(lB, sTok[QU][i][c], A * w));
-        if (n == 0) {
-          sOut[ODU][i][c] = pdu;
-          sOut[ODDT][i][c] = pddt;
-        }
-        mu = at * lam;
+        if (s % kSchedTokens == 0) __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    if (wl == kWin) {
+      sweeps(std::integral_constant<bool, true>());
+    } else {
+      sweeps(std::integral_constant<bool, false>());
     }
     {
       const int64_t d = g * kGroup + c;
@@ -286,21 +308,22 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
       for (int e = 0; e < 2; ++e) {
         const int i = i0 + e;
         if (i < wl) {
-          const float du = sOut[ODU][i][cc] + sTok[QDUSKIP][i][cc];
-          const float ddl = sOut[ODDT][i][cc] * sTok[QSIG][i][cc];
+          const float P = sOut(OP, i, cc);
+          const float du = fmaf(sTok[QDT][i][cc], P, sTok[QDUSKIP][i][cc]);
+          const float ddl = fmaf(sTok[QU][i][cc], P, sOut(OQ, i, cc)) * sTok[QSIG][i][cc];
           dbp += ddl;
           if (act) {
             IO::store(static_cast<T*>(gd.ddelta), row + i, ddl);
             if (OUT == kSingle) {
               IO::store(static_cast<T*>(a.du), row + i, du);
-              if (HAS_Z) IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * sOut[OY][i][cc]);
+              if (HAS_Z) IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * sOut(OY, i, cc));
             } else if (OUT == kFirst) {
               acc_du[row + i] = du;
-              if (HAS_Z) acc_y[row + i] = sOut[OY][i][cc];
+              if (HAS_Z) acc_y[row + i] = sOut(OY, i, cc);
             } else {
               IO::store(static_cast<T*>(a.du), row + i, du + acc_du[row + i]);
               if (HAS_Z)
-                IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (sOut[OY][i][cc] + acc_y[row + i]));
+                IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (sOut(OY, i, cc) + acc_y[row + i]));
             }
           }
         }
@@ -332,20 +355,43 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
   }
 }
 
-// dA, dD and delta_bias: per-window partials summed in window order.
-__global__ __launch_bounds__(256) void bwd_reduce_params_kernel(BwdArgs a, int64_t nwin,
-                                                                const float* __restrict__ part) {
+// dA, dD and delta_bias: the per-window partials summed over windows and batch
+// rows.  A block covers 64 channels of one (direction, row of the partials) with
+// four waves, each summing every fourth window with several loads in flight; the
+// four sums are added in a fixed order.  Accumulation is in double, so thousands
+// of partials add no error of their own (the partials carry float32 rounding only).
+constexpr int kReduceWaves = 4;
+
+__global__ __launch_bounds__(kLanes * kReduceWaves) void bwd_reduce_params_kernel(BwdArgs a, int64_t nwin,
+                                                                                const float* __restrict__ part) {
+  __shared__ double sh[kReduceWaves][kLanes];
   const ScanArgs& f = a.fwd;
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= int64_t(f.ndir) * kPartRows * f.dim) return;
-  const int64_t d = i % f.dim;
-  const int r = int((i / f.dim) % kPartRows);
-  const int dir = int(i / (f.dim * kPartRows));
-  // thousands of window partials: accumulate in double so the sum adds no error of
-  // its own (the partials carry float32 rounding only)
+  const int lane = threadIdx.x % kLanes, q = threadIdx.x / kLanes;
+  const int64_t d_raw = int64_t(blockIdx.x) * kLanes + lane;
+  const int64_t d = min64(d_raw, f.dim - 1);
+  const int r = int(blockIdx.y % kPartRows);
+  const int dir = int(blockIdx.y / kPartRows);
+  const int64_t m_total = f.batch * nwin;
+  constexpr int kUnroll = 8;
+  double acc[kUnroll] = {};
+  int64_t m = q;
+  for (; m + (kUnroll - 1) * kReduceWaves < m_total; m += kUnroll * kReduceWaves) {
+#pragma unroll
+    for (int e = 0; e < kUnroll; ++e) {
+      const int64_t mm = m + e * kReduceWaves;
+      acc[e] += part[part_index(dir, mm / nwin, mm % nwin, r, d, f.batch, f.dim, nwin)];
+    }
+  }
+  for (; m < m_total; m += kReduceWaves) acc[0] += part[part_index(dir, m / nwin, m % nwin, r, d, f.batch, f.dim, nwin)];
   double s = 0.0;
-  for (int64_t b = 0; b < f.batch; ++b)
-    for (int64_t k = 0; k < nwin; ++k) s += part[part_index(dir, b, k, r, d, f.batch, f.dim, nwin)];
+#pragma unroll
+  for (int e = 0; e < kUnroll; ++e) s += acc[e];
+  sh[q][lane] = s;
+  __syncthreads();
+  if (q != 0 || d_raw >= f.dim) return;
+  s = sh[0][lane];
+#pragma unroll
+  for (int w = 1; w < kReduceWaves; ++w) s += sh[w][lane];
   const DirGrads gd = dir ? a.grads[1] : a.grads[0];
   if (r < kDState) {
     gd.dA[d * kDState + r] = float(s);
@@ -385,7 +431,10 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(void* p, int64_t bytes) {
 bool aligned16_b(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
-hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStream_t stream) {
+hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
+  auto mark = [&](int i) {
+    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
+  };
   const ScanArgs& f = a.fwd;
   const int64_t ngroups = (f.dim + kLanes - 1) / kLanes;
   float* bc = w + p.off_bc;
@@ -399,12 +448,17 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
   float* acc_y = acc_du + (p.off_acc ? size_t(f.batch) * f.dim * f.len : 0);
 
   const int64_t bc_blocks = int64_t(f.ndir) * f.batch * ((f.len + 63) / 64);
+  mark(0);
   if (f.bc_bf16) {
     hipLaunchKernelGGL(stage_bc_kernel<true>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, f, bc);
   } else {
     hipLaunchKernelGGL(stage_bc_kernel<false>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, f, bc);
   }
-  if (p.nwin > 1) {
+  mark(1);
+  if (p.nwin <= 1) {
+    mark(2);
+    mark(3);
+  } else {
     const size_t esz = IO_BF16 ? 2 : 4;
     bool vec = (size_t(f.len) * esz) % 16 == 0 && aligned16_b(f.u) && aligned16_b(a.dout) &&
                (!f.z || aligned16_b(f.z));
@@ -418,6 +472,7 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
                        int(vec));
     hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nwin,
                        static_cast<const float*>(agg), hin, 0);
+    mark(2);
     // adjoints entering every window from the other side
     ScanArgs adj = f;
     adj.u = a.dout;
@@ -426,6 +481,7 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
                        p.nwin, static_cast<const float*>(bc), agga, int(vec));
     hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nwin,
                        static_cast<const float*>(agga), muin, 1);
+    mark(3);
   }
   const dim3 wgrid(unsigned(f.batch * p.nwin * p.csplit));
   const int64_t nw = p.nwin;
@@ -443,9 +499,9 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
     hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSecond>), wgrid, dim3(kLanes), 0, stream,
                        a, 1, nw, p.csplit, p.gps, bc, hin, muin, part, pbc, acc_du, acc_y);
   }
-  const int64_t np = int64_t(f.ndir) * kPartRows * f.dim;
-  hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned((np + 255) / 256)), dim3(256), 0, stream, a, p.nwin,
-                     static_cast<const float*>(part));
+  mark(4);
+  hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned((f.dim + kLanes - 1) / kLanes), unsigned(f.ndir * kPartRows)),
+                     dim3(kLanes * kReduceWaves), 0, stream, a, p.nwin, static_cast<const float*>(part));
   const int64_t nb = int64_t(f.ndir) * f.batch * 2 * kDState * f.len;
   if (f.bc_bf16) {
     hipLaunchKernelGGL(bwd_reduce_bc_kernel<true>, dim3(unsigned((nb + 255) / 256)), dim3(256), 0, stream, a,
@@ -454,18 +510,19 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
     hipLaunchKernelGGL(bwd_reduce_bc_kernel<false>, dim3(unsigned((nb + 255) / 256)), dim3(256), 0, stream, a,
                        p.csplit, static_cast<const float*>(pbc));
   }
+  mark(5);
   return hipGetLastError();
 }
 
 template <bool IO_BF16>
-hipError_t launch_bwd_io(const BwdArgs& a, const BwdPlan& p, float* w, hipStream_t stream) {
+hipError_t launch_bwd_io(const BwdArgs& a, const BwdPlan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
   const bool z = a.fwd.z != nullptr;
   if (a.fwd.softplus) {
-    return z ? launch_bwd_typed<IO_BF16, true, true>(a, p, w, stream)
-             : launch_bwd_typed<IO_BF16, true, false>(a, p, w, stream);
+    return z ? launch_bwd_typed<IO_BF16, true, true>(a, p, w, stream, ev)
+             : launch_bwd_typed<IO_BF16, true, false>(a, p, w, stream, ev);
   }
-  return z ? launch_bwd_typed<IO_BF16, false, true>(a, p, w, stream)
-           : launch_bwd_typed<IO_BF16, false, false>(a, p, w, stream);
+  return z ? launch_bwd_typed<IO_BF16, false, true>(a, p, w, stream, ev)
+           : launch_bwd_typed<IO_BF16, false, false>(a, p, w, stream, ev);
 }
 
 }  // namespace
@@ -526,8 +583,10 @@ hipError_t launch_bwd_zero(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, float* workspace, hipStream_t stream) {
-  return a.fwd.io_bf16 ? launch_bwd_io<true>(a, p, workspace, stream) : launch_bwd_io<false>(a, p, workspace, stream);
+hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, float* workspace, hipStream_t stream,
+                      hipEvent_t const* events) {
+  return a.fwd.io_bf16 ? launch_bwd_io<true>(a, p, workspace, stream, events)
+                       : launch_bwd_io<false>(a, p, workspace, stream, events);
 }
 
 }  // namespace sscan

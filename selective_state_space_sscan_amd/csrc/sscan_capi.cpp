@@ -12,6 +12,7 @@ namespace {
 
 constexpr int kVersion = 200;  // 0.2.0
 static_assert(SSCAN_PROFILE_EVENTS == sscan::kProfileEvents, "event count mismatch");
+static_assert(SSCAN_BWD_PROFILE_EVENTS == sscan::kBwdProfileEvents, "event count mismatch");
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -279,7 +280,7 @@ int validate_bwd(const void* u, const void* z, const void* dout, const void* du,
 int run_bwd(const void* u, const void* z, const void* dout, void* du, void* dz, const DirView* dirs,
             const sscan_dir_grads* grads, int ndir, int reverse, int softplus, int64_t batch, int64_t dim,
             int64_t len, int64_t dstate, void* stream, int io_dtype, int bc_dtype, void* workspace,
-            size_t workspace_bytes) {
+            size_t workspace_bytes, void* const* events = nullptr) {
   sscan::BwdPlan plan{};
   bool empty = false;
   const int st = validate_bwd(u, z, dout, du, dz, dirs, grads, ndir, batch, dim, len, dstate, io_dtype, bc_dtype,
@@ -294,9 +295,12 @@ int run_bwd(const void* u, const void* z, const void* dout, void* du, void* dz, 
   for (int k = 0; k < ndir; ++k)
     a.grads[k] = sscan::DirGrads{grads[k].ddelta, grads[k].ddelta_bias, grads[k].dA, grads[k].dB, grads[k].dC,
                                  grads[k].dD};
+  hipEvent_t ev[sscan::kBwdProfileEvents] = {};
+  if (events)
+    for (int i = 0; i < sscan::kBwdProfileEvents; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
   const hipError_t e = empty ? sscan::launch_bwd_zero(a, static_cast<hipStream_t>(stream))
                              : sscan::launch_bwd(a, plan, static_cast<float*>(workspace),
-                                                 static_cast<hipStream_t>(stream));
+                                                 static_cast<hipStream_t>(stream), events ? ev : nullptr);
   return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
 }
 
@@ -450,6 +454,29 @@ int sscan_bidir_bwd(const void* u, const void* z, const void* dout, void* du, vo
   const sscan_dir_grads g[2] = {*gfwd, *grev};
   return run_bwd(u, z, dout, du, dz, d, g, 2, 0, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype,
                  workspace, workspace_bytes);
+}
+
+int sscan_bwd_profiled(const void* u, const void* delta, const float* delta_bias, int softplus, const float* A,
+                       const void* B, const void* C, const float* D, const void* z, const void* dout, void* du,
+                       void* dz, const sscan_dir_grads* grads, int64_t batch, int64_t dim, int64_t len,
+                       int64_t dstate, int reverse, void* stream, int io_dtype, int bc_dtype, void* workspace,
+                       size_t workspace_bytes, void* const* events) {
+  if (!grads) return SSCAN_ERR_NULL;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  return run_bwd(u, z, dout, du, dz, &d, grads, 1, reverse, softplus, batch, dim, len, dstate, stream, io_dtype,
+                 bc_dtype, workspace, workspace_bytes, events);
+}
+
+int sscan_bidir_bwd_profiled(const void* u, const void* z, const void* dout, void* du, void* dz,
+                             const sscan_dir_params* fwd, const sscan_dir_params* rev, const sscan_dir_grads* gfwd,
+                             const sscan_dir_grads* grev, int softplus, int64_t batch, int64_t dim, int64_t len,
+                             int64_t dstate, void* stream, int io_dtype, int bc_dtype, void* workspace,
+                             size_t workspace_bytes, void* const* events) {
+  if (!fwd || !rev || !gfwd || !grev) return SSCAN_ERR_NULL;
+  const DirView d[2] = {view_of(fwd), view_of(rev)};
+  const sscan_dir_grads g[2] = {*gfwd, *grev};
+  return run_bwd(u, z, dout, du, dz, d, g, 2, 0, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype,
+                 workspace, workspace_bytes, events);
 }
 
 int sscan_validate_bwd(const void* u, const void* delta, const float* delta_bias, int softplus, const float* A,

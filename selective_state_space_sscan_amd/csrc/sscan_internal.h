@@ -93,7 +93,14 @@ struct BwdPlan {
 };
 
 BwdPlan make_bwd_plan(int64_t batch, int64_t dim, int64_t len, int ndir);
-hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, float* workspace, hipStream_t stream);
+
+// Step boundaries of a backward call: before staging, after staging, after the
+// window entry states, after the window adjoints, after the window pass(es), after
+// the reductions.
+constexpr int kBwdProfileEvents = 6;
+
+hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, float* workspace, hipStream_t stream,
+                      hipEvent_t const* events = nullptr);
 
 // Gradients of an empty call: the parameter gradients (dA, dD, delta_bias, dB, dC)
 // that have elements are zero.

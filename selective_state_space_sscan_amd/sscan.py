@@ -21,6 +21,8 @@ SSCAN_BF16 = 1
 DSTATE = 16
 PROFILE_EVENTS = 5  # step boundaries: start, staged B/C, aggregates, carry, output
 PROFILE_STEPS = ("stage_bc", "aggregate", "carry", "output")
+BWD_PROFILE_EVENTS = 6  # start, staged B/C, window states, window adjoints, window pass, sums
+BWD_PROFILE_STEPS = ("stage_bc", "window_states", "window_adjoints", "window_pass", "param_sums")
 
 _DT_CODE = {torch.float32: SSCAN_F32, torch.bfloat16: SSCAN_BF16}
 
@@ -84,6 +86,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_validate_bwd.restype = I
     lib.sscan_validate_bidir_bwd.argtypes = [V, V, V, V, V, DP, DP, DG, DG, I, I64, I64, I64, I64, I, I, V, SZ]
     lib.sscan_validate_bidir_bwd.restype = I
+    lib.sscan_bwd_profiled.argtypes = lib.sscan_bwd.argtypes + [V]
+    lib.sscan_bwd_profiled.restype = I
+    lib.sscan_bidir_bwd_profiled.argtypes = lib.sscan_bidir_bwd.argtypes + [V]
+    lib.sscan_bidir_bwd_profiled.restype = I
     lib.sscan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.sscan_bwd_workspace_bytes.restype = SZ
     lib.sscan_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
@@ -98,12 +104,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 
 class HipEvents:
-    """PROFILE_EVENTS timing events of the HIP runtime the library runs on, for the
-    profiled entry points (one set per call in flight)."""
+    """Timing events of the HIP runtime the library runs on, for the profiled entry
+    points (one set per call in flight): one event per boundary of ``steps``
+    (PROFILE_STEPS for the forward calls, BWD_PROFILE_STEPS for the backward)."""
 
     _hip = None
 
-    def __init__(self):
+    def __init__(self, steps=PROFILE_STEPS):
+        self.steps = tuple(steps)
+        nev = len(self.steps) + 1
         if HipEvents._hip is None:
             hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime already mapped by torch and libsscan
             hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -111,8 +120,8 @@ class HipEvents:
             hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
             hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
             HipEvents._hip = hip
-        self._ev = (ctypes.c_void_p * PROFILE_EVENTS)()
-        for i in range(PROFILE_EVENTS):
+        self._ev = (ctypes.c_void_p * nev)()
+        for i in range(nev):
             h = ctypes.c_void_p()
             if HipEvents._hip.hipEventCreate(ctypes.byref(h)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -125,9 +134,9 @@ class HipEvents:
     def step_ms(self):
         """Milliseconds of each step (dict keyed by PROFILE_STEPS); waits for the last event."""
         hip = HipEvents._hip
-        hip.hipEventSynchronize(self._ev[PROFILE_EVENTS - 1])
+        hip.hipEventSynchronize(self._ev[len(self.steps)])
         out = {}
-        for i, name in enumerate(PROFILE_STEPS):
+        for i, name in enumerate(self.steps):
             ms = ctypes.c_float()
             if hip.hipEventElapsedTime(ctypes.byref(ms), self._ev[i], self._ev[i + 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
@@ -137,9 +146,9 @@ class HipEvents:
     def total_ms(self) -> float:
         """Milliseconds from the first to the last event (the whole call)."""
         hip = HipEvents._hip
-        hip.hipEventSynchronize(self._ev[PROFILE_EVENTS - 1])
+        hip.hipEventSynchronize(self._ev[len(self.steps)])
         ms = ctypes.c_float()
-        if hip.hipEventElapsedTime(ctypes.byref(ms), self._ev[0], self._ev[PROFILE_EVENTS - 1]) != 0:
+        if hip.hipEventElapsedTime(ctypes.byref(ms), self._ev[0], self._ev[len(self.steps)]) != 0:
             raise RuntimeError("hipEventElapsedTime failed")
         return float(ms.value)
 
@@ -225,6 +234,8 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = Tru
     if events is None:
         st = lib.sscan_fwd(*args)
     else:
+        if events.steps != PROFILE_STEPS:
+            raise ValueError("sscan.fwd needs HipEvents(PROFILE_STEPS)")
         st = lib.sscan_fwd_profiled(*args, ctypes.cast(events.handles, ctypes.c_void_p))
     if st != 0:
         raise SScanError(st, "sscan_fwd")
@@ -345,6 +356,8 @@ def bidir(u, z, fwd: dict, rev: dict, softplus: bool = True, out: Optional[torch
     if events is None:
         st = lib.sscan_bidir(*args)
     else:
+        if events.steps != PROFILE_STEPS:
+            raise ValueError("sscan.bidir needs HipEvents(PROFILE_STEPS)")
         st = lib.sscan_bidir_profiled(*args, ctypes.cast(events.handles, ctypes.c_void_p))
     if st != 0:
         raise SScanError(st, "sscan_bidir")
@@ -369,8 +382,16 @@ def _grads_for(p: dict, u):
     return g, st
 
 
+def _bwd_events(events: Optional[HipEvents]):
+    if events is None:
+        return None
+    if events.steps != BWD_PROFILE_STEPS:
+        raise ValueError("the backward calls need HipEvents(BWD_PROFILE_STEPS)")
+    return ctypes.cast(events.handles, ctypes.c_void_p)
+
+
 def bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, softplus: bool = True, reverse: bool = False,
-        workspace: Optional[torch.Tensor] = None) -> dict:
+        workspace: Optional[torch.Tensor] = None, events: Optional[HipEvents] = None) -> dict:
     """Backward pass of ``fwd`` (``sscan_bwd``): gradients of sum(dout * out).
     Returns a dict with du, dz (None without z), ddelta, ddelta_bias, dA, dB, dC, dD
     (None for an absent optional input), in the dtypes of the matching inputs."""
@@ -395,16 +416,18 @@ def bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, softplus: bool
     du = torch.empty_like(u)
     dz = torch.empty_like(u) if z is not None else None
     ws, ws_bytes = _workspace(bwd_workspace_bytes(b, d, L, DSTATE, False), dev, workspace)
-    st = lib.sscan_bwd(_ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                       _ptr(z), _ptr(dout), _ptr(du), _ptr(dz), ctypes.byref(gst), b, d, L, DSTATE, int(bool(reverse)),
-                       _stream(dev), _DT_CODE[u.dtype], _DT_CODE[B.dtype], _ptr(ws), ws_bytes)
+    args = [_ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(z), _ptr(dout), _ptr(du), _ptr(dz), ctypes.byref(gst), b, d, L, DSTATE, int(bool(reverse)),
+            _stream(dev), _DT_CODE[u.dtype], _DT_CODE[B.dtype], _ptr(ws), ws_bytes]
+    ev = _bwd_events(events)
+    st = lib.sscan_bwd(*args) if ev is None else lib.sscan_bwd_profiled(*args, ev)
     if st != 0:
         raise SScanError(st, "sscan_bwd")
     return dict(g, du=du, dz=dz)
 
 
 def bidir_bwd(u, z, dout, fwd: dict, rev: dict, softplus: bool = True,
-              workspace: Optional[torch.Tensor] = None) -> dict:
+              workspace: Optional[torch.Tensor] = None, events: Optional[HipEvents] = None) -> dict:
     """Backward pass of ``bidir`` (``sscan_bidir_bwd``).  Returns {"du", "dz",
     "fwd": {...}, "rev": {...}} with each direction's gradients as in ``bwd``."""
     lib = load_library()
@@ -424,9 +447,11 @@ def bidir_bwd(u, z, dout, fwd: dict, rev: dict, softplus: bool = True,
     du = torch.empty_like(u)
     dz = torch.empty_like(u) if z is not None else None
     ws, ws_bytes = _workspace(bwd_workspace_bytes(b, d, L, DSTATE, True), dev, workspace)
-    st = lib.sscan_bidir_bwd(_ptr(u), _ptr(z), _ptr(dout), _ptr(du), _ptr(dz), ctypes.byref(pf), ctypes.byref(pr),
-                             ctypes.byref(gfs), ctypes.byref(grs), int(bool(softplus)), b, d, L, DSTATE, _stream(dev),
-                             _DT_CODE[u.dtype], _DT_CODE[fwd["B"].dtype], _ptr(ws), ws_bytes)
+    args = [_ptr(u), _ptr(z), _ptr(dout), _ptr(du), _ptr(dz), ctypes.byref(pf), ctypes.byref(pr),
+            ctypes.byref(gfs), ctypes.byref(grs), int(bool(softplus)), b, d, L, DSTATE, _stream(dev),
+            _DT_CODE[u.dtype], _DT_CODE[fwd["B"].dtype], _ptr(ws), ws_bytes]
+    ev = _bwd_events(events)
+    st = lib.sscan_bidir_bwd(*args) if ev is None else lib.sscan_bidir_bwd_profiled(*args, ev)
     if st != 0:
         raise SScanError(st, "sscan_bidir_bwd")
     return {"du": du, "dz": dz, "fwd": gf, "rev": gr}
