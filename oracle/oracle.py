@@ -19,6 +19,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "sscan_oracle.c")
 SRC_BWD = os.path.join(HERE, "sscan_oracle_bwd.c")
+SRC_CONV = os.path.join(HERE, "sscan_oracle_conv.c")
 LIB = os.path.join(HERE, "liboracle_sscan.so")
 
 _lib = None
@@ -29,7 +30,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(LIB):
         tmp = LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
-                               "-o", tmp, SRC, SRC_BWD, "-lm", "-lpthread"])
+                               "-o", tmp, SRC, SRC_BWD, SRC_CONV, "-lm", "-lpthread"])
         os.replace(tmp, LIB)
     return LIB
 
@@ -49,6 +50,8 @@ def _load():
         lib.oracle_sscan_bidir.restype = INT
         lib.oracle_sscan_bwd.argtypes = [P, P, P, P, P, INT, P, P, P, INT, I64, I64, I64, I64, INT]
         lib.oracle_sscan_bwd.restype = INT
+        lib.oracle_conv1d.argtypes = [P, P, P, P, I64, I64, I64, I64, INT, INT]
+        lib.oracle_conv1d.restype = INT
         lib.oracle_softplus_f64.argtypes = [ctypes.c_double]
         lib.oracle_softplus_f64.restype = ctypes.c_double
         lib.oracle_silu_f64.argtypes = [ctypes.c_double]
@@ -166,6 +169,29 @@ def sscan_bwd(u, z, g, dirs, softplus=True, reverse=False, nthreads: int = 1):
     if st != 0:
         raise RuntimeError(f"oracle_sscan_bwd failed with status {st}")
     return {"du": du, "dz": dz, "dirs": res}
+
+
+def conv1d(x, w, bias=None, same=False, silu=False):
+    """Depthwise 1-D convolution of each channel (causal, or 'same' for odd widths),
+    plus bias, optionally followed by silu; x [batch, dim, len], w [dim, width]."""
+    x = _c64(x)
+    b, d, L = x.shape
+    w = _c64(w)
+    if w.shape[0] != d:
+        raise ValueError("w must be [dim, width]")
+    bias = _c64(bias, (d,))
+    out = np.empty((b, d, L))
+    st = _load().oracle_conv1d(_p(x), _p(w), _p(bias), _p(out), b, d, L, w.shape[1], int(bool(same)), int(bool(silu)))
+    if st != 0:
+        raise RuntimeError(f"oracle_conv1d failed with status {st}")
+    return out
+
+
+def sscan_fwd_conv(x, conv_w, conv_bias, same, silu, delta, A, B, C, D=None, z=None, delta_bias=None,
+                   softplus=True, reverse=False, nthreads: int = 1):
+    """The scan of the convolved input: sscan_fwd(conv1d(x), ...)."""
+    u = conv1d(x, conv_w, conv_bias, same, silu)
+    return sscan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus=softplus, reverse=reverse, nthreads=nthreads)
 
 
 def softplus(x: float) -> float:
