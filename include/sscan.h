@@ -59,7 +59,7 @@ enum sscan_status {
   SSCAN_OK = 0,
   SSCAN_ERR_NULL = -1,        /* a required pointer is NULL */
   SSCAN_ERR_SHAPE = -2,       /* batch, dim or len < 0, or a size product overflows */
-  SSCAN_ERR_UNSUPPORTED = -3, /* dstate != 16 or unknown dtype code */
+  SSCAN_ERR_UNSUPPORTED = -3, /* dstate != 16, unknown dtype code or convolution shape */
   SSCAN_ERR_ALIGN = -4,       /* a pointer is not aligned to its element size */
   SSCAN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than sscan_workspace_bytes */
   SSCAN_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
@@ -130,6 +130,40 @@ SSCAN_API int sscan_step(float* state, const void* u, const void* delta, const f
                const float* A, const void* B, const void* C, const float* D,
                const void* z, void* y, int64_t batch, int64_t dim, int64_t dstate, void* stream,
                int io_dtype, int bc_dtype);
+
+/* Depthwise convolution in front of the scan (Hand-written simplified Mamba2 page,
+ * section 4.4: a per-channel Conv1d of d_conv taps padded by d_conv - 1 and cut back
+ * to the sequence length, i.e. causal; Reproducing Vision Mamba page, section 3.2:
+ * kernel 3 with 'same' padding).  For every (b, d, t):
+ *   causal: out = bias_d + sum_{j<width} weight[d,j] * x[b,d,t - (width-1) + j]
+ *   same:   out = bias_d + sum_{j<width} weight[d,j] * x[b,d,t - (width-1)/2 + j]
+ * with x = 0 outside [0, len); then silu(out) when silu != 0 (the pages' layers use
+ * no activation here; silu is an option). */
+typedef struct sscan_conv_params {
+  const float* weight;  /* [dim, width] float32, required */
+  const float* bias;    /* [dim] float32, optional (NULL = 0) */
+  int width;            /* taps: 1..4 causal, 1 or 3 centred */
+  int same;             /* 0 causal, 1 centred ('same') */
+  int silu;             /* 0 or 1 */
+} sscan_conv_params;
+
+/* The convolution alone: y = conv(x), x and y [batch, dim, len] io_dtype (device
+ * pointers; y must not overlap x).  No workspace. */
+SSCAN_API int sscan_conv1d(const void* x, const sscan_conv_params* conv, void* y,
+                 int64_t batch, int64_t dim, int64_t len, void* stream, int io_dtype);
+
+/* sscan_fwd / sscan_bidir on u = conv(x) computed inside the scan kernels: the
+ * convolved sequence is never written to memory (both scan passes recompute it
+ * from x and a 4-token halo).  Arguments as sscan_fwd / sscan_bidir with x in
+ * place of u; workspace as there (sscan_workspace_bytes). */
+SSCAN_API int sscan_fwd_conv(const void* x, const sscan_conv_params* conv, const void* delta, const float* delta_bias,
+                   int softplus, const float* A, const void* B, const void* C, const float* D,
+                   const void* z, void* y, int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                   int reverse, void* stream, int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+SSCAN_API int sscan_bidir_conv(const void* x, const sscan_conv_params* conv, const void* z, void* y,
+                     const sscan_dir_params* fwd, const sscan_dir_params* rev, int softplus,
+                     int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                     int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
 
 /* Gradients of one direction's parameters (all device pointers, written by the
  * backward entry points). */
@@ -254,6 +288,9 @@ SSCAN_API int sscan_validate_bidir_bwd(const void* u, const void* z, const void*
                              const sscan_dir_grads* gfwd, const sscan_dir_grads* grev, int softplus,
                              int64_t batch, int64_t dim, int64_t len, int64_t dstate,
                              int io_dtype, int bc_dtype, const void* workspace, size_t workspace_bytes);
+
+SSCAN_API int sscan_validate_conv1d(const void* x, const sscan_conv_params* conv, const void* y,
+                          int64_t batch, int64_t dim, int64_t len, int io_dtype);
 
 /* Bytes of device workspace a call with these sizes needs (0 if none); bidir != 0
  * for sscan_bidir.  Returns 0 for invalid sizes (the call itself reports them). */

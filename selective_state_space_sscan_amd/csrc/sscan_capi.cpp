@@ -77,11 +77,28 @@ int check_dir(const DirView& p, const Sizes& sz, int64_t dim, const Range& y) {
   return SSCAN_OK;
 }
 
+// The front-end convolution: causal kernels of 1..4 taps, or centred ('same') ones
+// of 1 or 3 taps; fp32 weights [dim][width] and optional bias [dim].
+int check_conv(const sscan_conv_params* c, int64_t dim, const Range& y) {
+  if (!c) return SSCAN_OK;
+  if (!c->weight) return SSCAN_ERR_NULL;
+  if (c->width < 1 || (c->same ? (c->width % 2 == 0 || c->width > 3) : c->width > 4) ||
+      (c->same != 0 && c->same != 1) || (c->silu != 0 && c->silu != 1))
+    return SSCAN_ERR_UNSUPPORTED;
+  if (!aligned(c->weight, 4) || !aligned(c->bias, 4)) return SSCAN_ERR_ALIGN;
+  if (overlap(y, range_of(c->weight, size_t(dim) * size_t(c->width) * 4)) ||
+      (c->bias && overlap(y, range_of(c->bias, size_t(dim) * 4))))
+    return SSCAN_ERR_ALIAS;
+  return SSCAN_OK;
+}
+
+int conv_left(const sscan_conv_params* c) { return c->same ? (c->width - 1) / 2 : c->width - 1; }
+
 // Shared by the run and validate entry points.  On success *plan is filled and
 // *empty tells whether there is nothing to do.
 int validate(const void* u, const void* z, const void* y, const DirView* dirs, int ndir, int64_t batch, int64_t dim,
              int64_t len, int64_t dstate, int io_dtype, int bc_dtype, const void* workspace, size_t workspace_bytes,
-             sscan::Plan* plan, bool* empty) {
+             sscan::Plan* plan, bool* empty, const sscan_conv_params* conv = nullptr) {
   Sizes sz{};
   int st = check_sizes(batch, dim, len, dstate, io_dtype, bc_dtype, &sz);
   if (st != SSCAN_OK) return st;
@@ -98,6 +115,8 @@ int validate(const void* u, const void* z, const void* y, const DirView* dirs, i
     st = check_dir(dirs[k], sz, dim, yr);
     if (st != SSCAN_OK) return st;
   }
+  st = check_conv(conv, dim, yr);
+  if (st != SSCAN_OK) return st;
   *plan = sscan::make_plan(batch, dim, len, ndir);
   if (plan->workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan->workspace_bytes) return SSCAN_ERR_WORKSPACE;
@@ -167,18 +186,25 @@ int validate_state_call(const void* u, const void* z, const void* y, const DirVi
 int run(const void* u, const void* z, void* y, const DirView* dirs, int ndir, int reverse, int softplus,
         int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream, int io_dtype, int bc_dtype,
         void* workspace, size_t workspace_bytes, void* const* events = nullptr, const float* h0 = nullptr,
-        float* h_last = nullptr) {
+        float* h_last = nullptr, const sscan_conv_params* conv = nullptr) {
   sscan::Plan plan{};
   bool empty = false;
   const bool state = h0 || h_last;
   const int st = state ? validate_state_call(u, z, y, dirs[0], h0, h_last, batch, dim, len, dstate, io_dtype,
                                              bc_dtype, workspace, workspace_bytes, &plan, &empty)
                        : validate(u, z, y, dirs, ndir, batch, dim, len, dstate, io_dtype, bc_dtype, workspace,
-                                  workspace_bytes, &plan, &empty);
+                                  workspace_bytes, &plan, &empty, conv);
   if (st != SSCAN_OK) return st;
   sscan::ScanArgs a = make_args(u, z, y, dirs, ndir, reverse, softplus, batch, dim, len, io_dtype, bc_dtype);
   a.h0 = h0;
   a.h_last = h_last;
+  if (conv) {
+    a.conv_w = conv->weight;
+    a.conv_b = conv->bias;
+    a.conv_width = conv->width;
+    a.conv_left = conv_left(conv);
+    a.conv_silu = conv->silu;
+  }
   if (empty) {
     // no tokens: the final state is the entry state
     if (len == 0 && h_last && h_last != h0 && batch > 0 && dim > 0) {
@@ -516,6 +542,50 @@ size_t sscan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_
   return sscan::make_bwd_plan(batch, dim, len, bidir ? 2 : 1).workspace_bytes;
 }
 
+int sscan_validate_conv1d(const void* x, const sscan_conv_params* conv, const void* y, int64_t batch, int64_t dim,
+                          int64_t len, int io_dtype) {
+  Sizes sz{};
+  int st = check_sizes(batch, dim, len, sscan::kDState, io_dtype, SSCAN_F32, &sz);
+  if (st != SSCAN_OK) return st;
+  if (!conv) return SSCAN_ERR_NULL;
+  if (batch == 0 || dim == 0 || len == 0) return SSCAN_OK;
+  if (!x || !y) return SSCAN_ERR_NULL;
+  if (!aligned(x, sz.io_esz) || !aligned(y, sz.io_esz)) return SSCAN_ERR_ALIGN;
+  const Range yr = range_of(y, sz.io_elems * sz.io_esz);
+  if (overlap(yr, range_of(x, sz.io_elems * sz.io_esz))) return SSCAN_ERR_ALIAS;
+  return check_conv(conv, dim, yr);
+}
+
+int sscan_conv1d(const void* x, const sscan_conv_params* conv, void* y, int64_t batch, int64_t dim, int64_t len,
+                 void* stream, int io_dtype) {
+  const int st = sscan_validate_conv1d(x, conv, y, batch, dim, len, io_dtype);
+  if (st != SSCAN_OK || batch == 0 || dim == 0 || len == 0) return st;
+  const sscan::ConvArgs a{x, y, conv->weight, conv->bias, conv->width, conv_left(conv), conv->silu,
+                          io_dtype == SSCAN_BF16, batch, dim, len};
+  const hipError_t e = sscan::launch_conv1d(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+}
+
+int sscan_fwd_conv(const void* x, const sscan_conv_params* conv, const void* delta, const float* delta_bias,
+                   int softplus, const float* A, const void* B, const void* C, const float* D, const void* z, void* y,
+                   int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse, void* stream, int io_dtype,
+                   int bc_dtype, void* workspace, size_t workspace_bytes) {
+  if (!conv) return SSCAN_ERR_NULL;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  return run(x, z, y, &d, 1, reverse, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype, workspace,
+             workspace_bytes, nullptr, nullptr, nullptr, conv);
+}
+
+int sscan_bidir_conv(const void* x, const sscan_conv_params* conv, const void* z, void* y, const sscan_dir_params* fwd,
+                     const sscan_dir_params* rev, int softplus, int64_t batch, int64_t dim, int64_t len,
+                     int64_t dstate, void* stream, int io_dtype, int bc_dtype, void* workspace,
+                     size_t workspace_bytes) {
+  if (!conv || !fwd || !rev) return SSCAN_ERR_NULL;
+  const DirView d[2] = {view_of(fwd), view_of(rev)};
+  return run(x, z, y, d, 2, 0, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype, workspace,
+             workspace_bytes, nullptr, nullptr, nullptr, conv);
+}
+
 size_t sscan_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir) {
   Sizes sz{};
   if (check_sizes(batch, dim, len, dstate, SSCAN_F32, SSCAN_F32, &sz) != SSCAN_OK) return 0;
@@ -528,7 +598,7 @@ const char* sscan_strerror(int status) {
     case SSCAN_OK: return "ok";
     case SSCAN_ERR_NULL: return "a required pointer is NULL";
     case SSCAN_ERR_SHAPE: return "invalid sizes (negative, or too large)";
-    case SSCAN_ERR_UNSUPPORTED: return "unsupported dstate (must be 16) or dtype code";
+    case SSCAN_ERR_UNSUPPORTED: return "unsupported dstate (must be 16), dtype code or convolution shape";
     case SSCAN_ERR_ALIGN: return "a pointer is not aligned to its element size (workspace: 16 bytes)";
     case SSCAN_ERR_WORKSPACE: return "workspace missing or smaller than sscan_workspace_bytes()";
     case SSCAN_ERR_HIP: return "HIP runtime error at launch";

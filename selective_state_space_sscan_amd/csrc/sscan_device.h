@@ -159,13 +159,26 @@ enum Mode : int {
                    // h holds mu and runs opposite to the direction's scan order
 };
 
-// One lane's view of one direction of one (batch, channel) row.  SOFTPLUS and
-// HAS_Z are compile-time so that a tile's 16 tokens form one straight-line block.
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
+// Front-end convolution modes of the lane scan.
+enum Conv : int {
+  kNoConv = 0,    // u is read as is
+  kConvLin = 1,   // u = bias + depthwise convolution of x
+  kConvSilu = 2,  // u = silu(bias + depthwise convolution of x)
+};
+
+// The convolution reads a fixed window of five tokens, x[t-3 .. t+1]; a kernel of
+// `width` taps starting `left` tokens before t sits in it with zeros elsewhere.
+constexpr int kConvTaps = 5;
+constexpr int kConvBack = 3;
+
+// One lane's view of one direction of one (batch, channel) row.  SOFTPLUS, HAS_Z
+// and CONV are compile-time so that a tile's tokens form one straight-line block.
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV = kNoConv>
 struct Lane {
   using IO = Io<IO_BF16>;
   using T = typename IO::T;
   static constexpr int kTok = IO::kTok;
+  static constexpr int kConv = CONV;
   const T* u;
   const T* delta;
   const T* z;     // nullable
@@ -177,6 +190,8 @@ struct Lane {
   float h[kDState];
   float bias, Dd;
   float sum_dt;
+  float cw[kConvTaps], cb;  // front-end convolution taps over x[t-3 .. t+1], bias
+  int64_t len;
   int lane;
   bool vec;       // 16-byte vector access is valid for full tiles
   bool active;    // lane maps to a real channel (stores enabled)
@@ -231,6 +246,17 @@ struct Lane {
 
   __device__ __forceinline__ float gate(float yv, float zv) const { return HAS_Z ? yv * silu_f32(zv) : yv; }
 
+  // u from the convolution window x[t-3 .. t+1]
+  __device__ __forceinline__ float conv_out(const float (&xw)[kConvTaps]) const {
+    float acc = cb;
+#pragma unroll
+    for (int k = 0; k < kConvTaps; ++k) acc = fmaf(cw[k], xw[k], acc);
+    return CONV == kConvSilu ? silu_f32(acc) : acc;
+  }
+
+  // x at token t, zero outside the sequence (the convolution's padding)
+  __device__ __forceinline__ float x_at(int64_t t) const { return (t >= 0 && t < len) ? IO::load(u, t) : 0.0f; }
+
   // Tokens [ta, tb) in scan order (descending when REV).  ta is a multiple of
   // kTok; tb too unless it is the end of the sequence, so only the top tile can be
   // partial.  Full tiles are software-pipelined: the next tile's u and delta are
@@ -279,6 +305,13 @@ struct Lane {
     // z is needed only for the gate at the end of the tile: its load latency hides
     // behind the tile's tokens (the adjoint reads it at every token)
     if ((kOut || MODE == kAdjoint) && HAS_Z) load_tile<IO_BF16>(wz, z, t, vec);
+    // the convolution's halo around the tile: three tokens before it, one after
+    float xl[kConvBack], xr = 0.0f;
+    if (CONV != kNoConv) {
+#pragma unroll
+      for (int k = 0; k < kConvBack; ++k) xl[k] = x_at(t - kConvBack + k);
+      xr = x_at(t + kTok);
+    }
     float yt[kTok];
     BC cur, nxt;
     load_bc<MODE>(cur, t + (REV ? kTok - 1 : 0));
@@ -287,8 +320,17 @@ struct Lane {
       const int j = REV ? kTok - 1 - jj : jj;
       // prefetch the next token's B/C: its scalar-load latency hides behind this token
       if (jj + 1 < kTok) load_bc<MODE>(nxt, t + (REV ? j - 1 : j + 1));
-      float yv = token<MODE>(IO::get(wu, j), IO::get(wd, j), cur,
-                             (MODE == kAdjoint && HAS_Z) ? IO::get(wz, j) : 0.0f);
+      float uu = IO::get(wu, j);
+      if (CONV != kNoConv) {
+        float xw[kConvTaps];
+#pragma unroll
+        for (int k = 0; k < kConvTaps; ++k) {
+          const int jk = j - kConvBack + k;  // compile-time: inside the tile or in the halo
+          xw[k] = jk < 0 ? xl[jk + kConvBack < 0 ? 0 : jk + kConvBack] : (jk >= kTok ? xr : IO::get(wu, jk < kTok ? jk : 0));
+        }
+        uu = conv_out(xw);
+      }
+      float yv = token<MODE>(uu, IO::get(wd, j), cur, (MODE == kAdjoint && HAS_Z) ? IO::get(wz, j) : 0.0f);
       // materialise this token's readout now: otherwise it is sunk towards the
       // tile's store and all tokens' states stay live
       if (MODE != kAggregate && MODE != kAdjoint) asm volatile("" : "+v"(yv));
@@ -316,7 +358,15 @@ struct Lane {
 
   template <int MODE>
   __device__ __forceinline__ void partial_token(int64_t t) {
-    const float uu = IO::load(u, t);
+    float uu;
+    if (CONV != kNoConv) {
+      float xw[kConvTaps];
+#pragma unroll
+      for (int k = 0; k < kConvTaps; ++k) xw[k] = x_at(t - kConvBack + k);
+      uu = conv_out(xw);
+    } else {
+      uu = IO::load(u, t);
+    }
     BC cur;
     load_bc<MODE>(cur, t);
     const float yv = token<MODE>(uu, IO::load(delta, t), cur, (MODE == kAdjoint && HAS_Z) ? IO::load(z, t) : 0.0f);
@@ -376,6 +426,19 @@ __device__ __forceinline__ void init_lane(LaneT& L, const ScanArgs& a, int dir, 
   L.bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
   L.Dd = p.D ? p.D[d] : 0.0f;
   L.sum_dt = 0.0f;
+  L.len = a.len;
+  L.cb = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kConvTaps; ++k) L.cw[k] = 0.0f;
+  if (LaneT::kConv != kNoConv) {
+    // tap j of the kernel multiplies x[t - conv_left + j], slot kConvBack - conv_left + j
+#pragma unroll
+    for (int k = 0; k < kConvTaps; ++k) {
+      const int j = k - (kConvBack - a.conv_left);
+      L.cw[k] = (j >= 0 && j < a.conv_width) ? a.conv_w[d * a.conv_width + j] : 0.0f;
+    }
+    L.cb = a.conv_b ? a.conv_b[d] : 0.0f;
+  }
   L.lane = lane;
   L.vec = vec;
 #pragma unroll
@@ -449,7 +512,7 @@ __global__ __launch_bounds__(256) void stage_bc_kernel(ScanArgs a, float* __rest
 // Step 1: end state (from zero) and sum of step sizes of every segment except the
 // last one in scan order.  Grid: batch * nseg * ngroups one-wave blocks;
 // blockIdx.y selects the direction.
-template <bool IO_BF16, bool SOFTPLUS>
+template <bool IO_BF16, bool SOFTPLUS, int CONV = kNoConv>
 __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_aggregate_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
                                                                 const float* __restrict__ bc,
                                                                 float* __restrict__ agg, int vec) {
@@ -458,7 +521,7 @@ __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_aggregate_kernel(
   const int dir = blockIdx.y;
   const int reverse = a.ndir == 2 ? dir : a.reverse;
   if (reverse ? s.seg == 0 : s.seg == nseg - 1) return;
-  Lane<IO_BF16, SOFTPLUS, false> L;
+  Lane<IO_BF16, SOFTPLUS, false, CONV> L;
   init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
   const int64_t t0 = s.seg * seg_len;
   const int64_t t1 = min64(a.len, t0 + seg_len);

@@ -41,6 +41,23 @@ struct ScanArgs {
   int64_t batch, dim, len;
   const float* h0;          // nullable: state before the first scanned token, [batch][dim][16]
   float* h_last;            // nullable: receives the state after the last scanned token (may equal h0)
+  // Depthwise convolution in front of the scan (conv_w != nullptr): u is then
+  // act(conv_b + sum_j conv_w[d][j] * x[t - conv_left + j]) of the x held in `u`.
+  const float* conv_w;      // [dim][conv_width]
+  const float* conv_b;      // nullable, [dim]
+  int conv_width;           // taps, with conv_left <= 3 and conv_width - 1 - conv_left <= 1
+  int conv_left;            // taps before the output token (causal: width - 1)
+  int conv_silu;            // silu after the bias
+};
+
+// A standalone depthwise convolution (the same operation as the scan's front-end).
+struct ConvArgs {
+  const void* x;
+  void* y;
+  const float* w;
+  const float* b;           // nullable
+  int width, left, silu, io_bf16;
+  int64_t batch, dim, len;
 };
 
 // One token of the recurrence from a stored state (single-step decode).
@@ -137,5 +154,7 @@ hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* workspace, hipSt
 hipError_t launch_state_passthrough(const ScanArgs& a, hipStream_t stream);
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream);
 
 }  // namespace sscan

@@ -38,13 +38,13 @@ namespace {
 
 // Step 3, one direction: every wave scans one segment of 64 channels from its entry
 // state and stores the gated output.
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV>
 __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_output_dir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
                                                                  const float* __restrict__ bc,
                                                                  const float* __restrict__ hin, int vec) {
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
-  Lane<IO_BF16, SOFTPLUS, HAS_Z> L;
+  Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV> L;
   init_lane(L, a, 0, s.b, s.g, bc, vec != 0);
   load_entry(L, a, 0, s.b, s.seg, s.g, nseg, hin);
   const int64_t t0 = s.seg * seg_len;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t 
 // Step 3, both directions: wave 0 scans the segment forward, wave 1 in reverse.
 // Each first covers the half it meets first and parks its outputs in LDS, then
 // covers the other half, adds the partner's parked outputs, gates and stores.
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV>
 __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
                                                                        const float* __restrict__ bc,
                                                                        const float* __restrict__ hin, int vec) {
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
   const int dir = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kLanes);  // wave-uniform
-  Lane<IO_BF16, SOFTPLUS, HAS_Z> L;
+  Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV> L;
   init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
   load_entry(L, a, dir, s.b, s.seg, s.g, nseg, hin);
   const int64_t t0 = s.seg * seg_len;
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV>
 hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
@@ -185,7 +185,7 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   }
   mark(1);
   if (p.nseg > 1) {
-    hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS>), dim3(unsigned(nblocks), unsigned(a.ndir)),
+    hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS, CONV>), dim3(unsigned(nblocks), unsigned(a.ndir)),
                        dim3(kLanes), 0, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), agg, int(vec));
     mark(2);
     const int64_t carry_blocks = int64_t(a.ndir) * a.batch * kDState * ngroups;
@@ -195,12 +195,12 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   if (p.nseg <= 1) mark(2);
   mark(3);
   if (a.ndir == 1) {
-    hipLaunchKernelGGL((scan_output_dir_kernel<IO_BF16, SOFTPLUS, HAS_Z>), dim3(unsigned(nblocks)), dim3(kLanes), 0,
+    hipLaunchKernelGGL((scan_output_dir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV>), dim3(unsigned(nblocks)), dim3(kLanes), 0,
                        stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), static_cast<const float*>(hin),
                        int(vec));
   } else {
     const size_t lds = size_t(p.seg_len) * kLanes * sizeof(float);
-    hipLaunchKernelGGL((scan_output_bidir_kernel<IO_BF16, SOFTPLUS, HAS_Z>), dim3(unsigned(nblocks)),
+    hipLaunchKernelGGL((scan_output_bidir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV>), dim3(unsigned(nblocks)),
                        dim3(2 * kLanes), lds, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc),
                        static_cast<const float*>(hin), int(vec));
   }
@@ -208,12 +208,61 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   return hipGetLastError();
 }
 
+template <bool IO_BF16, int CONV>
+hipError_t launch_conv_mode(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
+  if (a.softplus) {
+    return a.z ? launch_typed<IO_BF16, true, true, CONV>(a, p, w, stream, ev)
+               : launch_typed<IO_BF16, true, false, CONV>(a, p, w, stream, ev);
+  }
+  return a.z ? launch_typed<IO_BF16, false, true, CONV>(a, p, w, stream, ev)
+             : launch_typed<IO_BF16, false, false, CONV>(a, p, w, stream, ev);
+}
+
 template <bool IO_BF16>
 hipError_t launch_io(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
-  if (a.softplus) {
-    return a.z ? launch_typed<IO_BF16, true, true>(a, p, w, stream, ev) : launch_typed<IO_BF16, true, false>(a, p, w, stream, ev);
+  if (!a.conv_w) return launch_conv_mode<IO_BF16, kNoConv>(a, p, w, stream, ev);
+  return a.conv_silu ? launch_conv_mode<IO_BF16, kConvSilu>(a, p, w, stream, ev)
+                     : launch_conv_mode<IO_BF16, kConvLin>(a, p, w, stream, ev);
+}
+
+// Standalone depthwise convolution: each thread produces kConvRun consecutive outputs
+// of one row from the run's x and its halo (three tokens before, one after).
+constexpr int kConvRun = 8;
+
+template <bool IO_BF16, bool SILU>
+__global__ __launch_bounds__(256) void conv1d_kernel(ConvArgs a) {
+  using IO = Io<IO_BF16>;
+  using T = typename IO::T;
+  const int64_t runs = (a.len + kConvRun - 1) / kConvRun;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= a.batch * a.dim * runs) return;
+  const int64_t row = i / runs;
+  const int64_t t0 = (i % runs) * kConvRun;
+  const int64_t d = row % a.dim;
+  const T* x = static_cast<const T*>(a.x) + row * a.len;
+  T* y = static_cast<T*>(a.y) + row * a.len;
+  float cw[kConvTaps];
+#pragma unroll
+  for (int k = 0; k < kConvTaps; ++k) {
+    const int j = k - (kConvBack - a.left);
+    cw[k] = (j >= 0 && j < a.width) ? a.w[d * a.width + j] : 0.0f;
   }
-  return a.z ? launch_typed<IO_BF16, false, true>(a, p, w, stream, ev) : launch_typed<IO_BF16, false, false>(a, p, w, stream, ev);
+  const float cb = a.b ? a.b[d] : 0.0f;
+  constexpr int kSpan = kConvBack + kConvRun + 1;
+  float xs[kSpan];  // x[t0 - 3 .. t0 + kConvRun], zero outside the row
+#pragma unroll
+  for (int k = 0; k < kSpan; ++k) {
+    const int64_t t = t0 - kConvBack + k;
+    xs[k] = (t >= 0 && t < a.len) ? IO::load(x, t) : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < kConvRun; ++j) {
+    float acc = cb;
+#pragma unroll
+    for (int k = 0; k < kConvTaps; ++k) acc = fmaf(cw[k], xs[j + k], acc);
+    if (SILU) acc = silu_f32(acc);
+    if (t0 + j < a.len) IO::store(y, t0 + j, acc);
+  }
 }
 
 }  // namespace
@@ -265,6 +314,25 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
 
 hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* ws, hipStream_t stream, hipEvent_t const* events) {
   return a.io_bf16 ? launch_io<true>(a, p, ws, stream, events) : launch_io<false>(a, p, ws, stream, events);
+}
+
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream) {
+  const int64_t n = a.batch * a.dim * ((a.len + kConvRun - 1) / kConvRun);
+  const dim3 grid(unsigned((n + 255) / 256));
+  if (a.io_bf16) {
+    if (a.silu) {
+      hipLaunchKernelGGL((conv1d_kernel<true, true>), grid, dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((conv1d_kernel<true, false>), grid, dim3(256), 0, stream, a);
+    }
+  } else {
+    if (a.silu) {
+      hipLaunchKernelGGL((conv1d_kernel<false, true>), grid, dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((conv1d_kernel<false, false>), grid, dim3(256), 0, stream, a);
+    }
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_state_passthrough(const ScanArgs& a, hipStream_t stream) {

@@ -38,6 +38,11 @@ class DirParams(ctypes.Structure):
                 ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p)]
 
 
+class ConvParams(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("width", ctypes.c_int),
+                ("same", ctypes.c_int), ("silu", ctypes.c_int)]
+
+
 class DirGrads(ctypes.Structure):
     _fields_ = [("ddelta", ctypes.c_void_p), ("ddelta_bias", ctypes.c_void_p), ("dA", ctypes.c_void_p),
                 ("dB", ctypes.c_void_p), ("dC", ctypes.c_void_p), ("dD", ctypes.c_void_p)]
@@ -92,6 +97,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_bidir_bwd_profiled.restype = I
     lib.sscan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.sscan_bwd_workspace_bytes.restype = SZ
+    CP = ctypes.POINTER(ConvParams)
+    lib.sscan_conv1d.argtypes = [V, CP, V, I64, I64, I64, V, I]
+    lib.sscan_conv1d.restype = I
+    lib.sscan_validate_conv1d.argtypes = [V, CP, V, I64, I64, I64, I]
+    lib.sscan_validate_conv1d.restype = I
+    lib.sscan_fwd_conv.argtypes = [V, CP, V, V, I, V, V, V, V, V, V, I64, I64, I64, I64, I, V, I, I, V, SZ]
+    lib.sscan_fwd_conv.restype = I
+    lib.sscan_bidir_conv.argtypes = [V, CP, V, V, DP, DP, I, I64, I64, I64, I64, V, I, I, V, SZ]
+    lib.sscan_bidir_conv.restype = I
     lib.sscan_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.sscan_workspace_bytes.restype = SZ
     lib.sscan_strerror.argtypes = [I]
@@ -361,6 +375,105 @@ def bidir(u, z, fwd: dict, rev: dict, softplus: bool = True, out: Optional[torch
         st = lib.sscan_bidir_profiled(*args, ctypes.cast(events.handles, ctypes.c_void_p))
     if st != 0:
         raise SScanError(st, "sscan_bidir")
+    return out
+
+
+def _conv_params(conv: dict, dim: int, dev) -> ConvParams:
+    w = conv["weight"]
+    _check(w, "conv weight", dev, torch.float32)
+    if w.dim() != 2 or w.shape[0] != dim:
+        raise ValueError(f"conv weight must be [dim={dim}, width]")
+    _check(conv.get("bias"), "conv bias", dev, torch.float32, (dim,))
+    b = conv.get("bias")
+    return ConvParams(w.data_ptr(), b.data_ptr() if b is not None else None, int(w.shape[1]),
+                      int(bool(conv.get("same", False))), int(bool(conv.get("silu", False))))
+
+
+def conv1d(x, weight, bias=None, same: bool = False, silu: bool = False,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Depthwise convolution of each channel (``sscan_conv1d``): x [batch, dim, len]
+    f32/bf16, weight [dim, width] f32 (causal, or centred when ``same``), optional
+    bias [dim] f32, optional silu."""
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.conv1d needs CUDA (HIP) tensors")
+    if x.dtype not in _DT_CODE:
+        raise TypeError("x must be float32 or bfloat16")
+    b, d, L = x.shape
+    _check(x, "x", dev)
+    cp = _conv_params(dict(weight=weight, bias=bias, same=same, silu=silu), d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", dev, x.dtype, x.shape)
+    st = lib.sscan_conv1d(_ptr(x), ctypes.byref(cp), _ptr(out), b, d, L, _stream(dev), _DT_CODE[x.dtype])
+    if st != 0:
+        raise SScanError(st, "sscan_conv1d")
+    return out
+
+
+def fwd_conv(x, conv: dict, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+             reverse: bool = False, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``sscan_fwd_conv``: the scan of u = conv(x), the convolution computed inside
+    the scan kernels.  ``conv`` holds weight [dim, width] f32 and optional bias,
+    same, silu."""
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.fwd_conv needs CUDA (HIP) tensors")
+    if x.dtype not in _DT_CODE or B.dtype not in _DT_CODE:
+        raise TypeError("x/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = x.shape
+    _check(x, "x", dev)
+    _check(delta, "delta", dev, x.dtype, x.shape)
+    _check(z, "z", dev, x.dtype, x.shape)
+    _check(A, "A", dev, torch.float32, (d, DSTATE))
+    _check(B, "B", dev, None, (b, DSTATE, L))
+    _check(C, "C", dev, B.dtype, (b, DSTATE, L))
+    _check(D, "D", dev, torch.float32, (d,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (d,))
+    cp = _conv_params(conv, d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", dev, x.dtype, x.shape)
+    if x.numel() == 0:
+        return out
+    ws, ws_bytes = _workspace(workspace_bytes(b, d, L, DSTATE, False), dev, workspace)
+    st = lib.sscan_fwd_conv(_ptr(x), ctypes.byref(cp), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A),
+                            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out), b, d, L, DSTATE, int(bool(reverse)),
+                            _stream(dev), _DT_CODE[x.dtype], _DT_CODE[B.dtype], _ptr(ws), ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_fwd_conv")
+    return out
+
+
+def bidir_conv(x, conv: dict, z, fwd: dict, rev: dict, softplus: bool = True, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``sscan_bidir_conv``: both directions over u = conv(x), summed, gated once."""
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.bidir_conv needs CUDA (HIP) tensors")
+    if x.dtype not in _DT_CODE or fwd["B"].dtype not in _DT_CODE:
+        raise TypeError("x/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = x.shape
+    _check(x, "x", dev)
+    _check(z, "z", dev, x.dtype, x.shape)
+    pf = _dir(fwd, "fwd", dev, x, fwd["B"].dtype)
+    pr = _dir(rev, "rev", dev, x, fwd["B"].dtype)
+    cp = _conv_params(conv, d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", dev, x.dtype, x.shape)
+    if x.numel() == 0:
+        return out
+    ws, ws_bytes = _workspace(workspace_bytes(b, d, L, DSTATE, True), dev, workspace)
+    st = lib.sscan_bidir_conv(_ptr(x), ctypes.byref(cp), _ptr(z), _ptr(out), ctypes.byref(pf), ctypes.byref(pr),
+                              int(bool(softplus)), b, d, L, DSTATE, _stream(dev), _DT_CODE[x.dtype],
+                              _DT_CODE[fwd["B"].dtype], _ptr(ws), ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_bidir_conv")
     return out
 
 

@@ -279,3 +279,25 @@ def test_validate_bwd(lib):
     e = fwd_args(b, d, 0, u=None, delta=None, y=None)
     assert bwd_call(lib, dict(e, ws=None, ws_bytes=0), [None, g[1], g[2], None, None, g[5]], None, None, None) == OK
     assert bwd_call(lib, dict(e, ws=None, ws_bytes=0), [None, g[1], None, None, None, g[5]], None, None, None) == ENULL
+
+
+# --- front-end convolution --------------------------------------------------------------------
+
+def test_validate_conv1d(lib):
+    f = Fake()
+    f.next = 1 << 46
+    b, d, L = 2, 64, 100
+    x, y, w, bias = f(b * d * L * 4), f(b * d * L * 4), f(d * 16), f(d * 4)
+    V = lambda cp, **kw: lib.sscan_validate_conv1d(kw.get("x", x), ctypes.byref(cp) if cp else None, kw.get("y", y),
+                                                   b, d, L, kw.get("io", 0))
+    C = lambda width, same=0, silu=0, weight=w, bias_=bias: sscan.ConvParams(weight, bias_, width, same, silu)
+    for width in (1, 2, 3, 4):
+        assert V(C(width)) == OK
+    assert V(C(3, same=1)) == OK and V(C(1, same=1)) == OK and V(C(4, silu=1)) == OK
+    assert V(C(5)) == EUNSUP and V(C(0)) == EUNSUP
+    assert V(C(2, same=1)) == EUNSUP and V(C(5, same=1)) == EUNSUP  # centred needs an odd width <= 3
+    assert V(C(3, silu=2)) == EUNSUP
+    assert V(C(3, weight=None)) == ENULL and V(None) == ENULL
+    assert V(C(3), y=x) == EALIAS and V(C(3), y=w) == EALIAS
+    assert V(C(3, weight=w + 2)) == EALIGN
+    assert V(C(3), y=y + 2, io=1) == OK and V(C(3), y=y + 1, io=1) == EALIGN
