@@ -6,7 +6,7 @@ len 262144, dstate 16, bf16 u/delta/z/y, f32 B/C, seeded synthetic inputs alread
 resident in HBM).  One step = one sscan_fwd call (all its kernels).  Prints ONE
 JSON line on stdout.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd|conv|fwd-conv]
                  [--no-cpu] [--copy-calibration]
 
 Timing: K plain calls between two HIP events give ms_per_step (for a workload
@@ -270,6 +270,120 @@ def cpu_baseline_bwd(x, g, cfg, target_s: float = 8.0):
                       f"fp64 backward per row, {cores} threads, {dt:.1f} s", "seconds": dt, "cpu_model": cpu_model()}
 
 
+# Front-end convolution of the Mamba block: 4 causal taps with bias and silu
+# (the pages' layer has no activation; silu is the heavier case).
+CONV = dict(width=4, same=False, silu=True)
+
+
+def conv_params(torch, dim, dev):
+    import numpy as np
+
+    rng = np.random.default_rng(777)
+    return dict(weight=torch.from_numpy(rng.normal(0.0, 0.5, (dim, CONV["width"]))).float().to(dev),
+                bias=torch.from_numpy(rng.normal(0.0, 0.1, dim)).float().to(dev), same=CONV["same"], silu=CONV["silu"])
+
+
+def bench_conv(args, torch, I, sscan, cfg, ci):
+    """--pass conv: sscan_conv1d alone on the workload's input (HBM-bound);
+    --pass fwd-conv: the scan with the convolution fused in, beside conv1d
+    followed by the plain scan."""
+    dev = torch.device("cuda:0")
+    x = I.config_inputs(ci, 0)
+    xd = x.to(dev)
+    cp = conv_params(torch, cfg.dim, dev)
+    io = 2 if cfg.io_dtype == "bf16" else 4
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    u = torch.empty_like(xd.u)
+    conv_fn = lambda: sscan.conv1d(xd.u, cp["weight"], cp["bias"], same=cp["same"], silu=cp["silu"], out=u)
+    conv_ms = timed(conv_fn, args.steps)
+    conv_bytes = 2 * cfg.elems * io + cfg.dim * (CONV["width"] + 1) * 4
+    base = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded numpy PCG64, shapes of the pages' workloads)",
+            "metric": METRIC}
+    cfg_dict = {"workload": cfg.name, "batch": cfg.batch, "dim": cfg.dim, "len": cfg.len, "dstate": cfg.dstate,
+                "directions": cfg.ndir, "io_dtype": cfg.io_dtype, "bc_dtype": cfg.bc_dtype, "conv": CONV}
+    if args.pass_ == "conv":
+        gbs = conv_bytes / (conv_ms * 1e-3) / 1e9
+        out = dict(base, value=cfg.elems / (conv_ms * 1e-3) / 1e6, unit="Melem/s", ms_per_step=conv_ms,
+                   config=dict(cfg_dict, **{"pass": "conv"}),
+                   roofline={"bound": "hbm", "kernel": "conv1d", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                   hbm={"algorithmic_bytes_per_step": conv_bytes, "achievable_copy_GBs": copy_bandwidth(torch, dev)})
+        if not args.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_conv(x, cp, cfg)
+        return out
+    ws = torch.empty(max(1, sscan.workspace_bytes(cfg.batch, cfg.dim, cfg.len, cfg.dstate, cfg.bidir)),
+                     dtype=torch.uint8, device=dev)
+    y = torch.empty_like(xd.u)
+    mk = lambda p: dict(delta=xd.delta, delta_bias=p.delta_bias, A=p.A, B=p.B, C=p.C, D=p.D)
+
+    def fused(events=None):
+        if cfg.ndir == 1:
+            p = xd.dirs[0]
+            return sscan.fwd_conv(xd.u, cp, xd.delta, p.A, p.B, p.C, p.D, xd.z, p.delta_bias, out=y, workspace=ws,
+                                  events=events)
+        return sscan.bidir_conv(xd.u, cp, xd.z, mk(xd.dirs[0]), mk(xd.dirs[1]), out=y, workspace=ws, events=events)
+
+    xu = I.ScanInputs(u, xd.delta, xd.z, xd.dirs, xd.io_dtype, xd.bc_dtype)
+
+    def unfused():
+        conv_fn()
+        sscan.run_inputs(xu, out=y, workspace=ws)
+
+    ms = timed(fused, args.steps)
+    unfused_ms = timed(unfused, args.steps)
+    evsets = [sscan.HipEvents() for _ in range(args.steps)]
+    for ev in evsets:
+        fused(ev)
+    torch.cuda.synchronize()
+    kernel_ms = {k: sum(ev.step_ms()[k] for ev in evsets) / args.steps for k in sscan.PROFILE_STEPS}
+    flops = FLOPS_PER_ELEM_STATE * cfg.dstate * cfg.elems * cfg.ndir
+    achieved = flops / (kernel_ms["output"] * 1e-3) / 1e12
+    return dict(base, value=cfg.elems / (ms * 1e-3) / 1e6, unit="Melem/s", ms_per_step=ms,
+                config=dict(cfg_dict, **{"pass": "fwd-conv"}),
+                roofline={"bound": "alu", "kernel": "output", "achieved": achieved, "peak": ALU_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": achieved / ALU_PEAK_TFLOPS, "traffic": None},
+                kernels_ms=kernel_ms,
+                unfused={"ms_per_step": unfused_ms, "conv1d_ms": conv_ms,
+                         "note": "sscan_conv1d writing u, then sscan_fwd / sscan_bidir reading it"})
+
+
+def cpu_baseline_conv(x, cp, cfg, target_s: float = 4.0):
+    """The fp64 convolution oracle on whole sampled rows (single thread)."""
+    import numpy as np
+
+    from oracle import oracle
+    from selective_state_space_sscan_amd import inputs as I
+
+    w = cp["weight"].cpu().double().numpy()
+    b = cp["bias"].cpu().double().numpy()
+    rows, dt = 0, 0.0
+    rng = np.random.default_rng(99)
+    while dt < target_s and rows < cfg.batch * cfg.dim:
+        bi, di = int(rng.integers(cfg.batch)), int(rng.integers(cfg.dim))
+        xr = I.f64(x.u[bi:bi + 1, di:di + 1])
+        t0 = time.perf_counter()
+        oracle.conv1d(xr, w[di:di + 1], b[di:di + 1], cp["same"], cp["silu"])
+        dt += time.perf_counter() - t0
+        rows += 1
+    return {"value": rows * cfg.len / dt / 1e6, "unit": "Melem/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} whole rows of {cfg.len} tokens, fp64, one thread, {dt:.1f} s", "seconds": dt,
+            "cpu_model": cpu_model()}
+
+
 # Single-token decode (sscan_step): batch streams of the long-sequence workload's
 # 1536 channels, bf16 u/delta/z/y, f32 B/C and f32 state.
 DECODE = dict(name="decode-step", batch=256, dim=1536, io_dtype="bf16", bc_dtype="f32")
@@ -359,8 +473,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long-seq-fwd",
                     help="a scan workload of selective_state_space_sscan_amd.inputs.CONFIGS, or decode-step")
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
-                    help="time the forward call (default) or its backward pass")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "conv", "fwd-conv"), default="fwd",
+                    help="the forward call (default), its backward pass, the front-end convolution alone, "
+                         "or the scan with the convolution fused in")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with a 512 MiB negation kernel (counter calibration for rocprofv3 --pmc runs)")
@@ -383,6 +498,9 @@ def main():
     cfg = I.CONFIGS[ci]
     if args.pass_ == "bwd":
         print(json.dumps(bench_bwd(args, torch, I, sscan, cfg, ci)), flush=True)
+        return
+    if args.pass_ in ("conv", "fwd-conv"):
+        print(json.dumps(bench_conv(args, torch, I, sscan, cfg, ci)), flush=True)
         return
     dev = torch.device("cuda:0")
     x = I.config_inputs(ci, 0)

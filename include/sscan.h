@@ -232,6 +232,20 @@ SSCAN_API int sscan_bidir_profiled(const void* u, const void* z, void* y,
                          int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes,
                          void* const* events);
 
+/* Profiling variants of sscan_fwd_conv / sscan_bidir_conv: events as for
+ * sscan_fwd_profiled (SSCAN_PROFILE_EVENTS handles). */
+SSCAN_API int sscan_fwd_conv_profiled(const void* x, const sscan_conv_params* conv, const void* delta,
+                            const float* delta_bias, int softplus, const float* A, const void* B,
+                            const void* C, const float* D, const void* z, void* y,
+                            int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse, void* stream,
+                            int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes,
+                            void* const* events);
+SSCAN_API int sscan_bidir_conv_profiled(const void* x, const sscan_conv_params* conv, const void* z, void* y,
+                              const sscan_dir_params* fwd, const sscan_dir_params* rev, int softplus,
+                              int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                              int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes,
+                              void* const* events);
+
 /* Profiling variants of the backward entry points: the same work, and events[0]
  * is recorded before the first kernel and events[k] after step k: 1 = B/C staging,
  * 2 = states entering every window (segment aggregates and carry chain), 3 = the

@@ -586,6 +586,27 @@ int sscan_bidir_conv(const void* x, const sscan_conv_params* conv, const void* z
              workspace_bytes, nullptr, nullptr, nullptr, conv);
 }
 
+int sscan_fwd_conv_profiled(const void* x, const sscan_conv_params* conv, const void* delta, const float* delta_bias,
+                            int softplus, const float* A, const void* B, const void* C, const float* D, const void* z,
+                            void* y, int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse,
+                            void* stream, int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes,
+                            void* const* events) {
+  if (!conv) return SSCAN_ERR_NULL;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  return run(x, z, y, &d, 1, reverse, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype, workspace,
+             workspace_bytes, events, nullptr, nullptr, conv);
+}
+
+int sscan_bidir_conv_profiled(const void* x, const sscan_conv_params* conv, const void* z, void* y,
+                              const sscan_dir_params* fwd, const sscan_dir_params* rev, int softplus, int64_t batch,
+                              int64_t dim, int64_t len, int64_t dstate, void* stream, int io_dtype, int bc_dtype,
+                              void* workspace, size_t workspace_bytes, void* const* events) {
+  if (!conv || !fwd || !rev) return SSCAN_ERR_NULL;
+  const DirView d[2] = {view_of(fwd), view_of(rev)};
+  return run(x, z, y, d, 2, 0, softplus, batch, dim, len, dstate, stream, io_dtype, bc_dtype, workspace,
+             workspace_bytes, events, nullptr, nullptr, conv);
+}
+
 size_t sscan_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir) {
   Sizes sz{};
   if (check_sizes(batch, dim, len, dstate, SSCAN_F32, SSCAN_F32, &sz) != SSCAN_OK) return 0;

@@ -282,13 +282,42 @@ struct Lane {
     int64_t t = REV ? tb - kTok : ta;
     load_tile<IO_BF16>(cu, u, t, vec);
     load_tile<IO_BF16>(cd, delta, t, vec);
+    // convolution halo of the tile: the three tokens before it and the one after.
+    // Inside a run of tiles it comes from the neighbouring tiles' registers (the one
+    // just scanned, the one prefetched); only the run's ends read memory.
+    float xl[kConvBack] = {}, xr = 0.0f;
+    if (CONV != kNoConv) {
+      if (REV) {
+        xr = x_at(t + kTok);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kConvBack; ++k) xl[k] = x_at(t - kConvBack + k);
+      }
+    }
     for (int64_t i = 0; i < ntiles; ++i) {
       const int64_t tn = REV ? t - kTok : t + kTok;
-      if (i + 1 < ntiles) {
+      const bool more = i + 1 < ntiles;
+      if (more) {
         load_tile<IO_BF16>(nu, u, tn, vec);
         load_tile<IO_BF16>(nd, delta, tn, vec);
       }
-      tile<REV, MODE>(t, cu, cd);
+      if (CONV != kNoConv) {
+        if (REV) {
+#pragma unroll
+          for (int k = 0; k < kConvBack; ++k) xl[k] = more ? IO::get(nu, kTok - kConvBack + k) : x_at(t - kConvBack + k);
+        } else {
+          xr = more ? IO::get(nu, 0) : x_at(t + kTok);
+        }
+      }
+      tile<REV, MODE>(t, cu, cd, xl, xr);
+      if (CONV != kNoConv) {
+        if (REV) {
+          xr = IO::get(cu, 0);
+        } else {
+#pragma unroll
+          for (int k = 0; k < kConvBack; ++k) xl[k] = IO::get(cu, kTok - kConvBack + k);
+        }
+      }
 #pragma unroll
       for (int w = 0; w < kWords; ++w) {
         cu[w] = nu[w];
@@ -299,19 +328,13 @@ struct Lane {
   }
 
   template <bool REV, int MODE>
-  __device__ __forceinline__ void tile(int64_t t, const uint32_t (&wu)[kWords], const uint32_t (&wd)[kWords]) {
+  __device__ __forceinline__ void tile(int64_t t, const uint32_t (&wu)[kWords], const uint32_t (&wd)[kWords],
+                                      const float (&xl)[kConvBack], float xr) {
     constexpr bool kOut = (MODE == kStore || MODE == kMeet);
     uint32_t wz[kWords];
     // z is needed only for the gate at the end of the tile: its load latency hides
     // behind the tile's tokens (the adjoint reads it at every token)
     if ((kOut || MODE == kAdjoint) && HAS_Z) load_tile<IO_BF16>(wz, z, t, vec);
-    // the convolution's halo around the tile: three tokens before it, one after
-    float xl[kConvBack], xr = 0.0f;
-    if (CONV != kNoConv) {
-#pragma unroll
-      for (int k = 0; k < kConvBack; ++k) xl[k] = x_at(t - kConvBack + k);
-      xr = x_at(t + kTok);
-    }
     float yt[kTok];
     BC cur, nxt;
     load_bc<MODE>(cur, t + (REV ? kTok - 1 : 0));

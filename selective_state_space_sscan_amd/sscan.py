@@ -106,6 +106,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_fwd_conv.restype = I
     lib.sscan_bidir_conv.argtypes = [V, CP, V, V, DP, DP, I, I64, I64, I64, I64, V, I, I, V, SZ]
     lib.sscan_bidir_conv.restype = I
+    lib.sscan_fwd_conv_profiled.argtypes = lib.sscan_fwd_conv.argtypes + [V]
+    lib.sscan_fwd_conv_profiled.restype = I
+    lib.sscan_bidir_conv_profiled.argtypes = lib.sscan_bidir_conv.argtypes + [V]
+    lib.sscan_bidir_conv_profiled.restype = I
     lib.sscan_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.sscan_workspace_bytes.restype = SZ
     lib.sscan_strerror.argtypes = [I]
@@ -412,9 +416,17 @@ def conv1d(x, weight, bias=None, same: bool = False, silu: bool = False,
     return out
 
 
+def _fwd_events(events: Optional[HipEvents]):
+    if events is None:
+        return None
+    if events.steps != PROFILE_STEPS:
+        raise ValueError("the forward calls need HipEvents(PROFILE_STEPS)")
+    return ctypes.cast(events.handles, ctypes.c_void_p)
+
+
 def fwd_conv(x, conv: dict, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
              reverse: bool = False, out: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+             workspace: Optional[torch.Tensor] = None, events: Optional[HipEvents] = None) -> torch.Tensor:
     """``sscan_fwd_conv``: the scan of u = conv(x), the convolution computed inside
     the scan kernels.  ``conv`` holds weight [dim, width] f32 and optional bias,
     same, silu."""
@@ -440,16 +452,18 @@ def fwd_conv(x, conv: dict, delta, A, B, C, D=None, z=None, delta_bias=None, sof
     if x.numel() == 0:
         return out
     ws, ws_bytes = _workspace(workspace_bytes(b, d, L, DSTATE, False), dev, workspace)
-    st = lib.sscan_fwd_conv(_ptr(x), ctypes.byref(cp), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A),
-                            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out), b, d, L, DSTATE, int(bool(reverse)),
-                            _stream(dev), _DT_CODE[x.dtype], _DT_CODE[B.dtype], _ptr(ws), ws_bytes)
+    args = [_ptr(x), ctypes.byref(cp), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(z), _ptr(out), b, d, L, DSTATE, int(bool(reverse)), _stream(dev), _DT_CODE[x.dtype],
+            _DT_CODE[B.dtype], _ptr(ws), ws_bytes]
+    ev = _fwd_events(events)
+    st = lib.sscan_fwd_conv(*args) if ev is None else lib.sscan_fwd_conv_profiled(*args, ev)
     if st != 0:
         raise SScanError(st, "sscan_fwd_conv")
     return out
 
 
 def bidir_conv(x, conv: dict, z, fwd: dict, rev: dict, softplus: bool = True, out: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+               workspace: Optional[torch.Tensor] = None, events: Optional[HipEvents] = None) -> torch.Tensor:
     """``sscan_bidir_conv``: both directions over u = conv(x), summed, gated once."""
     lib = load_library()
     dev = x.device
@@ -469,9 +483,10 @@ def bidir_conv(x, conv: dict, z, fwd: dict, rev: dict, softplus: bool = True, ou
     if x.numel() == 0:
         return out
     ws, ws_bytes = _workspace(workspace_bytes(b, d, L, DSTATE, True), dev, workspace)
-    st = lib.sscan_bidir_conv(_ptr(x), ctypes.byref(cp), _ptr(z), _ptr(out), ctypes.byref(pf), ctypes.byref(pr),
-                              int(bool(softplus)), b, d, L, DSTATE, _stream(dev), _DT_CODE[x.dtype],
-                              _DT_CODE[fwd["B"].dtype], _ptr(ws), ws_bytes)
+    args = [_ptr(x), ctypes.byref(cp), _ptr(z), _ptr(out), ctypes.byref(pf), ctypes.byref(pr), int(bool(softplus)), b,
+            d, L, DSTATE, _stream(dev), _DT_CODE[x.dtype], _DT_CODE[fwd["B"].dtype], _ptr(ws), ws_bytes]
+    ev = _fwd_events(events)
+    st = lib.sscan_bidir_conv(*args) if ev is None else lib.sscan_bidir_conv_profiled(*args, ev)
     if st != 0:
         raise SScanError(st, "sscan_bidir_conv")
     return out
