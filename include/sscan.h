@@ -165,6 +165,43 @@ SSCAN_API int sscan_bidir_conv(const void* x, const sscan_conv_params* conv, con
                      int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
                      int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
 
+/* Scans of a 2-D feature map along several visiting orders (Mamba in the YOLO26
+ * backbone page, section 1.2: rows, columns or crosswise in several directions;
+ * sections 2.2 and 4.4: row scans both ways, four directions; Samba page, section
+ * 3.1: a centre-out spiral).  The map [height, width] is flattened row-major, token
+ * t = r * width + c, so u, z, y and every direction's delta are [batch, dim,
+ * height * width] and B, C [batch, dstate, height * width] in that token layout.
+ * Direction k visits the tokens in the order kinds[k] names and has its own
+ * parameters dirs[k]; its output is written at the tokens' own positions, the
+ * directions are summed (in fp32) and gated once:
+ *   out = (sum_k scan_k) * silu(z)          (z == NULL: no gate)
+ * kinds: rows, columns (column by column, top to bottom), or the permutation
+ * index[0 .. height*width) (a device int32 array, required when used; entries must
+ * be a permutation of the tokens -- others read as 0 and are not written), each
+ * forward or reversed; each kind at most once (1 to 6 directions).  Workspace:
+ * sscan_multi_workspace_bytes(...) bytes, 256-byte aligned. */
+enum sscan_order {
+  SSCAN_ORDER_ROW = 0,
+  SSCAN_ORDER_ROW_REV = 1,
+  SSCAN_ORDER_COL = 2,
+  SSCAN_ORDER_COL_REV = 3,
+  SSCAN_ORDER_INDEX = 4,
+  SSCAN_ORDER_INDEX_REV = 5
+};
+SSCAN_API int sscan_multi(const void* u, const void* z, void* y, const sscan_dir_params* dirs, const int* kinds,
+                int ndirs, const int32_t* index, int softplus, int64_t batch, int64_t dim,
+                int64_t height, int64_t width, int64_t dstate, void* stream, int io_dtype, int bc_dtype,
+                void* workspace, size_t workspace_bytes);
+SSCAN_API size_t sscan_multi_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width,
+                                   int64_t dstate, const int* kinds, int ndirs, int io_dtype, int bc_dtype);
+
+/* The Samba page's centre-out clockwise spiral over a [height, width] map, read as
+ * the square spiral right 1, down 1, left 2, up 2, right 3, ... from the centre cell
+ * (the lower middle index of an even side; rows grow downwards), skipping cells
+ * outside the map.  Writes height*width row-major token indices to `order` (HOST
+ * memory, caller-owned) for SSCAN_ORDER_INDEX. */
+SSCAN_API int sscan_spiral_order(int64_t height, int64_t width, int32_t* order);
+
 /* Gradients of one direction's parameters (all device pointers, written by the
  * backward entry points). */
 typedef struct sscan_dir_grads {
@@ -305,6 +342,11 @@ SSCAN_API int sscan_validate_bidir_bwd(const void* u, const void* z, const void*
 
 SSCAN_API int sscan_validate_conv1d(const void* x, const sscan_conv_params* conv, const void* y,
                           int64_t batch, int64_t dim, int64_t len, int io_dtype);
+
+SSCAN_API int sscan_validate_multi(const void* u, const void* z, const void* y, const sscan_dir_params* dirs,
+                         const int* kinds, int ndirs, const int32_t* index, int softplus, int64_t batch,
+                         int64_t dim, int64_t height, int64_t width, int64_t dstate, int io_dtype, int bc_dtype,
+                         const void* workspace, size_t workspace_bytes);
 
 /* Bytes of device workspace a call with these sizes needs (0 if none); bidir != 0
  * for sscan_bidir.  Returns 0 for invalid sizes (the call itself reports them). */

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsscan.so")
 
-SOURCES = ["sscan_kernels.hip", "sscan_bwd.hip", "sscan_capi.cpp"]
+SOURCES = ["sscan_kernels.hip", "sscan_bwd.hip", "sscan_multi.hip", "sscan_capi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -32,11 +32,10 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into ``libsscan.so`` next to this file; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + \
-        [os.path.join(CSRC, s) for s in SOURCES]
+OBJ_DIR = os.path.join(ROOT, "_build")
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,6 +46,25 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
     if verbose and lines:
         print("\n".join(lines))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel, into _build/) and link ``libsscan.so``
+    next to this file; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([hipcc()] + compile_flags + ["-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, os.path.join(CSRC, src)])
+    with ThreadPoolExecutor(max(1, min(len(cmds), os.cpu_count() or 1))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -607,6 +607,140 @@ int sscan_bidir_conv_profiled(const void* x, const sscan_conv_params* conv, cons
              workspace_bytes, events, nullptr, nullptr, conv);
 }
 
+// ---- several visiting orders of a 2-D map ------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+int check_kinds(const int* kinds, int ndirs, const int32_t* index) {
+  if (!kinds) return SSCAN_ERR_NULL;
+  if (ndirs < 1 || ndirs > sscan::kMaxMultiDirs) return SSCAN_ERR_UNSUPPORTED;
+  bool seen[sscan::kMaxMultiDirs] = {};
+  bool uses_index = false;
+  for (int k = 0; k < ndirs; ++k) {
+    if (kinds[k] < 0 || kinds[k] >= sscan::kMaxMultiDirs || seen[kinds[k]]) return SSCAN_ERR_UNSUPPORTED;
+    seen[kinds[k]] = true;
+    uses_index = uses_index || kinds[k] / 2 == sscan::kFamilyIndex;
+  }
+  if (uses_index && !index) return SSCAN_ERR_NULL;
+  return SSCAN_OK;
+}
+
+int validate_multi(const void* u, const void* z, const void* y, const sscan_dir_params* dirs, const int* kinds,
+                   int ndirs, const int32_t* index, int64_t batch, int64_t dim, int64_t height, int64_t width,
+                   int64_t dstate, int io_dtype, int bc_dtype, const void* workspace, size_t workspace_bytes,
+                   sscan::MultiPlan* plan, bool* empty) {
+  if (height < 0 || width < 0) return SSCAN_ERR_SHAPE;
+  if (height > 0 && width > (int64_t(1) << 40) / height) return SSCAN_ERR_SHAPE;
+  const int64_t len = height * width;
+  Sizes sz{};
+  int st = check_sizes(batch, dim, len, dstate, io_dtype, bc_dtype, &sz);
+  if (st != SSCAN_OK) return st;
+  st = check_kinds(kinds, ndirs, index);
+  if (st != SSCAN_OK) return st;
+  if (!dirs) return SSCAN_ERR_NULL;
+  *empty = (batch == 0 || dim == 0 || len == 0);
+  if (*empty) return SSCAN_OK;
+  if (!u || !y) return SSCAN_ERR_NULL;
+  if (!aligned(u, sz.io_esz) || !aligned(y, sz.io_esz) || !aligned(z, sz.io_esz) || !aligned(index, 4))
+    return SSCAN_ERR_ALIGN;
+  const Range yr = range_of(y, sz.io_elems * sz.io_esz);
+  if (overlap(yr, range_of(u, sz.io_elems * sz.io_esz)) || (z && overlap(yr, range_of(z, sz.io_elems * sz.io_esz))) ||
+      (index && overlap(yr, range_of(index, size_t(len) * 4))))
+    return SSCAN_ERR_ALIAS;
+  for (int k = 0; k < ndirs; ++k) {
+    st = check_dir(view_of(&dirs[k]), sz, dim, yr);
+    if (st != SSCAN_OK) return st;
+  }
+  *plan = sscan::make_multi_plan(batch, dim, height, width, kinds, ndirs, io_dtype == SSCAN_BF16,
+                                 bc_dtype == SSCAN_BF16);
+  if (!workspace || workspace_bytes < plan->workspace_bytes) return SSCAN_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return SSCAN_ERR_ALIGN;
+  if (overlap(yr, range_of(workspace, plan->workspace_bytes))) return SSCAN_ERR_ALIAS;
+  return SSCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sscan_validate_multi(const void* u, const void* z, const void* y, const sscan_dir_params* dirs, const int* kinds,
+                         int ndirs, const int32_t* index, int softplus, int64_t batch, int64_t dim, int64_t height,
+                         int64_t width, int64_t dstate, int io_dtype, int bc_dtype, const void* workspace,
+                         size_t workspace_bytes) {
+  (void)softplus;
+  sscan::MultiPlan plan{};
+  bool empty = false;
+  return validate_multi(u, z, y, dirs, kinds, ndirs, index, batch, dim, height, width, dstate, io_dtype, bc_dtype,
+                        workspace, workspace_bytes, &plan, &empty);
+}
+
+int sscan_multi(const void* u, const void* z, void* y, const sscan_dir_params* dirs, const int* kinds, int ndirs,
+                const int32_t* index, int softplus, int64_t batch, int64_t dim, int64_t height, int64_t width,
+                int64_t dstate, void* stream, int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes) {
+  sscan::MultiPlan plan{};
+  bool empty = false;
+  const int st = validate_multi(u, z, y, dirs, kinds, ndirs, index, batch, dim, height, width, dstate, io_dtype,
+                                bc_dtype, workspace, workspace_bytes, &plan, &empty);
+  if (st != SSCAN_OK || empty) return st;
+  sscan::MultiArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.u = u;
+  a.z = z;
+  a.y = y;
+  for (int k = 0; k < ndirs; ++k) {
+    const sscan_dir_params& p = dirs[k];
+    a.dir[k] = sscan::DirArgs{p.delta, p.delta_bias, p.A, p.B, p.C, p.D};
+    a.kind[k] = kinds[k];
+  }
+  a.ndir = ndirs;
+  a.index = index;
+  a.softplus = softplus ? 1 : 0;
+  a.io_bf16 = io_dtype == SSCAN_BF16;
+  a.bc_bf16 = bc_dtype == SSCAN_BF16;
+  a.batch = batch;
+  a.dim = dim;
+  a.height = height;
+  a.width = width;
+  const hipError_t e = sscan::launch_multi(a, plan, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+}
+
+size_t sscan_multi_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate,
+                                   const int* kinds, int ndirs, int io_dtype, int bc_dtype) {
+  if (height < 0 || width < 0 || (height > 0 && width > (int64_t(1) << 40) / height)) return 0;
+  Sizes sz{};
+  if (check_sizes(batch, dim, height * width, dstate, io_dtype, bc_dtype, &sz) != SSCAN_OK) return 0;
+  if (check_kinds(kinds, ndirs, reinterpret_cast<const int32_t*>(1)) != SSCAN_OK) return 0;
+  if (batch == 0 || dim == 0 || height * width == 0) return 0;
+  return sscan::make_multi_plan(batch, dim, height, width, kinds, ndirs, io_dtype == SSCAN_BF16,
+                                bc_dtype == SSCAN_BF16)
+      .workspace_bytes;
+}
+
+// The centre-out clockwise spiral: from the centre cell (the lower middle index of
+// an even side) walk right 1, down 1, left 2, up 2, right 3, down 3, ... (rows grow
+// downwards), listing the cells that fall inside the map.
+int sscan_spiral_order(int64_t height, int64_t width, int32_t* order) {
+  if (height < 0 || width < 0 || (height > 0 && width > (int64_t(1) << 31) / height)) return SSCAN_ERR_SHAPE;
+  const int64_t n = height * width;
+  if (n == 0) return SSCAN_OK;
+  if (!order) return SSCAN_ERR_NULL;
+  int64_t r = (height - 1) / 2, c = (width - 1) / 2, k = 0;
+  order[k++] = int32_t(r * width + c);
+  static const int dr[4] = {0, 1, 0, -1}, dc[4] = {1, 0, -1, 0};
+  for (int64_t leg = 0; k < n; ++leg) {
+    const int64_t steps = leg / 2 + 1;
+    for (int64_t i = 0; i < steps; ++i) {
+      r += dr[leg % 4];
+      c += dc[leg % 4];
+      if (r >= 0 && r < height && c >= 0 && c < width) order[k++] = int32_t(r * width + c);
+    }
+  }
+  return SSCAN_OK;
+}
+
 size_t sscan_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir) {
   Sizes sz{};
   if (check_sizes(batch, dim, len, dstate, SSCAN_F32, SSCAN_F32, &sz) != SSCAN_OK) return 0;

@@ -8,6 +8,7 @@
 #include "sscan_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sscan {
 namespace {
@@ -173,16 +174,19 @@ constexpr int kConvBack = 3;
 
 // One lane's view of one direction of one (batch, channel) row.  SOFTPLUS, HAS_Z
 // and CONV are compile-time so that a tile's tokens form one straight-line block.
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV = kNoConv>
+// Y_F32 stores y in fp32 whatever the input dtype (partial outputs that are summed
+// before rounding, in the multi-order scan).
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV = kNoConv, bool Y_F32 = false>
 struct Lane {
   using IO = Io<IO_BF16>;
   using T = typename IO::T;
+  using TY = typename std::conditional<Y_F32, float, T>::type;
   static constexpr int kTok = IO::kTok;
   static constexpr int kConv = CONV;
   const T* u;
   const T* delta;
   const T* z;     // nullable
-  T* y;
+  TY* y;
   const float* __restrict__ bc;  // staged B/C of this (direction, batch): bc[t * 32 + ...]
   lds_float* part;  // LDS meeting buffer (bidirectional kernel), [t - t0][64]
   int64_t t0;     // first token of the segment (LDS buffer origin)
@@ -245,6 +249,20 @@ struct Lane {
   }
 
   __device__ __forceinline__ float gate(float yv, float zv) const { return HAS_Z ? yv * silu_f32(zv) : yv; }
+
+  // a finished tile of y: the storage dtype, or fp32 for Y_F32
+  __device__ __forceinline__ void store_y(int64_t t, const float (&yt)[kTok]) {
+    if (!Y_F32) {
+      store_tile<IO_BF16>(reinterpret_cast<T*>(y), t, yt, vec);
+    } else if (vec) {
+      float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t);
+#pragma unroll
+      for (int i = 0; i < kTok / 4; ++i) p[i] = make_float4(yt[4 * i], yt[4 * i + 1], yt[4 * i + 2], yt[4 * i + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kTok; ++j) reinterpret_cast<float*>(y)[t + j] = yt[j];
+    }
+  }
 
   // u from the convolution window x[t-3 .. t+1]
   __device__ __forceinline__ float conv_out(const float (&xw)[kConvTaps]) const {
@@ -375,7 +393,7 @@ struct Lane {
         if (MODE == kMeet) v += part[(t + j - t0) * kLanes + lane];
         yt[j] = gate(v, HAS_Z ? IO::get(wz, j) : 0.0f);
       }
-      if (active) store_tile<IO_BF16>(y, t, yt, vec);
+      if (active) store_y(t, yt);
     }
   }
 
@@ -398,7 +416,13 @@ struct Lane {
     } else if (MODE == kStore || MODE == kMeet) {
       float v = (MODE == kMeet) ? yv + part[(t - t0) * kLanes + lane] : yv;
       if (HAS_Z) v *= silu_f32(IO::load(z, t));
-      if (active) IO::store(y, t, v);
+      if (active) {
+        if (Y_F32) {
+          reinterpret_cast<float*>(y)[t] = v;
+        } else {
+          IO::store(reinterpret_cast<T*>(y), t, v);
+        }
+      }
     }
   }
 };
@@ -440,7 +464,7 @@ __device__ __forceinline__ void init_lane(LaneT& L, const ScanArgs& a, int dir, 
   L.u = static_cast<const T*>(a.u) + row;
   L.delta = static_cast<const T*>(p.delta) + row;
   L.z = a.z ? static_cast<const T*>(a.z) + row : nullptr;
-  L.y = static_cast<T*>(a.y) + row;
+  L.y = static_cast<typename LaneT::TY*>(a.y) + row;
   L.bc = bc + ((size_t)dir * a.batch + b) * a.len * kBC;
   L.part = nullptr;
   L.t0 = 0;

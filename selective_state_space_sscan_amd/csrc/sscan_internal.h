@@ -48,7 +48,37 @@ struct ScanArgs {
   int conv_width;           // taps, with conv_left <= 3 and conv_width - 1 - conv_left <= 1
   int conv_left;            // taps before the output token (causal: width - 1)
   int conv_silu;            // silu after the bias
+  int y_f32;                // store y in fp32 whatever io_bf16 (no gate, no convolution)
 };
+
+// Scans of a 2-D map along several visiting orders.  A direction's kind is
+// family * 2 + (1 for the reversed order); families: row-major, column-major, and
+// a caller-given permutation of the tokens.
+constexpr int kFamilyRow = 0, kFamilyCol = 1, kFamilyIndex = 2, kFamilies = 3;
+constexpr int kMaxMultiDirs = 2 * kFamilies;
+
+struct MultiArgs {
+  const void* u;            // [batch][dim][height * width] io dtype, token t = r * width + c
+  const void* z;            // nullable
+  void* y;
+  DirArgs dir[kMaxMultiDirs];
+  int kind[kMaxMultiDirs];
+  int ndir;
+  const int32_t* index;     // [height * width] visiting order of the index family
+  int softplus, io_bf16, bc_bf16;
+  int64_t batch, dim, height, width;
+};
+
+// Workspace (byte offsets, 256-aligned): fp32 accumulator, one family's output,
+// gathered u, gathered delta/B/C of a family's two directions, the scan's own.
+struct MultiPlan {
+  size_t off_acc, off_y, off_u, off_delta[2], off_B[2], off_C[2], off_scan;
+  size_t workspace_bytes;
+};
+
+MultiPlan make_multi_plan(int64_t batch, int64_t dim, int64_t height, int64_t width, const int* kinds, int ndir,
+                          bool io_bf16, bool bc_bf16);
+hipError_t launch_multi(const MultiArgs& a, const MultiPlan& p, char* workspace, hipStream_t stream);
 
 // A standalone depthwise convolution (the same operation as the scan's front-end).
 struct ConvArgs {

@@ -38,13 +38,13 @@ namespace {
 
 // Step 3, one direction: every wave scans one segment of 64 channels from its entry
 // state and stores the gated output.
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV>
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false>
 __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_output_dir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
                                                                  const float* __restrict__ bc,
                                                                  const float* __restrict__ hin, int vec) {
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
-  Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV> L;
+  Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32> L;
   init_lane(L, a, 0, s.b, s.g, bc, vec != 0);
   load_entry(L, a, 0, s.b, s.seg, s.g, nseg, hin);
   const int64_t t0 = s.seg * seg_len;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t 
 // Step 3, both directions: wave 0 scans the segment forward, wave 1 in reverse.
 // Each first covers the half it meets first and parks its outputs in LDS, then
 // covers the other half, adds the partner's parked outputs, gates and stores.
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV>
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false>
 __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
                                                                        const float* __restrict__ bc,
                                                                        const float* __restrict__ hin, int vec) {
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
   const int dir = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kLanes);  // wave-uniform
-  Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV> L;
+  Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32> L;
   init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
   load_entry(L, a, dir, s.b, s.seg, s.g, nseg, hin);
   const int64_t t0 = s.seg * seg_len;
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV>
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false>
 hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
@@ -195,12 +195,12 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   if (p.nseg <= 1) mark(2);
   mark(3);
   if (a.ndir == 1) {
-    hipLaunchKernelGGL((scan_output_dir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV>), dim3(unsigned(nblocks)), dim3(kLanes), 0,
+    hipLaunchKernelGGL((scan_output_dir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32>), dim3(unsigned(nblocks)), dim3(kLanes), 0,
                        stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), static_cast<const float*>(hin),
                        int(vec));
   } else {
     const size_t lds = size_t(p.seg_len) * kLanes * sizeof(float);
-    hipLaunchKernelGGL((scan_output_bidir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV>), dim3(unsigned(nblocks)),
+    hipLaunchKernelGGL((scan_output_bidir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32>), dim3(unsigned(nblocks)),
                        dim3(2 * kLanes), lds, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc),
                        static_cast<const float*>(hin), int(vec));
   }
@@ -220,6 +220,12 @@ hipError_t launch_conv_mode(const ScanArgs& a, const Plan& p, float* w, hipStrea
 
 template <bool IO_BF16>
 hipError_t launch_io(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
+  if (a.y_f32 && IO_BF16) {
+    // fp32 partial outputs (ungated, no convolution): the multi-order scan
+    if (a.z || a.conv_w) return hipErrorInvalidValue;
+    return a.softplus ? launch_typed<IO_BF16, true, false, kNoConv, true>(a, p, w, stream, ev)
+                      : launch_typed<IO_BF16, false, false, kNoConv, true>(a, p, w, stream, ev);
+  }
   if (!a.conv_w) return launch_conv_mode<IO_BF16, kNoConv>(a, p, w, stream, ev);
   return a.conv_silu ? launch_conv_mode<IO_BF16, kConvSilu>(a, p, w, stream, ev)
                      : launch_conv_mode<IO_BF16, kConvLin>(a, p, w, stream, ev);

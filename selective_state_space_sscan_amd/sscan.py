@@ -110,6 +110,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_fwd_conv_profiled.restype = I
     lib.sscan_bidir_conv_profiled.argtypes = lib.sscan_bidir_conv.argtypes + [V]
     lib.sscan_bidir_conv_profiled.restype = I
+    IP = ctypes.POINTER(ctypes.c_int)
+    lib.sscan_multi.argtypes = [V, V, V, DP, IP, I, V, I, I64, I64, I64, I64, I64, V, I, I, V, SZ]
+    lib.sscan_multi.restype = I
+    lib.sscan_validate_multi.argtypes = [V, V, V, DP, IP, I, V, I, I64, I64, I64, I64, I64, I, I, V, SZ]
+    lib.sscan_validate_multi.restype = I
+    lib.sscan_multi_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, IP, I, I, I]
+    lib.sscan_multi_workspace_bytes.restype = SZ
+    lib.sscan_spiral_order.argtypes = [I64, I64, V]
+    lib.sscan_spiral_order.restype = I
     lib.sscan_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.sscan_workspace_bytes.restype = SZ
     lib.sscan_strerror.argtypes = [I]
@@ -489,6 +498,67 @@ def bidir_conv(x, conv: dict, z, fwd: dict, rev: dict, softplus: bool = True, ou
     st = lib.sscan_bidir_conv(*args) if ev is None else lib.sscan_bidir_conv_profiled(*args, ev)
     if st != 0:
         raise SScanError(st, "sscan_bidir_conv")
+    return out
+
+
+ORDER_ROW, ORDER_ROW_REV, ORDER_COL, ORDER_COL_REV, ORDER_INDEX, ORDER_INDEX_REV = range(6)
+
+
+def spiral_order(height: int, width: int) -> torch.Tensor:
+    """The centre-out clockwise spiral over a [height, width] map (``sscan_spiral_order``,
+    host code): int32 CPU tensor of row-major token indices."""
+    out = torch.empty(height * width, dtype=torch.int32)
+    st = load_library().sscan_spiral_order(height, width, ctypes.c_void_p(out.data_ptr()) if out.numel() else None)
+    if st != 0:
+        raise SScanError(st, "sscan_spiral_order")
+    return out
+
+
+def multi_workspace_bytes(batch, dim, height, width, kinds, io_dtype=torch.float32, bc_dtype=torch.float32) -> int:
+    k = (ctypes.c_int * len(kinds))(*kinds)
+    return int(load_library().sscan_multi_workspace_bytes(batch, dim, height, width, DSTATE, k, len(kinds),
+                                                          _DT_CODE[io_dtype], _DT_CODE[bc_dtype]))
+
+
+def multi(u, z, dirs, kinds, height: int, width: int, index: Optional[torch.Tensor] = None, softplus: bool = True,
+          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``sscan_multi``: the map [height, width] (flattened row-major in u's last
+    axis) scanned along the orders ``kinds`` (ORDER_*), one parameter dict per
+    direction (delta, A, B, C, optional D, delta_bias, all in token layout); the
+    directions' outputs are summed and gated once.  ``index`` (device int32
+    permutation) is needed by the index orders."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.multi needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or dirs[0]["B"].dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = u.shape
+    if L != height * width:
+        raise ValueError("u's last axis must be height * width")
+    if len(dirs) != len(kinds):
+        raise ValueError("one parameter dict per order")
+    _check(u, "u", dev)
+    _check(z, "z", dev, u.dtype, u.shape)
+    _check(index, "index", dev, torch.int32, (L,))
+    bdt = dirs[0]["B"].dtype
+    ps = [_dir(p, f"dirs[{k}]", dev, u, bdt) for k, p in enumerate(dirs)]
+    arr = (DirParams * len(ps))(*ps)
+    kk = (ctypes.c_int * len(kinds))(*kinds)
+    if out is None:
+        out = torch.empty_like(u)
+    _check(out, "out", dev, u.dtype, u.shape)
+    if u.numel() == 0:
+        return out
+    nbytes = multi_workspace_bytes(b, d, height, width, kinds, u.dtype, bdt)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", dev)
+    st = lib.sscan_multi(_ptr(u), _ptr(z), _ptr(out), arr, kk, len(kinds), _ptr(index), int(bool(softplus)), b, d,
+                         height, width, DSTATE, _stream(dev), _DT_CODE[u.dtype], _DT_CODE[bdt], _ptr(workspace),
+                         workspace.numel())
+    if st != 0:
+        raise SScanError(st, "sscan_multi")
     return out
 
 

@@ -301,3 +301,50 @@ def test_validate_conv1d(lib):
     assert V(C(3), y=x) == EALIAS and V(C(3), y=w) == EALIAS
     assert V(C(3, weight=w + 2)) == EALIGN
     assert V(C(3), y=y + 2, io=1) == OK and V(C(3), y=y + 1, io=1) == EALIGN
+
+
+# --- 2-D visiting orders -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("h,w", [(1, 1), (1, 7), (6, 1), (2, 2), (5, 5), (4, 6), (7, 3), (16, 16), (13, 9)])
+def test_spiral_order_matches_the_oracle(lib, h, w):
+    """The library's spiral (host code) and the oracle's, written separately from
+    the same description, agree index for index."""
+    from oracle import orders
+
+    assert sscan.spiral_order(h, w).tolist() == orders.spiral_order(h, w).tolist()
+
+
+def test_spiral_order_rejects_bad_sizes(lib):
+    assert lib.sscan_spiral_order(-1, 3, None) == ESHAPE
+    assert lib.sscan_spiral_order(3, 3, None) == ENULL
+    assert lib.sscan_spiral_order(0, 3, None) == OK
+
+
+def test_validate_multi(lib):
+    f = Fake()
+    f.next = 1 << 46
+    b, d, h, w = 2, 64, 8, 12
+    L = h * w
+    io, bc = b * d * L * 4, b * 16 * L * 4
+    u, z, y, index = f(io), f(io), f(io), f(L * 4)
+    mk = lambda: sscan.DirParams(f(io), f(d * 4), f(d * 64), f(bc), f(bc), f(d * 4))
+    dirs = (sscan.DirParams * 4)(*[mk() for _ in range(4)])
+    K = lambda *k: (ctypes.c_int * len(k))(*k)
+    kinds = K(0, 1, 2, 3)
+    ws = lib.sscan_multi_workspace_bytes(b, d, h, w, 16, kinds, 4, 0, 0)
+    assert ws > 0
+    wsp = f(ws)
+    V = lambda kk, n, **kw: lib.sscan_validate_multi(kw.get("u", u), z, kw.get("y", y), dirs, kk, n,
+                                                     kw.get("index", None), 1, b, d, kw.get("h", h), w, 16, 0, 0,
+                                                     kw.get("ws", wsp), kw.get("ws_bytes", ws))
+    assert V(kinds, 4) == OK
+    assert V(K(0, 0), 2) == EUNSUP          # a kind twice
+    assert V(K(6), 1) == EUNSUP             # unknown kind
+    assert V(kinds, 0) == EUNSUP and V(kinds, 7) == EUNSUP
+    assert V(K(4), 1) == ENULL              # the index orders need the index
+    ws4 = lib.sscan_multi_workspace_bytes(b, d, h, w, 16, K(4), 1, 0, 0)
+    assert V(K(4), 1, index=index, ws_bytes=ws4) == OK
+    assert V(kinds, 4, ws_bytes=ws - 1) == EWS
+    assert V(kinds, 4, ws=wsp + 16) == EALIGN  # 256-byte aligned workspace
+    assert V(kinds, 4, y=u) == EALIAS
+    assert V(kinds, 4, h=-1) == ESHAPE
