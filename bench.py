@@ -6,7 +6,8 @@ len 262144, dstate 16, bf16 u/delta/z/y, f32 B/C, seeded synthetic inputs alread
 resident in HBM).  One step = one sscan_fwd call (all its kernels).  Prints ONE
 JSON line on stdout.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd|conv|fwd-conv]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                 [--pass fwd|bwd|conv|fwd-conv|cross4|spiral]
                  [--no-cpu] [--copy-calibration]
 
 Timing: K plain calls between two HIP events give ms_per_step (for a workload
@@ -384,6 +385,61 @@ def cpu_baseline_conv(x, cp, cfg, target_s: float = 4.0):
             "cpu_model": cpu_model()}
 
 
+def bench_multi(args, torch, I, sscan, cfg, ci):
+    """--pass cross4: the map scanned by rows and columns, both ways (four
+    parameter sets); --pass spiral: the centre-out spiral both ways plus the row
+    pair.  The workload's sequence is read as a square map."""
+    import math
+
+    dev = torch.device("cuda:0")
+    side = int(math.isqrt(cfg.len))
+    if side * side != cfg.len:
+        sys.exit(f"--pass {args.pass_} needs a square map; {cfg.name} has len {cfg.len}")
+    x1 = I.make_inputs(cfg.batch, cfg.dim, cfg.len, bidir=True, io_dtype=cfg.io_dtype, bc_dtype=cfg.bc_dtype,
+                       seed=1000 * ci + 50)
+    x2 = I.make_inputs(cfg.batch, cfg.dim, cfg.len, bidir=True, io_dtype=cfg.io_dtype, bc_dtype=cfg.bc_dtype,
+                       seed=1000 * ci + 51)
+    xd = x1.to(dev)
+    dirs = [dict(delta=xd.delta, delta_bias=p.delta_bias.to(dev), A=p.A.to(dev), B=p.B.to(dev), C=p.C.to(dev),
+                 D=p.D.to(dev)) for p in x1.dirs + x2.dirs]
+    index = None
+    if args.pass_ == "cross4":
+        kinds = [sscan.ORDER_ROW, sscan.ORDER_ROW_REV, sscan.ORDER_COL, sscan.ORDER_COL_REV]
+    else:
+        kinds = [sscan.ORDER_INDEX, sscan.ORDER_INDEX_REV, sscan.ORDER_ROW, sscan.ORDER_ROW_REV]
+        index = sscan.spiral_order(side, side).to(dev)
+    y = torch.empty_like(xd.u)
+    ws = torch.empty(sscan.multi_workspace_bytes(cfg.batch, cfg.dim, side, side, kinds, xd.u.dtype,
+                                                 dirs[0]["B"].dtype), dtype=torch.uint8, device=dev)
+    step = lambda: sscan.multi(xd.u, xd.z, dirs, kinds, side, side, index=index, out=y, workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = FLOPS_PER_ELEM_STATE * cfg.dstate * cfg.elems * len(kinds)
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"metric": METRIC, "value": cfg.elems / (ms * 1e-3) / 1e6, "unit": "Melem/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded numpy PCG64, shapes of the pages' workloads)",
+            "config": {"workload": cfg.name, "pass": args.pass_, "batch": cfg.batch, "dim": cfg.dim,
+                       "height": side, "width": side, "dstate": cfg.dstate, "directions": len(kinds),
+                       "io_dtype": cfg.io_dtype, "bc_dtype": cfg.bc_dtype},
+            # every direction's scan plus the gathers, put-backs and gate: a lower bound
+            # for the scan kernels themselves
+            "roofline": {"bound": "alu", "kernel": "whole call", "achieved": achieved, "peak": ALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / ALU_PEAK_TFLOPS, "traffic": None},
+            "per_direction_Melem_s": cfg.elems * len(kinds) / (ms * 1e-3) / 1e6,
+            "workspace_bytes": ws.numel()}
+
+
 # Single-token decode (sscan_step): batch streams of the long-sequence workload's
 # 1536 channels, bf16 u/delta/z/y, f32 B/C and f32 state.
 DECODE = dict(name="decode-step", batch=256, dim=1536, io_dtype="bf16", bc_dtype="f32")
@@ -473,9 +529,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long-seq-fwd",
                     help="a scan workload of selective_state_space_sscan_amd.inputs.CONFIGS, or decode-step")
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "conv", "fwd-conv"), default="fwd",
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "conv", "fwd-conv", "cross4", "spiral"),
+                    default="fwd",
                     help="the forward call (default), its backward pass, the front-end convolution alone, "
-                         "or the scan with the convolution fused in")
+                         "the scan with the convolution fused in, or a square map scanned in four "
+                         "directions (rows and columns both ways) or along the spiral")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with a 512 MiB negation kernel (counter calibration for rocprofv3 --pmc runs)")
@@ -498,6 +556,9 @@ def main():
     cfg = I.CONFIGS[ci]
     if args.pass_ == "bwd":
         print(json.dumps(bench_bwd(args, torch, I, sscan, cfg, ci)), flush=True)
+        return
+    if args.pass_ in ("cross4", "spiral"):
+        print(json.dumps(bench_multi(args, torch, I, sscan, cfg, ci)), flush=True)
         return
     if args.pass_ in ("conv", "fwd-conv"):
         print(json.dumps(bench_conv(args, torch, I, sscan, cfg, ci)), flush=True)

@@ -13,9 +13,10 @@
 // sscan_kernels.hip, without the gate) on inputs gathered into the family's
 // visiting order: nothing to gather for rows; an LDS-tiled transpose for columns
 // (the column order of an H x W map is the row order of its W x H transpose);
-// a gather through the index for permutations.  Each family's output is put back
-// at the token positions and summed into an fp32 accumulator in a fixed order
-// (rows, columns, index); a last pass gates it and stores the result.
+// a gather through the index for permutations.  Each family's fp32 output is put
+// back at the token positions and summed into an fp32 accumulator in a fixed order
+// (rows, columns, index; the row family scans straight into it), and the last
+// family's put-back applies the gate and stores the result.
 #include "sscan_internal.h"
 
 #include <algorithm>
@@ -36,22 +37,18 @@ __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) {
   p[i] = uint16_t(__builtin_bit_cast(uint32_t, __builtin_convertvector(x, b2)) & 0xffffu);
 }
 
-// What a put-back does with the accumulator.
-enum Put : int { kCopy = 0, kSet = 1, kAdd = 2 };
-
-// out[row][c][r] = in[row][r][c] for every row of [rows][h][w] (kCopy, same type),
-// or acc[row][c][r] = / += in[row][r][c] (kSet / kAdd into fp32).  Grid:
+// out[row][c][r] = in[row][r][c] for every row of [rows][h][w].  Grid:
 // (ceil(w/32), ceil(h/32), up to 65535 row slots striding over the rows); block 32 x 8.
 constexpr int64_t kMaxGridZ = 65535;
 
-template <typename TI, typename TO, int PUT>
-__global__ __launch_bounds__(256) void transpose_kernel(const TI* __restrict__ in, TO* __restrict__ out, int64_t rows,
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, T* __restrict__ out, int64_t rows,
                                                         int64_t h, int64_t w) {
   __shared__ float tile[kTT][kTT + 1];
   const int64_t c0 = int64_t(blockIdx.x) * kTT, r0 = int64_t(blockIdx.y) * kTT;
   for (int64_t row = blockIdx.z; row < rows; row += gridDim.z) {
-    const TI* src = in + row * h * w;
-    TO* dst = out + row * h * w;
+    const T* src = in + row * h * w;
+    T* dst = out + row * h * w;
     __syncthreads();  // the previous row's tile has been read out
     for (int k = threadIdx.y; k < kTT; k += 8) {
       const int64_t r = r0 + k, c = c0 + threadIdx.x;
@@ -60,15 +57,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TI* __restrict__ i
     __syncthreads();
     for (int k = threadIdx.y; k < kTT; k += 8) {
       const int64_t c = c0 + k, r = r0 + threadIdx.x;
-      if (r < h && c < w) {
-        const float v = tile[threadIdx.x][k];
-        const int64_t o = c * h + r;
-        if (PUT == kAdd) {
-          st(dst, o, ld(dst, o) + v);
-        } else {
-          st(dst, o, v);
-        }
-      }
+      if (r < h && c < w) st(dst, c * h + r, tile[threadIdx.x][k]);
     }
   }
 }
@@ -88,41 +77,70 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ in, T
   st(out, i, (p >= 0 && p < len) ? ld(in, row * len + p) : 0.0f);
 }
 
-// acc[row][index[s]] = / += y[row][s] (index a permutation; entries outside
-// [0, len) are skipped).  With index == nullptr the identity.
-template <typename T, int PUT>
-__global__ __launch_bounds__(256) void put_kernel(const T* __restrict__ y, float* __restrict__ acc,
-                                                  const int32_t* __restrict__ index, int64_t rows, int64_t len) {
+__device__ __forceinline__ float silu_gate(float v, float zv) {
+  // v * silu(z), silu(z) = z / (1 + 2^(-z log2 e)), as in the scan kernels
+  return v * (zv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zv * 1.4426950408889634f)));
+}
+
+// Puts one family's fp32 output back at the token positions: FIRST sets the
+// accumulator, later families add to it; the LAST family adds, gates and stores
+// the result in the I/O dtype instead.  The index family: value s of a row goes
+// to token index[s] (entries outside [0, len) are skipped).
+template <typename TIO, bool FIRST, bool LAST>
+__global__ __launch_bounds__(256) void put_index_kernel(const float* __restrict__ yf, float* __restrict__ acc,
+                                                        const int32_t* __restrict__ index, const TIO* __restrict__ z,
+                                                        TIO* __restrict__ y, int64_t rows, int64_t len) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= rows * len) return;
   const int64_t row = i / len, s = i % len;
-  const int64_t p = index ? int64_t(index[s]) : s;
+  const int64_t p = index[s];
   if (p < 0 || p >= len) return;
-  const float v = ld(y, i);
-  float* o = acc + row * len + p;
-  *o = PUT == kAdd ? *o + v : v;
+  const int64_t o = row * len + p;
+  const float v = FIRST ? yf[i] : acc[o] + yf[i];
+  if (LAST) {
+    st(y, o, z ? silu_gate(v, ld(z, o)) : v);
+  } else {
+    acc[o] = v;
+  }
 }
 
-// y = acc * silu(z) (or acc), in the I/O dtype.
-template <typename T>
-__global__ __launch_bounds__(256) void gate_kernel(const float* __restrict__ acc, const T* __restrict__ z,
-                                                   T* __restrict__ y, int64_t n) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= n) return;
-  float v = acc[i];
-  if (z) {
-    const float zv = ld(z, i);
-    // silu(z) = z / (1 + 2^(-z log2 e)), as in the scan kernels
-    v *= zv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zv * 1.4426950408889634f));
+// The column family: its output is the [w][h] map of the visiting order,
+// transposed back onto [h][w] through an LDS tile (grid as transpose_kernel with
+// the [w][h] shape).
+template <typename TIO, bool FIRST, bool LAST>
+__global__ __launch_bounds__(256) void put_col_kernel(const float* __restrict__ yf, float* __restrict__ acc,
+                                                      const TIO* __restrict__ z, TIO* __restrict__ y, int64_t rows,
+                                                      int64_t h, int64_t w) {
+  __shared__ float tile[kTT][kTT + 1];
+  const int64_t c0 = int64_t(blockIdx.x) * kTT, r0 = int64_t(blockIdx.y) * kTT;
+  for (int64_t row = blockIdx.z; row < rows; row += gridDim.z) {
+    const float* src = yf + row * h * w;
+    __syncthreads();
+    for (int k = threadIdx.y; k < kTT; k += 8) {
+      const int64_t r = r0 + k, c = c0 + threadIdx.x;
+      tile[k][threadIdx.x] = (r < h && c < w) ? src[r * w + c] : 0.0f;
+    }
+    __syncthreads();
+    for (int k = threadIdx.y; k < kTT; k += 8) {
+      const int64_t c = c0 + k, r = r0 + threadIdx.x;
+      if (r < h && c < w) {
+        const int64_t o = row * h * w + c * h + r;
+        const float v = FIRST ? tile[threadIdx.x][k] : acc[o] + tile[threadIdx.x][k];
+        if (LAST) {
+          st(y, o, z ? silu_gate(v, ld(z, o)) : v);
+        } else {
+          acc[o] = v;
+        }
+      }
+    }
   }
-  st(y, i, v);
 }
 
 unsigned blocks_for(int64_t n) { return unsigned((n + 255) / 256); }
 
 template <typename T>
 void launch_transpose(const void* in, void* out, int64_t rows, int64_t h, int64_t w, hipStream_t s) {
-  hipLaunchKernelGGL((transpose_kernel<T, T, kCopy>), transpose_grid(rows, h, w), dim3(kTT, 8), 0, s,
+  hipLaunchKernelGGL((transpose_kernel<T>), transpose_grid(rows, h, w), dim3(kTT, 8), 0, s,
                      static_cast<const T*>(in), static_cast<T*>(out), rows, h, w);
 }
 
@@ -149,27 +167,31 @@ void gather_family(int family, bool bf16, const void* in, void* out, const int32
   }
 }
 
-template <typename T>
-void put_family(int family, const void* y, float* acc, const int32_t* index, int64_t rows, int64_t h, int64_t w,
-                bool first, hipStream_t s) {
-  const T* yy = static_cast<const T*>(y);
+template <typename TIO, bool FIRST, bool LAST>
+void put_family_t(int family, const float* yf, float* acc, const int32_t* index, const void* z, void* y,
+                  int64_t rows, int64_t h, int64_t w, hipStream_t s) {
+  const TIO* zz = static_cast<const TIO*>(z);
+  TIO* yy = static_cast<TIO*>(y);
   if (family == kFamilyCol) {
-    // y is in column order: the [w][h] map transposed back onto [h][w]
-    const dim3 grid = transpose_grid(rows, w, h);
-    if (first) {
-      hipLaunchKernelGGL((transpose_kernel<T, float, kSet>), grid, dim3(kTT, 8), 0, s, yy, acc, rows, w, h);
-    } else {
-      hipLaunchKernelGGL((transpose_kernel<T, float, kAdd>), grid, dim3(kTT, 8), 0, s, yy, acc, rows, w, h);
-    }
+    hipLaunchKernelGGL((put_col_kernel<TIO, FIRST, LAST>), transpose_grid(rows, w, h), dim3(kTT, 8), 0, s, yf, acc,
+                       zz, yy, rows, w, h);
   } else {
-    const int32_t* idx = family == kFamilyIndex ? index : nullptr;
-    if (first) {
-      hipLaunchKernelGGL((put_kernel<T, kSet>), dim3(blocks_for(rows * h * w)), dim3(256), 0, s, yy, acc, idx, rows,
-                         h * w);
-    } else {
-      hipLaunchKernelGGL((put_kernel<T, kAdd>), dim3(blocks_for(rows * h * w)), dim3(256), 0, s, yy, acc, idx, rows,
-                         h * w);
-    }
+    hipLaunchKernelGGL((put_index_kernel<TIO, FIRST, LAST>), dim3(blocks_for(rows * h * w)), dim3(256), 0, s, yf,
+                       acc, index, zz, yy, rows, h * w);
+  }
+}
+
+template <typename TIO>
+void put_family(int family, const float* yf, float* acc, const int32_t* index, const void* z, void* y, int64_t rows,
+                int64_t h, int64_t w, bool first, bool last, hipStream_t s) {
+  if (first && last) {
+    put_family_t<TIO, true, true>(family, yf, acc, index, z, y, rows, h, w, s);
+  } else if (first) {
+    put_family_t<TIO, true, false>(family, yf, acc, index, z, y, rows, h, w, s);
+  } else if (last) {
+    put_family_t<TIO, false, true>(family, yf, acc, index, z, y, rows, h, w, s);
+  } else {
+    put_family_t<TIO, false, false>(family, yf, acc, index, z, y, rows, h, w, s);
   }
 }
 
@@ -212,35 +234,59 @@ hipError_t launch_multi(const MultiArgs& a, const MultiPlan& p, char* ws, hipStr
   const int64_t len = a.height * a.width;
   const int64_t rows = a.batch * a.dim, bc_rows = a.batch * kDState;
   float* acc = reinterpret_cast<float*>(ws + p.off_acc);
-  bool first = true;
-  for (int f = 0; f < kFamilies; ++f) {
+  int fams[kFamilies], nf = 0;
+  for (int f = 0; f < kFamilies; ++f)
+    for (int k = 0; k < a.ndir; ++k)
+      if (a.kind[k] / 2 == f) {
+        fams[nf++] = f;
+        break;
+      }
+  for (int fi = 0; fi < nf; ++fi) {
+    const int f = fams[fi];
+    const bool first = fi == 0, last = fi == nf - 1;
     int idx[2] = {-1, -1};  // forward, reverse direction of this family
     for (int k = 0; k < a.ndir; ++k)
       if (a.kind[k] / 2 == f) idx[a.kind[k] % 2] = k;
-    if (idx[0] < 0 && idx[1] < 0) continue;
     ScanArgs s;
     std::memset(&s, 0, sizeof(s));
-    s.u = a.u;
-    s.y = ws + p.off_y;
-    s.y_f32 = 1;  // the families' outputs are summed before any rounding
     s.softplus = a.softplus;
     s.io_bf16 = a.io_bf16;
     s.bc_bf16 = a.bc_bf16;
     s.batch = a.batch;
     s.dim = a.dim;
     s.len = len;
-    if (f != kFamilyRow) s.u = ws + p.off_u;
-    if (f != kFamilyRow)
+    if (f == kFamilyRow) {
+      s.u = a.u;
+      if (last) {
+        // rows alone: the plain gated scan
+        s.z = a.z;
+        s.y = a.y;
+      } else {
+        // rows come first: scan straight into the accumulator
+        s.y = acc;
+        s.y_f32 = 1;
+      }
+    } else {
+      s.u = ws + p.off_u;
+      s.y = ws + p.off_y;
+      s.y_f32 = 1;  // summed before any rounding
       gather_family(f, a.io_bf16, a.u, ws + p.off_u, a.index, rows, a.height, a.width, stream);
+    }
     int slot = 0;
+    const void* gathered_delta = nullptr;  // a delta shared by the family's two directions is gathered once
     for (int j = 0; j < 2; ++j) {
       if (idx[j] < 0) continue;
       DirArgs d = a.dir[idx[j]];
       if (f != kFamilyRow) {
-        gather_family(f, a.io_bf16, d.delta, ws + p.off_delta[slot], a.index, rows, a.height, a.width, stream);
+        if (slot == 1 && d.delta == a.dir[idx[0]].delta && gathered_delta) {
+          d.delta = gathered_delta;
+        } else {
+          gather_family(f, a.io_bf16, d.delta, ws + p.off_delta[slot], a.index, rows, a.height, a.width, stream);
+          d.delta = ws + p.off_delta[slot];
+        }
+        if (slot == 0) gathered_delta = d.delta;
         gather_family(f, a.bc_bf16, d.B, ws + p.off_B[slot], a.index, bc_rows, a.height, a.width, stream);
         gather_family(f, a.bc_bf16, d.C, ws + p.off_C[slot], a.index, bc_rows, a.height, a.width, stream);
-        d.delta = ws + p.off_delta[slot];
         d.B = ws + p.off_B[slot];
         d.C = ws + p.off_C[slot];
       }
@@ -248,21 +294,19 @@ hipError_t launch_multi(const MultiArgs& a, const MultiPlan& p, char* ws, hipStr
     }
     s.ndir = slot;
     s.reverse = (slot == 1 && idx[1] >= 0) ? 1 : 0;  // a lone reverse direction
-    // for the gathered families the visiting order's tokens are in the order the
-    // scan expects; a column map is a [width][height] map in that order
+    // a gathered family's inputs are in its visiting order: the scan sees a plain
+    // sequence (for columns, the [width][height] transpose read row by row)
     const Plan plan = make_plan(a.batch, a.dim, len, s.ndir);
-    hipError_t e = launch_scan(s, plan, reinterpret_cast<float*>(ws + p.off_scan), stream);
+    const hipError_t e = launch_scan(s, plan, reinterpret_cast<float*>(ws + p.off_scan), stream);
     if (e != hipSuccess) return e;
-    put_family<float>(f, ws + p.off_y, acc, a.index, rows, a.height, a.width, first, stream);
-    first = false;
-  }
-  const int64_t n = rows * len;
-  if (a.io_bf16) {
-    hipLaunchKernelGGL((gate_kernel<uint16_t>), dim3(blocks_for(n)), dim3(256), 0, stream, acc,
-                       static_cast<const uint16_t*>(a.z), static_cast<uint16_t*>(a.y), n);
-  } else {
-    hipLaunchKernelGGL((gate_kernel<float>), dim3(blocks_for(n)), dim3(256), 0, stream, acc,
-                       static_cast<const float*>(a.z), static_cast<float*>(a.y), n);
+    if (f != kFamilyRow) {
+      const float* yf = reinterpret_cast<const float*>(ws + p.off_y);
+      if (a.io_bf16) {
+        put_family<uint16_t>(f, yf, acc, a.index, a.z, a.y, rows, a.height, a.width, first, last, stream);
+      } else {
+        put_family<float>(f, yf, acc, a.index, a.z, a.y, rows, a.height, a.width, first, last, stream);
+      }
+    }
   }
   return hipGetLastError();
 }
