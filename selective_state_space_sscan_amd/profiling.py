@@ -31,14 +31,17 @@ KERNELS = {"stage_bc_kernel": "stage_bc", "scan_aggregate_kernel": "aggregate", 
            "scan_output_dir_kernel": "output", "scan_output_bidir_kernel": "output"}
 
 
+# the files that define the forward scan's kernels (staging, aggregate, carry, output)
+FORWARD_SOURCES = ("sscan_device.h", "sscan_internal.h", "sscan_kernels.hip")
+
+
 def kernel_source_hash() -> str:
-    """SHA-256 over every kernel source file (name and contents, sorted by name)."""
+    """SHA-256 over the forward kernels' source files (name and contents)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as fh:
-                h.update(fh.read())
+    for name in FORWARD_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
