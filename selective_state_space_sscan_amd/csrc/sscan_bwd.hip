@@ -73,6 +73,22 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+// Sum over the four channel rows of a wavefront (lanes l, l+16, l+32, l+48 hold
+// the same state) of a chunk of four tokens' values v[0..3], reduce-scattered: row
+// c receives the sum for token c.  Round one pairs rows c and c^2 (xor 32): rows 0
+// and 1 keep tokens 0, 1 and pass on 2, 3, rows 2 and 3 the other way round; round
+// two pairs rows c and c^1 (xor 16): the even row keeps the first of its two, the
+// odd row the second.
+__device__ __forceinline__ float chunk_sum(const float (&v)[kGroup], int c) {
+  const bool lo = c < 2;
+  float k0 = lo ? v[0] : v[2], k1 = lo ? v[1] : v[3];
+  const float s0 = lo ? v[2] : v[0], s1 = lo ? v[3] : v[1];
+  k0 += __shfl_xor(s0, 32);
+  k1 += __shfl_xor(s1, 32);
+  const bool even = (c & 1) == 0;
+  return (even ? k0 : k1) + __shfl_xor(even ? k1 : k0, 16);
+}
+
 __device__ __forceinline__ size_t part_index(int dir, int64_t b, int64_t k, int r, int64_t d, int64_t batch,
                                              int64_t dim, int64_t nwin) {
   return ((((size_t)dir * batch + b) * nwin + k) * kPartRows + r) * dim + d;
@@ -171,9 +187,14 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
   const float* bcw = bc + (((size_t)dir * f.batch + b) * f.len + t0) * kBC;
   for (int e = lane; e < wl * kBC; e += kLanes) sBC[e / kBC][e % kBC] = bcw[e];
 
-  float accB[kWin], accC[kWin];
+  // dB and dC of this window over the block's channels.  Every 4 tokens the four
+  // channel rows' per-token terms are summed by a reduce-scatter (two shuffle
+  // rounds) that leaves row c owning token 4j + c: 8 accumulators per quantity
+  // per lane instead of 32.
+  constexpr int kChunks = kWin / kGroup;
+  float accB[kChunks], accC[kChunks];
 #pragma unroll
-  for (int i = 0; i < kWin; ++i) accB[i] = accC[i] = 0.0f;
+  for (int q = 0; q < kChunks; ++q) accB[q] = accC[q] = 0.0f;
 
   // software pipeline: the next group's inputs are in flight while this one runs
   TokIn<IO_BF16, HAS_Z> nx;
@@ -257,9 +278,12 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
         if (s % kSchedTokens == kSchedTokens - 1) __builtin_amdgcn_sched_barrier(0);
       }
       float mu = mu_in;
+      float tB[kGroup], tC[kGroup];  // this chunk's per-token dB / dC terms, slot i % 4
 #pragma unroll
       for (int s = kWin - 1; s >= 0; --s) {
         const int i = REV ? kWin - 1 - s : s;
+        tB[i % kGroup] = 0.0f;
+        tC[i % kGroup] = 0.0f;
         if (kFull || i < wl) {
           const float dt = sTok[QDT][i][c];
           const float dy = sTok[QDY][i][c];
@@ -276,12 +300,18 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           }
           const float w = lam * at * hprev;
           dA_acc = fmaf(w, dt, dA_acc);
-          accB[i] = fmaf(lam, sTok[QDTU][i][c], accB[i]);
-          accC[i] = fmaf(dy, hist[i], accC[i]);
+          tB[i % kGroup] = lam * sTok[QDTU][i][c];
+          tC[i % kGroup] = dy * hist[i];
           // du = dt * P + D dy and d(dt) = u * P + Q with P = sum_n lambda B, Q = sum_n A w
           sOutF[out_slot(OP, i)] = row_sum16(lam * sBC[i][n]);
           sOutF[out_slot(OQ, i)] = row_sum16(A * w);
           mu = at * lam;
+        }
+        // the sweep leaves a chunk of four tokens at i % 4 == 0 (ascending token
+        // order of a reverse scan: at i % 4 == 3)
+        if (i % kGroup == (REV ? kGroup - 1 : 0)) {
+          accB[i / kGroup] += chunk_sum(tB, c);
+          accC[i / kGroup] += chunk_sum(tC, c);
         }
         if (s % kSchedTokens == 0) __builtin_amdgcn_sched_barrier(0);
       }
@@ -336,21 +366,13 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
     }
   }
 
-  // dB and dC of this window over this block's channels: sum the four channel rows
+  // row c holds dB / dC of tokens 4q + c of the window
 #pragma unroll
-  for (int i = 0; i < kWin; ++i) {
-    accB[i] += __shfl_xor(accB[i], 16);
-    accB[i] += __shfl_xor(accB[i], 32);
-    accC[i] += __shfl_xor(accC[i], 16);
-    accC[i] += __shfl_xor(accC[i], 32);
-  }
-  if (c == 0) {
-#pragma unroll
-    for (int i = 0; i < kWin; ++i) {
-      if (i < wl) {
-        pbc[pbc_index(j, dir, b, 0, n, t0 + i, f.ndir, f.batch, f.len)] = accB[i];
-        pbc[pbc_index(j, dir, b, 1, n, t0 + i, f.ndir, f.batch, f.len)] = accC[i];
-      }
+  for (int q = 0; q < kChunks; ++q) {
+    const int i = q * kGroup + c;
+    if (i < wl) {
+      pbc[pbc_index(j, dir, b, 0, n, t0 + i, f.ndir, f.batch, f.len)] = accB[q];
+      pbc[pbc_index(j, dir, b, 1, n, t0 + i, f.ndir, f.batch, f.len)] = accC[q];
     }
   }
 }
