@@ -73,20 +73,47 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+// Sums over the 16 states of a channel for a chunk of four tokens v[0..3] (slot =
+// token % 4), reduce-scattered over the row: lane n of the row receives the sum
+// for slot (n >> 2) & 3.  Round one pairs lanes n and n^8 (row_ror:8): the lower
+// half keeps slots 0, 1 and passes on 2, 3, the upper half the other way round;
+// round two pairs n and n^7 (row_half_mirror), which keeps bit 3 and flips bit 2:
+// the lane keeps the first or second of its two slots by bit 2; the last two
+// rounds add over the quad (quad_perm xor 1, xor 2), the lanes n..n^3 whose
+// partial sums together cover the whole row.  11 VALU operations for four tokens,
+// where four all-lane sums take 16.
+__device__ __forceinline__ float row_scatter4(const float (&v)[kGroup], bool hi8, bool hi4) {
+  float k0 = hi8 ? v[2] : v[0], k1 = hi8 ? v[3] : v[1];
+  const float s0 = hi8 ? v[0] : v[2], s1 = hi8 ? v[1] : v[3];
+  k0 += dpp_mov<0x128>(s0);  // row_ror:8
+  k1 += dpp_mov<0x128>(s1);
+  float k = hi4 ? k1 : k0;
+  k += dpp_mov<0x141>(hi4 ? k0 : k1);  // row_half_mirror
+  k += dpp_mov<0xB1>(k);
+  k += dpp_mov<0x4E>(k);
+  return k;
+}
+
+// x + (x of the lane 32 apart) on lanes 0..31, y + (y of the lane 32 apart) on lanes
+// 32..63: v_permlane32_swap exchanges x's upper half with y's lower half.
+__device__ __forceinline__ float swap_add32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// The same between rows 2r and 2r + 1 (v_permlane16_swap): x's sum on even rows,
+// y's on odd rows.
+__device__ __forceinline__ float swap_add16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over the four channel rows of a wavefront (lanes l, l+16, l+32, l+48 hold
 // the same state) of a chunk of four tokens' values v[0..3], reduce-scattered: row
-// c receives the sum for token c.  Round one pairs rows c and c^2 (xor 32): rows 0
-// and 1 keep tokens 0, 1 and pass on 2, 3, rows 2 and 3 the other way round; round
-// two pairs rows c and c^1 (xor 16): the even row keeps the first of its two, the
-// odd row the second.
-__device__ __forceinline__ float chunk_sum(const float (&v)[kGroup], int c) {
-  const bool lo = c < 2;
-  float k0 = lo ? v[0] : v[2], k1 = lo ? v[1] : v[3];
-  const float s0 = lo ? v[2] : v[0], s1 = lo ? v[3] : v[1];
-  k0 += __shfl_xor(s0, 32);
-  k1 += __shfl_xor(s1, 32);
-  const bool even = (c & 1) == 0;
-  return (even ? k0 : k1) + __shfl_xor(even ? k1 : k0, 16);
+// c receives the sum for slot c.  Round one pairs rows c and c^2: rows 0, 1 keep
+// slots 0, 1 and rows 2, 3 slots 2, 3; round two pairs rows c and c^1: even rows
+// keep the first of their two slots, odd rows the second.
+__device__ __forceinline__ float chunk_sum(const float (&v)[kGroup]) {
+  return swap_add16(swap_add32(v[0], v[2]), swap_add32(v[1], v[3]));
 }
 
 __device__ __forceinline__ size_t part_index(int dir, int64_t b, int64_t k, int r, int64_t d, int64_t batch,
@@ -257,33 +284,42 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
     // then the reverse sweep: the adjoint and the gradient terms of every token.
     // Full windows take a copy without per-token conditions, so the unrolled tokens
     // form one block the scheduler can interleave (each lane carries one state, one
-    // dependency chain); the per-token sums over states are written to LDS by every
-    // lane of a row (the same value to the same word).
+    // dependency chain).  The per-token sums over states (y, P, Q) and over the
+    // channel rows (dB, dC) are taken a chunk of four tokens at a time,
+    // reduce-scattered over the lanes; the state sums go to LDS for step 4.
     const float A2 = A * kLog2e;
+    const bool hi8 = (n & 8) != 0, hi4 = (n & 4) != 0;
+    const int slot_off = ((n >> 2) & 3) * kGroup + c;
     float hist[kWin];
     float dA_acc = 0.0f;
     auto sweeps = [&](auto full_tag) {
       constexpr bool kFull = decltype(full_tag)::value;
-      // every lane of a row holds the row's sum: all of them store it to the same word
-      auto out_slot = [&](int q, int i) { return (q * kWin + i) * kGroup + c; };
+      // A chunk's row sums leave lane n holding token 4 * chunk + ((n >> 2) & 3) (the
+      // four lanes of a quad store the same value to the same word).
+      auto out_slot = [&](int q, int i) { return (q * kWin + (i & ~(kGroup - 1))) * kGroup + slot_off; };
+      // a chunk of four tokens is complete at its last token in sweep order
+      constexpr int kFwdLast = REV ? 0 : kGroup - 1, kRevLast = REV ? kGroup - 1 : 0;
       float h = h_in;
+      float tY[kGroup];  // this chunk's per-token terms of y, slot i % 4
 #pragma unroll
       for (int s = 0; s < kWin; ++s) {
         const int i = REV ? kWin - 1 - s : s;
+        tY[i % kGroup] = 0.0f;
         if (kFull || i < wl) {
           h = fmaf(exp2_hw(sTok[QDT][i][c] * A2), h, sTok[QDTU][i][c] * sBC[i][n]);
           hist[i] = h;
-          if (HAS_Z) sOutF[out_slot(OY, i)] = row_sum16(sBC[i][kDState + n] * h) + sTok[QYSKIP][i][c];
+          tY[i % kGroup] = sBC[i][kDState + n] * h;
         }
+        if (HAS_Z && i % kGroup == kFwdLast) sOutF[out_slot(OY, i)] = row_scatter4(tY, hi8, hi4);
         if (s % kSchedTokens == kSchedTokens - 1) __builtin_amdgcn_sched_barrier(0);
       }
       float mu = mu_in;
-      float tB[kGroup], tC[kGroup];  // this chunk's per-token dB / dC terms, slot i % 4
+      // this chunk's per-token dB, dC, P and Q terms, slot i % 4
+      float tB[kGroup], tC[kGroup], tP[kGroup], tQ[kGroup];
 #pragma unroll
       for (int s = kWin - 1; s >= 0; --s) {
         const int i = REV ? kWin - 1 - s : s;
-        tB[i % kGroup] = 0.0f;
-        tC[i % kGroup] = 0.0f;
+        tB[i % kGroup] = tC[i % kGroup] = tP[i % kGroup] = tQ[i % kGroup] = 0.0f;
         if (kFull || i < wl) {
           const float dt = sTok[QDT][i][c];
           const float dy = sTok[QDY][i][c];
@@ -303,15 +339,15 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           tB[i % kGroup] = lam * sTok[QDTU][i][c];
           tC[i % kGroup] = dy * hist[i];
           // du = dt * P + D dy and d(dt) = u * P + Q with P = sum_n lambda B, Q = sum_n A w
-          sOutF[out_slot(OP, i)] = row_sum16(lam * sBC[i][n]);
-          sOutF[out_slot(OQ, i)] = row_sum16(A * w);
+          tP[i % kGroup] = lam * sBC[i][n];
+          tQ[i % kGroup] = A * w;
           mu = at * lam;
         }
-        // the sweep leaves a chunk of four tokens at i % 4 == 0 (ascending token
-        // order of a reverse scan: at i % 4 == 3)
-        if (i % kGroup == (REV ? kGroup - 1 : 0)) {
-          accB[i / kGroup] += chunk_sum(tB, c);
-          accC[i / kGroup] += chunk_sum(tC, c);
+        if (i % kGroup == kRevLast) {
+          sOutF[out_slot(OP, i)] = row_scatter4(tP, hi8, hi4);
+          sOutF[out_slot(OQ, i)] = row_scatter4(tQ, hi8, hi4);
+          accB[i / kGroup] += chunk_sum(tB);
+          accC[i / kGroup] += chunk_sum(tC);
         }
         if (s % kSchedTokens == 0) __builtin_amdgcn_sched_barrier(0);
       }
@@ -341,19 +377,20 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           const float P = sOut(OP, i, cc);
           const float du = fmaf(sTok[QDT][i][cc], P, sTok[QDUSKIP][i][cc]);
           const float ddl = fmaf(sTok[QU][i][cc], P, sOut(OQ, i, cc)) * sTok[QSIG][i][cc];
+          const float y = HAS_Z ? sOut(OY, i, cc) + sTok[QYSKIP][i][cc] : 0.0f;  // y before the gate
           dbp += ddl;
           if (act) {
             IO::store(static_cast<T*>(gd.ddelta), row + i, ddl);
             if (OUT == kSingle) {
               IO::store(static_cast<T*>(a.du), row + i, du);
-              if (HAS_Z) IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * sOut(OY, i, cc));
+              if (HAS_Z) IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * y);
             } else if (OUT == kFirst) {
               acc_du[row + i] = du;
-              if (HAS_Z) acc_y[row + i] = sOut(OY, i, cc);
+              if (HAS_Z) acc_y[row + i] = y;
             } else {
               IO::store(static_cast<T*>(a.du), row + i, du + acc_du[row + i]);
               if (HAS_Z)
-                IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (sOut(OY, i, cc) + acc_y[row + i]));
+                IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (y + acc_y[row + i]));
             }
           }
         }

@@ -180,7 +180,9 @@ class HipEvents:
         return float(ms.value)
 
     def __del__(self):
-        hip = HipEvents._hip
+        # through the instance's class: at interpreter exit the module's globals may
+        # already be gone when the last events are collected
+        hip = getattr(type(self), "_hip", None)
         if hip is not None:
             for h in self._ev:
                 if h:
