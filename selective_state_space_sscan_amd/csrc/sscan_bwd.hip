@@ -12,11 +12,14 @@
 // d(dt_t) = sum_n lambda (B u_t + A a_t h_{t-1}), dA += lambda dt a_t h_{t-1},
 // ddelta = d(dt) softplus'(delta + bias), dz = dout y silu'(z).
 //
-// Work is cut into 32-token windows.  The state entering every window comes from
-// the forward segment aggregates and carry chain (the forward pass's kernels with
-// 32-token segments); the adjoint entering every window from the other side comes
-// from the same two steps run against the scan order (adjoint aggregates: mu from
-// zero across each window, then the carry chain flipped).  The window pass then
+// Work is cut into 32-token windows.  The state entering every window and the
+// adjoint entering it from the other side are two chains across the windows, each
+// found in two steps: one pass walks runs of consecutive windows in chain order
+// from zero (the scan order for the state, the opposite order for the adjoint),
+// storing after every window what it has so far and the summed step sizes; the
+// forward pass's carry kernel then chains the runs' totals.  A window's entry value
+// is the stored value of the window before it plus the run's entry value decayed
+// by exp(A * summed step sizes) -- the composition of two affine steps.  The window pass then
 // needs, for every token, the state before it while the adjoint walks backwards:
 // one lane per (channel, state) -- four channels x 16 states per wavefront -- keeps
 // the window's 32 states of its (channel, state) in registers, recomputed forward
@@ -126,32 +129,63 @@ __device__ __forceinline__ size_t pbc_index(int j, int dir, int64_t b, int which
   return (((((size_t)j * ndir + dir) * batch + b) * 2 + which) * kDState + n) * len + t;
 }
 
-// Adjoint aggregates: for every window except the last one the adjoint reaches,
-// mu from zero carried across the window against the scan order (H), and the sum
-// of its step sizes (S).  Same layout as the forward aggregates.  a.u is dout.
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z>
-__global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void bwd_adjoint_aggregate_kernel(
-    ScanArgs a, int64_t seg_len, int64_t nseg, const float* __restrict__ bc, float* __restrict__ agg, int vec) {
+// Chain buffers of the backward's window pass: a (window, channel)'s 16 states
+// contiguous, and its summed step sizes.
+__device__ __forceinline__ size_t win_state_index(int dir, int64_t b, int64_t k, int64_t d, int64_t batch,
+                                                  int64_t dim, int64_t nwin) {
+  return ((((size_t)dir * batch + b) * nwin + k) * dim + d) * kDState;
+}
+__device__ __forceinline__ size_t win_sum_index(int dir, int64_t b, int64_t k, int64_t d, int64_t batch,
+                                                int64_t dim, int64_t nwin) {
+  return (((size_t)dir * batch + b) * nwin + k) * dim + d;
+}
+
+// One chain across the windows, over a run of consecutive windows: walking the run
+// in chain order from zero -- the scan order for the state (kAggregate), the
+// opposite order for the adjoint (kAdjoint: mu, with a.u holding dout) -- the lane
+// stores after every window its 16 values so far and the summed step sizes, and at
+// the end the run's totals in the segment-aggregate layout the carry kernel reads.
+// Grid: batch * nrun * ngroups one-wave blocks (64 channels each); blockIdx.y is the
+// direction.
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, bool ADJ>
+__global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void bwd_chain_kernel(
+    ScanArgs a, int64_t nwin, int64_t run_len, int64_t nrun, const float* __restrict__ bc, float* __restrict__ pw,
+    float* __restrict__ sw, float* __restrict__ ragg, int vec) {
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
-  const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
+  const SegIndex s = decode_block(blockIdx.x, ngroups, nrun);
   const int dir = blockIdx.y;
-  const int reverse = a.ndir == 2 ? dir : a.reverse;
-  if (reverse ? s.seg == nseg - 1 : s.seg == 0) return;
-  Lane<IO_BF16, SOFTPLUS, HAS_Z> L;
+  const bool chain_rev = (a.ndir == 2 ? dir : a.reverse) != ADJ;  // windows visited high to low
+  constexpr int kMode = ADJ ? kAdjoint : kAggregate;
+  Lane<IO_BF16, SOFTPLUS, ADJ && HAS_Z> L;
   init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
-  const int64_t t0 = s.seg * seg_len;
-  const int64_t t1 = min64(a.len, t0 + seg_len);
-  if (reverse) {
-    L.template scan<false, kAdjoint>(t0, t1);
-  } else {
-    L.template scan<true, kAdjoint>(t0, t1);
+  const int64_t k_lo = s.seg * run_len, k_hi = min64(nwin, k_lo + run_len);
+  const int64_t d = s.g * kLanes + threadIdx.x;
+  for (int64_t i = k_lo; i < k_hi; ++i) {
+    const int64_t k = chain_rev ? k_lo + k_hi - 1 - i : i;
+    const int64_t t0 = k * kWin, t1 = min64(a.len, t0 + kWin);
+    if (chain_rev) {
+      L.template scan<true, kMode>(t0, t1);
+    } else {
+      L.template scan<false, kMode>(t0, t1);
+    }
+    if (L.active) {
+      store_state16(pw + win_state_index(dir, s.b, k, d, a.batch, a.dim, nwin), L.h);
+      sw[win_sum_index(dir, s.b, k, d, a.batch, a.dim, nwin)] = L.sum_dt;
+    }
   }
   if (!L.active) return;
-  const int64_t d = s.g * kLanes + threadIdx.x;
 #pragma unroll
-  for (int n = 0; n < kDState; ++n) agg[agg_index(dir, s.b, s.seg, n, d, a.batch, a.dim, nseg)] = L.h[n];
-  agg[agg_index(dir, s.b, s.seg, kDState, d, a.batch, a.dim, nseg)] = L.sum_dt;
+  for (int n = 0; n < kDState; ++n) ragg[agg_index(dir, s.b, s.seg, n, d, a.batch, a.dim, nrun)] = L.h[n];
+  ragg[agg_index(dir, s.b, s.seg, kDState, d, a.batch, a.dim, nrun)] = L.sum_dt;
 }
+
+// What the window pass reads of the two chains (0: state, 1: adjoint).
+struct WinChains {
+  const float* p[2];
+  const float* s[2];
+  const float* e[2];
+  int64_t run_len, nrun;
+};
 
 // One channel group's per-token inputs for one lane: two consecutive tokens of one
 // channel (lane >> 4) in the window.
@@ -185,9 +219,7 @@ __device__ __forceinline__ void load_tok(TokIn<IO_BF16, HAS_Z>& r, const BwdArgs
 // block j of a window covers channel groups [j*gps, (j+1)*gps).
 template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, bool REV, int OUT>
 __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, int64_t nwin, int csplit, int64_t gps,
-                                                           const float* __restrict__ bc,
-                                                           const float* __restrict__ hin,
-                                                           const float* __restrict__ muin,
+                                                           const float* __restrict__ bc, WinChains ch,
                                                            float* __restrict__ part, float* __restrict__ pbc,
                                                            float* __restrict__ acc_du, float* __restrict__ acc_y) {
   using IO = Io<IO_BF16>;
@@ -223,23 +255,48 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
 #pragma unroll
   for (int q = 0; q < kChunks; ++q) accB[q] = accC[q] = 0.0f;
 
+  // Each chain's entry into this window: the run's entry value alone when the window
+  // opens its run in that chain's order, else also the window before it (pred).
+  int64_t run = 0, pred[2] = {0, 0};
+  bool has_pred[2] = {false, false};
+  if (nwin > 1) {
+    run = k / ch.run_len;
+    const int64_t lo = run * ch.run_len, hi = min64(nwin, lo + ch.run_len) - 1;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bool down = (q == 0) == REV;  // the chain visits windows high to low
+      has_pred[q] = down ? k < hi : k > lo;
+      pred[q] = down ? k + 1 : k - 1;
+    }
+  }
+
   // software pipeline: the next group's inputs are in flight while this one runs
   TokIn<IO_BF16, HAS_Z> nx;
-  float nx_A = 0.0f, nx_h = 0.0f, nx_mu = 0.0f;
+  float nx_A = 0.0f, nx_e[2] = {0.0f, 0.0f}, nx_p[2] = {0.0f, 0.0f}, nx_s[2] = {0.0f, 0.0f};
   auto prefetch = [&](int64_t g) {
     load_tok(nx, a, pd, b, g, t0, wl);
     const int64_t d = min64(g * kGroup + c, f.dim - 1);
     nx_A = pd.A[d * kDState + n];
     if (nwin > 1) {
-      nx_h = hin[hin_index(dir, b, k, n, d, f.batch, f.dim, nwin)];
-      nx_mu = muin[hin_index(dir, b, k, n, d, f.batch, f.dim, nwin)];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        nx_e[q] = ch.e[q][hin_index(dir, b, run, n, d, f.batch, f.dim, ch.nrun)];
+        if (has_pred[q]) {
+          nx_p[q] = ch.p[q][win_state_index(dir, b, pred[q], d, f.batch, f.dim, nwin) + n];
+          nx_s[q] = ch.s[q][win_sum_index(dir, b, pred[q], d, f.batch, f.dim, nwin)];
+        }
+      }
     }
   };
   if (g_begin < g_end) prefetch(g_begin);
 
   for (int64_t g = g_begin; g < g_end; ++g) {
     const TokIn<IO_BF16, HAS_Z> cur = nx;
-    const float A = nx_A, h_in = nx_h, mu_in = nx_mu;
+    const float A = nx_A;
+    const float A2 = A * kLog2e;
+    // entry state and adjoint: p + exp(A s) e (e alone where p, s are zero)
+    const float h_in = fmaf(exp2_hw(A2 * nx_s[0]), nx_e[0], nx_p[0]);
+    const float mu_in = fmaf(exp2_hw(A2 * nx_s[1]), nx_e[1], nx_p[1]);
     __syncthreads();  // the previous group is done with the LDS buffers (and sBC is written)
     if (g + 1 < g_end) prefetch(g + 1);
 
@@ -287,7 +344,6 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
     // dependency chain).  The per-token sums over states (y, P, Q) and over the
     // channel rows (dB, dC) are taken a chunk of four tokens at a time,
     // reduce-scattered over the lanes; the state sums go to LDS for step 4.
-    const float A2 = A * kLog2e;
     const bool hi8 = (n & 8) != 0, hi4 = (n & 4) != 0;
     const int slot_off = ((n >> 2) & 3) * kGroup + c;
     float hist[kWin];
@@ -497,10 +553,14 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
   const ScanArgs& f = a.fwd;
   const int64_t ngroups = (f.dim + kLanes - 1) / kLanes;
   float* bc = w + p.off_bc;
-  float* agg = w + p.off_agg;
-  float* hin = w + p.off_hin;
-  float* agga = w + p.off_agga;
-  float* muin = w + p.off_muin;
+  WinChains ch{};
+  ch.run_len = p.run_len;
+  ch.nrun = p.nrun;
+  for (int q = 0; q < 2; ++q) {
+    ch.p[q] = w + p.off_p[q];
+    ch.s[q] = w + p.off_s[q];
+    ch.e[q] = w + p.off_e[q];
+  }
   float* part = w + p.off_part;
   float* pbc = w + p.off_pbc;
   float* acc_du = w + p.off_acc;
@@ -522,24 +582,27 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
     bool vec = (size_t(f.len) * esz) % 16 == 0 && aligned16_b(f.u) && aligned16_b(a.dout) &&
                (!f.z || aligned16_b(f.z));
     for (int k = 0; k < f.ndir; ++k) vec = vec && aligned16_b(f.dir[k].delta);
-    const int64_t nblocks = f.batch * p.nwin * ngroups;
+    const int64_t chain_blocks = f.batch * p.nrun * ngroups;
     const int64_t carry_blocks = int64_t(f.ndir) * f.batch * kDState * ngroups;
-    const dim3 carry_block(kLanes * carry_parts(p.nwin));
-    // states entering every window
-    hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS>), dim3(unsigned(nblocks), unsigned(f.ndir)),
-                       dim3(kLanes), 0, stream, f, int64_t(kWin), p.nwin, static_cast<const float*>(bc), agg,
-                       int(vec));
-    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nwin,
-                       static_cast<const float*>(agg), hin, 0);
+    const dim3 cgrid(unsigned(chain_blocks), unsigned(f.ndir));
+    const dim3 carry_block(kLanes * carry_parts(p.nrun));
+    float* pw[2] = {w + p.off_p[0], w + p.off_p[1]};
+    float* sw[2] = {w + p.off_s[0], w + p.off_s[1]};
+    float* rw[2] = {w + p.off_r[0], w + p.off_r[1]};
+    float* ew[2] = {w + p.off_e[0], w + p.off_e[1]};
+    // the state entering every window
+    hipLaunchKernelGGL((bwd_chain_kernel<IO_BF16, SOFTPLUS, false, false>), cgrid, dim3(kLanes), 0, stream, f, p.nwin,
+                       p.run_len, p.nrun, static_cast<const float*>(bc), pw[0], sw[0], rw[0], int(vec));
+    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nrun,
+                       static_cast<const float*>(rw[0]), ew[0], 0);
     mark(2);
-    // adjoints entering every window from the other side
+    // the adjoint entering every window from the other side
     ScanArgs adj = f;
     adj.u = a.dout;
-    hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<IO_BF16, SOFTPLUS, HAS_Z>),
-                       dim3(unsigned(nblocks), unsigned(f.ndir)), dim3(kLanes), 0, stream, adj, int64_t(kWin),
-                       p.nwin, static_cast<const float*>(bc), agga, int(vec));
-    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nwin,
-                       static_cast<const float*>(agga), muin, 1);
+    hipLaunchKernelGGL((bwd_chain_kernel<IO_BF16, SOFTPLUS, HAS_Z, true>), cgrid, dim3(kLanes), 0, stream, adj,
+                       p.nwin, p.run_len, p.nrun, static_cast<const float*>(bc), pw[1], sw[1], rw[1], int(vec));
+    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nrun,
+                       static_cast<const float*>(rw[1]), ew[1], 1);
     mark(3);
   }
   const dim3 wgrid(unsigned(f.batch * p.nwin * p.csplit));
@@ -547,16 +610,16 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
   if (f.ndir == 1) {
     if (f.reverse) {
       hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSingle>), wgrid, dim3(kLanes), 0, stream,
-                         a, 0, nw, p.csplit, p.gps, bc, hin, muin, part, pbc, acc_du, acc_y);
+                         a, 0, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
     } else {
       hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, false, kSingle>), wgrid, dim3(kLanes), 0,
-                         stream, a, 0, nw, p.csplit, p.gps, bc, hin, muin, part, pbc, acc_du, acc_y);
+                         stream, a, 0, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
     }
   } else {
     hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, false, kFirst>), wgrid, dim3(kLanes), 0, stream, a,
-                       0, nw, p.csplit, p.gps, bc, hin, muin, part, pbc, acc_du, acc_y);
+                       0, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
     hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSecond>), wgrid, dim3(kLanes), 0, stream,
-                       a, 1, nw, p.csplit, p.gps, bc, hin, muin, part, pbc, acc_du, acc_y);
+                       a, 1, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
   }
   mark(4);
   hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned((f.dim + kLanes - 1) / kLanes), unsigned(f.ndir * kPartRows)),
@@ -588,6 +651,10 @@ hipError_t launch_bwd_io(const BwdArgs& a, const BwdPlan& p, float* w, hipStream
 
 // Resident window-pass waves the plan aims for (about four per SIMD).
 constexpr int64_t kBwdWaveTarget = 256 * 4 * 4;
+// Chain passes: blocks per pass the run length aims for (about eight waves per
+// SIMD), and the longest run.
+constexpr int64_t kChainWaveTarget = 256 * 4 * 8;
+constexpr int64_t kMaxRun = 64;
 
 BwdPlan make_bwd_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   BwdPlan p{};
@@ -601,16 +668,22 @@ BwdPlan make_bwd_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   size_t off = 0;
   p.off_bc = off;
   off += up(size_t(ndir) * batch * len * kBC);
-  const size_t seg_agg = p.nwin > 1 ? up(size_t(ndir) * batch * p.nwin * (kDState + 1) * dim) : 0;
-  const size_t seg_in = p.nwin > 1 ? up(size_t(ndir) * batch * p.nwin * kDState * dim) : 0;
-  p.off_agg = off;
-  off += seg_agg;
-  p.off_hin = off;
-  off += seg_in;
-  p.off_agga = off;
-  off += seg_agg;
-  p.off_muin = off;
-  off += seg_in;
+  // chain runs: about kChainWaveTarget one-wave blocks per chain pass, runs of at
+  // most kMaxRun windows
+  const int64_t ngroups64 = std::max<int64_t>(1, (dim + 63) / 64);
+  p.run_len = std::max<int64_t>(1, std::min<int64_t>(kMaxRun, base * ngroups64 / kChainWaveTarget));
+  p.nrun = (p.nwin + p.run_len - 1) / p.run_len;
+  const bool chains = p.nwin > 1;
+  for (int q = 0; q < 2; ++q) {
+    p.off_p[q] = off;
+    off += chains ? up(size_t(ndir) * batch * p.nwin * dim * kDState) : 0;
+    p.off_s[q] = off;
+    off += chains ? up(size_t(ndir) * batch * p.nwin * dim) : 0;
+    p.off_r[q] = off;
+    off += chains ? up(size_t(ndir) * batch * p.nrun * (kDState + 1) * dim) : 0;
+    p.off_e[q] = off;
+    off += chains ? up(size_t(ndir) * batch * p.nrun * kDState * dim) : 0;
+  }
   p.off_part = off;
   off += up(size_t(ndir) * batch * p.nwin * kPartRows * dim);
   p.off_pbc = off;

@@ -125,9 +125,15 @@ struct BwdArgs {
 };
 
 // Backward split into 32-token windows, and its workspace (float offsets):
-//   bc   [ndir][batch][len][32]           staged B/C
-//   agg, hin [ndir][batch][nwin][17|16][dim]  forward window aggregates / entry states
-//   agga, muin                            the same for the adjoint (nwin > 1 only)
+//   bc   [ndir][batch][len][32]             staged B/C
+// Two chains cross the windows: the state in scan order (chain 0) and the adjoint
+// against it (chain 1).  Each is walked over runs of run_len consecutive windows
+// (nwin > 1 only):
+//   p    [ndir][batch][nwin][dim][16]  after each window, the chain walked from zero
+//                                      at the start of its run
+//   s    [ndir][batch][nwin][dim]      the step sizes summed over the same stretch
+//   r    [ndir][batch][nrun][17][dim]  run totals (16 states, step-size sum)
+//   e    [ndir][batch][nrun][16][dim]  the chain entering each run (carry over runs)
 //   part [ndir][batch][nwin][18][dim]      per-window dA[16], dD, delta_bias
 //   pbc  [csplit][ndir][batch][2][16][len] dB, dC per channel split
 //   acc  [2][batch][dim][len]              first direction's du and y (two directions)
@@ -135,7 +141,9 @@ struct BwdPlan {
   int64_t nwin;             // windows per row
   int csplit;               // channel splits per window (blocks per window)
   int64_t gps;              // 4-channel groups per split
-  size_t off_bc, off_agg, off_hin, off_agga, off_muin, off_part, off_pbc, off_acc;
+  int64_t run_len, nrun;    // windows per chain run, runs per row
+  size_t off_bc, off_part, off_pbc, off_acc;
+  size_t off_p[2], off_s[2], off_r[2], off_e[2];
   size_t workspace_bytes;
 };
 
