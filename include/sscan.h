@@ -177,7 +177,8 @@ SSCAN_API int sscan_bidir_conv(const void* x, const sscan_conv_params* conv, con
  *   out = (sum_k scan_k) * silu(z)          (z == NULL: no gate)
  * kinds: rows, columns (column by column, top to bottom), or the permutation
  * index[0 .. height*width) (a device int32 array, required when used; entries must
- * be a permutation of the tokens -- others read as 0 and are not written), each
+ * be a permutation of the tokens -- an entry outside [0, height*width) reads as 0,
+ * and a token no entry names gets nothing from the index directions), each
  * forward or reversed; each kind at most once (1 to 6 directions).  Workspace:
  * sscan_multi_workspace_bytes(...) bytes, 256-byte aligned. */
 enum sscan_order {

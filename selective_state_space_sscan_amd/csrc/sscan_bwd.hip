@@ -129,17 +129,6 @@ __device__ __forceinline__ size_t pbc_index(int j, int dir, int64_t b, int which
   return (((((size_t)j * ndir + dir) * batch + b) * 2 + which) * kDState + n) * len + t;
 }
 
-// Chain buffers of the backward's window pass: a (window, channel)'s 16 states
-// contiguous, and its summed step sizes.
-__device__ __forceinline__ size_t win_state_index(int dir, int64_t b, int64_t k, int64_t d, int64_t batch,
-                                                  int64_t dim, int64_t nwin) {
-  return ((((size_t)dir * batch + b) * nwin + k) * dim + d) * kDState;
-}
-__device__ __forceinline__ size_t win_sum_index(int dir, int64_t b, int64_t k, int64_t d, int64_t batch,
-                                                int64_t dim, int64_t nwin) {
-  return (((size_t)dir * batch + b) * nwin + k) * dim + d;
-}
-
 // One chain across the windows, over a run of consecutive windows: walking the run
 // in chain order from zero -- the scan order for the state (kAggregate), the
 // opposite order for the adjoint (kAdjoint: mu, with a.u holding dout) -- the lane
@@ -169,8 +158,8 @@ __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void bwd_chain_kernel(
       L.template scan<false, kMode>(t0, t1);
     }
     if (L.active) {
-      store_state16(pw + win_state_index(dir, s.b, k, d, a.batch, a.dim, nwin), L.h);
-      sw[win_sum_index(dir, s.b, k, d, a.batch, a.dim, nwin)] = L.sum_dt;
+      store_state16(pw + chain_state_index(dir, s.b, k, d, a.batch, a.dim, nwin), L.h);
+      sw[chain_sum_index(dir, s.b, k, d, a.batch, a.dim, nwin)] = L.sum_dt;
     }
   }
   if (!L.active) return;
@@ -282,8 +271,8 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
       for (int q = 0; q < 2; ++q) {
         nx_e[q] = ch.e[q][hin_index(dir, b, run, n, d, f.batch, f.dim, ch.nrun)];
         if (has_pred[q]) {
-          nx_p[q] = ch.p[q][win_state_index(dir, b, pred[q], d, f.batch, f.dim, nwin) + n];
-          nx_s[q] = ch.s[q][win_sum_index(dir, b, pred[q], d, f.batch, f.dim, nwin)];
+          nx_p[q] = ch.p[q][chain_state_index(dir, b, pred[q], d, f.batch, f.dim, nwin) + n];
+          nx_s[q] = ch.s[q][chain_sum_index(dir, b, pred[q], d, f.batch, f.dim, nwin)];
         }
       }
     }
@@ -472,10 +461,13 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
 
 // dA, dD and delta_bias: the per-window partials summed over windows and batch
 // rows.  A block covers 64 channels of one (direction, row of the partials) with
-// four waves, each summing every fourth window with several loads in flight; the
-// four sums are added in a fixed order.  Accumulation is in double, so thousands
+// kReduceWaves waves, the q-th summing every kReduceWaves-th (batch row, window)
+// from q with several loads in flight; the waves' sums are added in a fixed order.  Accumulation is in double, so thousands
 // of partials add no error of their own (the partials carry float32 rounding only).
-constexpr int kReduceWaves = 4;
+#ifndef SSCAN_BWD_REDUCE_WAVES
+#define SSCAN_BWD_REDUCE_WAVES 16
+#endif
+constexpr int kReduceWaves = SSCAN_BWD_REDUCE_WAVES;
 
 __global__ __launch_bounds__(kLanes * kReduceWaves) void bwd_reduce_params_kernel(BwdArgs a, int64_t nwin,
                                                                                 const float* __restrict__ part) {
@@ -486,18 +478,18 @@ __global__ __launch_bounds__(kLanes * kReduceWaves) void bwd_reduce_params_kerne
   const int64_t d = min64(d_raw, f.dim - 1);
   const int r = int(blockIdx.y % kPartRows);
   const int dir = int(blockIdx.y / kPartRows);
+  // the (batch row, window) pairs m of one direction are consecutive in the layout
   const int64_t m_total = f.batch * nwin;
+  const float* base = part + ((size_t)dir * m_total * kPartRows + r) * f.dim + d;
+  const size_t stride = size_t(kPartRows) * f.dim;
   constexpr int kUnroll = 8;
   double acc[kUnroll] = {};
   int64_t m = q;
   for (; m + (kUnroll - 1) * kReduceWaves < m_total; m += kUnroll * kReduceWaves) {
 #pragma unroll
-    for (int e = 0; e < kUnroll; ++e) {
-      const int64_t mm = m + e * kReduceWaves;
-      acc[e] += part[part_index(dir, mm / nwin, mm % nwin, r, d, f.batch, f.dim, nwin)];
-    }
+    for (int e = 0; e < kUnroll; ++e) acc[e] += base[(m + e * kReduceWaves) * stride];
   }
-  for (; m < m_total; m += kReduceWaves) acc[0] += part[part_index(dir, m / nwin, m % nwin, r, d, f.batch, f.dim, nwin)];
+  for (; m < m_total; m += kReduceWaves) acc[0] += base[m * stride];
   double s = 0.0;
 #pragma unroll
   for (int e = 0; e < kUnroll; ++e) s += acc[e];

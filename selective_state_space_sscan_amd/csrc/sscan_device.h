@@ -450,6 +450,30 @@ __device__ __forceinline__ size_t hin_index(int dir, int64_t b, int64_t seg, int
   return ((((size_t)dir * batch + b) * nseg + seg) * kDState + n) * dim + d;
 }
 
+// Chains walked over runs of consecutive segments (or windows): after each one, a
+// (segment, channel)'s 16 values so far contiguous, and its summed step sizes.
+__device__ __forceinline__ size_t chain_state_index(int dir, int64_t b, int64_t k, int64_t d, int64_t batch,
+                                                    int64_t dim, int64_t nseg) {
+  return ((((size_t)dir * batch + b) * nseg + k) * dim + d) * kDState;
+}
+__device__ __forceinline__ size_t chain_sum_index(int dir, int64_t b, int64_t k, int64_t d, int64_t batch,
+                                                  int64_t dim, int64_t nseg) {
+  return (((size_t)dir * batch + b) * nseg + k) * dim + d;
+}
+
+// The state chain across the segments of a split sequence.  Segments are grouped
+// in runs of run_len: p and s hold, after each segment, the state reached walking
+// its run from a zero state and the step sizes summed so far (not kept for a
+// run's last segment, so absent when run_len is 1); r holds each run's totals in
+// the layout the carry kernel reads; e the state entering each run.
+struct SegChain {
+  float* p;  // [ndir][batch][nseg][dim][16]
+  float* s;  // [ndir][batch][nseg][dim]
+  float* r;  // [ndir][batch][nrun][17][dim]
+  float* e;  // [ndir][batch][nrun][16][dim]
+  int64_t run_len, nrun;
+};
+
 // Sets up a lane for direction `dir` of batch b, channel group g.
 template <class LaneT>
 __device__ __forceinline__ void init_lane(LaneT& L, const ScanArgs& a, int dir, int64_t b, int64_t g,
@@ -511,18 +535,31 @@ __device__ __forceinline__ void store_state16(float* p, const float (&h)[kDState
   for (int i = 0; i < kDState / 4; ++i) q[i] = make_float4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
 }
 
-// State entering a segment: from the carry chain when the sequence is split, else
-// the caller's entry state (or zero).
+// State entering a segment: the caller's entry state (or zero) when the sequence
+// is not split; else the state entering the segment's run, advanced over the
+// run's segments before this one: p + exp(A s) e, the composition of two affine
+// steps (e alone for the run's first segment in scan order).  Needs L.A2.
 template <class LaneT>
 __device__ __forceinline__ void load_entry(LaneT& L, const ScanArgs& a, int dir, int64_t b, int64_t seg,
-                                           int64_t g, int64_t nseg, const float* hin) {
+                                           int64_t g, int64_t nseg, const SegChain& ch) {
   const int64_t d = min64(g * kLanes + threadIdx.x % kLanes, a.dim - 1);
   if (nseg <= 1) {
     if (a.h0) load_state16(L.h, a.h0 + (b * a.dim + d) * kDState);
     return;
   }
+  const int64_t run = seg / ch.run_len;
 #pragma unroll
-  for (int n = 0; n < kDState; ++n) L.h[n] = hin[hin_index(dir, b, seg, n, d, a.batch, a.dim, nseg)];
+  for (int n = 0; n < kDState; ++n) L.h[n] = ch.e[hin_index(dir, b, run, n, d, a.batch, a.dim, ch.nrun)];
+  const bool rev = (a.ndir == 2 ? dir : a.reverse) != 0;
+  const int64_t lo = run * ch.run_len, hi = min64(nseg, lo + ch.run_len) - 1;
+  if (rev ? seg < hi : seg > lo) {
+    const int64_t k = rev ? seg + 1 : seg - 1;
+    float p[kDState];
+    load_state16(p, ch.p + chain_state_index(dir, b, k, d, a.batch, a.dim, nseg));
+    const float sd = ch.s[chain_sum_index(dir, b, k, d, a.batch, a.dim, nseg)];
+#pragma unroll
+    for (int n = 0; n < kDState; ++n) L.h[n] = fmaf(exp2_hw(L.A2[n] * sd), L.h[n], p[n]);
+  }
 }
 
 // Stage B and C token-major in fp32: bc[dir][b][t][0..15] = B[b][:, t],
@@ -556,35 +593,60 @@ __global__ __launch_bounds__(256) void stage_bc_kernel(ScanArgs a, float* __rest
   }
 }
 
-// Step 1: end state (from zero) and sum of step sizes of every segment except the
-// last one in scan order.  Grid: batch * nseg * ngroups one-wave blocks;
-// blockIdx.y selects the direction.
-template <bool IO_BF16, bool SOFTPLUS, int CONV = kNoConv>
+// Step 1: the segments of a run walked in scan order from a zero state, storing
+// after each one (but the run's last) the state so far and the summed step sizes,
+// and at the end the run's totals.  The segment scanned last in the whole row is
+// skipped (nothing follows it).  Grid: batch * nrun * ngroups one-wave blocks;
+// blockIdx.y selects the direction.  RUNS = false is the one-segment-per-run form
+// without the loop (fewer registers: four waves per SIMD in the plain scan).
+template <bool IO_BF16, bool SOFTPLUS, int CONV = kNoConv, bool RUNS = false>
 __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_aggregate_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
-                                                                const float* __restrict__ bc,
-                                                                float* __restrict__ agg, int vec) {
+                                                                SegChain ch, const float* __restrict__ bc, int vec) {
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
-  const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
+  const SegIndex s = decode_block(blockIdx.x, ngroups, ch.nrun);  // s.seg: the run
   const int dir = blockIdx.y;
   const int reverse = a.ndir == 2 ? dir : a.reverse;
-  if (reverse ? s.seg == 0 : s.seg == nseg - 1) return;
+  const int64_t last = reverse ? 0 : nseg - 1;
   Lane<IO_BF16, SOFTPLUS, false, CONV> L;
-  init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
-  const int64_t t0 = s.seg * seg_len;
-  const int64_t t1 = min64(a.len, t0 + seg_len);
-  if (reverse) {
-    L.template scan<true, kAggregate>(t0, t1);
+  const int64_t d = s.g * kLanes + threadIdx.x;
+  if (!RUNS) {
+    if (s.seg == last) return;
+    init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
+    const int64_t t0 = s.seg * seg_len;
+    const int64_t t1 = min64(a.len, t0 + seg_len);
+    if (reverse) {
+      L.template scan<true, kAggregate>(t0, t1);
+    } else {
+      L.template scan<false, kAggregate>(t0, t1);
+    }
   } else {
-    L.template scan<false, kAggregate>(t0, t1);
+    const int64_t k_lo = s.seg * ch.run_len, k_hi = min64(nseg, k_lo + ch.run_len);
+    if (k_hi - k_lo == 1 && k_lo == last) return;
+    init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
+    for (int64_t i = k_lo; i < k_hi; ++i) {
+      const int64_t k = reverse ? k_lo + k_hi - 1 - i : i;
+      if (k == last) break;
+      const int64_t t0 = k * seg_len;
+      const int64_t t1 = min64(a.len, t0 + seg_len);
+      if (reverse) {
+        L.template scan<true, kAggregate>(t0, t1);
+      } else {
+        L.template scan<false, kAggregate>(t0, t1);
+      }
+      if (i + 1 < k_hi && L.active) {
+        store_state16(ch.p + chain_state_index(dir, s.b, k, d, a.batch, a.dim, nseg), L.h);
+        ch.s[chain_sum_index(dir, s.b, k, d, a.batch, a.dim, nseg)] = L.sum_dt;
+      }
+    }
   }
   if (!L.active) return;
-  const int64_t d = s.g * kLanes + threadIdx.x;
 #pragma unroll
-  for (int n = 0; n < kDState; ++n) agg[agg_index(dir, s.b, s.seg, n, d, a.batch, a.dim, nseg)] = L.h[n];
-  agg[agg_index(dir, s.b, s.seg, kDState, d, a.batch, a.dim, nseg)] = L.sum_dt;
+  for (int n = 0; n < kDState; ++n) ch.r[agg_index(dir, s.b, s.seg, n, d, a.batch, a.dim, ch.nrun)] = L.h[n];
+  ch.r[agg_index(dir, s.b, s.seg, kDState, d, a.batch, a.dim, ch.nrun)] = L.sum_dt;
 }
 
-// Step 2: the chain of segment aggregates in scan order,
+// Step 2: the chain of run totals (segments grouped in runs; a run may be one
+// segment) in scan order,
 //   h_in[k+1] = exp(A sum_dt[k]) h_in[k] + H[k],   h_in[0] = h0 (or 0),
 // for every (direction, batch, state, channel).  The combine is associative, so
 // each chain is split into runs of consecutive segments, one wave per run (up to

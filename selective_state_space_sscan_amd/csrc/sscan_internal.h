@@ -72,7 +72,7 @@ struct MultiArgs {
 // Workspace (byte offsets, 256-aligned): fp32 accumulator, one family's output,
 // gathered u, gathered delta/B/C of a family's two directions, the scan's own.
 struct MultiPlan {
-  size_t off_acc, off_y, off_u, off_delta[2], off_B[2], off_C[2], off_scan;
+  size_t off_acc, off_y, off_u, off_delta[2], off_B[2], off_C[2], off_inv, off_scan;
   size_t workspace_bytes;
 };
 
@@ -170,9 +170,13 @@ hipError_t launch_bwd_zero(const BwdArgs& a, hipStream_t stream);
 struct Plan {
   int64_t seg_len;          // tokens per segment
   int64_t nseg;             // segments per row (1: no aggregate/carry kernels)
-  size_t bc_floats;
-  size_t agg_floats;
-  size_t hin_floats;
+  int64_t run_len;          // segments per aggregate run
+  int64_t nrun;             // runs per row
+  size_t bc_floats;         // workspace sections, in order (floats, 64-aligned)
+  size_t p_floats;          // per segment: state so far in its run (run_len > 1 only)
+  size_t s_floats;          // per segment: summed step sizes so far (run_len > 1 only)
+  size_t r_floats;          // per run: totals
+  size_t e_floats;          // per run: entry state
   size_t workspace_bytes;
 };
 

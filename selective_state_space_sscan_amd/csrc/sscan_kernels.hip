@@ -40,13 +40,13 @@ namespace {
 // state and stores the gated output.
 template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false>
 __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_output_dir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
-                                                                 const float* __restrict__ bc,
-                                                                 const float* __restrict__ hin, int vec) {
+                                                                 const float* __restrict__ bc, SegChain ch,
+                                                                 int vec) {
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
   Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32> L;
   init_lane(L, a, 0, s.b, s.g, bc, vec != 0);
-  load_entry(L, a, 0, s.b, s.seg, s.g, nseg, hin);
+  load_entry(L, a, 0, s.b, s.seg, s.g, nseg, ch);
   const int64_t t0 = s.seg * seg_len;
   const int64_t t1 = min64(a.len, t0 + seg_len);
   if (a.reverse) {
@@ -133,15 +133,15 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t 
 // covers the other half, adds the partner's parked outputs, gates and stores.
 template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false>
 __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
-                                                                       const float* __restrict__ bc,
-                                                                       const float* __restrict__ hin, int vec) {
+                                                                       const float* __restrict__ bc, SegChain ch,
+                                                                       int vec) {
   extern __shared__ float part[];  // [seg_len][64]
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
   const int dir = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kLanes);  // wave-uniform
   Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32> L;
   init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
-  load_entry(L, a, dir, s.b, s.seg, s.g, nseg, hin);
+  load_entry(L, a, dir, s.b, s.seg, s.g, nseg, ch);
   const int64_t t0 = s.seg * seg_len;
   const int64_t t1 = min64(a.len, t0 + seg_len);
   const int64_t mid = t0 + ((t1 - t0) / 2) / kTile * kTile;  // a multiple of both tile sizes
@@ -173,8 +173,19 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   bool vec = (size_t(a.len) * esz) % 16 == 0 && aligned16(a.u) && aligned16(a.y) && (!a.z || aligned16(a.z));
   for (int k = 0; k < a.ndir; ++k) vec = vec && aligned16(a.dir[k].delta);
   float* bc = w;
-  float* agg = p.nseg > 1 ? w + p.bc_floats : nullptr;
-  float* hin = p.nseg > 1 ? agg + p.agg_floats : nullptr;
+  SegChain ch{};
+  ch.run_len = p.run_len;
+  ch.nrun = p.nrun;
+  if (p.nseg > 1) {
+    float* q = w + p.bc_floats;
+    ch.p = p.p_floats ? q : nullptr;
+    q += p.p_floats;
+    ch.s = p.s_floats ? q : nullptr;
+    q += p.s_floats;
+    ch.r = q;
+    q += p.r_floats;
+    ch.e = q;
+  }
 
   const int64_t bc_blocks = int64_t(a.ndir) * a.batch * ((a.len + 63) / 64);
   mark(0);
@@ -185,24 +196,31 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   }
   mark(1);
   if (p.nseg > 1) {
-    hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS, CONV>), dim3(unsigned(nblocks), unsigned(a.ndir)),
-                       dim3(kLanes), 0, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), agg, int(vec));
+    const int64_t agg_blocks = a.batch * p.nrun * ngroups;
+    if (p.run_len > 1) {
+      hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS, CONV, true>),
+                         dim3(unsigned(agg_blocks), unsigned(a.ndir)), dim3(kLanes), 0, stream, a, p.seg_len, p.nseg,
+                         ch, static_cast<const float*>(bc), int(vec));
+    } else {
+      hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS, CONV, false>),
+                         dim3(unsigned(agg_blocks), unsigned(a.ndir)), dim3(kLanes), 0, stream, a, p.seg_len, p.nseg,
+                         ch, static_cast<const float*>(bc), int(vec));
+    }
     mark(2);
     const int64_t carry_blocks = int64_t(a.ndir) * a.batch * kDState * ngroups;
-    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), dim3(kLanes * carry_parts(p.nseg)), 0, stream,
-                       a, p.nseg, static_cast<const float*>(agg), hin, 0);
+    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), dim3(kLanes * carry_parts(p.nrun)), 0, stream,
+                       a, p.nrun, static_cast<const float*>(ch.r), ch.e, 0);
   }
   if (p.nseg <= 1) mark(2);
   mark(3);
   if (a.ndir == 1) {
     hipLaunchKernelGGL((scan_output_dir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32>), dim3(unsigned(nblocks)), dim3(kLanes), 0,
-                       stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), static_cast<const float*>(hin),
-                       int(vec));
+                       stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), ch, int(vec));
   } else {
     const size_t lds = size_t(p.seg_len) * kLanes * sizeof(float);
     hipLaunchKernelGGL((scan_output_bidir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32>), dim3(unsigned(nblocks)),
-                       dim3(2 * kLanes), lds, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc),
-                       static_cast<const float*>(hin), int(vec));
+                       dim3(2 * kLanes), lds, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), ch,
+                       int(vec));
   }
   mark(4);
   return hipGetLastError();
@@ -316,6 +334,11 @@ constexpr int64_t kWaveSlots = 256 * 4 * 3;
 // Bidirectional segments: the LDS meeting buffer (seg_len x 64 lanes x 4 B) must
 // leave room for eight two-wave blocks per CU.
 constexpr int64_t kBidirSegment = 64;
+// Segments are grouped in aggregate runs only where one wave per segment would
+// give the aggregate pass more than about four rounds of resident waves (very long
+// bidirectional sequences, cut into 64-token segments): the run form holds more
+// registers, and a short chain costs the carry little.
+constexpr int64_t kAggWaves = 4 * kWaveSlots;
 
 // Splitting along the sequence.  Sequences up to kShortMax tokens are scanned whole.
 // Longer ones are cut into equal segments (multiples of kTile tokens) so that the
@@ -344,14 +367,22 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
     p.seg_len = seg_len;
     p.nseg = (len + seg_len - 1) / seg_len;
   }
-  p.bc_floats = size_t(ndir) * batch * len * kBC;
+  // Aggregate runs: enough segments per run that the aggregate pass has about
+  // kAggWaves waves and the carry chains fewer runs.
+  p.run_len = std::max<int64_t>(1, int64_t(ndir) * groups * p.nseg / kAggWaves);
+  p.nrun = (p.nseg + p.run_len - 1) / p.run_len;
   // keep the sections 256-byte aligned
-  p.bc_floats = (p.bc_floats + 63) / 64 * 64;
+  auto up = [](size_t n) { return (n + 63) / 64 * 64; };
+  p.bc_floats = up(size_t(ndir) * batch * len * kBC);
   if (p.nseg > 1) {
-    p.agg_floats = (size_t(ndir) * batch * p.nseg * (kDState + 1) * dim + 63) / 64 * 64;
-    p.hin_floats = size_t(ndir) * batch * p.nseg * kDState * dim;
+    if (p.run_len > 1) {
+      p.p_floats = up(size_t(ndir) * batch * p.nseg * dim * kDState);
+      p.s_floats = up(size_t(ndir) * batch * p.nseg * dim);
+    }
+    p.r_floats = up(size_t(ndir) * batch * p.nrun * (kDState + 1) * dim);
+    p.e_floats = up(size_t(ndir) * batch * p.nrun * kDState * dim);
   }
-  p.workspace_bytes = (p.bc_floats + p.agg_floats + p.hin_floats) * sizeof(float);
+  p.workspace_bytes = (p.bc_floats + p.p_floats + p.s_floats + p.r_floats + p.e_floats) * sizeof(float);
   return p;
 }
 

@@ -66,15 +66,36 @@ dim3 transpose_grid(int64_t rows, int64_t h, int64_t w) {
   return dim3(unsigned((w + kTT - 1) / kTT), unsigned((h + kTT - 1) / kTT), unsigned(std::min(rows, kMaxGridZ)));
 }
 
+// The index family's kernels: a thread owns one position of the sequence and
+// walks the rows (grid: (ceil(len/256), up to 65535 row slots striding over the
+// rows)), so the position's index entry is read once and no thread divides.
+
 // out[row][s] = in[row][index[s]]; entries outside [0, len) read as 0.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ in, T* __restrict__ out,
                                                      const int32_t* __restrict__ index, int64_t rows, int64_t len) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= rows * len) return;
-  const int64_t row = i / len, s = i % len;
+  const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (s >= len) return;
   const int64_t p = index[s];
-  st(out, i, (p >= 0 && p < len) ? ld(in, row * len + p) : 0.0f);
+  const bool valid = p >= 0 && p < len;
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+    const int64_t base = row * len;
+    st(out, base + s, valid ? ld(in, base + p) : 0.0f);
+  }
+}
+
+// inv[p] = s for index[s] = p (inv filled with -1 first): the position at which
+// the index family visits token p.
+__global__ __launch_bounds__(256) void fill_kernel(int32_t* __restrict__ a, int64_t n, int32_t v) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) a[i] = v;
+}
+__global__ __launch_bounds__(256) void invert_kernel(const int32_t* __restrict__ index, int32_t* __restrict__ inv,
+                                                     int64_t len) {
+  const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (s >= len) return;
+  const int64_t p = index[s];
+  if (p >= 0 && p < len) inv[p] = int32_t(s);
 }
 
 __device__ __forceinline__ float silu_gate(float v, float zv) {
@@ -84,24 +105,33 @@ __device__ __forceinline__ float silu_gate(float v, float zv) {
 
 // Puts one family's fp32 output back at the token positions: FIRST sets the
 // accumulator, later families add to it; the LAST family adds, gates and stores
-// the result in the I/O dtype instead.  The index family: value s of a row goes
-// to token index[s] (entries outside [0, len) are skipped).
+// the result in the I/O dtype instead.  The index family reads, for token t, the
+// value at the position inv[t] that visits it (nothing where no position does), so
+// every store is coalesced and the permutation only scatters the reads.
 template <typename TIO, bool FIRST, bool LAST>
 __global__ __launch_bounds__(256) void put_index_kernel(const float* __restrict__ yf, float* __restrict__ acc,
-                                                        const int32_t* __restrict__ index, const TIO* __restrict__ z,
+                                                        const int32_t* __restrict__ inv, const TIO* __restrict__ z,
                                                         TIO* __restrict__ y, int64_t rows, int64_t len) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= rows * len) return;
-  const int64_t row = i / len, s = i % len;
-  const int64_t p = index[s];
-  if (p < 0 || p >= len) return;
-  const int64_t o = row * len + p;
-  const float v = FIRST ? yf[i] : acc[o] + yf[i];
-  if (LAST) {
-    st(y, o, z ? silu_gate(v, ld(z, o)) : v);
-  } else {
-    acc[o] = v;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= len) return;
+  const int64_t s = inv[t];
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+    const int64_t o = row * len + t;
+    const float yv = s >= 0 ? yf[row * len + s] : 0.0f;
+    const float v = FIRST ? yv : acc[o] + yv;
+    if (LAST) {
+      st(y, o, z ? silu_gate(v, ld(z, o)) : v);
+    } else {
+      acc[o] = v;
+    }
   }
+}
+
+// About 16K blocks: each block walks several rows, reusing its index entries.
+dim3 index_grid(int64_t rows, int64_t len) {
+  const int64_t gx = (len + 255) / 256;
+  const int64_t slots = std::min(std::min(rows, kMaxGridZ), std::max<int64_t>(64, 16384 / gx));
+  return dim3(unsigned(gx), unsigned(slots));
 }
 
 // The column family: its output is the [w][h] map of the visiting order,
@@ -146,7 +176,7 @@ void launch_transpose(const void* in, void* out, int64_t rows, int64_t h, int64_
 
 template <typename T>
 void launch_gather(const void* in, void* out, const int32_t* index, int64_t rows, int64_t len, hipStream_t s) {
-  hipLaunchKernelGGL((gather_kernel<T>), dim3(blocks_for(rows * len)), dim3(256), 0, s, static_cast<const T*>(in),
+  hipLaunchKernelGGL((gather_kernel<T>), index_grid(rows, len), dim3(256), 0, s, static_cast<const T*>(in),
                      static_cast<T*>(out), index, rows, len);
 }
 
@@ -168,7 +198,7 @@ void gather_family(int family, bool bf16, const void* in, void* out, const int32
 }
 
 template <typename TIO, bool FIRST, bool LAST>
-void put_family_t(int family, const float* yf, float* acc, const int32_t* index, const void* z, void* y,
+void put_family_t(int family, const float* yf, float* acc, const int32_t* inv, const void* z, void* y,
                   int64_t rows, int64_t h, int64_t w, hipStream_t s) {
   const TIO* zz = static_cast<const TIO*>(z);
   TIO* yy = static_cast<TIO*>(y);
@@ -176,22 +206,22 @@ void put_family_t(int family, const float* yf, float* acc, const int32_t* index,
     hipLaunchKernelGGL((put_col_kernel<TIO, FIRST, LAST>), transpose_grid(rows, w, h), dim3(kTT, 8), 0, s, yf, acc,
                        zz, yy, rows, w, h);
   } else {
-    hipLaunchKernelGGL((put_index_kernel<TIO, FIRST, LAST>), dim3(blocks_for(rows * h * w)), dim3(256), 0, s, yf,
-                       acc, index, zz, yy, rows, h * w);
+    hipLaunchKernelGGL((put_index_kernel<TIO, FIRST, LAST>), index_grid(rows, h * w), dim3(256), 0, s, yf, acc, inv,
+                       zz, yy, rows, h * w);
   }
 }
 
 template <typename TIO>
-void put_family(int family, const float* yf, float* acc, const int32_t* index, const void* z, void* y, int64_t rows,
+void put_family(int family, const float* yf, float* acc, const int32_t* inv, const void* z, void* y, int64_t rows,
                 int64_t h, int64_t w, bool first, bool last, hipStream_t s) {
   if (first && last) {
-    put_family_t<TIO, true, true>(family, yf, acc, index, z, y, rows, h, w, s);
+    put_family_t<TIO, true, true>(family, yf, acc, inv, z, y, rows, h, w, s);
   } else if (first) {
-    put_family_t<TIO, true, false>(family, yf, acc, index, z, y, rows, h, w, s);
+    put_family_t<TIO, true, false>(family, yf, acc, inv, z, y, rows, h, w, s);
   } else if (last) {
-    put_family_t<TIO, false, true>(family, yf, acc, index, z, y, rows, h, w, s);
+    put_family_t<TIO, false, true>(family, yf, acc, inv, z, y, rows, h, w, s);
   } else {
-    put_family_t<TIO, false, false>(family, yf, acc, index, z, y, rows, h, w, s);
+    put_family_t<TIO, false, false>(family, yf, acc, inv, z, y, rows, h, w, s);
   }
 }
 
@@ -224,6 +254,10 @@ MultiPlan make_multi_plan(int64_t batch, int64_t dim, int64_t height, int64_t wi
     p.off_C[j] = off;
     off += up(size_t(batch) * kDState * len * bc);
   }
+  bool has_index = false;
+  for (int k = 0; k < ndir; ++k) has_index = has_index || kinds[k] / 2 == kFamilyIndex;
+  p.off_inv = off;
+  off += has_index ? up(size_t(len) * 4) : 0;
   p.off_scan = off;
   off += up(scan);
   p.workspace_bytes = off;
@@ -301,10 +335,15 @@ hipError_t launch_multi(const MultiArgs& a, const MultiPlan& p, char* ws, hipStr
     if (e != hipSuccess) return e;
     if (f != kFamilyRow) {
       const float* yf = reinterpret_cast<const float*>(ws + p.off_y);
+      int32_t* inv = reinterpret_cast<int32_t*>(ws + p.off_inv);
+      if (f == kFamilyIndex) {
+        hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(len)), dim3(256), 0, stream, inv, len, -1);
+        hipLaunchKernelGGL(invert_kernel, dim3(blocks_for(len)), dim3(256), 0, stream, a.index, inv, len);
+      }
       if (a.io_bf16) {
-        put_family<uint16_t>(f, yf, acc, a.index, a.z, a.y, rows, a.height, a.width, first, last, stream);
+        put_family<uint16_t>(f, yf, acc, inv, a.z, a.y, rows, a.height, a.width, first, last, stream);
       } else {
-        put_family<float>(f, yf, acc, a.index, a.z, a.y, rows, a.height, a.width, first, last, stream);
+        put_family<float>(f, yf, acc, inv, a.z, a.y, rows, a.height, a.width, first, last, stream);
       }
     }
   }
