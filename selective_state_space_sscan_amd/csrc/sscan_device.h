@@ -175,8 +175,9 @@ constexpr int kConvBack = 3;
 // One lane's view of one direction of one (batch, channel) row.  SOFTPLUS, HAS_Z
 // and CONV are compile-time so that a tile's tokens form one straight-line block.
 // Y_F32 stores y in fp32 whatever the input dtype (partial outputs that are summed
-// before rounding, in the multi-order scan).
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV = kNoConv, bool Y_F32 = false>
+// before rounding, in the multi-order scan).  GPARK moves the bidirectional
+// kernel's meeting buffer from LDS to global memory.
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV = kNoConv, bool Y_F32 = false, bool GPARK = false>
 struct Lane {
   using IO = Io<IO_BF16>;
   using T = typename IO::T;
@@ -188,7 +189,9 @@ struct Lane {
   const T* z;     // nullable
   TY* y;
   const float* __restrict__ bc;  // staged B/C of this (direction, batch): bc[t * 32 + ...]
-  lds_float* part;  // LDS meeting buffer (bidirectional kernel), [t - t0][64]
+  // meeting buffer of the bidirectional kernel, [t - t0][64]: LDS, or (GPARK) the
+  // block's slice of a workspace buffer
+  typename std::conditional<GPARK, float*, lds_float*>::type part;
   int64_t t0;     // first token of the segment (LDS buffer origin)
   float A2[kDState];  // A * log2(e)
   float h[kDState];

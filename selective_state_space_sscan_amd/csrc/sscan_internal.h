@@ -177,6 +177,7 @@ struct Plan {
   size_t s_floats;          // per segment: summed step sizes so far (run_len > 1 only)
   size_t r_floats;          // per run: totals
   size_t e_floats;          // per run: entry state
+  size_t park_floats;       // bidirectional meeting buffers kept in global memory
   size_t workspace_bytes;
 };
 

@@ -129,23 +129,30 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t 
 }
 
 // Step 3, both directions: wave 0 scans the segment forward, wave 1 in reverse.
-// Each first covers the half it meets first and parks its outputs in LDS, then
-// covers the other half, adds the partner's parked outputs, gates and stores.
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false>
+// Each first covers the half it meets first and parks its outputs, then covers the
+// other half, adds the partner's parked outputs, gates and stores.  The meeting
+// buffer is LDS for segments up to kBidirSegment tokens; longer (single) segments
+// park in the block's slice of a workspace buffer (GPARK), so that LDS does not
+// cut the number of resident blocks (a 197-token buffer is 50 KB).
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false, bool GPARK = false>
 __global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
                                                                        const float* __restrict__ bc, SegChain ch,
-                                                                       int vec) {
+                                                                       float* __restrict__ gpark, int vec) {
   extern __shared__ float part[];  // [seg_len][64]
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
   const int dir = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kLanes);  // wave-uniform
-  Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32> L;
+  Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32, GPARK> L;
   init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
   load_entry(L, a, dir, s.b, s.seg, s.g, nseg, ch);
   const int64_t t0 = s.seg * seg_len;
   const int64_t t1 = min64(a.len, t0 + seg_len);
   const int64_t mid = t0 + ((t1 - t0) / 2) / kTile * kTile;  // a multiple of both tile sizes
-  L.part = (lds_float*)part;
+  if constexpr (GPARK) {
+    L.part = gpark + size_t(blockIdx.x) * size_t(seg_len) * kLanes;
+  } else {
+    L.part = (lds_float*)part;
+  }
   L.t0 = t0;
   if (dir == 0) {
     L.template scan<false, kPark>(t0, mid);
@@ -216,10 +223,15 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   if (a.ndir == 1) {
     hipLaunchKernelGGL((scan_output_dir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32>), dim3(unsigned(nblocks)), dim3(kLanes), 0,
                        stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), ch, int(vec));
+  } else if (p.park_floats) {
+    float* gpark = w + p.bc_floats + p.p_floats + p.s_floats + p.r_floats + p.e_floats;
+    hipLaunchKernelGGL((scan_output_bidir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32, true>), dim3(unsigned(nblocks)),
+                       dim3(2 * kLanes), 0, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), ch, gpark,
+                       int(vec));
   } else {
     const size_t lds = size_t(p.seg_len) * kLanes * sizeof(float);
-    hipLaunchKernelGGL((scan_output_bidir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32>), dim3(unsigned(nblocks)),
-                       dim3(2 * kLanes), lds, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), ch,
+    hipLaunchKernelGGL((scan_output_bidir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32, false>), dim3(unsigned(nblocks)),
+                       dim3(2 * kLanes), lds, stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), ch, nullptr,
                        int(vec));
   }
   mark(4);
@@ -332,7 +344,8 @@ __global__ __launch_bounds__(256) void conv1d_kernel(ConvArgs a, int vec) {
 // (the scan kernels are held to <= 168 VGPRs).
 constexpr int64_t kWaveSlots = 256 * 4 * 3;
 // Bidirectional segments: the LDS meeting buffer (seg_len x 64 lanes x 4 B) must
-// leave room for eight two-wave blocks per CU.
+// leave room for eight two-wave blocks per CU.  (A sequence short enough to be one
+// segment may be longer; its meeting buffer is in global memory.)
 constexpr int64_t kBidirSegment = 64;
 // Segments are grouped in aggregate runs only where one wave per segment would
 // give the aggregate pass more than about four rounds of resident waves (very long
@@ -340,12 +353,14 @@ constexpr int64_t kBidirSegment = 64;
 // registers, and a short chain costs the carry little.
 constexpr int64_t kAggWaves = 4 * kWaveSlots;
 
-// Splitting along the sequence.  Sequences up to kShortMax tokens are scanned whole.
-// Longer ones are cut into equal segments (multiples of kTile tokens) so that the
-// output step has about two rounds of resident waves: enough waves to cover load
-// latency and even out per-wave speed, without the long carry chain and large
-// aggregate buffers of many short segments (measured on the long-sequence and
-// Mamba-YOLO workloads).
+// Splitting along the sequence.  Sequences up to kShortMax tokens are scanned whole
+// (splitting a 197-token Vim sequence that fills only a quarter of the resident
+// wave slots was measured slower: its 64-token aggregate waves and short carry cost
+// more than the output pass gains).  Longer ones are cut into equal segments
+// (multiples of kTile tokens) so that the output step has about two rounds of
+// resident waves: enough waves to cover load latency and even out per-wave speed,
+// without the long carry chain and large aggregate buffers of many short segments
+// (measured on the long-sequence and Mamba-YOLO workloads).
 Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   Plan p{};
   const int64_t ngroups = (dim + kLanes - 1) / kLanes;
@@ -382,7 +397,11 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
     p.r_floats = up(size_t(ndir) * batch * p.nrun * (kDState + 1) * dim);
     p.e_floats = up(size_t(ndir) * batch * p.nrun * kDState * dim);
   }
-  p.workspace_bytes = (p.bc_floats + p.p_floats + p.s_floats + p.r_floats + p.e_floats) * sizeof(float);
+  // bidirectional segments longer than kBidirSegment park in global memory
+  if (ndir == 2 && p.seg_len > kBidirSegment)
+    p.park_floats = up(size_t(batch) * p.nseg * ngroups * p.seg_len * kLanes);
+  p.workspace_bytes =
+      (p.bc_floats + p.p_floats + p.s_floats + p.r_floats + p.e_floats + p.park_floats) * sizeof(float);
   return p;
 }
 

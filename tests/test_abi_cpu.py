@@ -124,9 +124,20 @@ def staging_bytes(ndir, b, L):
     return (ndir * b * L * 32 + 63) // 64 * 64 * 4
 
 
+def park_bytes(b, d, L):
+    # bidirectional meeting buffers of an unsplit sequence longer than 64 tokens,
+    # kept in global memory: per (batch row, 64-channel group) L tokens x 64 lanes
+    return (b * ((d + 63) // 64) * L * 64 + 63) // 64 * 64 * 4
+
+
 def test_workspace_rules(lib):
-    short = lib.sscan_workspace_bytes(64, 384, 197, 16, 1)
-    assert short == staging_bytes(2, 64, 197)  # unsplit sequence: B/C staging only
+    # unsplit sequence: B/C staging, plus global meeting buffers for a bidirectional
+    # one longer than 64 tokens
+    assert lib.sscan_workspace_bytes(128, 768, 64, 16, 1) == staging_bytes(2, 128, 64)
+    short = lib.sscan_workspace_bytes(128, 768, 197, 16, 1)
+    assert short == staging_bytes(2, 128, 197) + park_bytes(128, 768, 197)
+    assert lib.sscan_workspace_bytes(128, 768, 197, 16, 0) == staging_bytes(1, 128, 197)
+    assert lib.sscan_workspace_bytes(64, 384, 197, 16, 1) == staging_bytes(2, 64, 197) + park_bytes(64, 384, 197)
     assert lib.sscan_workspace_bytes(2, 64, 32, 16, 0) == staging_bytes(1, 2, 32)
     assert call_validate_fwd(lib, fwd_args(2, 64, 32, ws=None, ws_bytes=0)) == EWS
     long_f = lib.sscan_workspace_bytes(1, 1536, 262144, 16, 0)
