@@ -510,24 +510,26 @@ __global__ __launch_bounds__(kLanes * kReduceWaves) void bwd_reduce_params_kerne
 }
 
 // dB and dC: the channel splits' partials summed in split order, stored in B/C's dtype.
+// Grid: x over tokens (256 per block), y over the (direction, batch row, dB/dC,
+// state) rows, striding above the grid limit; no thread divides.
 template <bool BC_BF16>
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdArgs a, int csplit, const float* __restrict__ pbc) {
   const ScanArgs& f = a.fwd;
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= int64_t(f.ndir) * f.batch * 2 * kDState * f.len) return;
-  const int64_t t = i % f.len;
-  int64_t r = i / f.len;
-  const int n = int(r % kDState);
-  r /= kDState;
-  const int which = int(r % 2);
-  r /= 2;
-  const int64_t b = r % f.batch;
-  const int dir = int(r / f.batch);
-  double s = 0.0;
-  for (int j = 0; j < csplit; ++j) s += pbc[pbc_index(j, dir, b, which, n, t, f.ndir, f.batch, f.len)];
-  const DirGrads gd = dir ? a.grads[1] : a.grads[0];
-  void* out = which ? gd.dC : gd.dB;
-  Io<BC_BF16>::store(static_cast<typename Io<BC_BF16>::T*>(out), (b * kDState + n) * f.len + t, float(s));
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= f.len) return;
+  const int64_t rows = int64_t(f.ndir) * f.batch * 2 * kDState;
+  for (int64_t rr = blockIdx.y; rr < rows; rr += gridDim.y) {
+    const int n = int(rr & (kDState - 1));
+    const int which = int((rr >> 4) & 1);
+    const int64_t db = rr >> 5;  // dir * batch + b
+    const int dir = db >= f.batch ? 1 : 0;
+    const int64_t b = db - dir * f.batch;
+    double s = 0.0;
+    for (int j = 0; j < csplit; ++j) s += pbc[pbc_index(j, dir, b, which, n, t, f.ndir, f.batch, f.len)];
+    const DirGrads gd = dir ? a.grads[1] : a.grads[0];
+    void* out = which ? gd.dC : gd.dB;
+    Io<BC_BF16>::store(static_cast<typename Io<BC_BF16>::T*>(out), (b * kDState + n) * f.len + t, float(s));
+  }
 }
 
 __global__ __launch_bounds__(256) void bwd_zero_kernel(void* p, int64_t bytes) {
@@ -616,13 +618,14 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
   mark(4);
   hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned((f.dim + kLanes - 1) / kLanes), unsigned(f.ndir * kPartRows)),
                      dim3(kLanes * kReduceWaves), 0, stream, a, p.nwin, static_cast<const float*>(part));
-  const int64_t nb = int64_t(f.ndir) * f.batch * 2 * kDState * f.len;
+  const int64_t bc_rows = int64_t(f.ndir) * f.batch * 2 * kDState;
+  const dim3 bc_grid(unsigned((f.len + 255) / 256), unsigned(std::min<int64_t>(bc_rows, 65535)));
   if (f.bc_bf16) {
-    hipLaunchKernelGGL(bwd_reduce_bc_kernel<true>, dim3(unsigned((nb + 255) / 256)), dim3(256), 0, stream, a,
-                       p.csplit, static_cast<const float*>(pbc));
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel<true>, bc_grid, dim3(256), 0, stream, a, p.csplit,
+                       static_cast<const float*>(pbc));
   } else {
-    hipLaunchKernelGGL(bwd_reduce_bc_kernel<false>, dim3(unsigned((nb + 255) / 256)), dim3(256), 0, stream, a,
-                       p.csplit, static_cast<const float*>(pbc));
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel<false>, bc_grid, dim3(256), 0, stream, a, p.csplit,
+                       static_cast<const float*>(pbc));
   }
   mark(5);
   return hipGetLastError();

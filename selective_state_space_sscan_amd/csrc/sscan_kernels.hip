@@ -262,80 +262,93 @@ hipError_t launch_io(const ScanArgs& a, const Plan& p, float* w, hipStream_t str
 }
 
 // Standalone depthwise convolution: each thread produces kConvRun consecutive outputs
-// of one row.  The run itself moves as 16-byte vectors when rows are 16-byte aligned
-// (the halo -- three tokens before the run, one after -- as single elements, which
-// the neighbouring threads' vectors have already brought into the caches).
+// of one row.  The run itself moves as 16-byte vectors when rows are 16-byte aligned.
+// Block (64 runs, 4 channels): a wavefront holds 64 consecutive runs of one row, so
+// the halo -- three tokens before the run, one after -- is the neighbouring lanes'
+// data, moved across lanes; only the wave's first and last lanes read theirs from
+// memory.  Grid (run chunks, channel quads, batch rows -- striding above the grid
+// limit), so every thread knows its run and channel without dividing and loads its
+// channel's taps once.  Lanes past the row's end stay active (zeros) for the
+// cross-lane moves.
 constexpr int kConvRun = 8;
+constexpr int kConvRows = 4;
 
 template <bool IO_BF16, bool SILU>
-__global__ __launch_bounds__(256) void conv1d_kernel(ConvArgs a, int vec) {
+__global__ __launch_bounds__(kLanes * kConvRows) void conv1d_kernel(ConvArgs a, int vec) {
   using IO = Io<IO_BF16>;
   using T = typename IO::T;
-  const int64_t runs = (a.len + kConvRun - 1) / kConvRun;
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= a.batch * a.dim * runs) return;
-  const int64_t row = i / runs;
-  const int64_t t0 = (i % runs) * kConvRun;
-  const int64_t d = row % a.dim;
-  const T* x = static_cast<const T*>(a.x) + row * a.len;
-  T* y = static_cast<T*>(a.y) + row * a.len;
-  float cw[kConvTaps];
-#pragma unroll
-  for (int k = 0; k < kConvTaps; ++k) {
-    const int j = k - (kConvBack - a.left);
-    cw[k] = (j >= 0 && j < a.width) ? a.w[d * a.width + j] : 0.0f;
-  }
-  const float cb = a.b ? a.b[d] : 0.0f;
+  const int64_t r = int64_t(blockIdx.x) * kLanes + threadIdx.x;
+  const int64_t t0 = r * kConvRun;  // may be past the row's end: the lane loads and stores nothing
   const bool full = vec && t0 + kConvRun <= a.len;
   constexpr int kSpan = kConvBack + kConvRun + 1;
-  float xs[kSpan];  // x[t0 - 3 .. t0 + kConvRun], zero outside the row
+  for (int64_t d = int64_t(blockIdx.y) * kConvRows + threadIdx.y; d < a.dim; d += int64_t(gridDim.y) * kConvRows) {
+    float cw[kConvTaps];
 #pragma unroll
-  for (int k = 0; k < kConvBack; ++k) {
-    const int64_t t = t0 - kConvBack + k;
-    xs[k] = t >= 0 ? IO::load(x, t) : 0.0f;
-  }
-  xs[kSpan - 1] = t0 + kConvRun < a.len ? IO::load(x, t0 + kConvRun) : 0.0f;
-  if (full) {
-    if (IO_BF16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(x + t0);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int k = 0; k < kConvTaps; ++k) {
+      const int j = k - (kConvBack - a.left);
+      cw[k] = (j >= 0 && j < a.width) ? a.w[d * a.width + j] : 0.0f;
+    }
+    const float cb = a.b ? a.b[d] : 0.0f;
+    for (int64_t b = blockIdx.z; b < a.batch; b += gridDim.z) {
+      const int64_t row = b * a.dim + d;
+      const T* x = static_cast<const T*>(a.x) + row * a.len;
+      T* y = static_cast<T*>(a.y) + row * a.len;
+      float xs[kSpan];  // x[t0 - 3 .. t0 + kConvRun], zero outside the row
+      if (full) {
+        if (IO_BF16) {
+          const uint4 v = *reinterpret_cast<const uint4*>(x + t0);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        xs[kConvBack + 2 * k] = bf16_lo(w[k]);
-        xs[kConvBack + 2 * k + 1] = bf16_hi(w[k]);
+          for (int k = 0; k < 4; ++k) {
+            xs[kConvBack + 2 * k] = bf16_lo(w[k]);
+            xs[kConvBack + 2 * k + 1] = bf16_hi(w[k]);
+          }
+        } else {
+          const float4* p = reinterpret_cast<const float4*>(x + t0);
+          const float4 v0 = p[0], v1 = p[1];
+          const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) xs[kConvBack + k] = f[k];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kConvRun; ++k) xs[kConvBack + k] = t0 + k < a.len ? IO::load(x, t0 + k) : 0.0f;
       }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(x + t0);
-      const float4 v0 = p[0], v1 = p[1];
-      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      // the halo: the previous lane's last three tokens, the next lane's first
 #pragma unroll
-      for (int k = 0; k < 8; ++k) xs[kConvBack + k] = f[k];
+      for (int k = 0; k < kConvBack; ++k) xs[k] = __shfl_up(xs[kConvRun + k], 1);
+      xs[kSpan - 1] = __shfl_down(xs[kConvBack], 1);
+      if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < kConvBack; ++k) {
+          const int64_t t = t0 - kConvBack + k;
+          xs[k] = (t >= 0 && t < a.len) ? IO::load(x, t) : 0.0f;
+        }
+      }
+      if (threadIdx.x == kLanes - 1) xs[kSpan - 1] = t0 + kConvRun < a.len ? IO::load(x, t0 + kConvRun) : 0.0f;
+      float out[kConvRun];
+#pragma unroll
+      for (int j = 0; j < kConvRun; ++j) {
+        float acc = cb;
+#pragma unroll
+        for (int k = 0; k < kConvTaps; ++k) acc = fmaf(cw[k], xs[j + k], acc);
+        out[j] = SILU ? silu_f32(acc) : acc;
+      }
+      if (full) {
+        if (IO_BF16) {
+          *reinterpret_cast<uint4*>(y + t0) = make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
+                                                         pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
+        } else {
+          float4* p = reinterpret_cast<float4*>(y + t0);
+          p[0] = make_float4(out[0], out[1], out[2], out[3]);
+          p[1] = make_float4(out[4], out[5], out[6], out[7]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kConvRun; ++j)
+          if (t0 + j < a.len) IO::store(y, t0 + j, out[j]);
+      }
     }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kConvRun; ++k) xs[kConvBack + k] = t0 + k < a.len ? IO::load(x, t0 + k) : 0.0f;
-  }
-  float out[kConvRun];
-#pragma unroll
-  for (int j = 0; j < kConvRun; ++j) {
-    float acc = cb;
-#pragma unroll
-    for (int k = 0; k < kConvTaps; ++k) acc = fmaf(cw[k], xs[j + k], acc);
-    out[j] = SILU ? silu_f32(acc) : acc;
-  }
-  if (full) {
-    if (IO_BF16) {
-      *reinterpret_cast<uint4*>(y + t0) = make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
-                                                     pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
-    } else {
-      float4* p = reinterpret_cast<float4*>(y + t0);
-      p[0] = make_float4(out[0], out[1], out[2], out[3]);
-      p[1] = make_float4(out[4], out[5], out[6], out[7]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kConvRun; ++j)
-      if (t0 + j < a.len) IO::store(y, t0 + j, out[j]);
   }
 }
 }  // namespace
@@ -410,22 +423,26 @@ hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* ws, hipStream_t 
 }
 
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream) {
-  const int64_t n = a.batch * a.dim * ((a.len + kConvRun - 1) / kConvRun);
-  const dim3 grid(unsigned((n + 255) / 256));
+  constexpr int64_t kMaxGridYZ = 65535;
+  const int64_t runs = (a.len + kConvRun - 1) / kConvRun;
+  const int64_t quads = (a.dim + kConvRows - 1) / kConvRows;
+  const dim3 grid(unsigned((runs + kLanes - 1) / kLanes), unsigned(std::min(quads, kMaxGridYZ)),
+                  unsigned(std::min(a.batch, kMaxGridYZ)));
+  const dim3 block(kLanes, kConvRows);
   // runs start at multiples of 8 tokens: 16-byte aligned when every row is
   const size_t esz = a.io_bf16 ? 2 : 4;
   const int vec = (size_t(a.len) * esz) % 16 == 0 && aligned16(a.x) && aligned16(a.y);
   if (a.io_bf16) {
     if (a.silu) {
-      hipLaunchKernelGGL((conv1d_kernel<true, true>), grid, dim3(256), 0, stream, a, vec);
+      hipLaunchKernelGGL((conv1d_kernel<true, true>), grid, block, 0, stream, a, vec);
     } else {
-      hipLaunchKernelGGL((conv1d_kernel<true, false>), grid, dim3(256), 0, stream, a, vec);
+      hipLaunchKernelGGL((conv1d_kernel<true, false>), grid, block, 0, stream, a, vec);
     }
   } else {
     if (a.silu) {
-      hipLaunchKernelGGL((conv1d_kernel<false, true>), grid, dim3(256), 0, stream, a, vec);
+      hipLaunchKernelGGL((conv1d_kernel<false, true>), grid, block, 0, stream, a, vec);
     } else {
-      hipLaunchKernelGGL((conv1d_kernel<false, false>), grid, dim3(256), 0, stream, a, vec);
+      hipLaunchKernelGGL((conv1d_kernel<false, false>), grid, block, 0, stream, a, vec);
     }
   }
   return hipGetLastError();
