@@ -353,6 +353,15 @@ SSCAN_API int sscan_validate_multi(const void* u, const void* z, const void* y, 
  * for sscan_bidir.  Returns 0 for invalid sizes (the call itself reports them). */
 SSCAN_API size_t sscan_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir);
 
+/* How sscan_fwd / sscan_bidir (and the scans inside sscan_multi) split a sequence
+ * of these sizes, for tools and tests: out[0] tokens per segment, out[1] segments
+ * per row (1: scanned whole, no aggregate or carry kernels), out[2] segments per
+ * aggregate run (runs > 1 segment: the aggregate pass walks a run from a zero state
+ * and the carry chains only the runs' totals), out[3] runs per row.  out is HOST
+ * memory (4 entries).  Returns SSCAN_OK, SSCAN_ERR_NULL, SSCAN_ERR_SHAPE or
+ * SSCAN_ERR_UNSUPPORTED (dstate != 16). */
+SSCAN_API int sscan_scan_plan(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir, int64_t* out);
+
 /* Static description of a status code; never NULL. */
 SSCAN_API const char* sscan_strerror(int status);
 

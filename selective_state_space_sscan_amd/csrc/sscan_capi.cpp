@@ -748,6 +748,19 @@ size_t sscan_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t ds
   return sscan::make_plan(batch, dim, len, bidir ? 2 : 1).workspace_bytes;
 }
 
+int sscan_scan_plan(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir, int64_t* out) {
+  if (!out) return SSCAN_ERR_NULL;
+  Sizes sz{};
+  const int st = check_sizes(batch, dim, len, dstate, SSCAN_F32, SSCAN_F32, &sz);
+  if (st != SSCAN_OK) return st;
+  const sscan::Plan p = sscan::make_plan(batch, dim, len, bidir ? 2 : 1);
+  out[0] = p.seg_len;
+  out[1] = p.nseg;
+  out[2] = p.run_len;
+  out[3] = p.nrun;
+  return SSCAN_OK;
+}
+
 const char* sscan_strerror(int status) {
   switch (status) {
     case SSCAN_OK: return "ok";

@@ -121,6 +121,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_spiral_order.restype = I
     lib.sscan_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.sscan_workspace_bytes.restype = SZ
+    lib.sscan_scan_plan.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(ctypes.c_int64)]
+    lib.sscan_scan_plan.restype = I
     lib.sscan_strerror.argtypes = [I]
     lib.sscan_strerror.restype = ctypes.c_char_p
     lib.sscan_version.argtypes = []
@@ -195,6 +197,16 @@ def strerror(status: int) -> str:
 
 def workspace_bytes(batch: int, dim: int, length: int, dstate: int = DSTATE, bidir: bool = False) -> int:
     return int(load_library().sscan_workspace_bytes(batch, dim, length, dstate, int(bool(bidir))))
+
+
+def scan_plan(batch: int, dim: int, length: int, dstate: int = DSTATE, bidir: bool = False) -> dict:
+    """How a scan of these sizes is split (sscan_scan_plan): segment length, segments
+    per row, segments per aggregate run, runs per row."""
+    out = (ctypes.c_int64 * 4)()
+    st = load_library().sscan_scan_plan(batch, dim, length, dstate, int(bool(bidir)), out)
+    if st != 0:
+        raise SScanError(st, "sscan_scan_plan")
+    return dict(seg_len=out[0], nseg=out[1], run_len=out[2], nrun=out[3])
 
 
 def _ptr(t: Optional[torch.Tensor]):

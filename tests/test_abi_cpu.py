@@ -359,3 +359,20 @@ def test_validate_multi(lib):
     assert V(kinds, 4, ws=wsp + 16) == EALIGN  # 256-byte aligned workspace
     assert V(kinds, 4, y=u) == EALIAS
     assert V(kinds, 4, h=-1) == ESHAPE
+
+def test_scan_plan_splits():
+    """How calls are split: short sequences whole; long one-direction sequences in
+    1024-token segments, one per aggregate run; long bidirectional ones in 64-token
+    segments, grouped in aggregate runs only when one wave per segment would exceed
+    four rounds of resident waves."""
+    plan = sscan.scan_plan
+    assert plan(128, 768, 197, bidir=True) == dict(seg_len=197, nseg=1, run_len=1, nrun=1)
+    assert plan(2, 64, 256) == dict(seg_len=256, nseg=1, run_len=1, nrun=1)
+    assert plan(1, 1536, 262144) == dict(seg_len=1024, nseg=256, run_len=1, nrun=256)
+    assert plan(8, 192, 16384, bidir=True) == dict(seg_len=64, nseg=256, run_len=1, nrun=256)
+    long_b = plan(1, 64, 1 << 20, bidir=True)
+    assert long_b["seg_len"] == 64 and long_b["run_len"] == 2 and long_b["nrun"] * 2 == long_b["nseg"]
+    assert plan(1, 192, 512 * 512, bidir=True)["run_len"] == 2
+    assert plan(1, 1536, 512 * 512, bidir=True)["run_len"] == 16
+    with pytest.raises(sscan.SScanError):
+        plan(1, 64, 100, dstate=8)

@@ -91,3 +91,26 @@ def test_yolo_stage1_map_cross4():
     """The Mamba-YOLO stage-1 map (128 x 128 tokens, 192 channels, bf16) in the
     four-direction cross order (two batch rows)."""
     run_both("yolo-cross4", 2, 192, 128, 128, [R, RR, C, CR], "bf16", "bf16", True)
+
+
+def test_large_map_cross4_aggregate_runs():
+    """A 512 x 512 map, 192 channels, four directions: each direction pair's 64-token
+    segments are grouped in aggregate runs (sscan_scan_plan).  Whole maps of sampled
+    channels against the oracle."""
+    b, d, h, w = 1, 192, 512, 512
+    assert sscan.scan_plan(b, d, h * w, bidir=True)["run_len"] > 1
+    kinds = [R, RR, C, CR]
+    x, dirs = draw("large-cross4", b, d, h, w, len(kinds), "bf16", "bf16")
+    xd = x.to(DEV)
+    gd = [dict(delta=xd.delta, delta_bias=p.delta_bias.to(DEV), A=p.A.to(DEV), B=p.B.to(DEV), C=p.C.to(DEV),
+               D=p.D.to(DEV)) for p in dirs]
+    got = sscan.multi(xd.u, xd.z, gd, kinds, h, w)
+    torch.cuda.synchronize()
+    rows = [0, 100, 191]
+    sl = lambda t: I.f64(t[:, rows].contiguous())  # sliced before widening
+    od = [dict(delta=sl(x.delta), A=I.f64(p.A[rows].contiguous()), B=I.f64(p.B), C=I.f64(p.C),
+               D=I.f64(p.D[rows].contiguous()), delta_bias=I.f64(p.delta_bias[rows].contiguous())) for p in dirs]
+    ref = orders.scan_multi(sl(x.u), sl(x.z), od, kinds, h, w, nthreads=NTHREADS)
+    m = metrics(I.f64(got.cpu()[:, rows]), ref)
+    print(f"large-cross4 rows {rows}: floored {m['floored_max']:.3e}", flush=True)
+    assert m["floored_max"] <= TOL["bf16"], m

@@ -88,6 +88,33 @@ def test_config4_long_sequence_sampled_rows():
     check(np.concatenate(gots, 1), np.concatenate(refs, 1), "bf16", f"config 4 rows {rows}")
 
 
+def channel_rows(x, rows):
+    """The oracle's fp64 inputs restricted to channels `rows` (B and C are per batch
+    row and stay whole), sliced before widening."""
+    sl = lambda t: I.f64(t[:, rows].contiguous())
+    return dict(u=sl(x.u), delta=sl(x.delta), z=sl(x.z),
+                dirs=[dict(A=I.f64(p.A[rows].contiguous()), B=I.f64(p.B), C=I.f64(p.C), D=I.f64(p.D[rows].contiguous()),
+                           delta_bias=I.f64(p.delta_bias[rows].contiguous())) for p in x.dirs])
+
+
+def test_bidir_long_aggregate_runs():
+    """A 1M-token bidirectional scan: 16384 segments of 64 tokens, grouped in aggregate
+    runs (sscan_scan_plan) so that the carry chains the runs and the output kernels
+    rebuild each segment's entry state from its run; whole rows of sampled channels
+    against the oracle."""
+    b, d, L = 1, 64, 1 << 20
+    assert sscan.scan_plan(b, d, L, bidir=True)["run_len"] > 1
+    x = I.make_inputs(b, d, L, bidir=True, io_dtype="bf16", bc_dtype="bf16", seed=77, dt_range=(1e-4, 1e-2))
+    got = gpu_run(x).cpu()
+    rows = [0, 17, 63]
+    ref = oracle_run_dict(channel_rows(x, rows))
+    check(I.f64(got[:, rows]), ref, "bf16", f"1M-token bidirectional, rows {rows}")
+
+
+def oracle_run_dict(x64):
+    return oracle.run_inputs(x64, nthreads=NTHREADS)
+
+
 EDGE = [
     # name, batch, dim, len, bidir, io, bc, kwargs
     ("len1-fwd", 2, 64, 1, False, "f32", "f32", {}),
