@@ -20,6 +20,7 @@
 #include "sscan_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <cstring>
 
 namespace sscan {
@@ -64,6 +65,53 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
 
 dim3 transpose_grid(int64_t rows, int64_t h, int64_t w) {
   return dim3(unsigned((w + kTT - 1) / kTT), unsigned((h + kTT - 1) / kTT), unsigned(std::min(rows, kMaxGridZ)));
+}
+
+// The same for bf16 maps with even sides, on 64 x 64 tiles moving element pairs:
+// a thread loads two neighbours of a row as one 4-byte word and stores two
+// neighbours of an output row as one word (128 contiguous bytes per 32 lanes
+// either way, where single 2-byte elements give 64).  The LDS tile keeps the loaded
+// words; a column's pair is taken from two of them.  Block 32 x 8.
+constexpr int kPT = 64;
+
+__device__ __forceinline__ uint32_t half_of(uint32_t w, int hi) { return hi ? w >> 16 : w & 0xffffu; }
+
+// two floats rounded to bf16 (nearest even) in one word, lo in the low half
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const f2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, b2));
+}
+
+__global__ __launch_bounds__(256) void transpose_pairs_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                              int64_t rows, int64_t h, int64_t w) {
+  __shared__ uint32_t tile[kPT][kPT / 2 + 1];  // [row in tile][column pair]
+  const int64_t c0 = int64_t(blockIdx.x) * kPT, r0 = int64_t(blockIdx.y) * kPT;
+  const int tx = threadIdx.x, ty = threadIdx.y;
+  for (int64_t row = blockIdx.z; row < rows; row += gridDim.z) {
+    const uint16_t* src = in + row * h * w;
+    uint16_t* dst = out + row * h * w;
+    __syncthreads();  // the previous row's tile has been read out
+    for (int k = ty; k < kPT; k += 8) {
+      const int64_t r = r0 + k, c = c0 + 2 * tx;
+      tile[k][tx] = (r < h && c < w) ? *reinterpret_cast<const uint32_t*>(src + r * w + c) : 0u;
+    }
+    __syncthreads();
+    for (int k = ty; k < kPT; k += 8) {
+      // output row c0 + k holds input column c0 + k; this thread's pair: input rows
+      // r0 + 2 tx and r0 + 2 tx + 1
+      const int64_t c = c0 + k, r = r0 + 2 * tx;
+      if (c < w && r < h) {
+        const uint32_t lo = half_of(tile[2 * tx][k >> 1], k & 1), hi = half_of(tile[2 * tx + 1][k >> 1], k & 1);
+        *reinterpret_cast<uint32_t*>(dst + c * h + r) = lo | (hi << 16);
+      }
+    }
+  }
+}
+
+dim3 pairs_grid(int64_t rows, int64_t h, int64_t w) {
+  return dim3(unsigned((w + kPT - 1) / kPT), unsigned((h + kPT - 1) / kPT), unsigned(std::min(rows, kMaxGridZ)));
 }
 
 // The index family's kernels: a thread owns one position of the sequence and
@@ -166,7 +214,62 @@ __global__ __launch_bounds__(256) void put_col_kernel(const float* __restrict__ 
   }
 }
 
+// put_col_kernel for bf16 maps with even sides, on 64 x 64 tiles moving pairs: the
+// family's fp32 output ([w][h], a column per row) is read as float2 along the
+// column, and two neighbouring tokens of a map row are handled per thread (float2
+// accumulator, a 4-byte word of z and of y).  Block 32 x 8; grid as
+// transpose_pairs_kernel with the [w][h] shape.
+template <bool FIRST, bool LAST>
+__global__ __launch_bounds__(256) void put_col_pairs_kernel(const float* __restrict__ yf, float* __restrict__ acc,
+                                                            const uint16_t* __restrict__ z, uint16_t* __restrict__ y,
+                                                            int64_t rows, int64_t h, int64_t w) {
+  __shared__ float tile[kPT][kPT + 1];  // [column in tile][map row in tile]
+  // the tile covers map rows r0 .. r0+63 (yf's columns) and map columns c0 .. c0+63
+  const int64_t r0 = int64_t(blockIdx.x) * kPT, c0 = int64_t(blockIdx.y) * kPT;
+  const int tx = threadIdx.x, ty = threadIdx.y;
+  for (int64_t row = blockIdx.z; row < rows; row += gridDim.z) {
+    const float* src = yf + row * h * w;
+    __syncthreads();
+    for (int k = ty; k < kPT; k += 8) {
+      const int64_t c = c0 + k, r = r0 + 2 * tx;
+      float2 v = make_float2(0.0f, 0.0f);
+      if (c < w && r < h) v = *reinterpret_cast<const float2*>(src + c * h + r);
+      tile[k][2 * tx] = v.x;
+      tile[k][2 * tx + 1] = v.y;
+    }
+    __syncthreads();
+    for (int k = ty; k < kPT; k += 8) {
+      const int64_t r = r0 + k, c = c0 + 2 * tx;
+      if (r >= h || c >= w) continue;
+      const int64_t o = row * h * w + r * w + c;
+      float v0 = tile[2 * tx][k], v1 = tile[2 * tx + 1][k];
+      if (!FIRST) {
+        const float2 a = *reinterpret_cast<const float2*>(acc + o);
+        v0 += a.x;
+        v1 += a.y;
+      }
+      if (LAST) {
+        if (z) {
+          const uint32_t zw = *reinterpret_cast<const uint32_t*>(z + o);
+          v0 = silu_gate(v0, __uint_as_float(zw << 16));
+          v1 = silu_gate(v1, __uint_as_float(zw & 0xffff0000u));
+        }
+        *reinterpret_cast<uint32_t*>(y + o) = bf16_pair(v0, v1);
+      } else {
+        *reinterpret_cast<float2*>(acc + o) = make_float2(v0, v1);
+      }
+    }
+  }
+}
+
 unsigned blocks_for(int64_t n) { return unsigned((n + 255) / 256); }
+
+// Element pairs of a [h][w] map and its transpose are 4-byte words when both sides
+// are even and the bases are 4-byte aligned.
+bool pairs_ok(const void* a, const void* b, int64_t h, int64_t w) {
+  return h % 2 == 0 && w % 2 == 0 && (reinterpret_cast<uintptr_t>(a) & 3u) == 0 &&
+         (reinterpret_cast<uintptr_t>(b) & 3u) == 0;
+}
 
 template <typename T>
 void launch_transpose(const void* in, void* out, int64_t rows, int64_t h, int64_t w, hipStream_t s) {
@@ -185,7 +288,10 @@ void launch_gather(const void* in, void* out, const int32_t* index, int64_t rows
 void gather_family(int family, bool bf16, const void* in, void* out, const int32_t* index, int64_t rows,
                    int64_t h, int64_t w, hipStream_t s) {
   if (family == kFamilyCol) {
-    if (bf16) {
+    if (bf16 && pairs_ok(in, out, h, w)) {
+      hipLaunchKernelGGL(transpose_pairs_kernel, pairs_grid(rows, h, w), dim3(32, 8), 0, s,
+                         static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), rows, h, w);
+    } else if (bf16) {
       launch_transpose<uint16_t>(in, out, rows, h, w, s);
     } else {
       launch_transpose<float>(in, out, rows, h, w, s);
@@ -203,8 +309,13 @@ void put_family_t(int family, const float* yf, float* acc, const int32_t* inv, c
   const TIO* zz = static_cast<const TIO*>(z);
   TIO* yy = static_cast<TIO*>(y);
   if (family == kFamilyCol) {
-    hipLaunchKernelGGL((put_col_kernel<TIO, FIRST, LAST>), transpose_grid(rows, w, h), dim3(kTT, 8), 0, s, yf, acc,
-                       zz, yy, rows, w, h);
+    if (std::is_same<TIO, uint16_t>::value && pairs_ok(y, z ? z : y, h, w)) {
+      hipLaunchKernelGGL((put_col_pairs_kernel<FIRST, LAST>), pairs_grid(rows, w, h), dim3(32, 8), 0, s, yf, acc,
+                         reinterpret_cast<const uint16_t*>(zz), reinterpret_cast<uint16_t*>(yy), rows, h, w);
+    } else {
+      hipLaunchKernelGGL((put_col_kernel<TIO, FIRST, LAST>), transpose_grid(rows, w, h), dim3(kTT, 8), 0, s, yf,
+                         acc, zz, yy, rows, w, h);
+    }
   } else {
     hipLaunchKernelGGL((put_index_kernel<TIO, FIRST, LAST>), index_grid(rows, h * w), dim3(256), 0, s, yf, acc, inv,
                        zz, yy, rows, h * w);

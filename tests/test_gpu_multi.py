@@ -66,6 +66,9 @@ CASES = [
     ("col-rev-only", 2, 64, 16, 9, [CR], "f32", "f32", True),
     ("row-and-col", 1, 96, 33, 31, [R, C], "f32", "f32", False),
     ("cross4-bf16", 2, 128, 32, 48, [CR, R, C, RR], "bf16", "bf16", True),
+    # odd sides: the bf16 column family's element-pair kernels do not apply
+    ("cross4-bf16-odd-map", 2, 64, 17, 33, [R, RR, C, CR], "bf16", "bf16", True),
+    ("col-pair-bf16-no-gate", 1, 64, 32, 20, [C, CR], "bf16", "bf16", False),
 ]
 
 
