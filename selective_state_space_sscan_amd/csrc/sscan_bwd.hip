@@ -473,7 +473,8 @@ __global__ __launch_bounds__(kLanes * kReduceWaves) void bwd_reduce_params_kerne
                                                                                 const float* __restrict__ part) {
   __shared__ double sh[kReduceWaves][kLanes];
   const ScanArgs& f = a.fwd;
-  const int lane = threadIdx.x % kLanes, q = threadIdx.x / kLanes;
+  const int lane = threadIdx.x % kLanes;
+  const int q = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kLanes);  // wave-uniform
   const int64_t d_raw = int64_t(blockIdx.x) * kLanes + lane;
   const int64_t d = min64(d_raw, f.dim - 1);
   const int r = int(blockIdx.y % kPartRows);

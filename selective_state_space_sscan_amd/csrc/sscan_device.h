@@ -673,7 +673,8 @@ __global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanAr
   __shared__ float sh_h[kCarryParts][kLanes];
   const int nparts = int(blockDim.x) / kLanes;
   const int lane = threadIdx.x % kLanes;
-  const int part = threadIdx.x / kLanes;
+  // wave-uniform: read through readfirstlane so the chain's indices stay scalar
+  const int part = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kLanes);
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   int64_t r = blockIdx.x;
   const int64_t g = r % ngroups;
@@ -695,18 +696,26 @@ __global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanAr
   auto seg_of = [&](int64_t k) { return reverse ? nseg - 1 - k : k; };
   // the last segment in scan order has no aggregate (nothing follows it)
   const int64_t kagg = min64(k1, nseg - 1);
+  // Addresses split into a wave-uniform row (scalar registers) and the lane's
+  // channel offset, so the per-step loads and stores cost no vector arithmetic.
+  const uint32_t dl = uint32_t(d);
+  auto agg_row = [&](int64_t seg, int row) {  // row n: H of state n; row kDState: S
+    return agg + ((((size_t)dir * a.batch + b) * nseg + seg) * (kDState + 1) + row) * a.dim;
+  };
+  auto hin_row = [&](int64_t seg) { return hin + ((((size_t)dir * a.batch + b) * nseg + seg) * kDState + n) * a.dim; };
   // a run's aggregates are loaded kBatch at a time, all loads in flight together
-  // (they do not depend on the chain); runs of up to kBatch segments are loaded once
-  constexpr int kBatch = 32;
+  // (they do not depend on the chain); runs of up to kBatch segments are loaded once.
+  // 16 keeps the kernel near 48 VGPRs, so two 16-wave blocks share a CU.
+  constexpr int kBatch = 16;
   float hb[kBatch], sb[kBatch];
   auto load_batch = [&](int64_t kb) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int64_t k = kb + i;
       const bool has = k < kagg;
-      const int64_t seg = seg_of(has ? k : 0);  // a valid segment even when the run is empty
-      hb[i] = has ? agg[agg_index(dir, b, seg, n, d, a.batch, a.dim, nseg)] : 0.0f;
-      sb[i] = has ? agg[agg_index(dir, b, seg, kDState, d, a.batch, a.dim, nseg)] : 0.0f;
+      const int64_t seg = seg_of(has ? k : 0);  // a valid segment even past the run's end
+      hb[i] = has ? agg_row(seg, n)[dl] : 0.0f;
+      sb[i] = has ? agg_row(seg, kDState)[dl] : 0.0f;
     }
   };
   float S = 0.0f, H = 0.0f;
@@ -732,7 +741,7 @@ __global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanAr
     for (int i = 0; i < kBatch; ++i) {
       const int64_t k = kb + i;
       if (k < k1) {
-        if (active) hin[hin_index(dir, b, seg_of(k), n, d, a.batch, a.dim, nseg)] = h;
+        if (active) hin_row(seg_of(k))[dl] = h;
         if (k < kagg) h = fmaf(exp2_hw(A2 * sb[i]), h, hb[i]);
       }
     }
