@@ -114,36 +114,64 @@ dim3 pairs_grid(int64_t rows, int64_t h, int64_t w) {
   return dim3(unsigned((w + kPT - 1) / kPT), unsigned((h + kPT - 1) / kPT), unsigned(std::min(rows, kMaxGridZ)));
 }
 
-// The index family's kernels: a thread owns one position of the sequence and
-// walks the rows (grid: (ceil(len/256), up to 65535 row slots striding over the
-// rows)), so the position's index entry is read once and no thread divides.
+// The index family's kernels.  On large maps the gather takes one element per
+// thread in flat (row, position) order, so the whole GPU works through a few
+// channel rows at a time: the column runs of a spatial order (a spiral) read a new
+// 128-byte line per element, and a channel row (a few hundred KB) stays in the
+// caches while its lines are reused.  On small maps, and for the put-back (which
+// reads through the inverse permutation and writes coalesced), a thread walks
+// groups of kIndexRows rows with their loads in flight together, which measured
+// faster there.
+constexpr int kIndexRows = 4;
+
+// The gather in row groups, for maps small enough that the flat order's cache
+// reuse does not matter: a thread walks groups of kIndexRows rows with their loads
+// in flight together (same result as gather_kernel).
+template <typename T>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const T* __restrict__ in, T* __restrict__ out,
+                                                          const int32_t* __restrict__ index, int64_t rows,
+                                                          int64_t len) {
+  const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (s >= len) return;
+  const int64_t p = index[s];
+  const bool valid = p >= 0 && p < len;
+  const int64_t pp = valid ? p : 0;
+  for (int64_t row0 = int64_t(blockIdx.y) * kIndexRows; row0 < rows; row0 += int64_t(gridDim.y) * kIndexRows) {
+    float v[kIndexRows];
+#pragma unroll
+    for (int j = 0; j < kIndexRows; ++j) {
+      const int64_t row = row0 + j;
+      v[j] = (valid && row < rows) ? ld(in, row * len + pp) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kIndexRows; ++j)
+      if (row0 + j < rows) st(out, (row0 + j) * len + s, v[j]);
+  }
+}
 
 // out[row][s] = in[row][index[s]]; entries outside [0, len) read as 0.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ in, T* __restrict__ out,
                                                      const int32_t* __restrict__ index, int64_t rows, int64_t len) {
-  const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (s >= len) return;
-  const int64_t p = index[s];
-  const bool valid = p >= 0 && p < len;
-  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
-    const int64_t base = row * len;
-    st(out, base + s, valid ? ld(in, base + p) : 0.0f);
+  const int64_t n = rows * len;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const int64_t row = i / len, s = i - row * len;
+    const int64_t p = index[s];
+    st(out, i, (p >= 0 && p < len) ? ld(in, row * len + p) : 0.0f);
   }
 }
 
 // inv[p] = s for index[s] = p (inv filled with -1 first): the position at which
 // the index family visits token p.
 __global__ __launch_bounds__(256) void fill_kernel(int32_t* __restrict__ a, int64_t n, int32_t v) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) a[i] = v;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) a[i] = v;
 }
 __global__ __launch_bounds__(256) void invert_kernel(const int32_t* __restrict__ index, int32_t* __restrict__ inv,
                                                      int64_t len) {
-  const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (s >= len) return;
-  const int64_t p = index[s];
-  if (p >= 0 && p < len) inv[p] = int32_t(s);
+  for (int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x; s < len; s += int64_t(gridDim.x) * 256) {
+    const int64_t p = index[s];
+    if (p >= 0 && p < len) inv[p] = int32_t(s);
+  }
 }
 
 __device__ __forceinline__ float silu_gate(float v, float zv) {
@@ -163,22 +191,34 @@ __global__ __launch_bounds__(256) void put_index_kernel(const float* __restrict_
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= len) return;
   const int64_t s = inv[t];
-  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
-    const int64_t o = row * len + t;
-    const float yv = s >= 0 ? yf[row * len + s] : 0.0f;
-    const float v = FIRST ? yv : acc[o] + yv;
-    if (LAST) {
-      st(y, o, z ? silu_gate(v, ld(z, o)) : v);
-    } else {
-      acc[o] = v;
+  for (int64_t row0 = int64_t(blockIdx.y) * kIndexRows; row0 < rows; row0 += int64_t(gridDim.y) * kIndexRows) {
+    float yv[kIndexRows];
+#pragma unroll
+    for (int j = 0; j < kIndexRows; ++j) {
+      const int64_t row = row0 + j;
+      yv[j] = (s >= 0 && row < rows) ? yf[row * len + s] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kIndexRows; ++j) {
+      const int64_t row = row0 + j;
+      if (row >= rows) break;
+      const int64_t o = row * len + t;
+      const float v = FIRST ? yv[j] : acc[o] + yv[j];
+      if (LAST) {
+        st(y, o, z ? silu_gate(v, ld(z, o)) : v);
+      } else {
+        acc[o] = v;
+      }
     }
   }
 }
 
-// About 16K blocks: each block walks several rows, reusing its index entries.
+// The put-back's grid: x over token positions (256 per block), y over groups of
+// kIndexRows rows (about 64K blocks, striding above that).
 dim3 index_grid(int64_t rows, int64_t len) {
   const int64_t gx = (len + 255) / 256;
-  const int64_t slots = std::min(std::min(rows, kMaxGridZ), std::max<int64_t>(64, 16384 / gx));
+  const int64_t groups = (rows + kIndexRows - 1) / kIndexRows;
+  const int64_t slots = std::min(std::min(groups, kMaxGridZ), std::max<int64_t>(16, 65536 / gx));
   return dim3(unsigned(gx), unsigned(slots));
 }
 
@@ -262,7 +302,8 @@ __global__ __launch_bounds__(256) void put_col_pairs_kernel(const float* __restr
   }
 }
 
-unsigned blocks_for(int64_t n) { return unsigned((n + 255) / 256); }
+// 256-thread blocks covering n elements, capped (the flat kernels stride past it).
+unsigned blocks_for(int64_t n) { return unsigned(std::min<int64_t>((n + 255) / 256, int64_t(1) << 22)); }
 
 // Element pairs of a [h][w] map and its transpose are 4-byte words when both sides
 // are even and the bases are 4-byte aligned.
@@ -277,10 +318,19 @@ void launch_transpose(const void* in, void* out, int64_t rows, int64_t h, int64_
                      static_cast<const T*>(in), static_cast<T*>(out), rows, h, w);
 }
 
+// Maps of at least this many tokens gather in flat order (measured: 2.2 -> 1.5 ms per
+// bf16 tensor on a 512 x 512 map, while row groups were faster on 128 x 128).
+constexpr int64_t kFlatGatherLen = 65536;
+
 template <typename T>
 void launch_gather(const void* in, void* out, const int32_t* index, int64_t rows, int64_t len, hipStream_t s) {
-  hipLaunchKernelGGL((gather_kernel<T>), index_grid(rows, len), dim3(256), 0, s, static_cast<const T*>(in),
-                     static_cast<T*>(out), index, rows, len);
+  if (len >= kFlatGatherLen) {
+    hipLaunchKernelGGL((gather_kernel<T>), dim3(blocks_for(rows * len)), dim3(256), 0, s, static_cast<const T*>(in),
+                       static_cast<T*>(out), index, rows, len);
+  } else {
+    hipLaunchKernelGGL((gather_rows_kernel<T>), index_grid(rows, len), dim3(256), 0, s, static_cast<const T*>(in),
+                       static_cast<T*>(out), index, rows, len);
+  }
 }
 
 // Gathers one [rows][len] tensor into a family's visiting order (forward order;

@@ -77,10 +77,10 @@ def test_multi_order_parity(name, b, d, h, w, kinds, io, bc, gate):
     run_both(name, b, d, h, w, kinds, io, bc, gate)
 
 
-@pytest.mark.parametrize("h,w", [(9, 9), (16, 24)])
+@pytest.mark.parametrize("h,w", [(9, 9), (16, 24), (256, 256)])
 def test_spiral_orders(h, w):
     """The Samba spiral (from the library's helper) forward and reversed, next to
-    the row pair."""
+    the row pair (256 x 256: large enough for the flat-order gather)."""
     spiral = sscan.spiral_order(h, w).numpy()
     run_both(f"spiral-{h}x{w}", 2, 64, h, w, [X, XR, R, RR], index=spiral)
 
