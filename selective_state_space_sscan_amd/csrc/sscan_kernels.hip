@@ -360,6 +360,13 @@ constexpr int64_t kWaveSlots = 256 * 4 * 3;
 // leave room for eight two-wave blocks per CU.  (A sequence short enough to be one
 // segment may be longer; its meeting buffer is in global memory.)
 constexpr int64_t kBidirSegment = 64;
+// Rounds of resident waves the output step of a long one-direction scan aims for.
+// Measured on the long-sequence workload (1 x 1536 x 262144): 1 round (2048-token
+// segments) 3.19 ms per call, 2 rounds 2.66, 3 rounds 2.67, 4 rounds (512 tokens)
+// 2.59, 5 rounds 2.61, 6 rounds 2.63, 8 rounds 2.60: four rounds even out the
+// waves' finishing times best before the longer carry chain costs more than it
+// saves.
+constexpr int64_t kSegRounds = 4;
 // Segments are grouped in aggregate runs only where one wave per segment would
 // give the aggregate pass more than about four rounds of resident waves (very long
 // bidirectional sequences, cut into 64-token segments): the run form holds more
@@ -370,10 +377,10 @@ constexpr int64_t kAggWaves = 4 * kWaveSlots;
 // (splitting a 197-token Vim sequence that fills only a quarter of the resident
 // wave slots was measured slower: its 64-token aggregate waves and short carry cost
 // more than the output pass gains).  Longer ones are cut into equal segments
-// (multiples of kTile tokens) so that the output step has about two rounds of
-// resident waves: enough waves to cover load latency and even out per-wave speed,
-// without the long carry chain and large aggregate buffers of many short segments
-// (measured on the long-sequence and Mamba-YOLO workloads).
+// (multiples of kTile tokens) so that the output step has about kSegRounds rounds
+// of resident waves: enough waves to cover load latency and even out per-wave
+// speed, without the long carry chain and large aggregate buffers of many short
+// segments.
 Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   Plan p{};
   const int64_t ngroups = (dim + kLanes - 1) / kLanes;
@@ -385,7 +392,7 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
     if (ndir == 2) {
       seg_len = kBidirSegment;
     } else {
-      const int64_t target_segs = std::max<int64_t>(2, 2 * kWaveSlots / groups);
+      const int64_t target_segs = std::max<int64_t>(2, kSegRounds * kWaveSlots / groups);
       seg_len = (len + target_segs - 1) / target_segs;
       seg_len = std::max<int64_t>(kSegAlign, (seg_len + kTile - 1) / kTile * kTile);
     }

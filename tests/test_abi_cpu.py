@@ -362,13 +362,13 @@ def test_validate_multi(lib):
 
 def test_scan_plan_splits():
     """How calls are split: short sequences whole; long one-direction sequences in
-    1024-token segments, one per aggregate run; long bidirectional ones in 64-token
+    512-token segments (1536 channels), one per aggregate run; long bidirectional ones in 64-token
     segments, grouped in aggregate runs only when one wave per segment would exceed
     four rounds of resident waves."""
     plan = sscan.scan_plan
     assert plan(128, 768, 197, bidir=True) == dict(seg_len=197, nseg=1, run_len=1, nrun=1)
     assert plan(2, 64, 256) == dict(seg_len=256, nseg=1, run_len=1, nrun=1)
-    assert plan(1, 1536, 262144) == dict(seg_len=1024, nseg=256, run_len=1, nrun=256)
+    assert plan(1, 1536, 262144) == dict(seg_len=512, nseg=512, run_len=1, nrun=512)
     assert plan(8, 192, 16384, bidir=True) == dict(seg_len=64, nseg=256, run_len=1, nrun=256)
     long_b = plan(1, 64, 1 << 20, bidir=True)
     assert long_b["seg_len"] == 64 and long_b["run_len"] == 2 and long_b["nrun"] * 2 == long_b["nseg"]
