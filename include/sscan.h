@@ -29,9 +29,11 @@
  * library allocates no memory on these calls and keeps no state after return.
  * Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
  * call returns; y is valid once the stream reaches that point, and inputs must stay
- * alive until then.  y must not overlap any input.  Long sequences need a
- * caller-provided device workspace of sscan_workspace_bytes(...) bytes (NULL is
- * allowed when that size is 0); its contents on entry do not matter.
+ * alive until then.  y must not overlap any input.  Calls take a caller-provided
+ * device workspace of sscan_workspace_bytes(...) bytes (B/C re-laid token-major;
+ * for long sequences the segment chains; for one-segment bidirectional sequences
+ * over 64 tokens the two directions' meeting buffers; NULL is allowed when that
+ * size is 0); its contents on entry do not matter.
  *
  * Errors: every argument is checked before any HIP call; on error nothing is
  * enqueued and a negative status is returned (see sscan_strerror).  A failure
