@@ -578,9 +578,7 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
                (!f.z || aligned16_b(f.z));
     for (int k = 0; k < f.ndir; ++k) vec = vec && aligned16_b(f.dir[k].delta);
     const int64_t chain_blocks = f.batch * p.nrun * ngroups;
-    const int64_t carry_blocks = int64_t(f.ndir) * f.batch * kDState * ngroups;
     const dim3 cgrid(unsigned(chain_blocks), unsigned(f.ndir));
-    const dim3 carry_block(kLanes * carry_parts(p.nrun));
     float* pw[2] = {w + p.off_p[0], w + p.off_p[1]};
     float* sw[2] = {w + p.off_s[0], w + p.off_s[1]};
     float* rw[2] = {w + p.off_r[0], w + p.off_r[1]};
@@ -588,16 +586,14 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
     // the state entering every window
     hipLaunchKernelGGL((bwd_chain_kernel<IO_BF16, SOFTPLUS, false, false>), cgrid, dim3(kLanes), 0, stream, f, p.nwin,
                        p.run_len, p.nrun, static_cast<const float*>(bc), pw[0], sw[0], rw[0], int(vec));
-    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nrun,
-                       static_cast<const float*>(rw[0]), ew[0], 0);
+    launch_carry(f, p.nrun, rw[0], ew[0], 0, stream);
     mark(2);
     // the adjoint entering every window from the other side
     ScanArgs adj = f;
     adj.u = a.dout;
     hipLaunchKernelGGL((bwd_chain_kernel<IO_BF16, SOFTPLUS, HAS_Z, true>), cgrid, dim3(kLanes), 0, stream, adj,
                        p.nwin, p.run_len, p.nrun, static_cast<const float*>(bc), pw[1], sw[1], rw[1], int(vec));
-    hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(carry_blocks)), carry_block, 0, stream, f, p.nrun,
-                       static_cast<const float*>(rw[1]), ew[1], 1);
+    launch_carry(f, p.nrun, rw[1], ew[1], 1, stream);
     mark(3);
   }
   const dim3 wgrid(unsigned(f.batch * p.nwin * p.csplit));

@@ -666,6 +666,10 @@ int carry_parts(int64_t nseg) {
   return p;
 }
 
+// kBatch: aggregates a lane keeps in flight; runs of up to kBatch elements are
+// loaded once.  16 keeps the kernel near 56 VGPRs (two 16-wave blocks per CU); 32
+// (about 80 VGPRs, one block per CU) serves longer runs, which 16 would read twice.
+template <int kBatch>
 __global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanArgs a, int64_t nseg,
                                                                        const float* __restrict__ agg,
                                                                        float* __restrict__ hin, int flip) {
@@ -704,9 +708,7 @@ __global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanAr
   };
   auto hin_row = [&](int64_t seg) { return hin + ((((size_t)dir * a.batch + b) * nseg + seg) * kDState + n) * a.dim; };
   // a run's aggregates are loaded kBatch at a time, all loads in flight together
-  // (they do not depend on the chain); runs of up to kBatch segments are loaded once.
-  // 16 keeps the kernel near 48 VGPRs, so two 16-wave blocks share a CU.
-  constexpr int kBatch = 16;
+  // (they do not depend on the chain)
   float hb[kBatch], sb[kBatch];
   auto load_batch = [&](int64_t kb) {
 #pragma unroll
@@ -745,6 +747,22 @@ __global__ __launch_bounds__(kLanes * kCarryParts) void scan_carry_kernel(ScanAr
         if (k < kagg) h = fmaf(exp2_hw(A2 * sb[i]), h, hb[i]);
       }
     }
+  }
+}
+
+// The carry over nseg chain elements for every (direction, batch row, state,
+// 64-channel group): the batch size by run length (on the long-sequence forward,
+// 512 segments in runs of 32: 48 us with 16, 38 us with 32).
+inline void launch_carry(const ScanArgs& a, int64_t nseg, const float* agg, float* hin, int flip,
+                         hipStream_t stream) {
+  const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
+  const int parts = carry_parts(nseg);
+  const int64_t run = (nseg + parts - 1) / parts;
+  const dim3 grid(unsigned(int64_t(a.ndir) * a.batch * kDState * ngroups)), block(kLanes * parts);
+  if (run <= 16) {
+    hipLaunchKernelGGL((scan_carry_kernel<16>), grid, block, 0, stream, a, nseg, agg, hin, flip);
+  } else {
+    hipLaunchKernelGGL((scan_carry_kernel<32>), grid, block, 0, stream, a, nseg, agg, hin, flip);
   }
 }
 
