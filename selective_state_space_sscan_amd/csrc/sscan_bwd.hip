@@ -220,7 +220,9 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
   const ScanArgs& f = a.fwd;
   const int lane = threadIdx.x;
   const int c = lane >> 4, n = lane & 15;
-  int64_t blk = blockIdx.x;
+  // A window's row of each per-token tensor is half a 128-byte line; the other half
+  // is the next window's, which the same XCD then takes up soon after.
+  int64_t blk = xcd_stretch(blockIdx.x, gridDim.x);
   const int j = int(blk % csplit);
   blk /= csplit;
   const int64_t k = blk % nwin;
@@ -641,8 +643,15 @@ hipError_t launch_bwd_io(const BwdArgs& a, const BwdPlan& p, float* w, hipStream
 
 }  // namespace
 
-// Resident window-pass waves the plan aims for (about four per SIMD).
-constexpr int64_t kBwdWaveTarget = 256 * 4 * 4;
+// Window pass: the channel groups of a window are split over several one-wave
+// blocks, aiming for about kBwdBlockTarget blocks per launch (32 per SIMD) with at
+// least kMinGroupsPerBlock groups each.  Measured splits (window pass, ms):
+// long sequence (8192 windows, 384 groups) 1: 7.61, 2: 7.33, 3: 7.44, 4: 7.11,
+// 8: 7.24, 16: 7.48; Mamba-YOLO map rows (8 x 512 windows per direction, 48 groups)
+// 1: 1.18, 2: 1.09, 3: 1.06, 4: 1.08, 8: 1.14; Vim-small (128 x 7 windows per
+// direction, 192 groups) 3: 1.00, 8: 0.96, 16: 0.93.
+constexpr int64_t kBwdBlockTarget = 32768;
+constexpr int64_t kMinGroupsPerBlock = 16;
 // Chain passes: blocks per pass the run length aims for (about eight waves per
 // SIMD), and the longest run.
 constexpr int64_t kChainWaveTarget = 256 * 4 * 8;
@@ -653,7 +662,9 @@ BwdPlan make_bwd_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   p.nwin = std::max<int64_t>(1, (len + kWin - 1) / kWin);
   const int64_t ngroups = std::max<int64_t>(1, (dim + kGroup - 1) / kGroup);
   const int64_t base = std::max<int64_t>(1, int64_t(ndir) * batch * p.nwin);
-  int64_t split = std::min<int64_t>(ngroups, std::max<int64_t>(1, (kBwdWaveTarget + base - 1) / base));
+  const int64_t per_launch = std::max<int64_t>(1, batch * p.nwin);  // one direction per launch
+  const int64_t split = std::max<int64_t>(1, std::min<int64_t>((kBwdBlockTarget + per_launch - 1) / per_launch,
+                                                               ngroups / kMinGroupsPerBlock));
   p.gps = (ngroups + split - 1) / split;
   p.csplit = int((ngroups + p.gps - 1) / p.gps);
   auto up = [](size_t n) { return (n + 63) / 64 * 64; };

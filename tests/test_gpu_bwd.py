@@ -109,6 +109,8 @@ CASES = [
     ("bidir-ragged-dim", 3, 70, 61, True, "f32", "f32", {}),
     ("bidir-bf16", 2, 128, 500, True, "bf16", "bf16", {}),
     ("bidir-no-gate", 2, 64, 40, True, "f32", "f32", dict(gate=False)),
+    # 51 channel groups (the last one partial) over three window-pass blocks
+    ("bidir-split-ragged", 2, 202, 150, True, "bf16", "bf16", {}),
 ]
 
 
