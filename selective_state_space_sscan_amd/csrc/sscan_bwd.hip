@@ -563,13 +563,8 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
   float* acc_du = w + p.off_acc;
   float* acc_y = acc_du + (p.off_acc ? size_t(f.batch) * f.dim * f.len : 0);
 
-  const int64_t bc_blocks = int64_t(f.ndir) * f.batch * ((f.len + 63) / 64);
   mark(0);
-  if (f.bc_bf16) {
-    hipLaunchKernelGGL(stage_bc_kernel<true>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, f, bc);
-  } else {
-    hipLaunchKernelGGL(stage_bc_kernel<false>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, f, bc);
-  }
+  launch_stage_bc(f, bc, stream);
   mark(1);
   if (p.nwin <= 1) {
     mark(2);

@@ -578,9 +578,13 @@ __device__ __forceinline__ void load_entry(LaneT& L, const ScanArgs& a, int dir,
 }
 
 // Stage B and C token-major in fp32: bc[dir][b][t][0..15] = B[b][:, t],
-// bc[dir][b][t][16..31] = C[b][:, t].  One block per (direction, batch, 64 tokens).
+// bc[dir][b][t][16..31] = C[b][:, t].  One block per (direction, batch row, 64
+// tokens).  Each thread reads 8 consecutive tokens of one of the 32 rows (one
+// 16-byte load for bf16, two for fp32, when the rows start 16-byte aligned: vec);
+// the tile turns through LDS and each thread writes two 16-byte pieces of the
+// token-major rows (128 bytes per token, always aligned in the workspace).
 template <bool BC_BF16>
-__global__ __launch_bounds__(256) void stage_bc_kernel(ScanArgs a, float* __restrict__ bc) {
+__global__ __launch_bounds__(256) void stage_bc_kernel(ScanArgs a, float* __restrict__ bc, int vec) {
   __shared__ float tile[kBC][65];
   const int64_t ntiles = (a.len + 63) / 64;
   const int64_t tt = blockIdx.x % ntiles;
@@ -589,22 +593,60 @@ __global__ __launch_bounds__(256) void stage_bc_kernel(ScanArgs a, float* __rest
   const int64_t b = db % a.batch;
   const DirArgs p = dir ? a.dir[1] : a.dir[0];
   const int64_t t0 = tt * 64;
-  for (int i = threadIdx.x; i < kBC * 64; i += 256) {
-    const int r = i / 64, c = i % 64;
-    const int64_t t = t0 + c;
-    float v = 0.0f;
-    if (t < a.len) {
-      const size_t idx = ((size_t)b * kDState + (r % kDState)) * a.len + t;
-      const void* src = r < kDState ? p.B : p.C;
-      v = BC_BF16 ? Io<true>::load(static_cast<const uint16_t*>(src), idx) : static_cast<const float*>(src)[idx];
+  const int r = int(threadIdx.x) >> 3, c0 = (int(threadIdx.x) & 7) * 8;  // row r, tokens c0 .. c0 + 7
+  const void* src = r < kDState ? p.B : p.C;
+  const size_t at = ((size_t)b * kDState + (r % kDState)) * a.len + t0 + c0;
+  float v[8];
+  if (vec && t0 + c0 + 8 <= a.len) {
+    if (BC_BF16) {
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + at);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = bf16_lo(ws[k]);
+        v[2 * k + 1] = bf16_hi(ws[k]);
+      }
+    } else {
+      const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(src) + at);
+      const float4 x0 = q[0], x1 = q[1];
+      v[0] = x0.x, v[1] = x0.y, v[2] = x0.z, v[3] = x0.w;
+      v[4] = x1.x, v[5] = x1.y, v[6] = x1.z, v[7] = x1.w;
     }
-    tile[r][c] = v;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool in = t0 + c0 + k < a.len;
+      v[k] = !in ? 0.0f
+                 : BC_BF16 ? Io<true>::load(static_cast<const uint16_t*>(src), at + k)
+                           : static_cast<const float*>(src)[at + k];
+    }
   }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) tile[r][c0 + k] = v[k];
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * kBC; i += 256) {
-    const int c = i / kBC, r = i % kBC;
-    const int64_t t = t0 + c;
-    if (t < a.len) bc[((size_t)db * a.len + t) * kBC + r] = tile[r][c];
+  float* out = bc + ((size_t)db * a.len + t0) * kBC;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = int(threadIdx.x) + h * 256;
+    const int t = i >> 3, q = (i & 7) * 4;  // token t, rows q .. q + 3
+    if (t0 + t < a.len)
+      *reinterpret_cast<float4*>(out + (size_t)t * kBC + q) =
+          make_float4(tile[q][t], tile[q + 1][t], tile[q + 2][t], tile[q + 3][t]);
+  }
+}
+
+// Stages B and C of every direction of a call into bc (ndir * batch * len * 32 floats).
+inline void launch_stage_bc(const ScanArgs& a, float* bc, hipStream_t stream) {
+  const size_t esz = a.bc_bf16 ? 2 : 4;
+  bool vec = (size_t(a.len) * esz) % 16 == 0;
+  for (int k = 0; k < a.ndir; ++k)
+    vec = vec && (reinterpret_cast<uintptr_t>(a.dir[k].B) & 15u) == 0 &&
+          (reinterpret_cast<uintptr_t>(a.dir[k].C) & 15u) == 0;
+  const dim3 grid(unsigned(int64_t(a.ndir) * a.batch * ((a.len + 63) / 64)));
+  if (a.bc_bf16) {
+    hipLaunchKernelGGL(stage_bc_kernel<true>, grid, dim3(256), 0, stream, a, bc, int(vec));
+  } else {
+    hipLaunchKernelGGL(stage_bc_kernel<false>, grid, dim3(256), 0, stream, a, bc, int(vec));
   }
 }
 

@@ -215,13 +215,8 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
     ch.e = q;
   }
 
-  const int64_t bc_blocks = int64_t(a.ndir) * a.batch * ((a.len + 63) / 64);
   mark(0);
-  if (a.bc_bf16) {
-    hipLaunchKernelGGL(stage_bc_kernel<true>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, a, bc);
-  } else {
-    hipLaunchKernelGGL(stage_bc_kernel<false>, dim3(unsigned(bc_blocks)), dim3(256), 0, stream, a, bc);
-  }
+  launch_stage_bc(a, bc, stream);
   mark(1);
   if (p.nseg > 1) {
     const int64_t agg_blocks = a.batch * p.nrun * ngroups;
