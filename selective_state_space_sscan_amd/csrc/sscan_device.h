@@ -374,6 +374,17 @@ struct Lane {
 #pragma unroll
     for (int jj = 0; jj < kTok; ++jj) {
       const int j = REV ? kTok - 1 - jj : jj;
+      // Scalar loads return out of order, so the wait before this token's B/C is a
+      // wait for every scalar load in flight.  Take it here, before the next token's
+      // loads go out: that wait then finds nothing issued less than a token ago
+      // (long-sequence forward: output pass 1.435 -> 1.381 ms, aggregate 1.039 ->
+      // 1.025 ms).  The adjoint chain, which also waits for z at every token, and
+      // the aggregate with the convolution in front ran 5% slower with it and keep
+      // the compiler's placement.
+      if constexpr (MODE != kAdjoint && !(MODE == kAggregate && CONV != kNoConv)) {
+        asm volatile("" ::"s"(cur.v[0]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // prefetch the next token's B/C: its scalar-load latency hides behind this token
       if (jj + 1 < kTok) load_bc<MODE>(nxt, t + (REV ? j - 1 : j + 1));
       float uu = IO::get(wu, j);
