@@ -23,6 +23,12 @@ constexpr int kBC = 2 * kDState;  // floats per token in the staged B/C buffer
 // SIMD and stops the scheduler from hoisting many tokens' exponentials ahead at the
 // cost of occupancy.
 #define SSCAN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3, 8)))
+// The one-direction output kernel with bf16 I/O and no convolution is held to 128
+// VGPRs, four waves per SIMD, at the cost of a few spill slots at tile boundaries
+// (long-sequence output pass 1.386 -> 1.369 ms).  The two-wave bidirectional blocks
+// ran slower so (Mamba-YOLO rows 0.187 -> 0.194 ms, Vim-small 0.188 -> 0.227 ms),
+// and the other variants spill several times more: they keep three.
+#define SSCAN_DIR_OCCUPANCY(FOUR) __attribute__((amdgpu_waves_per_eu((FOUR) ? 4 : 3, 8)))
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
