@@ -82,7 +82,7 @@ def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(x, y_gpu, cfg, target_s: float = 8.0):
+def cpu_baseline(x, y_gpu, cfg, target_s: float = 12.0):
     """The fp64 oracle, as it stands, on whole sampled rows of the same inputs,
     using every host core available to this process."""
     import numpy as np
@@ -237,7 +237,7 @@ def bench_bwd(args, torch, I, sscan, cfg, ci):
     return out
 
 
-def cpu_baseline_bwd(x, g, cfg, target_s: float = 8.0):
+def cpu_baseline_bwd(x, g, cfg, target_s: float = 12.0):
     """The fp64 backward oracle, as it stands, on whole sampled rows (each row's
     forward and adjoint sweeps; the per-channel sums over rows are left out)."""
     import numpy as np
@@ -362,7 +362,7 @@ def bench_conv(args, torch, I, sscan, cfg, ci):
                          "note": "sscan_conv1d writing u, then sscan_fwd / sscan_bidir reading it"})
 
 
-def cpu_baseline_conv(x, cp, cfg, target_s: float = 4.0):
+def cpu_baseline_conv(x, cp, cfg, target_s: float = 12.0):
     """The fp64 convolution oracle on whole sampled rows (single thread)."""
     import numpy as np
 
