@@ -135,6 +135,10 @@ EDGE = [
     ("no-gate", 2, 64, 300, True, "f32", "f32", dict(gate=False)),
     ("no-softplus", 2, 64, 50, False, "f32", "f32", dict(softplus=False)),
     ("rev-short", 2, 64, 50, False, "bf16", "bf16", dict(reverse=True)),
+    # the one-direction bf16 output kernel (held to four waves per SIMD) in its
+    # reverse and ungated instances, over several segments with a ragged end
+    ("long-bf16-rev", 2, 64, 3001, False, "bf16", "bf16", dict(reverse=True)),
+    ("long-bf16-no-gate", 1, 128, 2050, False, "bf16", "bf16", dict(gate=False)),
 ]
 
 
