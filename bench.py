@@ -540,7 +540,7 @@ def main():
                     help="finish with a 512 MiB negation kernel (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        sys.exit("bench.py measures one GPU only: this build has no multi-GPU path "
+        sys.exit("bench.py measures one GPU only: the library has no multi-GPU path "
                  "(run with --gpus 1)")
 
     import torch
