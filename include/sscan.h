@@ -364,6 +364,15 @@ SSCAN_API size_t sscan_workspace_bytes(int64_t batch, int64_t dim, int64_t len, 
  * SSCAN_ERR_UNSUPPORTED (dstate != 16). */
 SSCAN_API int sscan_scan_plan(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir, int64_t* out);
 
+/* How sscan_bwd / sscan_bidir_bwd split a call of these sizes, for tools and
+ * tests: out[0] 32-token windows per row, out[1] blocks each window's channel
+ * groups (four channels each) are split over, out[2] channel groups per block,
+ * out[3] windows per chain run (the window entry states and adjoints are walked
+ * over runs of consecutive windows), out[4] runs per row.  out is HOST memory
+ * (5 entries).  Returns SSCAN_OK, SSCAN_ERR_NULL, SSCAN_ERR_SHAPE or
+ * SSCAN_ERR_UNSUPPORTED (dstate != 16). */
+SSCAN_API int sscan_bwd_plan(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir, int64_t* out);
+
 /* Static description of a status code; never NULL. */
 SSCAN_API const char* sscan_strerror(int status);
 

@@ -761,6 +761,20 @@ int sscan_scan_plan(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int
   return SSCAN_OK;
 }
 
+int sscan_bwd_plan(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir, int64_t* out) {
+  if (!out) return SSCAN_ERR_NULL;
+  Sizes sz{};
+  const int st = check_sizes(batch, dim, len, dstate, SSCAN_F32, SSCAN_F32, &sz);
+  if (st != SSCAN_OK) return st;
+  const sscan::BwdPlan p = sscan::make_bwd_plan(batch, dim, len, bidir ? 2 : 1);
+  out[0] = p.nwin;
+  out[1] = p.csplit;
+  out[2] = p.gps;
+  out[3] = p.run_len;
+  out[4] = p.nrun;
+  return SSCAN_OK;
+}
+
 const char* sscan_strerror(int status) {
   switch (status) {
     case SSCAN_OK: return "ok";

@@ -123,6 +123,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_workspace_bytes.restype = SZ
     lib.sscan_scan_plan.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(ctypes.c_int64)]
     lib.sscan_scan_plan.restype = I
+    lib.sscan_bwd_plan.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(ctypes.c_int64)]
+    lib.sscan_bwd_plan.restype = I
     lib.sscan_strerror.argtypes = [I]
     lib.sscan_strerror.restype = ctypes.c_char_p
     lib.sscan_version.argtypes = []
@@ -207,6 +209,17 @@ def scan_plan(batch: int, dim: int, length: int, dstate: int = DSTATE, bidir: bo
     if st != 0:
         raise SScanError(st, "sscan_scan_plan")
     return dict(seg_len=out[0], nseg=out[1], run_len=out[2], nrun=out[3])
+
+
+def bwd_plan(batch: int, dim: int, length: int, dstate: int = DSTATE, bidir: bool = False) -> dict:
+    """How a backward call of these sizes is split (sscan_bwd_plan): windows per
+    row, blocks per window, channel groups per block, windows per chain run, runs
+    per row."""
+    out = (ctypes.c_int64 * 5)()
+    st = load_library().sscan_bwd_plan(batch, dim, length, dstate, int(bool(bidir)), out)
+    if st != 0:
+        raise SScanError(st, "sscan_bwd_plan")
+    return dict(nwin=out[0], csplit=out[1], gps=out[2], run_len=out[3], nrun=out[4])
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -360,6 +360,33 @@ def test_validate_multi(lib):
     assert V(kinds, 4, y=u) == EALIAS
     assert V(kinds, 4, h=-1) == ESHAPE
 
+def test_bwd_plan_splits():
+    """How backward calls are split: a window's channel groups go to about 32768
+    blocks per launch (one direction per launch) with at least 16 groups per block,
+    the last block taking what remains."""
+    plan = sscan.bwd_plan
+    assert plan(1, 1536, 262144) == dict(nwin=8192, csplit=4, gps=96, run_len=24, nrun=342)
+    assert plan(8, 192, 16384, bidir=True) == dict(nwin=512, csplit=3, gps=16, run_len=3, nrun=171)
+    assert plan(128, 768, 197, bidir=True) == dict(nwin=7, csplit=12, gps=16, run_len=2, nrun=4)
+    p = plan(64, 384, 197, bidir=True)
+    assert (p["csplit"], p["gps"]) == (6, 16)
+    # fewer than 32 groups: one block per window
+    assert plan(2, 64, 300)["csplit"] == 1 and plan(2, 124, 300)["csplit"] == 1
+    # 51 groups: three blocks of 17, the last group partial
+    p = plan(2, 202, 150, bidir=True)
+    assert (p["csplit"], p["gps"]) == (3, 17)
+    # 33 groups: two blocks, 17 + 16
+    p = plan(1, 130, 777)
+    assert (p["csplit"], p["gps"]) == (2, 17)
+    for b, d, L in [(1, 1536, 262144), (3, 1000, 5000), (2, 202, 150), (1, 4, 1)]:
+        p = plan(b, d, L)
+        groups = -(-d // 4)
+        assert p["nwin"] == -(-L // 32) and p["csplit"] * p["gps"] >= groups > (p["csplit"] - 1) * p["gps"]
+        assert p["nrun"] * p["run_len"] >= p["nwin"] > (p["nrun"] - 1) * p["run_len"]
+    with pytest.raises(sscan.SScanError):
+        plan(1, 64, 100, dstate=8)
+
+
 def test_scan_plan_splits():
     """How calls are split: short sequences whole; long one-direction sequences in
     512-token segments (1536 channels), one per aggregate run; long bidirectional ones in 64-token
