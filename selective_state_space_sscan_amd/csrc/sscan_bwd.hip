@@ -25,10 +25,12 @@
 // the window's 32 states of its (channel, state) in registers, recomputed forward
 // from the window's entry state, and walks back through them.  Sums over the 16
 // states of a channel use DPP within a 16-lane row.  A wavefront holds one
-// (batch, window) and loops over channel groups, so the sums over channels that dB
-// and dC need stay in registers (a sum per token and state, no atomics); sums over
-// tokens and batch rows (dA, dD, delta_bias) go through per-window partials and a
-// fixed-order reduction, so results are bitwise reproducible.
+// (batch, window) and loops over its share of the channel groups (a window's groups
+// are split over a few blocks), so the sums over channels that dB and dC need stay
+// in registers (a sum per token and state, no atomics) and the few splits' partials
+// are added afterwards; sums over tokens and batch rows (dA, dD, delta_bias) go
+// through per-window partials.  Every reduction runs in a fixed order, so results
+// are bitwise reproducible.
 #include "sscan_device.h"
 
 #include <type_traits>
