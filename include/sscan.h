@@ -60,7 +60,7 @@ extern "C" {
 enum sscan_status {
   SSCAN_OK = 0,
   SSCAN_ERR_NULL = -1,        /* a required pointer is NULL */
-  SSCAN_ERR_SHAPE = -2,       /* batch, dim or len < 0, or a size product overflows */
+  SSCAN_ERR_SHAPE = -2,       /* batch, dim or len < 0, a size product overflows, or batch * len > 2^36 */
   SSCAN_ERR_UNSUPPORTED = -3, /* dstate != 16, unknown dtype code or convolution shape */
   SSCAN_ERR_ALIGN = -4,       /* a pointer is not aligned to its element size */
   SSCAN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than sscan_workspace_bytes */

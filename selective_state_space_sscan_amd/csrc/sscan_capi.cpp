@@ -43,9 +43,13 @@ int check_sizes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int io_
   if (dstate != sscan::kDState) return SSCAN_ERR_UNSUPPORTED;
   if ((io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16) || (bc_dtype != SSCAN_F32 && bc_dtype != SSCAN_BF16))
     return SSCAN_ERR_UNSUPPORTED;
-  int64_t bd = 0, n_io = 0, n_bc = 0, b16 = 0;
+  int64_t bd = 0, n_io = 0, n_bc = 0, b16 = 0, bl = 0;
+  // batch * len <= 2^36 keeps every one-dimensional grid of the kernels below 2^32
+  // blocks (the B/C staging launches one block per 64 tokens of each row); inputs
+  // that large would not fit in device memory anyway.
   if (__builtin_mul_overflow(batch, dim, &bd) || __builtin_mul_overflow(bd, len, &n_io) ||
       __builtin_mul_overflow(batch, int64_t(sscan::kDState), &b16) || __builtin_mul_overflow(b16, len, &n_bc) ||
+      __builtin_mul_overflow(batch, len, &bl) || bl > (int64_t(1) << 36) ||
       n_io > (int64_t(1) << 50) || n_bc > (int64_t(1) << 50) || dim > (int64_t(1) << 40))
     return SSCAN_ERR_SHAPE;
   sz->io_elems = size_t(n_io);

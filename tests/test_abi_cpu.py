@@ -90,6 +90,7 @@ def test_validate_fwd_null_required(lib, name):
 @pytest.mark.parametrize("over,status", [
     (dict(b=-1), ESHAPE), (dict(d=-5), ESHAPE), (dict(L=-1), ESHAPE),
     (dict(b=1 << 40, d=1 << 20, L=1 << 20), ESHAPE),
+    (dict(b=1 << 20, d=1, L=(1 << 16) + 1), ESHAPE),  # batch * len above 2^36
     (dict(N=8), EUNSUP), (dict(N=32), EUNSUP), (dict(io=2), EUNSUP), (dict(bc=-1), EUNSUP),
 ])
 def test_validate_fwd_bad_sizes_and_codes(lib, over, status):
