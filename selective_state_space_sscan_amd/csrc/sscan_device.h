@@ -24,10 +24,10 @@ constexpr int kBC = 2 * kDState;  // floats per token in the staged B/C buffer
 // cost of occupancy.
 #define SSCAN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3, 8)))
 // The one-direction output kernel with bf16 I/O and no convolution is held to 128
-// VGPRs, four waves per SIMD, at the cost of a few spill slots at tile boundaries
-// (long-sequence output pass 1.386 -> 1.369 ms).  The two-wave bidirectional blocks
+// VGPRs, four waves per SIMD (long-sequence output pass 1.386 -> 1.369 ms with the
+// tile prefetch spilled, 1.328 ms without it).  The two-wave bidirectional blocks
 // ran slower so (Mamba-YOLO rows 0.187 -> 0.194 ms, Vim-small 0.188 -> 0.227 ms),
-// and the other variants spill several times more: they keep three.
+// and the other variants would spill several times more: they keep three.
 #define SSCAN_DIR_OCCUPANCY(FOUR) __attribute__((amdgpu_waves_per_eu((FOUR) ? 4 : 3, 8)))
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -318,9 +318,18 @@ struct Lane {
     const int64_t ntiles = (tb - ta) / kTok;
     if (ntiles <= 0) return;
     uint32_t cu[kWords], cd[kWords], nu[kWords], nd[kWords];
+    // The next tile is loaded while this one runs, except in the one-direction bf16
+    // output pass (four waves per SIMD in 128 VGPRs): there the prefetched tile did
+    // not fit, and spilling it waited for its loads anyway, so each tile is loaded
+    // at its start (long-sequence output pass 1.363 -> 1.328 ms, no spills).  For
+    // the bidirectional pass the same change helped the Mamba-YOLO rows by 1.5% and
+    // cost Vim-small 11%, so it keeps the prefetch.
+    constexpr bool kAhead = !(MODE == kStore && CONV == kNoConv && IO_BF16);
     int64_t t = REV ? tb - kTok : ta;
-    load_tile<IO_BF16>(cu, u, t, vec);
-    load_tile<IO_BF16>(cd, delta, t, vec);
+    if (kAhead) {
+      load_tile<IO_BF16>(cu, u, t, vec);
+      load_tile<IO_BF16>(cd, delta, t, vec);
+    }
     // convolution halo of the tile: the three tokens before it and the one after.
     // Inside a run of tiles it comes from the neighbouring tiles' registers (the one
     // just scanned, the one prefetched); only the run's ends read memory.
@@ -336,7 +345,10 @@ struct Lane {
     for (int64_t i = 0; i < ntiles; ++i) {
       const int64_t tn = REV ? t - kTok : t + kTok;
       const bool more = i + 1 < ntiles;
-      if (more) {
+      if (!kAhead) {
+        load_tile<IO_BF16>(cu, u, t, vec);
+        load_tile<IO_BF16>(cd, delta, t, vec);
+      } else if (more) {
         load_tile<IO_BF16>(nu, u, tn, vec);
         load_tile<IO_BF16>(nd, delta, tn, vec);
       }
@@ -357,10 +369,12 @@ struct Lane {
           for (int k = 0; k < kConvBack; ++k) xl[k] = IO::get(cu, kTok - kConvBack + k);
         }
       }
+      if (kAhead) {
 #pragma unroll
-      for (int w = 0; w < kWords; ++w) {
-        cu[w] = nu[w];
-        cd[w] = nd[w];
+        for (int w = 0; w < kWords; ++w) {
+          cu[w] = nu[w];
+          cd[w] = nd[w];
+        }
       }
       t = tn;
     }
