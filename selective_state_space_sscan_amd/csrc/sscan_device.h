@@ -23,12 +23,13 @@ constexpr int kBC = 2 * kDState;  // floats per token in the staged B/C buffer
 // SIMD and stops the scheduler from hoisting many tokens' exponentials ahead at the
 // cost of occupancy.
 #define SSCAN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3, 8)))
-// The one-direction output kernel with bf16 I/O and no convolution is held to 128
-// VGPRs, four waves per SIMD (long-sequence output pass 1.386 -> 1.369 ms with the
-// tile prefetch spilled, 1.328 ms without it).  The two-wave bidirectional blocks
-// ran slower so (Mamba-YOLO rows 0.187 -> 0.194 ms, Vim-small 0.188 -> 0.227 ms),
-// and the other variants would spill several times more: they keep three.
-#define SSCAN_DIR_OCCUPANCY(FOUR) __attribute__((amdgpu_waves_per_eu((FOUR) ? 4 : 3, 8)))
+// The output kernels with bf16 I/O and no convolution (one direction, and two
+// directions meeting in LDS) are held to 128 VGPRs, four waves per SIMD, and load
+// each tile at its start (long-sequence output pass 1.386 -> 1.328 ms).  With the
+// tile prefetch kept, the bidirectional blocks ran slower at four waves (Mamba-YOLO
+// rows 0.187 -> 0.194 ms); the other variants would spill several times more and
+// keep three.
+#define SSCAN_OUT_OCCUPANCY(FOUR) __attribute__((amdgpu_waves_per_eu((FOUR) ? 4 : 3, 8)))
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
@@ -318,13 +319,15 @@ struct Lane {
     const int64_t ntiles = (tb - ta) / kTok;
     if (ntiles <= 0) return;
     uint32_t cu[kWords], cd[kWords], nu[kWords], nd[kWords];
-    // The next tile is loaded while this one runs, except in the one-direction bf16
-    // output pass (four waves per SIMD in 128 VGPRs): there the prefetched tile did
-    // not fit, and spilling it waited for its loads anyway, so each tile is loaded
-    // at its start (long-sequence output pass 1.363 -> 1.328 ms, no spills).  For
-    // the bidirectional pass the same change helped the Mamba-YOLO rows by 1.5% and
-    // cost Vim-small 11%, so it keeps the prefetch.
-    constexpr bool kAhead = !(MODE == kStore && CONV == kNoConv && IO_BF16);
+    // The next tile is loaded while this one runs, except in the bf16 output passes
+    // held to four waves per SIMD (one direction, and two directions meeting in LDS):
+    // there the prefetched tile does not fit in 128 VGPRs, and spilling it waited for
+    // its loads anyway, so each tile is loaded at its start (long-sequence output
+    // pass 1.363 -> 1.328 ms; Mamba-YOLO rows 0.185 -> 0.181 ms).  Long single
+    // bidirectional segments (meeting in global memory, Vim) ran 11% slower so and
+    // keep three waves and the prefetch.
+    constexpr bool kAhead =
+        !(IO_BF16 && CONV == kNoConv && (MODE == kStore || ((MODE == kPark || MODE == kMeet) && !GPARK)));
     int64_t t = REV ? tb - kTok : ta;
     if (kAhead) {
       load_tile<IO_BF16>(cu, u, t, vec);

@@ -39,7 +39,7 @@ namespace {
 // Step 3, one direction: every wave scans one segment of 64 channels from its entry
 // state and stores the gated output.
 template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false>
-__global__ __launch_bounds__(kLanes) SSCAN_DIR_OCCUPANCY(IO_BF16 && CONV == kNoConv) void scan_output_dir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
+__global__ __launch_bounds__(kLanes) SSCAN_OUT_OCCUPANCY(IO_BF16 && CONV == kNoConv) void scan_output_dir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
                                                                  const float* __restrict__ bc, SegChain ch,
                                                                  int vec) {
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t 
 // park in the block's slice of a workspace buffer (GPARK), so that LDS does not
 // cut the number of resident blocks (a 197-token buffer is 50 KB).
 template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false, bool GPARK = false>
-__global__ __launch_bounds__(2 * kLanes) SSCAN_OCCUPANCY void scan_output_bidir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
+__global__ __launch_bounds__(2 * kLanes) SSCAN_OUT_OCCUPANCY(IO_BF16 && CONV == kNoConv && !GPARK) void scan_output_bidir_kernel(ScanArgs a, int64_t seg_len, int64_t nseg,
                                                                        const float* __restrict__ bc, SegChain ch,
                                                                        float* __restrict__ gpark, int vec) {
   extern __shared__ float part[];  // [seg_len][64]
