@@ -396,9 +396,9 @@ def bench_multi(args, torch, I, sscan, cfg, ci):
     if side * side != cfg.len:
         sys.exit(f"--pass {args.pass_} needs a square map; {cfg.name} has len {cfg.len}")
     x1 = I.make_inputs(cfg.batch, cfg.dim, cfg.len, bidir=True, io_dtype=cfg.io_dtype, bc_dtype=cfg.bc_dtype,
-                       seed=1000 * ci + 50)
+                       seed=1000 * ci + 50, a_init="s4d")
     x2 = I.make_inputs(cfg.batch, cfg.dim, cfg.len, bidir=True, io_dtype=cfg.io_dtype, bc_dtype=cfg.bc_dtype,
-                       seed=1000 * ci + 51)
+                       seed=1000 * ci + 51, a_init="s4d")
     xd = x1.to(dev)
     dirs = [dict(delta=xd.delta, delta_bias=p.delta_bias.to(dev), A=p.A.to(dev), B=p.B.to(dev), C=p.C.to(dev),
                  D=p.D.to(dev)) for p in x1.dirs + x2.dirs]
@@ -457,7 +457,8 @@ def bench_decode(args, torch, I, sscan):
     c = DECODE
     b, d = c["batch"], c["dim"]
     dev = torch.device("cuda:0")
-    x = I.make_inputs(b, d, 1, io_dtype=c["io_dtype"], bc_dtype=c["bc_dtype"], seed=9000, dt_range=(1e-4, 1e-2))
+    x = I.make_inputs(b, d, 1, io_dtype=c["io_dtype"], bc_dtype=c["bc_dtype"], seed=9000, dt_range=(1e-4, 1e-2),
+                      a_init="s4d")
     h0 = torch.from_numpy(np.random.default_rng(9001).normal(0.0, 1.0, (b, d, 16))).float()
     xd = x.to(dev)
     p = xd.dirs[0]

@@ -12,7 +12,12 @@ draw order is fixed as listed):
   bias and softplus; shared by both directions of a bidirectional scan);
 * ``z``      ~ N(0, 1), shape [batch, dim, len], drawn in float32;
 * then, per direction (forward first, then reverse):
-  - ``A[d, n] = -(n + 1)``  (S4D-real initialisation, no draw), float32;
+  - ``A``: with ``a_init="s4d"`` (the workloads' recipe) ``A[d, n] = -(n + 1)``
+    (S4D-real initialisation, no draw); with ``a_init="random"`` (the default of
+    ``make_inputs``) ``A[d, n] = -exp(a_log[d, n])`` with ``a_log ~ U(-1, 1.5)``
+    drawn per (channel, state), the learned parameterisation A = -exp(A_log) of the
+    Hand-written simplified Mamba2 page (sections 4.2 and 4.4), so every channel
+    and state has its own decay; float32;
   - ``v_d`` log-uniform in ``dt_range``; ``delta_bias_d = log(expm1(v_d))``
     (the value whose softplus is ``v_d``), float64 then float32;
   - ``D_d`` ~ N(0, 1), float64 then float32;
@@ -137,8 +142,10 @@ def _cast(arr: np.ndarray, dtype: str) -> torch.Tensor:
 
 def make_inputs(batch: int, dim: int, length: int, *, dstate: int = DSTATE, bidir: bool = False,
                 io_dtype: str = "f32", bc_dtype: str = "f32", seed: int = 0,
-                dt_range: Tuple[float, float] = (1e-3, 1e-1)) -> ScanInputs:
+                dt_range: Tuple[float, float] = (1e-3, 1e-1), a_init: str = "random") -> ScanInputs:
     """Draw one seeded set of inputs (see the module docstring for the recipe)."""
+    if a_init not in ("s4d", "random"):
+        raise ValueError(f"a_init must be 's4d' or 'random', not {a_init!r}")
     rng = np.random.default_rng(seed)
     shp = (batch, dim, length)
     u = rng.standard_normal(shp, dtype=np.float32)
@@ -148,7 +155,10 @@ def make_inputs(batch: int, dim: int, length: int, *, dstate: int = DSTATE, bidi
     dirs = []
     lo, hi = np.log(dt_range[0]), np.log(dt_range[1])
     for _ in range(2 if bidir else 1):
-        A = -np.broadcast_to(np.arange(1, dstate + 1, dtype=np.float64), (dim, dstate))
+        if a_init == "s4d":
+            A = -np.broadcast_to(np.arange(1, dstate + 1, dtype=np.float64), (dim, dstate))
+        else:
+            A = -np.exp(rng.uniform(-1.0, 1.5, size=(dim, dstate)))
         v = np.exp(rng.uniform(lo, hi, size=dim))
         bias = np.log(np.expm1(v))
         D = rng.standard_normal(dim)
@@ -160,11 +170,12 @@ def make_inputs(batch: int, dim: int, length: int, *, dstate: int = DSTATE, bidi
                       io_dtype, bc_dtype)
 
 
-def config_inputs(cfg_index: int, k: int = 0) -> ScanInputs:
-    """Inputs of config ``cfg_index`` drawn with seed ``1000*cfg_index + k``."""
+def config_inputs(cfg_index: int, k: int = 0, a_init: str = "s4d") -> ScanInputs:
+    """Inputs of config ``cfg_index`` drawn with seed ``1000*cfg_index + k``; A by
+    the workloads' recipe (S4D-real) unless ``a_init="random"``."""
     c = CONFIGS[cfg_index]
     return make_inputs(c.batch, c.dim, c.len, dstate=c.dstate, bidir=c.bidir, io_dtype=c.io_dtype,
-                       bc_dtype=c.bc_dtype, seed=config_seed(cfg_index, k), dt_range=c.dt_range)
+                       bc_dtype=c.bc_dtype, seed=config_seed(cfg_index, k), dt_range=c.dt_range, a_init=a_init)
 
 
 def f64(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:

@@ -21,7 +21,7 @@ OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mp_tiny.json")
 
 
 def main():
-    x = as_f64_dict(make_inputs(1, 2, 6, dstate=4, bidir=True, seed=7))
+    x = as_f64_dict(make_inputs(1, 2, 6, dstate=4, bidir=True, seed=7, a_init="s4d"))
     f, r = [dict(p, delta=x["delta"]) for p in x["dirs"]]
     cases = {}
     for name, dirs, rev in (("fwd", [f], False), ("rev", [r], True), ("bidir", [f, r], False)):
@@ -33,7 +33,7 @@ def main():
                 "materialised (dual) form, rounded to float64",
         "source": "Hand-written simplified Mamba2 page sections 2.2, 3.1, 4.4; Reproducing Vision Mamba "
                   "page section 3.2 (bidirectional sum before the gate)",
-        "generator": "selective_state_space_sscan_amd.inputs.make_inputs(1, 2, 6, dstate=4, bidir=True, seed=7)",
+        "generator": "selective_state_space_sscan_amd.inputs.make_inputs(1, 2, 6, dstate=4, bidir=True, seed=7, a_init='s4d')",
         "softplus": True,
         "inputs": {"u": tolist(x["u"]), "delta": tolist(x["delta"]), "z": tolist(x["z"]),
                    "dirs": [{k: tolist(v) for k, v in p.items()} for p in x["dirs"]]},

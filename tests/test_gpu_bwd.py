@@ -126,18 +126,20 @@ def test_bwd_parity(name, b, d, L, bidir, io, bc, kw):
     compare(gpu_grads(x, dout, **kw), oracle_grads(x, dout, **kw), name, kw.get("gate", True), kw.get("opt", True))
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 3])
-def test_bwd_config_full(cfg):
-    x = I.config_inputs(cfg, 0)
+@pytest.mark.parametrize("a_init", ["s4d", "random"])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_bwd_config_full(cfg, a_init):
+    x = I.config_inputs(cfg, 0, a_init=a_init)
     dout = make_dout(x, 77 + cfg)
-    compare(gpu_grads(x, dout), oracle_grads(x, dout), f"config {cfg}")
+    compare(gpu_grads(x, dout), oracle_grads(x, dout), f"config {cfg} A {a_init}")
 
 
-def test_bwd_long_sequence():
+@pytest.mark.parametrize("a_init", ["s4d", "random"])
+def test_bwd_long_sequence(a_init):
     """The long-sequence workload's shape and launch configuration (8192 windows
     of one row): per-channel gradients on sampled channels of the full call, and
     dB/dC (sums over all channels) on a 64-channel slice at the full length."""
-    x = I.config_inputs(4, 0)
+    x = I.config_inputs(4, 0, a_init=a_init)
     dout = make_dout(x, 81)
     got = gpu_grads(x, dout)
     x64 = I.as_f64_dict(x)
