@@ -65,7 +65,8 @@ enum sscan_status {
   SSCAN_ERR_ALIGN = -4,       /* a pointer is not aligned to its element size */
   SSCAN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than sscan_workspace_bytes */
   SSCAN_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
-  SSCAN_ERR_ALIAS = -7        /* an output overlaps an input, another output or the workspace */
+  SSCAN_ERR_ALIAS = -7,       /* an output overlaps an input, another output or the workspace */
+  SSCAN_ERR_TOO_LARGE = -8    /* a no-alloc call needs more than SSCAN_NOALLOC_SCRATCH_BYTES of workspace */
 };
 
 enum sscan_dtype { SSCAN_F32 = 0, SSCAN_BF16 = 1 };
@@ -350,6 +351,26 @@ SSCAN_API int sscan_validate_multi(const void* u, const void* z, const void* y, 
                          const int* kinds, int ndirs, const int32_t* index, int softplus, int64_t batch,
                          int64_t dim, int64_t height, int64_t width, int64_t dstate, int io_dtype, int bc_dtype,
                          const void* workspace, size_t workspace_bytes);
+
+/* sscan_fwd for callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same operation,
+ * arguments, layouts and checks as sscan_fwd, without the workspace arguments.  The
+ * workspace comes from a fixed device array of the library, SSCAN_NOALLOC_SCRATCH_BYTES
+ * bytes on every GPU the library runs on, held until the process ends.  A call that
+ * needs more (sscan_workspace_bytes(batch, dim, len, dstate, 0) above that) returns
+ * SSCAN_ERR_TOO_LARGE before any HIP call.  The array of the CURRENT device is used,
+ * so `stream` must belong to the current device.  The call allocates no memory (no
+ * hipMalloc, no allocating library routine); the first call on a device looks up
+ * that device's copy of the array once.  Every call on one GPU shares that GPU's
+ * array: calls that may overlap in time on one GPU (different streams, different
+ * host threads) race and must be ordered by the caller.  The array's contents on
+ * entry do not matter. */
+#define SSCAN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+SSCAN_API int sscan_fwd_noalloc(const void* u, const void* delta, const float* delta_bias, int softplus,
+                      const float* A, const void* B, const void* C, const float* D,
+                      const void* z, void* y,
+                      int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                      int reverse, void* stream, int io_dtype, int bc_dtype);
 
 /* Bytes of device workspace a call with these sizes needs (0 if none); bidir != 0
  * for sscan_bidir.  Returns 0 for invalid sizes (the call itself reports them). */

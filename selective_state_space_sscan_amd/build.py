@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsscan.so")
 
-SOURCES = ["sscan_kernels.hip", "sscan_bwd.hip", "sscan_multi.hip", "sscan_capi.cpp"]
+SOURCES = ["sscan_kernels.hip", "sscan_bwd.hip", "sscan_multi.hip", "sscan_noalloc.hip", "sscan_capi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -48,9 +48,33 @@ def _run(cmd, verbose):
         print("\n".join(lines))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (in parallel, into _build/) and link ``libsscan.so``
-    next to this file; returns its path."""
+def _deps(src: str) -> set:
+    """``src`` and the local headers it includes (``#include "..."``), transitively."""
+    import re
+
+    seen, todo = set(), [src]
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(f):
+            continue
+        seen.add(f)
+        with open(f) as fh:
+            for name in re.findall(r'^\s*#\s*include\s+"([^"]+)"', fh.read(), re.M):
+                todo += [os.path.join(d, name) for d in (CSRC, INCLUDE)]
+    return seen
+
+
+def _stale(obj: str, src: str) -> bool:
+    """True when ``obj`` is missing or older than its source or a header it includes."""
+    if not os.path.exists(obj):
+        return True
+    return max(os.path.getmtime(d) for d in _deps(src)) > os.path.getmtime(obj)
+
+
+def build(verbose: bool = False, force: bool = True) -> str:
+    """Compile the sources (in parallel, into _build/) and link ``libsscan.so``
+    next to this file; returns its path.  ``force=False`` recompiles only the
+    objects older than their source or a header."""
     from concurrent.futures import ThreadPoolExecutor
 
     os.makedirs(OBJ_DIR, exist_ok=True)
@@ -60,6 +84,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
+        if not force and not _stale(obj, os.path.join(CSRC, src)):
+            continue
         cmds.append([hipcc()] + compile_flags + ["-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, os.path.join(CSRC, src)])
     with ThreadPoolExecutor(max(1, min(len(cmds), os.cpu_count() or 1))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
@@ -70,4 +96,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, force="--changed" not in sys.argv))

@@ -789,6 +789,7 @@ const char* sscan_strerror(int status) {
     case SSCAN_ERR_WORKSPACE: return "workspace missing or smaller than sscan_workspace_bytes()";
     case SSCAN_ERR_HIP: return "HIP runtime error at launch";
     case SSCAN_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
+    case SSCAN_ERR_TOO_LARGE: return "the call needs more workspace than the no-alloc scratch array holds";
     default: return "unknown status";
   }
 }

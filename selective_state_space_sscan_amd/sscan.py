@@ -66,6 +66,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_fwd.restype = I
     lib.sscan_bidir.argtypes = [V, V, V, DP, DP, I, I64, I64, I64, I64, V, I, I, V, SZ]
     lib.sscan_bidir.restype = I
+    lib.sscan_fwd_noalloc.argtypes = lib.sscan_fwd.argtypes[:-2]
+    lib.sscan_fwd_noalloc.restype = I
     lib.sscan_fwd_profiled.argtypes = lib.sscan_fwd.argtypes + [V]
     lib.sscan_fwd_profiled.restype = I
     lib.sscan_bidir_profiled.argtypes = lib.sscan_bidir.argtypes + [V]
@@ -293,6 +295,40 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = Tru
         st = lib.sscan_fwd_profiled(*args, ctypes.cast(events.handles, ctypes.c_void_p))
     if st != 0:
         raise SScanError(st, "sscan_fwd")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SSCAN_NOALLOC_SCRATCH_BYTES
+
+
+def fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, reverse: bool = False,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``sscan_fwd_noalloc``: ``fwd`` with the library's fixed scratch array of the
+    current device as its workspace (for callers that cannot allocate).  Allocates
+    only ``out`` when it is not given."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.fwd_noalloc needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or B.dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = u.shape
+    _check(u, "u", dev)
+    _check(delta, "delta", dev, u.dtype, u.shape)
+    _check(z, "z", dev, u.dtype, u.shape)
+    _check(A, "A", dev, torch.float32, (d, DSTATE))
+    _check(B, "B", dev, None, (b, DSTATE, L))
+    _check(C, "C", dev, B.dtype, (b, DSTATE, L))
+    _check(D, "D", dev, torch.float32, (d,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (d,))
+    if out is None:
+        out = torch.empty_like(u)
+    _check(out, "out", dev, u.dtype, u.shape)
+    st = lib.sscan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C),
+                               _ptr(D), _ptr(z), _ptr(out), b, d, L, DSTATE, int(bool(reverse)), _stream(dev),
+                               _DT_CODE[u.dtype], _DT_CODE[B.dtype])
+    if st != 0:
+        raise SScanError(st, "sscan_fwd_noalloc")
     return out
 
 

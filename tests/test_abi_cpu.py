@@ -186,6 +186,24 @@ def test_run_entry_points_reject_before_any_hip_call(lib):
     assert st == ENULL
 
 
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """sscan_fwd_noalloc refuses a call that needs more workspace than its scratch
+    array, and every invalid argument, without touching HIP (no GPU here)."""
+    ETOO = -8
+    assert sscan.strerror(ETOO) != "unknown status"
+    b, d, L = 1, 1536, 262144
+    assert sscan.workspace_bytes(b, d, L) > sscan.NOALLOC_SCRATCH_BYTES
+    a = fwd_args(b, d, L, io=1)
+    call = lambda a, N=16: lib.sscan_fwd_noalloc(a["u"], a["delta"], a["bias"], 1, a["A"], a["B"], a["C"], a["D"],
+                                                 a["z"], a["y"], a["b"], a["d"], a["L"], N, 0, None, a["io"], a["bc"])
+    assert call(a) == ETOO
+    small = fwd_args(2, 64, 300, io=1)
+    assert call(dict(small, u=None)) == ENULL
+    assert call(dict(small, y=small["u"])) == EALIAS
+    assert call(small, N=8) == EUNSUP
+    assert call(dict(small, b=-1)) == ESHAPE
+
+
 # --- state I/O and single-step decode ------------------------------------------------------------
 
 def call_validate_state(lib, a, h0, hl):
