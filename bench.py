@@ -37,11 +37,35 @@ if ROOT not in sys.path:
 
 METRIC = "selective-scan Melem/s (batch·dim·len) + achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
-VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9  # CUs x SIMDs x lanes x clock: non-packed fp32 lane-instructions/s
-EXP_SLOTS = 2.0                 # v_exp_f32 issue cost in VALU slots (measured: half the FMA rate)
-FLOPS_PER_ELEM_STATE = 6.0      # dt*A (1) + dt*u*B (1) + state FMA (2) + readout FMA (2)
-SLOTS_PER_ELEM_STATE = 4.0 + EXP_SLOTS  # the same four VALU ops plus one exp
-ALU_PEAK_TFLOPS = VALU_LANE_OPS / SLOTS_PER_ELEM_STATE * FLOPS_PER_ELEM_STATE / 1e12
+# Published unit counts: 256 CUs x 4 SIMDs at 2.4 GHz; a SIMD issues one wave64 VALU
+# instruction every 4 cycles (16 lanes per cycle).
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
+CYCLES_PER_VALU_INST = 4
+
+
+def valu_view(valu_doc, kernel: str, kernel_ms: float):
+    """VALU side of a kernel from a committed counter summary (profiles/valu_*.json,
+    taken with the current kernel source): measured VALUBusy, and the time its
+    counted VALU instructions take at one instruction per SIMD per 4 cycles at the
+    published clock (the issue floor), as a fraction of its measured time."""
+    if not valu_doc or kernel not in valu_doc["per_launch"]:
+        return None
+    k = valu_doc["per_launch"][kernel]
+    if not k.get("valu_insts_per_wave"):
+        return None
+    floor_ms = k["valu_insts_per_wave"] * k["waves_per_launch"] * CYCLES_PER_VALU_INST / (SIMDS * CLOCK_HZ) * 1e3
+    return {"kernel": kernel, "busy_pct": k["valu_busy_pct"], "insts_per_wave": k["valu_insts_per_wave"],
+            "waves_per_launch": k["waves_per_launch"], "trans_share": k["trans_share"],
+            "issue_floor_ms": floor_ms, "frac_of_issue_floor": floor_ms / kernel_ms if kernel_ms else None}
+
+
+def hbm_roofline(kernel: str, nbytes: int, kernel_ms: float, traffic=None) -> dict:
+    """The dominant kernel against the HBM roofline: algorithmic bytes of one launch
+    over its measured average duration."""
+    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "bytes_per_launch": nbytes, "launch_ms": kernel_ms}
 
 
 def alg_bytes(cfg) -> int:
@@ -82,9 +106,10 @@ def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(x, y_gpu, cfg, target_s: float = 12.0):
+def cpu_baseline(x, y_gpu, cfg, target_s: float = 15.0):
     """The fp64 oracle, as it stands, on whole sampled rows of the same inputs,
-    using every host core available to this process."""
+    using every host core available to this process: the median of three timed
+    runs over the same sample (about target_s in all), and the same on one core."""
     import numpy as np
 
     from oracle import oracle
@@ -113,23 +138,29 @@ def cpu_baseline(x, y_gpu, cfg, target_s: float = 12.0):
     rng = np.random.default_rng(1234)
     all_rows = [(b, d) for b in range(cfg.batch) for d in range(cfg.dim)]
     order = [all_rows[i] for i in rng.permutation(len(all_rows))]
-    # calibrate on one row per core, then size the sample to about target_s
+    # calibrate on one row per core, then size each of the three runs to about target_s / 3
     t0 = time.perf_counter()
     with ThreadPoolExecutor(cores) as ex:
         list(ex.map(lambda r: run_rows([r]), order[:cores]))
     t_cal = time.perf_counter() - t0
-    n_rows = int(min(len(order), max(cores, cores * target_s / max(t_cal, 1e-6))))
+    n_rows = int(min(len(order), max(cores, cores * target_s / 3 / max(t_cal, 1e-6))))
     sample = order[:n_rows]
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(cores) as ex:
-        refs = list(ex.map(lambda r: run_rows([r])[0], sample))
-    dt = time.perf_counter() - t0
+    times, refs = [], None
+    for _ in range(3):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(cores) as ex:
+            refs = list(ex.map(lambda r: run_rows([r])[0], sample))
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[1]
     elems = n_rows * cfg.len
     # the same oracle on one core, on a smaller sample of the same rows
-    n1 = max(1, min(n_rows, int(target_s / 4 / max(t_cal, 1e-6))))
-    t1 = time.perf_counter()
-    run_rows(sample[:n1])
-    dt1 = time.perf_counter() - t1
+    n1 = max(1, min(n_rows, int(target_s / 12 / max(t_cal, 1e-6))))
+    times1 = []
+    for _ in range(3):
+        t1 = time.perf_counter()
+        run_rows(sample[:n1])
+        times1.append(time.perf_counter() - t1)
+    dt1 = sorted(times1)[1]
     # parity of the GPU output on the same sampled rows (the oracle output is at hand)
     got = np.concatenate([I.f64(y_gpu[b:b + 1, d:d + 1].cpu()) for b, d in sample[:64]], 1)
     ref = np.concatenate(refs[:64], 1)
@@ -138,33 +169,39 @@ def cpu_baseline(x, y_gpu, cfg, target_s: float = 12.0):
     return {
         "value": elems / dt / 1e6, "unit": "Melem/s", "cores": cores, "kind": "oracle",
         "sample": f"{n_rows} whole rows of {cfg.len} tokens ({elems} elements, {cfg.ndir} direction(s)) "
-                  f"of the same seeded inputs, fp64 sequential per row, {cores} threads, {dt:.1f} s",
-        "seconds": dt, "cpu_model": cpu_model(),
-        "one_core": {"value": n1 * cfg.len / dt1 / 1e6, "unit": "Melem/s", "rows": n1, "seconds": dt1},
+                  f"of the same seeded inputs, fp64 sequential per row, {cores} threads; median of 3 runs "
+                  f"({', '.join(f'{t:.2f}' for t in times)} s)",
+        "seconds": dt, "runs_s": times, "cpu": cpu_model(),
+        "one_core": {"value": n1 * cfg.len / dt1 / 1e6, "unit": "Melem/s", "rows": n1, "seconds": dt1,
+                     "runs_s": times1},
         "gpu_parity_on_sample": {"floored_max_err": err, "rows_compared": min(64, n_rows)},
     }
 
 
-def cpu_model() -> str:
+def cpu_model() -> dict:
+    """The host CPU as /proc/cpuinfo describes it (model name, family, model and
+    stepping numbers, cache), with the logical CPUs of the machine and of this
+    process."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if info:
+                        break  # the first processor's block is enough
+                    continue
+                k, v = (t.strip() for t in line.split(":", 1))
+                if k in ("vendor_id", "model name", "cpu family", "model", "stepping", "cache size", "cpu MHz",
+                         "cpu cores", "siblings") and k not in info:
+                    info[k] = v
     except OSError:
         pass
-    return "unknown"
-
-
-# Backward: per (element, state, direction) the algorithm recomputes the state (dt*A,
-# dt*u*B, state FMA: 4 flops, 1 exp), reads it out for dz (1), and walks the adjoint
-# back: lambda FMA (2), lambda*a*h_prev (2), dA FMA (2), dB FMA (2), dC FMA (2),
-# lambda*B (1), du term (1), A*w (1), d(dt) FMA (2), mu = a*lambda (1), one exp, and
-# the three sums over states for du, d(dt), y (3): 25 flops and 2 exps in
-# 21 + 2 * EXP_SLOTS = 25 VALU slots.
-BWD_FLOPS_PER_ELEM_STATE = 25.0
-BWD_SLOTS_PER_ELEM_STATE = 21.0 + 2 * EXP_SLOTS
-BWD_ALU_PEAK_TFLOPS = VALU_LANE_OPS / BWD_SLOTS_PER_ELEM_STATE * BWD_FLOPS_PER_ELEM_STATE / 1e12
+    info["logical_cpus"] = os.cpu_count()
+    try:
+        info["cpus_available_to_process"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        pass
+    return info
 
 
 def bwd_alg_bytes(cfg) -> int:
@@ -213,9 +250,6 @@ def bench_bwd(args, torch, I, sscan, cfg, ci):
     torch.cuda.synchronize()
     kernel_ms = {k: sum(ev.step_ms()[k] for ev in evsets) / args.steps for k in sscan.BWD_PROFILE_STEPS}
     per_call = [ev.total_ms() for ev in evsets]
-    t_win = kernel_ms["window_pass"] * 1e-3
-    flops = BWD_FLOPS_PER_ELEM_STATE * cfg.dstate * cfg.elems * cfg.ndir
-    achieved = flops / t_win / 1e12
     nbytes = bwd_alg_bytes(cfg)
     out = {
         "metric": METRIC, "value": cfg.elems / (ms * 1e-3) / 1e6, "unit": "Melem/s", "n_gpus": 1,
@@ -223,8 +257,8 @@ def bench_bwd(args, torch, I, sscan, cfg, ci):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded numpy PCG64, shapes of the pages' workloads)",
         "config": {"workload": cfg.name, "pass": "bwd", "batch": cfg.batch, "dim": cfg.dim, "len": cfg.len,
                    "dstate": cfg.dstate, "directions": cfg.ndir, "io_dtype": cfg.io_dtype, "bc_dtype": cfg.bc_dtype},
-        "roofline": {"bound": "alu", "kernel": "window_pass", "achieved": achieved, "peak": BWD_ALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / BWD_ALU_PEAK_TFLOPS, "traffic": None},
+        # the window pass reads every per-token input and writes every per-token gradient
+        "roofline": hbm_roofline("window_pass", nbytes, kernel_ms["window_pass"]),
         "kernels_ms": kernel_ms,
         "call_ms": {"median": percentile(per_call, 50), "p10": percentile(per_call, 10),
                     "p90": percentile(per_call, 90), "calls": len(per_call)},
@@ -268,7 +302,7 @@ def cpu_baseline_bwd(x, g, cfg, target_s: float = 12.0):
     dt = time.perf_counter() - t0
     return {"value": n * cfg.len / dt / 1e6, "unit": "Melem/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} whole rows of {cfg.len} tokens ({cfg.ndir} direction(s)) of the same seeded inputs, "
-                      f"fp64 backward per row, {cores} threads, {dt:.1f} s", "seconds": dt, "cpu_model": cpu_model()}
+                      f"fp64 backward per row, {cores} threads, {dt:.1f} s", "seconds": dt, "cpu": cpu_model()}
 
 
 # Front-end convolution of the Mamba block: 4 causal taps with bias and silu
@@ -351,12 +385,13 @@ def bench_conv(args, torch, I, sscan, cfg, ci):
         fused(ev)
     torch.cuda.synchronize()
     kernel_ms = {k: sum(ev.step_ms()[k] for ev in evsets) / args.steps for k in sscan.PROFILE_STEPS}
-    flops = FLOPS_PER_ELEM_STATE * cfg.dstate * cfg.elems * cfg.ndir
-    achieved = flops / (kernel_ms["output"] * 1e-3) / 1e12
+    # the scan's algorithmic bytes with x in place of u, plus the convolution's taps and bias
+    nbytes = alg_bytes(cfg) + cfg.dim * (CONV["width"] + 1) * 4
     return dict(base, value=cfg.elems / (ms * 1e-3) / 1e6, unit="Melem/s", ms_per_step=ms,
                 config=dict(cfg_dict, **{"pass": "fwd-conv"}),
-                roofline={"bound": "alu", "kernel": "output", "achieved": achieved, "peak": ALU_PEAK_TFLOPS,
-                          "unit": "TFLOP/s", "frac": achieved / ALU_PEAK_TFLOPS, "traffic": None},
+                roofline=hbm_roofline("output", nbytes, kernel_ms["output"]),
+                hbm={"achieved_GBs": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "algorithmic_bytes_per_step": nbytes},
                 kernels_ms=kernel_ms,
                 unfused={"ms_per_step": unfused_ms, "conv1d_ms": conv_ms,
                          "note": "sscan_conv1d writing u, then sscan_fwd / sscan_bidir reading it"})
@@ -382,7 +417,7 @@ def cpu_baseline_conv(x, cp, cfg, target_s: float = 12.0):
         rows += 1
     return {"value": rows * cfg.len / dt / 1e6, "unit": "Melem/s", "cores": 1, "kind": "oracle",
             "sample": f"{rows} whole rows of {cfg.len} tokens, fp64, one thread, {dt:.1f} s", "seconds": dt,
-            "cpu_model": cpu_model()}
+            "cpu": cpu_model()}
 
 
 def bench_multi(args, torch, I, sscan, cfg, ci):
@@ -423,8 +458,12 @@ def bench_multi(args, torch, I, sscan, cfg, ci):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    flops = FLOPS_PER_ELEM_STATE * cfg.dstate * cfg.elems * len(kinds)
-    achieved = flops / (ms * 1e-3) / 1e12
+    io = 2 if cfg.io_dtype == "bf16" else 4
+    bc = 2 if cfg.bc_dtype == "bf16" else 4
+    # u, the shared raw delta and z read once, y written once; per direction its
+    # B, C and parameters
+    nbytes = 4 * cfg.elems * io + len(kinds) * (2 * cfg.batch * cfg.dstate * cfg.len * bc +
+                                                cfg.dim * (cfg.dstate + 2) * 4)
     return {"metric": METRIC, "value": cfg.elems / (ms * 1e-3) / 1e6, "unit": "Melem/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -432,10 +471,8 @@ def bench_multi(args, torch, I, sscan, cfg, ci):
             "config": {"workload": cfg.name, "pass": args.pass_, "batch": cfg.batch, "dim": cfg.dim,
                        "height": side, "width": side, "dstate": cfg.dstate, "directions": len(kinds),
                        "io_dtype": cfg.io_dtype, "bc_dtype": cfg.bc_dtype},
-            # every direction's scan plus the gathers, put-backs and gate: a lower bound
-            # for the scan kernels themselves
-            "roofline": {"bound": "alu", "kernel": "whole call", "achieved": achieved, "peak": ALU_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": achieved / ALU_PEAK_TFLOPS, "traffic": None},
+            # the whole call (every direction's scan, the gathers, put-backs and gate)
+            "roofline": hbm_roofline("whole call", nbytes, ms),
             "per_direction_Melem_s": cfg.elems * len(kinds) / (ms * 1e-3) / 1e6,
             "workspace_bytes": ws.numel()}
 
@@ -519,7 +556,7 @@ def bench_decode(args, torch, I, sscan):
         dt = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": b * d / dt / 1e6, "unit": "Melem/s", "cores": cores, "kind": "oracle",
                                "sample": f"the whole step ({b * d} channels, one token) from the same state, "
-                                         f"fp64, {cores} threads, {dt:.2f} s", "cpu_model": cpu_model()}
+                                         f"fp64, {cores} threads, {dt:.2f} s", "cpu": cpu_model()}
     return out
 
 
@@ -632,39 +669,33 @@ def main():
         del src, dst
 
     nbytes = alg_bytes(cfg)
-    # algorithmic work of the output kernel: the full recurrence and readout of
-    # every element and direction (it also moves every algorithmic byte)
-    flops = FLOPS_PER_ELEM_STATE * cfg.dstate * cfg.elems * cfg.ndir
-    t_dom = kernel_ms[dominant] * 1e-3
-    achieved_tflops = flops / t_dom / 1e12
+    from selective_state_space_sscan_amd import profiling
+
+    traffic = profiling.load_traffic(os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json"))
+    valu_doc = profiling.load_valu(os.path.join(ROOT, "profiles", f"valu_{cfg.name}.json"))
+    # the output kernel reads u, delta, z and the staged B/C and writes y: every
+    # algorithmic byte of the call passes through one launch of it
     out = {
         "metric": METRIC, "value": value, "unit": "Melem/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded numpy PCG64, shapes of the pages' workloads)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "dim": cfg.dim, "len": cfg.len, "dstate": cfg.dstate,
                    "directions": cfg.ndir, "io_dtype": cfg.io_dtype, "bc_dtype": cfg.bc_dtype},
-        "roofline": {"bound": "alu", "kernel": dominant, "achieved": achieved_tflops, "peak": ALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / ALU_PEAK_TFLOPS, "traffic": None},
+        "roofline": hbm_roofline(dominant, nbytes, kernel_ms[dominant],
+                                 traffic["per_launch"][dominant]["bytes"]
+                                 if traffic and dominant in traffic["per_launch"] else None),
+        "valu": valu_view(valu_doc, dominant, kernel_ms[dominant]),
         "kernels_ms": kernel_ms,
         "call_ms": {"median": percentile(per_call, 50), "p10": percentile(per_call, 10),
                     "p90": percentile(per_call, 90), "calls": len(per_call)},
         "per_direction_Melem_s": value * cfg.ndir,
         "cache": ("cold: footprint %.0f MB per call, above the 256 MB Infinity Cache" % (footprint / 1e6))
         if warm is None else ("cold: rotating over copies of the inputs; warm (one set) %.4f ms" % warm),
-        "step_alu": {"achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
-                     "frac": flops / (ms * 1e-3) / 1e12 / ALU_PEAK_TFLOPS},
         "hbm": {"achieved_GBs": nbytes / (ms * 1e-3) / 1e9, "peak_GBs": HBM_PEAK_GBS,
                 "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes_per_step": nbytes,
                 "achievable_copy_GBs": copy_gbs},
         "wall_s_timed": wall,
     }
-    if dominant != "output":
-        out["roofline"]["kernel"] = dominant
-    from selective_state_space_sscan_amd import profiling
-
-    traffic = profiling.load_traffic(os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json"))
-    if traffic and dominant in traffic["per_launch"]:
-        out["roofline"]["traffic"] = traffic["per_launch"][dominant]["bytes"]
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x, y, cfg)
     print(json.dumps(out), flush=True)

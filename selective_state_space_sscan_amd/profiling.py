@@ -12,6 +12,14 @@ recognisably stale.
 
 FETCH_DIR / WRITE_DIR are the rocprofv3 output directories (containing
 *counter_collection.csv) of ``bench.py --copy-calibration`` runs.
+
+VALU issue of the same kernels, from one ``rocprofv3 --pmc VALUBusy SQ_WAVES
+SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32`` run of bench.py:
+
+  python -m selective_state_space_sscan_amd.profiling valu SQ_DIR OUT.json
+
+gives per kernel the VALUBusy percentage, the VALU instructions per wave (and the
+share of transcendentals) and the waves per launch, keyed by the same source hash.
 """
 from __future__ import annotations
 
@@ -43,6 +51,15 @@ def kernel_source_hash() -> str:
         with open(os.path.join(CSRC, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def _rows(directory: str):
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            yield f, r
 
 
 def _per_dispatch(directory: str, counter: str):
@@ -81,6 +98,31 @@ def summarize(fetch_dir: str, write_dir: str) -> dict:
             "copy_bytes": COPY_BYTES, "per_launch": steps}
 
 
+VALU_COUNTERS = ("VALUBusy", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32")
+
+
+def summarize_valu(sq_dir: str) -> dict:
+    """Per scan kernel: mean VALUBusy (%), waves per launch, VALU and
+    transcendental instructions per wave, over the launches of one counter run."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for f, r in _rows(sq_dir):
+        key = next((v for k, v in KERNELS.items() if k in r["Kernel_Name"]), None)
+        if key is None or r["Counter_Name"] not in VALU_COUNTERS:
+            continue
+        vals[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[key].add((f, r["Dispatch_Id"]))
+    out = {}
+    for k, v in vals.items():
+        n = len(disp[k])
+        waves = v["SQ_WAVES"] / n
+        out[k] = {"valu_busy_pct": v["VALUBusy"] / n, "waves_per_launch": waves,
+                  "valu_insts_per_wave": v["SQ_INSTS_VALU"] / v["SQ_WAVES"] if v["SQ_WAVES"] else None,
+                  "trans_share": v["SQ_INSTS_VALU_TRANS_F32"] / v["SQ_INSTS_VALU"] if v["SQ_INSTS_VALU"] else None,
+                  "launches": n}
+    return {"kernel_source_sha256": kernel_source_hash(), "per_launch": out}
+
+
 def load_traffic(path: str):
     """The per-launch traffic summary if it matches the current kernel source, else None."""
     if not os.path.exists(path):
@@ -91,10 +133,16 @@ def load_traffic(path: str):
     return doc
 
 
+load_valu = load_traffic  # the same staleness rule (kernel source hash)
+
+
 if __name__ == "__main__":
-    if len(sys.argv) != 4:
+    if len(sys.argv) == 4 and sys.argv[1] == "valu":
+        doc = summarize_valu(sys.argv[2])
+    elif len(sys.argv) == 4:
+        doc = summarize(sys.argv[1], sys.argv[2])
+    else:
         sys.exit(__doc__)
-    doc = summarize(sys.argv[1], sys.argv[2])
     with open(sys.argv[3], "w") as fh:
         json.dump(doc, fh, indent=1)
     print(json.dumps(doc, indent=1))
