@@ -65,6 +65,15 @@ __device__ __forceinline__ float softplus_f32(float x) {
 
 __device__ __forceinline__ float silu_f32(float x) { return x * rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
+// Sum over each group of four lanes (DPP quad permutations: xor 1, then xor 2).
+// (bound_ctrl set: every quad lane is a valid source, and it lets the compiler fold
+// each move into the add as its DPP source)
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+  return v;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

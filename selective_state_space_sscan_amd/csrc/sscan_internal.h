@@ -179,6 +179,8 @@ struct Plan {
   size_t e_floats;          // per run: entry state
   size_t park_floats;       // bidirectional meeting buffers kept in global memory
   size_t workspace_bytes;
+  bool quad;                // one segment scanned by the four-lanes-per-channel kernel (when the call
+                            // has no convolution, fp32 partial output or state I/O)
 };
 
 Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir);
@@ -192,6 +194,10 @@ constexpr int kProfileEvents = 5;
 // also recorded on the stream.
 hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* workspace, hipStream_t stream,
                        hipEvent_t const* events = nullptr);
+
+// The scan of one-segment sequences with four lanes per channel (Plan::quad): B/C
+// already staged in bc.
+hipError_t launch_short_quad(const ScanArgs& a, const float* bc, hipStream_t stream);
 
 // A call with len == 0 and a final state requested: h_last = h0 (or 0).
 hipError_t launch_state_passthrough(const ScanArgs& a, hipStream_t stream);

@@ -75,12 +75,6 @@ __global__ __launch_bounds__(256) void state_passthrough_kernel(const float* h0,
 constexpr int kStepThreads = 256;
 constexpr int kStepChannels = kStepThreads / 4;
 
-__device__ __forceinline__ float quad_sum(float v) {
-  // xor 1 then xor 2 within each group of four lanes (DPP quad permutations)
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
-  return v;
-}
 
 // Each thread handles kStepReps channel quads (kStepChannels apart), all their loads
 // issued before any arithmetic: more bytes in flight per wave for a kernel that is
@@ -218,6 +212,15 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   mark(0);
   launch_stage_bc(a, bc, stream);
   mark(1);
+  if constexpr (CONV == kNoConv && !Y_F32) {
+    if (p.quad && !a.h0 && !a.h_last) {
+      mark(2);
+      mark(3);
+      const hipError_t e = launch_short_quad(a, bc, stream);
+      mark(4);
+      return e;
+    }
+  }
   if (p.nseg > 1) {
     const int64_t agg_blocks = a.batch * p.nrun * ngroups;
     if (p.run_len > 1) {
@@ -386,6 +389,10 @@ constexpr int64_t kSegRounds = 4;
 // bidirectional sequences, cut into 64-token segments): the run form holds more
 // registers, and a short chain costs the carry little.
 constexpr int64_t kAggWaves = 4 * kWaveSlots;
+// Short sequences use the four-lanes-per-channel kernel below this many rounds of
+// lane = channel waves (Vim-tiny, 768 waves: output pass 108 -> 74 us; Vim-small,
+// 3072 waves, one full round: 188 -> 217 us, so it keeps lane = channel).
+constexpr int64_t kQuadRounds = 1;
 
 // Splitting along the sequence.  Sequences up to kShortMax tokens are scanned whole
 // (splitting a 197-token Vim sequence that fills only a quarter of the resident
@@ -416,6 +423,10 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
     p.seg_len = seg_len;
     p.nseg = (len + seg_len - 1) / seg_len;
   }
+  // A one-segment sequence whose lane = channel waves fill less than kQuadRounds
+  // rounds of the resident slots goes to the four-lanes-per-channel kernel (four
+  // times the waves).
+  p.quad = p.nseg == 1 && int64_t(ndir) * groups < kQuadRounds * kWaveSlots;
   // Aggregate runs: enough segments per run that the aggregate pass has about
   // kAggWaves waves and the carry chains fewer runs.
   p.run_len = std::max<int64_t>(1, int64_t(ndir) * groups * p.nseg / kAggWaves);

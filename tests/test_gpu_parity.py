@@ -156,6 +156,17 @@ EDGE = [
     # reverse and ungated instances, over several segments with a ragged end
     ("long-bf16-rev", 2, 64, 3001, False, "bf16", "bf16", dict(reverse=True)),
     ("long-bf16-no-gate", 1, 128, 2050, False, "bf16", "bf16", dict(gate=False)),
+    # one-segment sequences of the four-lanes-per-channel kernel: 16-token tiles
+    # (whole, one short of, one past), the two directions' meeting point (at 0 below
+    # 32 tokens), channel counts that leave a wave's 16 channels partly idle
+    ("quad-len15-bidir", 3, 16, 15, True, "f32", "f32", {}),
+    ("quad-len16-bidir", 2, 32, 16, True, "bf16", "bf16", {}),
+    ("quad-len17-fwd", 2, 48, 17, False, "f32", "f32", {}),
+    ("quad-len33-bidir", 2, 37, 33, True, "f32", "f32", {}),
+    ("quad-len100-rev", 3, 21, 100, False, "f32", "f32", dict(reverse=True)),
+    ("quad-len197-bf16-rev", 2, 50, 197, False, "bf16", "f32", dict(reverse=True)),
+    ("quad-len255-bidir-no-gate", 2, 40, 255, True, "bf16", "bf16", dict(gate=False)),
+    ("quad-len64-bidir-no-softplus", 2, 24, 64, True, "f32", "f32", dict(softplus=False)),
 ]
 
 
@@ -192,10 +203,11 @@ def test_deterministic_reruns():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_nan_propagates_like_the_oracle():
+@pytest.mark.parametrize("L", [600, 150])
+def test_nan_propagates_like_the_oracle(L):
     for bidir in (False, True):
-        x = I.make_inputs(2, 64, 600, bidir=bidir, seed=9)
-        x.u[1, 5, 333] = float("nan")
+        x = I.make_inputs(2, 64, L, bidir=bidir, seed=9)
+        x.u[1, 5, L // 2 + 33] = float("nan")
         got = I.f64(gpu_run(x).cpu())
         ref = oracle_run(x)
         assert np.array_equal(np.isnan(got), np.isnan(ref)), bidir
