@@ -194,6 +194,32 @@ def sscan_fwd_conv(x, conv_w, conv_bias, same, silu, delta, A, B, C, D=None, z=N
     return sscan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus=softplus, reverse=reverse, nthreads=nthreads)
 
 
+def sscan_step_conv(state, conv_state, x, conv_w, conv_bias, silu, delta, A, B, C, D=None, z=None, delta_bias=None,
+                    softplus=True):
+    """One decode token through the causal front-end convolution and the scan
+    (Hand-written simplified Mamba2 page, section 5.2: the recurrent step keeps the
+    state h and the last d_conv - 1 inputs of the convolution, and returns the new
+    output, state and convolution state).  Steps, in the page's order:
+      1. the window is the stored inputs (oldest first) followed by x_t;
+      2. u_t is the causal convolution's output at the window's last position
+         (``conv1d`` over the window, its last output: every tap inside it);
+      3. one token of the scan from ``state`` (``sscan_fwd`` with h0, len 1);
+      4. the convolution state drops its oldest input and appends x_t.
+    Shapes: state [b, d, N]; conv_state [b, d, width - 1]; x, delta, z [b, d];
+    B, C [b, N].  Returns (y [b, d], new state, new conv_state), all float64."""
+    x = _c64(x)
+    b, d = x.shape
+    w = _c64(conv_w)
+    width = w.shape[1]
+    cs = _c64(conv_state, (b, d, width - 1))
+    window = np.concatenate([cs, x[:, :, None]], axis=2)
+    u = conv1d(window, w, conv_bias, same=False, silu=silu)[:, :, -1]
+    col = lambda a: None if a is None else _c64(a)[:, :, None]
+    y, h = sscan_fwd(u[:, :, None], col(delta), A, col(B), col(C), D, col(z), delta_bias, softplus=softplus,
+                     h0=state, return_last_state=True)
+    return y[:, :, 0], h, window[:, :, 1:].copy()
+
+
 def softplus(x: float) -> float:
     return _load().oracle_softplus_f64(float(x))
 

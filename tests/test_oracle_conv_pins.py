@@ -64,3 +64,63 @@ def test_impulse_response_and_edges():
         np.testing.assert_array_equal(out[0, di], ref)
     with pytest.raises(RuntimeError):
         oracle.conv1d(x, w, same=True)  # even width has no centred 'same'
+
+
+# --- the decode step through the convolution (oracle.sscan_step_conv) ---------------------------
+
+def _decode_case(seed, b=2, d=5, L=13, width=4, silu=True):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(b, d, L))
+    delta = 0.5 * rng.normal(size=(b, d, L))
+    z = rng.normal(size=(b, d, L))
+    A = -np.exp(rng.uniform(-1.0, 1.5, size=(d, 16)))
+    B = rng.normal(size=(b, 16, L))
+    C = rng.normal(size=(b, 16, L))
+    D = rng.normal(size=d)
+    bias = np.log(np.expm1(np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=d))))
+    w = rng.normal(0.0, 0.5, size=(d, width))
+    wb = rng.normal(0.0, 0.2, size=d)
+    return x, delta, z, A, B, C, D, bias, w, wb
+
+
+@pytest.mark.parametrize("width,silu", [(4, True), (3, False), (2, True), (1, False)])
+def test_decode_steps_equal_the_sequence_call(width, silu):
+    """Token-by-token steps from zero states (zero state = the causal padding)
+    reproduce the fused sequence call's outputs, its final scan state, and leave
+    the last width - 1 inputs in the convolution state."""
+    x, delta, z, A, B, C, D, bias, w, wb = _decode_case(20 + width, width=width, silu=silu)
+    b, d, L = x.shape
+    ref = oracle.sscan_fwd_conv(x, w, wb, False, silu, delta, A, B, C, D, z, bias)
+    u = oracle.conv1d(x, w, wb, same=False, silu=silu)
+    _, ref_h = oracle.sscan_fwd(u, delta, A, B, C, D, z, bias, return_last_state=True)
+    h = np.zeros((b, d, 16))
+    cs = np.zeros((b, d, width - 1))
+    ys = []
+    for t in range(L):
+        y, h, cs = oracle.sscan_step_conv(h, cs, x[:, :, t], w, wb, silu, delta[:, :, t], A, B[:, :, t], C[:, :, t],
+                                          D, z[:, :, t], bias)
+        ys.append(y)
+    np.testing.assert_allclose(np.stack(ys, -1), ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(h, ref_h, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(cs, x[:, :, L - (width - 1):] if width > 1 else np.zeros((b, d, 0)))
+
+
+def test_decode_conv_state_is_the_input_history():
+    """A nonzero convolution state acts as the inputs before the first step: the
+    step outputs equal the sequence call on [history, x] at x's positions, with the
+    scan state taken over history first."""
+    width = 4
+    x, delta, z, A, B, C, D, bias, w, wb = _decode_case(31, L=9, width=width)
+    b, d, L = x.shape
+    rng = np.random.default_rng(32)
+    hist = rng.normal(size=(b, d, width - 1))
+    h0 = rng.normal(size=(b, d, 16))
+    # the convolved sequence over [history, x], restricted to x's positions
+    u_full = oracle.conv1d(np.concatenate([hist, x], 2), w, wb, same=False, silu=True)[:, :, width - 1:]
+    ref = oracle.sscan_fwd(u_full, delta, A, B, C, D, z, bias, h0=h0)
+    h, cs, ys = h0, hist, []
+    for t in range(L):
+        y, h, cs = oracle.sscan_step_conv(h, cs, x[:, :, t], w, wb, True, delta[:, :, t], A, B[:, :, t], C[:, :, t],
+                                          D, z[:, :, t], bias)
+        ys.append(y)
+    np.testing.assert_allclose(np.stack(ys, -1), ref, rtol=1e-12, atol=1e-12)
