@@ -168,6 +168,25 @@ SSCAN_API int sscan_bidir_conv(const void* x, const sscan_conv_params* conv, con
                      int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
                      int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
 
+/* The decode step (sscan_step) through the causal convolution in front of the
+ * scan: the recurrent step of the Hand-written simplified Mamba2 page (section 5.2,
+ * step(x_t, h, conv_state)), which keeps the last width - 1 inputs of the
+ * convolution beside the scan state.  For every (b, d):
+ *   window  = conv_state[b,d,0 .. width-2] (oldest first), then x[b,d]
+ *   u       = bias_d + sum_{j<width} weight[d,j] * window[j]    (then silu(u) if conv->silu)
+ *   state, y: one token of sscan_step on u
+ *   conv_state[b,d,:] <- window[1 .. width-1]                    (x[b,d] appended, oldest dropped)
+ * A zero conv_state is the convolution's zero padding before the first token, so
+ * steps from zero states reproduce sscan_fwd_conv token by token.  conv must be
+ * causal (conv->same == 0; a centred window needs the next token: SSCAN_ERR_UNSUPPORTED).
+ * Layouts: conv_state [batch, dim, width - 1] io_dtype (read and updated in place;
+ * NULL allowed when width == 1), x [batch, dim] io_dtype; the rest as sscan_step.
+ * conv_state must not overlap any other argument.  No workspace. */
+SSCAN_API int sscan_step_conv(float* state, void* conv_state, const void* x, const sscan_conv_params* conv,
+                    const void* delta, const float* delta_bias, int softplus, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, void* y, int64_t batch, int64_t dim,
+                    int64_t dstate, void* stream, int io_dtype, int bc_dtype);
+
 /* Scans of a 2-D feature map along several visiting orders (Mamba in the YOLO26
  * backbone page, section 1.2: rows, columns or crosswise in several directions;
  * sections 2.2 and 4.4: row scans both ways, four directions; Samba page, section
@@ -331,6 +350,11 @@ SSCAN_API int sscan_validate_step(const float* state, const void* u, const void*
                         int softplus, const float* A, const void* B, const void* C, const float* D,
                         const void* z, const void* y, int64_t batch, int64_t dim, int64_t dstate,
                         int io_dtype, int bc_dtype);
+
+SSCAN_API int sscan_validate_step_conv(const float* state, const void* conv_state, const void* x,
+                             const sscan_conv_params* conv, const void* delta, const float* delta_bias, int softplus,
+                             const float* A, const void* B, const void* C, const float* D, const void* z,
+                             const void* y, int64_t batch, int64_t dim, int64_t dstate, int io_dtype, int bc_dtype);
 
 SSCAN_API int sscan_validate_bwd(const void* u, const void* delta, const float* delta_bias, int softplus,
                        const float* A, const void* B, const void* C, const float* D,

@@ -453,6 +453,53 @@ int sscan_validate_step(const float* state, const void* u, const void* delta, co
   return SSCAN_OK;
 }
 
+int sscan_validate_step_conv(const float* state, const void* conv_state, const void* x, const sscan_conv_params* conv,
+                             const void* delta, const float* delta_bias, int softplus, const float* A, const void* B,
+                             const void* C, const float* D, const void* z, const void* y, int64_t batch, int64_t dim,
+                             int64_t dstate, int io_dtype, int bc_dtype) {
+  int st = sscan_validate_step(state, x, delta, delta_bias, softplus, A, B, C, D, z, y, batch, dim, dstate, io_dtype,
+                               bc_dtype);
+  if (st != SSCAN_OK) return st;
+  if (!conv) return SSCAN_ERR_NULL;
+  if (conv->same != 0) return SSCAN_ERR_UNSUPPORTED;  // a centred window needs the next token
+  Sizes sz{};
+  check_sizes(batch, dim, 1, dstate, io_dtype, bc_dtype, &sz);
+  const Range yr = range_of(y, batch * dim > 0 ? sz.io_elems * sz.io_esz : 0);
+  st = check_conv(conv, dim, yr);
+  if (st != SSCAN_OK || batch == 0 || dim == 0) return st;
+  const size_t cs_bytes = sz.io_elems * size_t(conv->width - 1) * sz.io_esz;
+  if (cs_bytes > 0 && !conv_state) return SSCAN_ERR_NULL;
+  if (!aligned(conv_state, sz.io_esz)) return SSCAN_ERR_ALIGN;
+  // the window is updated in place: it overlaps nothing else the call reads or writes
+  const size_t io = sz.io_elems * sz.io_esz, bcb = sz.bc_elems * sz.bc_esz, vec = size_t(dim) * 4;
+  const Range cr = range_of(conv_state, cs_bytes);
+  const Range others[] = {range_of(state, sz.io_elems * sscan::kDState * 4), yr, range_of(x, io),
+                          range_of(delta, io), range_of(z, z ? io : 0), range_of(B, bcb), range_of(C, bcb),
+                          range_of(A, vec * sscan::kDState), range_of(delta_bias, delta_bias ? vec : 0),
+                          range_of(D, D ? vec : 0), range_of(conv->weight, vec * size_t(conv->width)),
+                          range_of(conv->bias, conv->bias ? vec : 0)};
+  for (const Range& r : others)
+    if (overlap(cr, r)) return SSCAN_ERR_ALIAS;
+  if (overlap(range_of(state, sz.io_elems * sscan::kDState * 4), range_of(conv->weight, vec * size_t(conv->width))) ||
+      (conv->bias && overlap(range_of(state, sz.io_elems * sscan::kDState * 4), range_of(conv->bias, vec))))
+    return SSCAN_ERR_ALIAS;
+  return SSCAN_OK;
+}
+
+int sscan_step_conv(float* state, void* conv_state, const void* x, const sscan_conv_params* conv, const void* delta,
+                    const float* delta_bias, int softplus, const float* A, const void* B, const void* C,
+                    const float* D, const void* z, void* y, int64_t batch, int64_t dim, int64_t dstate, void* stream,
+                    int io_dtype, int bc_dtype) {
+  const int st = sscan_validate_step_conv(state, conv_state, x, conv, delta, delta_bias, softplus, A, B, C, D, z, y,
+                                          batch, dim, dstate, io_dtype, bc_dtype);
+  if (st != SSCAN_OK || batch == 0 || dim == 0) return st;
+  sscan::StepArgs a{state, x, delta, z, y, delta_bias, A, B, C, D, softplus ? 1 : 0, io_dtype == SSCAN_BF16,
+                    bc_dtype == SSCAN_BF16, batch, dim, conv_state, conv->weight, conv->bias, conv->width,
+                    conv->silu};
+  const hipError_t e = sscan::launch_step(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+}
+
 int sscan_step(float* state, const void* u, const void* delta, const float* delta_bias, int softplus,
                const float* A, const void* B, const void* C, const float* D, const void* z, void* y, int64_t batch,
                int64_t dim, int64_t dstate, void* stream, int io_dtype, int bc_dtype) {
@@ -460,7 +507,7 @@ int sscan_step(float* state, const void* u, const void* delta, const float* delt
                                      io_dtype, bc_dtype);
   if (st != SSCAN_OK || batch == 0 || dim == 0) return st;
   sscan::StepArgs a{state, u, delta, z, y, delta_bias, A, B, C, D, softplus ? 1 : 0, io_dtype == SSCAN_BF16,
-                    bc_dtype == SSCAN_BF16, batch, dim};
+                    bc_dtype == SSCAN_BF16, batch, dim, nullptr, nullptr, nullptr, 0, 0};
   const hipError_t e = sscan::launch_step(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
 }

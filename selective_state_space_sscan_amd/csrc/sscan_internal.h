@@ -104,6 +104,15 @@ struct StepArgs {
   const float* D;           // nullable, [dim]
   int softplus, io_bf16, bc_bf16;
   int64_t batch, dim;
+  // Causal convolution in front of the step (conv_w != nullptr): `u` holds x_t, and
+  // u_t = act(conv_b + sum_j conv_w[d][j] * window[j]) over the window of the
+  // stored last conv_width - 1 inputs (conv_state [batch][dim][conv_width - 1], io
+  // dtype, oldest first) followed by x_t; the window then drops its oldest input.
+  void* conv_state;         // read and updated in place (nullable when conv_width == 1)
+  const float* conv_w;      // [dim][conv_width], nullable: no convolution
+  const float* conv_b;      // nullable, [dim]
+  int conv_width;           // 1 .. 4
+  int conv_silu;
 };
 
 // Gradients of one direction (backward pass); nullable members are not computed.

@@ -83,7 +83,9 @@ constexpr int kStepChannels = kStepThreads / 4;
 // quad 13.8 us, two 13.7 us, four 15.9 us.
 constexpr int kStepReps = 2;
 
-template <bool IO_BF16, bool BC_BF16, bool SOFTPLUS>
+constexpr int kStepConvMax = 4;  // taps of the causal convolution in front of the step
+
+template <bool IO_BF16, bool BC_BF16, bool SOFTPLUS, bool CONV>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t b0) {
   using IO = Io<IO_BF16>;
   using T = typename IO::T;
@@ -103,6 +105,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t 
   }
   float4 hv[kStepReps], av[kStepReps];
   float uu[kStepReps], xr[kStepReps], zr[kStepReps], Dd[kStepReps];
+  float win[kStepReps][kStepConvMax];  // the convolution window (CONV)
   int64_t idx[kStepReps];
   bool active[kStepReps];
 #pragma unroll
@@ -118,6 +121,23 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t 
     xr[r] = IO::load(static_cast<const T*>(a.delta), i) + (a.delta_bias ? a.delta_bias[d] : 0.0f);
     zr[r] = a.z ? IO::load(static_cast<const T*>(a.z), i) : 0.0f;
     Dd[r] = a.D ? a.D[d] : 0.0f;
+    if (CONV) {
+      // window: the stored inputs (oldest first), then x_t; every lane of the quad
+      // computes u_t (four taps at most), the quad's first lane stores the shifted window
+      const int W = a.conv_width;
+      const T* cs = static_cast<const T*>(a.conv_state) + i * (W - 1);
+      float acc = a.conv_b ? a.conv_b[d] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < kStepConvMax - 1; ++j) {
+        if (j < W - 1) {
+          win[r][j] = IO::load(cs, j);
+          acc = fmaf(a.conv_w[d * W + j], win[r][j], acc);
+        }
+      }
+      acc = fmaf(a.conv_w[d * W + W - 1], uu[r], acc);
+      win[r][kStepConvMax - 1] = uu[r];  // x_t, the newest input
+      uu[r] = a.conv_silu ? silu_f32(acc) : acc;
+    }
   }
 #pragma unroll
   for (int r = 0; r < kStepReps; ++r) {
@@ -135,6 +155,14 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a, int64_t 
     if (!active[r]) continue;
     const int64_t i = idx[r];
     reinterpret_cast<float4*>(a.state + i * kDState)[q] = make_float4(h[0], h[1], h[2], h[3]);
+    if (CONV && q == 0) {
+      // the window without its oldest input: win[1 .. W-2], then x_t
+      const int W = a.conv_width;
+      T* cs = static_cast<T*>(a.conv_state) + i * (W - 1);
+#pragma unroll
+      for (int j = 0; j < kStepConvMax - 1; ++j)
+        if (j < W - 1) IO::store(cs, j, j + 1 < W - 1 ? win[r][j + 1] : win[r][kStepConvMax - 1]);
+    }
     if (q == 0) {
       float yv = fmaf(Dd[r], uu[r], s);
       if (a.z) yv *= silu_f32(zr[r]);
@@ -494,16 +522,23 @@ hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
     const int64_t per_block = int64_t(kStepChannels) * kStepReps;
     const dim3 grid(unsigned((a.dim + per_block - 1) / per_block), unsigned(std::min(kMaxRows, a.batch - b0)));
     const dim3 block(kStepThreads);
-    switch (key) {
-      case 0: hipLaunchKernelGGL((step_kernel<false, false, false>), grid, block, 0, stream, a, b0); break;
-      case 1: hipLaunchKernelGGL((step_kernel<false, false, true>), grid, block, 0, stream, a, b0); break;
-      case 2: hipLaunchKernelGGL((step_kernel<false, true, false>), grid, block, 0, stream, a, b0); break;
-      case 3: hipLaunchKernelGGL((step_kernel<false, true, true>), grid, block, 0, stream, a, b0); break;
-      case 4: hipLaunchKernelGGL((step_kernel<true, false, false>), grid, block, 0, stream, a, b0); break;
-      case 5: hipLaunchKernelGGL((step_kernel<true, false, true>), grid, block, 0, stream, a, b0); break;
-      case 6: hipLaunchKernelGGL((step_kernel<true, true, false>), grid, block, 0, stream, a, b0); break;
-      default: hipLaunchKernelGGL((step_kernel<true, true, true>), grid, block, 0, stream, a, b0); break;
+#define SSCAN_STEP_LAUNCH(CONV)                                                                            \
+  switch (key) {                                                                                          \
+    case 0: hipLaunchKernelGGL((step_kernel<false, false, false, CONV>), grid, block, 0, stream, a, b0); break; \
+    case 1: hipLaunchKernelGGL((step_kernel<false, false, true, CONV>), grid, block, 0, stream, a, b0); break;  \
+    case 2: hipLaunchKernelGGL((step_kernel<false, true, false, CONV>), grid, block, 0, stream, a, b0); break;  \
+    case 3: hipLaunchKernelGGL((step_kernel<false, true, true, CONV>), grid, block, 0, stream, a, b0); break;   \
+    case 4: hipLaunchKernelGGL((step_kernel<true, false, false, CONV>), grid, block, 0, stream, a, b0); break;  \
+    case 5: hipLaunchKernelGGL((step_kernel<true, false, true, CONV>), grid, block, 0, stream, a, b0); break;   \
+    case 6: hipLaunchKernelGGL((step_kernel<true, true, false, CONV>), grid, block, 0, stream, a, b0); break;   \
+    default: hipLaunchKernelGGL((step_kernel<true, true, true, CONV>), grid, block, 0, stream, a, b0); break;  \
+  }
+    if (a.conv_w) {
+      SSCAN_STEP_LAUNCH(true)
+    } else {
+      SSCAN_STEP_LAUNCH(false)
     }
+#undef SSCAN_STEP_LAUNCH
   }
   return hipGetLastError();
 }

@@ -84,6 +84,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_step.restype = I
     lib.sscan_validate_step.argtypes = [V, V, V, V, I, V, V, V, V, V, V, I64, I64, I64, I, I]
     lib.sscan_validate_step.restype = I
+    CPP = ctypes.POINTER(ConvParams)
+    lib.sscan_step_conv.argtypes = [V, V, V, CPP, V, V, I, V, V, V, V, V, V, I64, I64, I64, V, I, I]
+    lib.sscan_step_conv.restype = I
+    lib.sscan_validate_step_conv.argtypes = [V, V, V, CPP, V, V, I, V, V, V, V, V, V, I64, I64, I64, I, I]
+    lib.sscan_validate_step_conv.restype = I
     DG = ctypes.POINTER(DirGrads)
     lib.sscan_bwd.argtypes = [V, V, V, I, V, V, V, V, V, V, V, V, DG, I64, I64, I64, I64, I, V, I, I, V, SZ]
     lib.sscan_bwd.restype = I
@@ -404,6 +409,47 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bo
                         _DT_CODE[B.dtype])
     if st != 0:
         raise SScanError(st, "sscan_step")
+    return out
+
+
+def step_conv(state, conv_state, x, conv: dict, delta, A, B, C, D=None, z=None, delta_bias=None,
+              softplus: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token through the causal convolution and the scan (``sscan_step_conv``):
+    ``conv_state`` [batch, dim, width - 1] (x's dtype, may be None for width 1) and
+    ``state`` [batch, dim, 16] f32 are updated in place; x, delta, z [batch, dim];
+    B, C [batch, 16]; ``conv`` holds weight [dim, width] f32 and optional bias and
+    silu.  Returns y [batch, dim] in x's dtype."""
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.step_conv needs CUDA (HIP) tensors")
+    if x.dtype not in _DT_CODE or B.dtype not in _DT_CODE:
+        raise TypeError("x/delta/z and B/C must be float32 or bfloat16")
+    if conv.get("same", False):
+        raise ValueError("the decode step needs a causal convolution")
+    b, d = x.shape
+    cp = _conv_params(dict(conv, same=False), d, dev)
+    _check(state, "state", dev, torch.float32, (b, d, DSTATE))
+    _check(conv_state, "conv_state", dev, x.dtype, (b, d, cp.width - 1))
+    _check(x, "x", dev)
+    _check(delta, "delta", dev, x.dtype, x.shape)
+    _check(z, "z", dev, x.dtype, x.shape)
+    _check(A, "A", dev, torch.float32, (d, DSTATE))
+    _check(B, "B", dev, None, (b, DSTATE))
+    _check(C, "C", dev, B.dtype, (b, DSTATE))
+    _check(D, "D", dev, torch.float32, (d,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (d,))
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", dev, x.dtype, x.shape)
+    if x.numel() == 0:
+        return out
+    st = lib.sscan_step_conv(_ptr(state), _ptr(conv_state) if conv_state is not None and conv_state.numel() else None,
+                             _ptr(x), ctypes.byref(cp), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A),
+                             _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out), b, d, DSTATE, _stream(dev),
+                             _DT_CODE[x.dtype], _DT_CODE[B.dtype])
+    if st != 0:
+        raise SScanError(st, "sscan_step_conv")
     return out
 
 

@@ -273,6 +273,41 @@ def test_validate_step(lib):
     assert st == ENULL
 
 
+def test_validate_step_conv(lib):
+    """The decode step through the causal convolution: the step's checks, a causal
+    convolution of 1..4 taps, and a window buffer that overlaps nothing else."""
+    f = Fake()
+    f.next = 1 << 47
+
+    def call(a, cs, width=4, same=0, silu=1, weight=True, bias=True):
+        w = f(a["d"] * width * 4) if weight else None
+        cb = f(a["d"] * 4) if bias else None
+        cp = sscan.ConvParams(w, cb, width, same, silu)
+        return lib.sscan_validate_step_conv(a["state"], cs, a["u"], ctypes.byref(cp), a["delta"], a["bias"], 1, a["A"],
+                                            a["B"], a["C"], a["D"], a["z"], a["y"], a["b"], a["d"], a["N"], a["io"],
+                                            a["bc"])
+
+    for io in (0, 1):
+        a = step_args(4, 100, io, io)
+        cs = f(4 * 100 * 3 * 4)
+        assert call(a, cs) == OK
+        assert call(a, None, width=1) == OK      # no window to keep
+        assert call(a, None) == ENULL
+        assert call(a, cs, same=1, width=3) == EUNSUP
+        assert call(a, cs, width=5) == EUNSUP
+        assert call(a, cs, weight=False) == ENULL
+        assert call(a, cs + (1 if io else 2)) == EALIGN
+        assert call(a, a["u"]) == EALIAS          # the window overlaps x
+        assert call(a, a["state"] + 64) == EALIAS
+        assert call(dict(a, y=None), cs) == ENULL
+    assert call(step_args(0, 100), None) == OK  # empty
+    a = step_args(4, 100)
+    cp = sscan.ConvParams(None, None, 4, 0, 0)
+    st = lib.sscan_step_conv(a["state"], None, a["u"], ctypes.byref(cp), a["delta"], a["bias"], 1, a["A"], a["B"],
+                             a["C"], a["D"], a["z"], a["y"], 4, 100, 16, None, 0, 0)
+    assert st == ENULL  # rejected before any HIP call
+
+
 # --- backward -------------------------------------------------------------------------------
 
 def bwd_call(lib, a, g, dout, du, dz):

@@ -170,3 +170,50 @@ def test_step_matches_one_token_sequence_call():
     torch.cuda.synchronize()
     check(y_step, I.f64(y_seq[:, :, 0].cpu()), 1e-6, "step vs len-1 call y")
     check(state, I.f64(h_seq.cpu()), 1e-6, "step vs len-1 call state")
+
+
+STEP_CONV_CASES = [
+    # name, batch, dim, io, bc, width, silu, gate
+    ("w4-silu-f32", 3, 100, "f32", "f32", 4, True, True),
+    ("w4-bf16", 2, 1536, "bf16", "f32", 4, False, True),
+    ("w3-bf16-bc", 2, 70, "bf16", "bf16", 3, True, False),
+    ("w2", 2, 64, "f32", "f32", 2, False, True),
+    ("w1", 2, 40, "f32", "f32", 1, True, True),
+]
+
+
+@pytest.mark.parametrize("name,b,d,io,bc,width,silu,gate", STEP_CONV_CASES, ids=[c[0] for c in STEP_CONV_CASES])
+def test_step_conv_decode_loop(name, b, d, io, bc, width, silu, gate):
+    """T decode steps through the causal convolution, from a random scan state and a
+    random window (input history), against the oracle's step run token by token:
+    every output, the final scan state and the final window (bitwise: it holds the
+    inputs themselves)."""
+    T = 20
+    x, h0 = draw("stepconv-" + name, b, d, T, io, bc)
+    rng = np.random.default_rng(zlib.crc32(name.encode()) % 1000 + 3)
+    w = torch.from_numpy(rng.normal(0.0, 0.5, (d, width))).float()
+    wb = torch.from_numpy(rng.normal(0.0, 0.2, d)).float()
+    hist = torch.from_numpy(rng.normal(0.0, 1.0, (b, d, width - 1))).float().to(x.u.dtype)
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    conv = dict(weight=w.to(DEV), bias=wb.to(DEV), silu=silu)
+    state = h0.to(DEV).clone()
+    cs = hist.to(DEV).clone()
+    ys = []
+    for t in range(T):
+        col = lambda v: v[:, :, t].contiguous()
+        ys.append(sscan.step_conv(state, cs, col(xd.u), conv, col(xd.delta), p.A, col(p.B), col(p.C), p.D,
+                                  col(xd.z) if gate else None, p.delta_bias))
+    y = torch.stack(ys, -1)
+    torch.cuda.synchronize()
+    x64 = I.as_f64_dict(x)
+    q = x64["dirs"][0]
+    h, c, refs = h0.double().numpy(), I.f64(hist), []
+    for t in range(T):
+        yt, h, c = oracle.sscan_step_conv(h, c, x64["u"][:, :, t], I.f64(w), I.f64(wb), silu, x64["delta"][:, :, t],
+                                          q["A"], q["B"][:, :, t], q["C"][:, :, t], q["D"],
+                                          x64["z"][:, :, t] if gate else None, q["delta_bias"])
+        refs.append(yt)
+    check(y, np.stack(refs, -1), TOL[io], f"step_conv {name} y")
+    check(state, h, STATE_TOL, f"step_conv {name} state")
+    assert np.array_equal(I.f64(cs.cpu()), c), "window"
