@@ -187,6 +187,49 @@ def conv1d(x, w, bias=None, same=False, silu=False):
     return out
 
 
+def conv1d_bwd(x, w, bias, same, silu, dout):
+    """Gradients of sum(dout * conv1d(x, w, bias, same, silu)) with respect to x, w
+    and the bias, by the chain rule through the two steps of ``conv1d``:
+      pre[t] = bias + sum_j w[j] x[t - left + j]   (x = 0 outside [0, len))
+      out[t] = silu(pre[t]) or pre[t],  silu'(p) = s (1 + p (1 - s)), s = 1 / (1 + e^-p)
+    so with g = dout * out'(pre):  dx[s] = sum_j w[j] g[s + left - j] (t inside
+    [0, len)), dw[j] = sum_{b,t} g[t] x[t - left + j], dbias = sum_{b,t} g[t].
+    Returns (dx [b, d, L], dw [d, width], dbias [d]) in float64."""
+    x = _c64(x)
+    b, d, L = x.shape
+    w = _c64(w)
+    width = w.shape[1]
+    pre = conv1d(x, w, bias, same=same, silu=False)
+    g = _c64(dout, (b, d, L))
+    if silu:
+        s = 1.0 / (1.0 + np.exp(-pre))
+        g = g * s * (1.0 + pre * (1.0 - s))
+    left = (width - 1) // 2 if same else width - 1
+    dx = np.zeros_like(x)
+    dw = np.zeros((d, width))
+    for j in range(width):
+        # tap j joins x[t - left + j] to out[t]: pairs (t, s = t - left + j), both in range
+        sh = j - left
+        t0, t1 = max(0, -sh), min(L, L - sh)
+        if t1 <= t0:
+            continue
+        dx[:, :, t0 + sh:t1 + sh] += w[None, :, j, None] * g[:, :, t0:t1]
+        dw[:, j] = np.sum(g[:, :, t0:t1] * x[:, :, t0 + sh:t1 + sh], axis=(0, 2))
+    return dx, dw, g.sum(axis=(0, 2))
+
+
+def sscan_bwd_conv(x, conv_w, conv_bias, same, silu, z, g, dirs, softplus=True, reverse=False, nthreads: int = 1):
+    """Backward of the scan with the convolution in front (sscan_fwd_conv /
+    sscan_bidir_conv): the scan's gradients taken at u = conv1d(x) (``sscan_bwd``),
+    then its du carried back through the convolution (``conv1d_bwd``).  Returns the
+    dict of ``sscan_bwd`` without du, plus dx, dconv_w, dconv_b."""
+    u = conv1d(x, conv_w, conv_bias, same=same, silu=silu)
+    r = sscan_bwd(u, z, g, dirs, softplus=softplus, reverse=reverse, nthreads=nthreads)
+    dx, dw, db = conv1d_bwd(x, conv_w, conv_bias, same, silu, r.pop("du"))
+    r.update(dx=dx, dconv_w=dw, dconv_b=db)
+    return r
+
+
 def sscan_fwd_conv(x, conv_w, conv_bias, same, silu, delta, A, B, C, D=None, z=None, delta_bias=None,
                    softplus=True, reverse=False, nthreads: int = 1):
     """The scan of the convolved input: sscan_fwd(conv1d(x), ...)."""

@@ -124,3 +124,96 @@ def test_decode_conv_state_is_the_input_history():
                                           D, z[:, :, t], bias)
         ys.append(y)
     np.testing.assert_allclose(np.stack(ys, -1), ref, rtol=1e-12, atol=1e-12)
+
+
+# --- the backward through the convolution (oracle.conv1d_bwd, oracle.sscan_bwd_conv) -----------
+
+@pytest.mark.parametrize("width,same,silu", [(4, False, True), (3, False, False), (3, True, True), (1, True, False),
+                                             (2, False, True)])
+def test_conv1d_bwd_matches_torch_autograd(width, same, silu):
+    """PyTorch's reverse mode (a library routine) through its grouped conv1d with the
+    pages' paddings, cut to L, and silu."""
+    rng = np.random.default_rng(40 + width + 7 * same)
+    b, d, L = 2, 5, 19
+    x = rng.normal(size=(b, d, L))
+    w = rng.normal(size=(d, width))
+    bias = rng.normal(size=d)
+    g = rng.normal(size=(b, d, L))
+    dx, dw, db = oracle.conv1d_bwd(x, w, bias, same, silu, g)
+    T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    xt, wt, bt = T(x), T(w), T(bias)
+    pad = (width - 1) // 2 if same else width - 1
+    out = torch.nn.functional.conv1d(xt, wt[:, None, :], bt, padding=pad, groups=d)[:, :, :L]
+    if silu:
+        out = torch.nn.functional.silu(out)
+    (out * torch.tensor(g)).sum().backward()
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(db, bt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def _fused_loss(x, w, wb, same, silu, z, g, dirs, reverse):
+    if len(dirs) == 1:
+        p = dirs[0]
+        y = oracle.sscan_fwd_conv(x, w, wb, same, silu, p["delta"], p["A"], p["B"], p["C"], p["D"], z,
+                                  p["delta_bias"], reverse=reverse)
+    else:
+        u = oracle.conv1d(x, w, wb, same, silu)
+        y = oracle.sscan_bidir(u, z, dirs[0], dirs[1])
+    return float(np.sum(g * y))
+
+
+@pytest.mark.parametrize("ndir,width,same,silu,reverse", [(1, 4, False, True, False), (1, 3, False, False, True),
+                                                          (2, 3, True, True, False)])
+def test_sscan_bwd_conv_matches_central_differences(ndir, width, same, silu, reverse):
+    """dx, dconv_w, dconv_b and a parameter gradient of the fused backward against
+    central differences of the fused forward oracle (the convolution's output feeds
+    the scan as u; its pins and the scan's are separate)."""
+    rng = np.random.default_rng(60 + ndir + width)
+    b, d, L = 2, 3, 10
+    x = rng.normal(size=(b, d, L))
+    z = rng.normal(size=(b, d, L))
+    g = rng.normal(size=(b, d, L))
+    w = rng.normal(0.0, 0.5, size=(d, width))
+    wb = rng.normal(0.0, 0.2, size=d)
+    dirs = [dict(delta=rng.normal(0.0, 0.5, (b, d, L)), A=-np.exp(rng.uniform(-1.0, 1.5, (d, 16))),
+                 B=rng.normal(size=(b, 16, L)), C=rng.normal(size=(b, 16, L)), D=rng.normal(size=d),
+                 delta_bias=rng.uniform(-3.0, 0.5, d)) for _ in range(ndir)]
+    got = oracle.sscan_bwd_conv(x, w, wb, same, silu, z, g, dirs, reverse=reverse)
+    h = 1e-5
+
+    def loss(args):
+        xx, ww, bb, dd = args
+        return _fused_loss(xx, ww, bb, same, silu, z, g, dd, reverse)
+
+    def central(mutate):
+        return (loss(mutate(h)) - loss(mutate(-h))) / (2 * h)
+
+    checks = []
+    for idx in [(0, 0, 0), (1, 2, 9), (0, 1, 5), (1, 0, L - 2)]:
+        def mx(e, idx=idx):
+            xx = x.copy()
+            xx[idx] += e
+            return xx, w, wb, dirs
+        checks.append(("dx", got["dx"][idx], central(mx)))
+    for idx in [(0, 0), (2, width - 1), (1, width // 2)]:
+        def mw(e, idx=idx):
+            ww = w.copy()
+            ww[idx] += e
+            return x, ww, wb, dirs
+        checks.append(("dconv_w", got["dconv_w"][idx], central(mw)))
+    for i in range(d):
+        def mb(e, i=i):
+            bb = wb.copy()
+            bb[i] += e
+            return x, w, bb, dirs
+        checks.append(("dconv_b", got["dconv_b"][i], central(mb)))
+    def md(e):
+        nd = [dict(p) for p in dirs]
+        arr = nd[0]["delta"].copy()
+        arr[1, 1, 3] += e
+        nd[0]["delta"] = arr
+        return x, w, wb, nd
+    checks.append(("ddelta", got["dirs"][0]["ddelta"][1, 1, 3], central(md)))
+    for name, val, ref in checks:
+        assert abs(val - ref) <= 1e-6 * (1.0 + abs(ref)), (name, val, ref)
