@@ -267,6 +267,38 @@ SSCAN_API int sscan_bidir_bwd(const void* u, const void* z, const void* dout, vo
                     int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
                     int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
 
+/* Backward of sscan_fwd_conv / sscan_bidir_conv: the scan's gradients taken at
+ * u = conv(x), and du carried back through the convolution (Reproducing Vision
+ * Mamba page, section 1.3: the block is trained with hand-written gradients;
+ * Hand-written simplified Mamba2 page, sections 4.4 and 5.1: the convolution sits
+ * inside the trained block).  Arguments as sscan_bwd / sscan_bidir_bwd with x in
+ * place of u and dx [batch, dim, len] io_dtype in place of du, and
+ *   dconv_w [dim, width] float32 (required), dconv_b [dim] float32 (required when
+ *   conv->bias is given, else ignored): sums over batch rows and tokens.
+ * u = conv(x) is recomputed in float32, as the fused forward computes it (never
+ * rounded to the io dtype), and du reaches the convolution's backward in float32.  Results are
+ * bitwise reproducible (fixed-order sums).  Workspace:
+ * sscan_bwd_conv_workspace_bytes(..., bidir, io_dtype) bytes, 256-byte aligned.  An
+ * empty call writes zeros to the parameter gradients that have elements. */
+SSCAN_API int sscan_bwd_conv(const void* x, const sscan_conv_params* conv, const void* delta, const float* delta_bias,
+                   int softplus, const float* A, const void* B, const void* C, const float* D, const void* z,
+                   const void* dout, void* dx, void* dz, const sscan_dir_grads* grads, float* dconv_w,
+                   float* dconv_b, int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse,
+                   void* stream, int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+SSCAN_API int sscan_bidir_bwd_conv(const void* x, const sscan_conv_params* conv, const void* z, const void* dout,
+                         void* dx, void* dz, const sscan_dir_params* fwd, const sscan_dir_params* rev,
+                         const sscan_dir_grads* gfwd, const sscan_dir_grads* grev, float* dconv_w, float* dconv_b,
+                         int softplus, int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                         int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+SSCAN_API int sscan_validate_bwd_conv(const void* x, const sscan_conv_params* conv, const void* delta,
+                            const float* delta_bias, int softplus, const float* A, const void* B, const void* C,
+                            const float* D, const void* z, const void* dout, const void* dx, const void* dz,
+                            const sscan_dir_grads* grads, const float* dconv_w, const float* dconv_b,
+                            int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse, int io_dtype,
+                            int bc_dtype, const void* workspace, size_t workspace_bytes);
+SSCAN_API size_t sscan_bwd_conv_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir,
+                                      int io_dtype);
+
 /* Bytes of device workspace a backward call needs (0 if none or invalid sizes). */
 SSCAN_API size_t sscan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir);
 

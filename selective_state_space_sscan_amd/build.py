@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsscan.so")
 
-SOURCES = ["sscan_kernels.hip", "sscan_short.hip", "sscan_bwd.hip", "sscan_multi.hip", "sscan_noalloc.hip", "sscan_capi.cpp"]
+SOURCES = ["sscan_kernels.hip", "sscan_short.hip", "sscan_bwd.hip", "sscan_conv_bwd.hip", "sscan_multi.hip", "sscan_noalloc.hip", "sscan_capi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

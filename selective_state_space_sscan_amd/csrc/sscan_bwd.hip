@@ -138,16 +138,19 @@ __device__ __forceinline__ size_t pbc_index(int j, int dir, int64_t b, int which
 // the end the run's totals in the segment-aggregate layout the carry kernel reads.
 // Grid: batch * nrun * ngroups one-wave blocks (64 channels each); blockIdx.y is the
 // direction.
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, bool ADJ>
+// CONV (state chain only): u is recomputed from x (a.u) by the front-end convolution,
+// as in the fused forward.
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, bool ADJ, int CONV = kNoConv>
 __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void bwd_chain_kernel(
     ScanArgs a, int64_t nwin, int64_t run_len, int64_t nrun, const float* __restrict__ bc, float* __restrict__ pw,
     float* __restrict__ sw, float* __restrict__ ragg, int vec) {
+  static_assert(!ADJ || CONV == kNoConv, "the adjoint chain reads dout, not x");
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const SegIndex s = decode_block(blockIdx.x, ngroups, nrun);
   const int dir = blockIdx.y;
   const bool chain_rev = (a.ndir == 2 ? dir : a.reverse) != ADJ;  // windows visited high to low
   constexpr int kMode = ADJ ? kAdjoint : kAggregate;
-  Lane<IO_BF16, SOFTPLUS, ADJ && HAS_Z> L;
+  Lane<IO_BF16, SOFTPLUS, ADJ && HAS_Z, CONV> L;
   init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
   const int64_t k_lo = s.seg * run_len, k_hi = min64(nwin, k_lo + run_len);
   const int64_t d = s.g * kLanes + threadIdx.x;
@@ -199,7 +202,7 @@ __device__ __forceinline__ void load_tok(TokIn<IO_BF16, HAS_Z>& r, const BwdArgs
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int i = i0 + e < wl ? i0 + e : wl - 1;  // a valid token for the ragged tail
-    r.u[e] = IO::load(static_cast<const T*>(a.fwd.u), row + i);
+    r.u[e] = a.u32 ? a.u32[row + i] : IO::load(static_cast<const T*>(a.fwd.u), row + i);
     r.draw[e] = IO::load(static_cast<const T*>(pd.delta), row + i);
     r.g[e] = IO::load(static_cast<const T*>(a.dout), row + i);
     r.z[e] = HAS_Z ? IO::load(static_cast<const T*>(a.fwd.z), row + i) : 0.0f;
@@ -431,13 +434,21 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           if (act) {
             IO::store(static_cast<T*>(gd.ddelta), row + i, ddl);
             if (OUT == kSingle) {
-              IO::store(static_cast<T*>(a.du), row + i, du);
+              if (a.du_f32) {
+                static_cast<float*>(a.du)[row + i] = du;
+              } else {
+                IO::store(static_cast<T*>(a.du), row + i, du);
+              }
               if (HAS_Z) IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * y);
             } else if (OUT == kFirst) {
               acc_du[row + i] = du;
               if (HAS_Z) acc_y[row + i] = y;
             } else {
-              IO::store(static_cast<T*>(a.du), row + i, du + acc_du[row + i]);
+              if (a.du_f32) {
+                static_cast<float*>(a.du)[row + i] = du + acc_du[row + i];
+              } else {
+                IO::store(static_cast<T*>(a.du), row + i, du + acc_du[row + i]);
+              }
               if (HAS_Z)
                 IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (y + acc_y[row + i]));
             }
@@ -583,8 +594,18 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
     float* rw[2] = {w + p.off_r[0], w + p.off_r[1]};
     float* ew[2] = {w + p.off_e[0], w + p.off_e[1]};
     // the state entering every window
-    hipLaunchKernelGGL((bwd_chain_kernel<IO_BF16, SOFTPLUS, false, false>), cgrid, dim3(kLanes), 0, stream, f, p.nwin,
-                       p.run_len, p.nrun, static_cast<const float*>(bc), pw[0], sw[0], rw[0], int(vec));
+    if (!f.conv_w) {
+      hipLaunchKernelGGL((bwd_chain_kernel<IO_BF16, SOFTPLUS, false, false>), cgrid, dim3(kLanes), 0, stream, f,
+                         p.nwin, p.run_len, p.nrun, static_cast<const float*>(bc), pw[0], sw[0], rw[0], int(vec));
+    } else if (f.conv_silu) {
+      hipLaunchKernelGGL((bwd_chain_kernel<IO_BF16, SOFTPLUS, false, false, kConvSilu>), cgrid, dim3(kLanes), 0,
+                         stream, f, p.nwin, p.run_len, p.nrun, static_cast<const float*>(bc), pw[0], sw[0], rw[0],
+                         int(vec));
+    } else {
+      hipLaunchKernelGGL((bwd_chain_kernel<IO_BF16, SOFTPLUS, false, false, kConvLin>), cgrid, dim3(kLanes), 0,
+                         stream, f, p.nwin, p.run_len, p.nrun, static_cast<const float*>(bc), pw[0], sw[0], rw[0],
+                         int(vec));
+    }
     launch_carry(f, p.nrun, rw[0], ew[0], 0, stream);
     mark(2);
     // the adjoint entering every window from the other side

@@ -231,13 +231,13 @@ DirView view_of(const sscan_dir_params* p) {
 
 // ---- backward ----------------------------------------------------------------------
 
-constexpr int kMaxRanges = 32;
+constexpr int kMaxRanges = 64;
 
 struct RangeSet {
   Range r[kMaxRanges];
   int n = 0;
   void add(const void* p, size_t bytes) {
-    if (p && bytes) r[n++] = range_of(p, bytes);
+    if (p && bytes && n < kMaxRanges) r[n++] = range_of(p, bytes);
   }
 };
 
@@ -334,9 +334,195 @@ int run_bwd(const void* u, const void* z, const void* dout, void* du, void* dz, 
   return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
 }
 
+// ---- backward through the front-end convolution ------------------------------------
+
+// Workspace of a backward call through the convolution: the scan backward's own,
+// then u = conv(x) and its gradient du (both float32: u as the fused forward
+// computes it, du unrounded for the convolution's gradients), then the
+// convolution's partial sums (floats); sections 256-byte aligned.
+struct ConvBwdLayout {
+  sscan::BwdPlan plan;
+  size_t off_u, off_du, off_part, bytes;
+};
+
+ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t dim, int64_t len, int ndir, size_t io_esz) {
+  ConvBwdLayout l{};
+  auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+  l.plan = sscan::make_bwd_plan(batch, dim, len, ndir);
+  (void)io_esz;
+  const size_t n32 = size_t(batch) * size_t(dim) * size_t(len) * sizeof(float);
+  l.off_u = up(l.plan.workspace_bytes);
+  l.off_du = l.off_u + up(n32);
+  l.off_part = l.off_du + up(n32);
+  l.bytes = l.off_part + up(sscan::conv_bwd_partial_floats(batch, dim, len) * sizeof(float));
+  return l;
+}
+
+// The scan backward's checks with x in u's place and dx in du's, the convolution's,
+// and its weight and bias gradients (fp32 [dim][width] and [dim], dbias required
+// when conv->bias is given) overlapping nothing the call reads or writes.
+int validate_bwd_conv(const void* x, const sscan_conv_params* conv, const void* z, const void* dout, const void* dx,
+                      const void* dz, const DirView* dirs, const sscan_dir_grads* grads, float* dconv_w,
+                      float* dconv_b, int ndir, int64_t batch, int64_t dim, int64_t len, int64_t dstate,
+                      int io_dtype, int bc_dtype, const void* workspace, size_t workspace_bytes,
+                      ConvBwdLayout* layout, bool* empty) {
+  if (!conv) return SSCAN_ERR_NULL;
+  Sizes sz{};
+  int st = check_sizes(batch, dim, len, dstate, io_dtype, bc_dtype, &sz);
+  if (st != SSCAN_OK) return st;
+  *layout = conv_bwd_layout(batch, dim, len, ndir, sz.io_esz);
+  const bool nonempty = batch > 0 && dim > 0 && len > 0;
+  // the scan backward's own checks, its workspace being the front of ours
+  st = validate_bwd(x, z, dout, dx, dz, dirs, grads, ndir, batch, dim, len, dstate, io_dtype, bc_dtype, workspace,
+                    nonempty ? layout->plan.workspace_bytes : workspace_bytes, &layout->plan, empty);
+  if (st != SSCAN_OK) return st;
+  const size_t io = sz.io_elems * sz.io_esz;
+  st = check_conv(conv, dim, range_of(dx, nonempty ? io : 0));
+  if (st != SSCAN_OK) return st;
+  if (dim > 0 && (!dconv_w || (conv->bias && !dconv_b))) return SSCAN_ERR_NULL;
+  if (!aligned(dconv_w, 4) || !aligned(dconv_b, 4)) return SSCAN_ERR_ALIGN;
+  if (nonempty) {
+    if (!workspace || workspace_bytes < layout->bytes) return SSCAN_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SSCAN_ERR_ALIGN;
+  }
+  // the convolution's gradients against every other buffer of the call
+  const size_t vec = size_t(dim) * 4, bcb = sz.bc_elems * sz.bc_esz;
+  RangeSet all;
+  all.add(x, nonempty ? io : 0);
+  all.add(z, nonempty && z ? io : 0);
+  all.add(dout, nonempty ? io : 0);
+  all.add(dx, nonempty ? io : 0);
+  all.add(dz, nonempty && dz ? io : 0);
+  all.add(conv->weight, vec * size_t(conv->width));
+  all.add(conv->bias, conv->bias ? vec : 0);
+  all.add(workspace, nonempty ? layout->bytes : 0);
+  for (int k = 0; k < ndir; ++k) {
+    all.add(dirs[k].delta, nonempty ? io : 0);
+    all.add(dirs[k].B, bcb);
+    all.add(dirs[k].C, bcb);
+    all.add(dirs[k].A, vec * sscan::kDState);
+    all.add(dirs[k].delta_bias, dirs[k].delta_bias ? vec : 0);
+    all.add(dirs[k].D, dirs[k].D ? vec : 0);
+    all.add(grads[k].ddelta, nonempty ? io : 0);
+    all.add(grads[k].dA, vec * sscan::kDState);
+    all.add(grads[k].dB, bcb);
+    all.add(grads[k].dC, bcb);
+    all.add(grads[k].ddelta_bias, grads[k].ddelta_bias ? vec : 0);
+    all.add(grads[k].dD, grads[k].dD ? vec : 0);
+  }
+  const Range wr = range_of(dconv_w, vec * size_t(conv->width)), br = range_of(dconv_b, dconv_b ? vec : 0);
+  if (overlap(wr, br)) return SSCAN_ERR_ALIAS;
+  for (int i = 0; i < all.n; ++i)
+    if (overlap(wr, all.r[i]) || overlap(br, all.r[i])) return SSCAN_ERR_ALIAS;
+  // the whole workspace (the scan backward checked only its own front part)
+  const Range wsr = range_of(workspace, nonempty ? layout->bytes : 0);
+  for (int i = 0; i < all.n; ++i)
+    if (all.r[i].lo != wsr.lo && overlap(wsr, all.r[i])) return SSCAN_ERR_ALIAS;
+  return SSCAN_OK;
+}
+
+int run_bwd_conv(const void* x, const sscan_conv_params* conv, const void* z, const void* dout, void* dx, void* dz,
+                 const DirView* dirs, const sscan_dir_grads* grads, float* dconv_w, float* dconv_b, int ndir,
+                 int reverse, int softplus, int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                 int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes) {
+  ConvBwdLayout l{};
+  bool empty = false;
+  const int st = validate_bwd_conv(x, conv, z, dout, dx, dz, dirs, grads, dconv_w, dconv_b, ndir, batch, dim, len,
+                                   dstate, io_dtype, bc_dtype, workspace, workspace_bytes, &l, &empty);
+  if (st != SSCAN_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  sscan::ConvBwdArgs c{x, nullptr, dx, conv->weight, conv->bias, dconv_w, dconv_b, conv->width, conv_left(conv),
+                       conv->silu, io_dtype == SSCAN_BF16, batch, dim, len};
+  sscan::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int k = 0; k < ndir; ++k)
+    a.grads[k] = sscan::DirGrads{grads[k].ddelta, grads[k].ddelta_bias, grads[k].dA, grads[k].dB, grads[k].dC,
+                                 grads[k].dD};
+  if (empty) {
+    a.fwd = make_args(x, z, nullptr, dirs, ndir, reverse, softplus, batch, dim, len, io_dtype, bc_dtype);
+    hipError_t e = sscan::launch_bwd_zero(a, s);
+    if (e == hipSuccess && dim > 0) e = sscan::launch_conv1d_bwd(c, nullptr, s);
+    return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+  }
+  float* u = reinterpret_cast<float*>(ws + l.off_u);
+  void* du = ws + l.off_du;
+  // u = conv(x) in float32 (the window pass reads it; the state chain recomputes it
+  // from x, as the fused forward does), the scan's backward at u, then du back
+  // through the convolution
+  const sscan::ConvArgs fa{x, u, conv->weight, conv->bias, conv->width, conv_left(conv), conv->silu,
+                           io_dtype == SSCAN_BF16, batch, dim, len, 1};
+  hipError_t e = sscan::launch_conv1d(fa, s);
+  if (e != hipSuccess) return SSCAN_ERR_HIP;
+  a.fwd = make_args(x, z, nullptr, dirs, ndir, reverse, softplus, batch, dim, len, io_dtype, bc_dtype);
+  a.fwd.conv_w = conv->weight;
+  a.fwd.conv_b = conv->bias;
+  a.fwd.conv_width = conv->width;
+  a.fwd.conv_left = conv_left(conv);
+  a.fwd.conv_silu = conv->silu;
+  a.u32 = u;
+  a.dout = dout;
+  a.du = du;
+  a.dz = dz;
+  a.du_f32 = 1;
+  e = sscan::launch_bwd(a, l.plan, reinterpret_cast<float*>(ws), s);
+  if (e != hipSuccess) return SSCAN_ERR_HIP;
+  c.du = static_cast<const float*>(du);
+  e = sscan::launch_conv1d_bwd(c, reinterpret_cast<float*>(ws + l.off_part), s);
+  return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sscan_bwd_conv(const void* x, const sscan_conv_params* conv, const void* delta, const float* delta_bias,
+                   int softplus, const float* A, const void* B, const void* C, const float* D, const void* z,
+                   const void* dout, void* dx, void* dz, const sscan_dir_grads* grads, float* dconv_w,
+                   float* dconv_b, int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse,
+                   void* stream, int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes) {
+  if (!grads) return SSCAN_ERR_NULL;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  return run_bwd_conv(x, conv, z, dout, dx, dz, &d, grads, dconv_w, dconv_b, 1, reverse, softplus, batch, dim, len,
+                      dstate, stream, io_dtype, bc_dtype, workspace, workspace_bytes);
+}
+
+int sscan_bidir_bwd_conv(const void* x, const sscan_conv_params* conv, const void* z, const void* dout, void* dx,
+                         void* dz, const sscan_dir_params* fwd, const sscan_dir_params* rev,
+                         const sscan_dir_grads* gfwd, const sscan_dir_grads* grev, float* dconv_w, float* dconv_b,
+                         int softplus, int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
+                         int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes) {
+  if (!fwd || !rev || !gfwd || !grev) return SSCAN_ERR_NULL;
+  const DirView d[2] = {view_of(fwd), view_of(rev)};
+  const sscan_dir_grads g[2] = {*gfwd, *grev};
+  return run_bwd_conv(x, conv, z, dout, dx, dz, d, g, dconv_w, dconv_b, 2, 0, softplus, batch, dim, len, dstate,
+                      stream, io_dtype, bc_dtype, workspace, workspace_bytes);
+}
+
+int sscan_validate_bwd_conv(const void* x, const sscan_conv_params* conv, const void* delta, const float* delta_bias,
+                            int softplus, const float* A, const void* B, const void* C, const float* D,
+                            const void* z, const void* dout, const void* dx, const void* dz,
+                            const sscan_dir_grads* grads, const float* dconv_w, const float* dconv_b, int64_t batch,
+                            int64_t dim, int64_t len, int64_t dstate, int reverse, int io_dtype, int bc_dtype,
+                            const void* workspace, size_t workspace_bytes) {
+  (void)softplus;
+  (void)reverse;
+  if (!grads) return SSCAN_ERR_NULL;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  ConvBwdLayout l{};
+  bool empty = false;
+  return validate_bwd_conv(x, conv, z, dout, dx, dz, &d, grads, const_cast<float*>(dconv_w),
+                           const_cast<float*>(dconv_b), 1, batch, dim, len, dstate, io_dtype, bc_dtype, workspace,
+                           workspace_bytes, &l, &empty);
+}
+
+size_t sscan_bwd_conv_workspace_bytes(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int bidir,
+                                      int io_dtype) {
+  Sizes sz{};
+  if (check_sizes(batch, dim, len, dstate, io_dtype, SSCAN_F32, &sz) != SSCAN_OK) return 0;
+  if (batch == 0 || dim == 0 || len == 0) return 0;
+  return conv_bwd_layout(batch, dim, len, bidir ? 2 : 1, sz.io_esz).bytes;
+}
 
 int sscan_fwd(const void* u, const void* delta, const float* delta_bias, int softplus, const float* A,
               const void* B, const void* C, const float* D, const void* z, void* y, int64_t batch, int64_t dim,

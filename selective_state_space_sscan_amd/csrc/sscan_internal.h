@@ -83,12 +83,31 @@ hipError_t launch_multi(const MultiArgs& a, const MultiPlan& p, char* workspace,
 // A standalone depthwise convolution (the same operation as the scan's front-end).
 struct ConvArgs {
   const void* x;
-  void* y;
+  void* y;                  // io dtype, or float32 when y_f32
   const float* w;
   const float* b;           // nullable
   int width, left, silu, io_bf16;
   int64_t batch, dim, len;
+  int y_f32;
 };
+
+// Backward of that convolution: du = dLoss/d(its output) gives dx, and the sums
+// over batch rows and tokens dw [dim][width] and db [dim] (nullable).
+struct ConvBwdArgs {
+  const void* x;
+  const float* du;          // float32 [batch][dim][len]
+  void* dx;
+  const float* w;
+  const float* b;           // nullable
+  float* dw;
+  float* db;                // nullable
+  int width, left, silu, io_bf16;
+  int64_t batch, dim, len;
+};
+
+// Partial sums (floats) of the weight and bias gradients the backward kernel keeps.
+size_t conv_bwd_partial_floats(int64_t batch, int64_t dim, int64_t len);
+hipError_t launch_conv1d_bwd(const ConvBwdArgs& a, float* partials, hipStream_t stream);
 
 // One token of the recurrence from a stored state (single-step decode).
 struct StepArgs {
@@ -128,9 +147,14 @@ struct DirGrads {
 struct BwdArgs {
   ScanArgs fwd;             // the forward call's inputs (y, h0 and h_last unused)
   const void* dout;         // dLoss/dout, [batch][dim][len] io dtype
-  void* du;
+  void* du;                 // io dtype, or float32 when du_f32
   void* dz;                 // written when fwd.z is set
   DirGrads grads[2];
+  int du_f32;               // du stored in float32 whatever the io dtype (for the convolution's backward)
+  // With the convolution in front (fwd.conv_w set, fwd.u holding x): u = conv(x) in
+  // float32, as the fused forward computes it.  The state chain recomputes it from
+  // x itself; the window pass reads it here.
+  const float* u32;
 };
 
 // Backward split into 32-token windows, and its workspace (float offsets):

@@ -318,10 +318,12 @@ hipError_t launch_io(const ScanArgs& a, const Plan& p, float* w, hipStream_t str
 constexpr int kConvRun = 8;
 constexpr int kConvRows = 4;
 
-template <bool IO_BF16, bool SILU>
+template <bool IO_BF16, bool SILU, bool Y_F32 = false>
 __global__ __launch_bounds__(kLanes * kConvRows) void conv1d_kernel(ConvArgs a, int vec) {
   using IO = Io<IO_BF16>;
   using T = typename IO::T;
+  using TY = typename std::conditional<Y_F32, float, T>::type;
+  using IOY = Io<!Y_F32 && IO_BF16>;
   const int64_t r = int64_t(blockIdx.x) * kLanes + threadIdx.x;
   const int64_t t0 = r * kConvRun;  // may be past the row's end: the lane loads and stores nothing
   const bool full = vec && t0 + kConvRun <= a.len;
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(kLanes * kConvRows) void conv1d_kernel(ConvArgs a, 
     for (int64_t b = blockIdx.z; b < a.batch; b += gridDim.z) {
       const int64_t row = b * a.dim + d;
       const T* x = static_cast<const T*>(a.x) + row * a.len;
-      T* y = static_cast<T*>(a.y) + row * a.len;
+      TY* y = static_cast<TY*>(a.y) + row * a.len;
       float xs[kSpan];  // x[t0 - 3 .. t0 + kConvRun], zero outside the row
       if (full) {
         if (IO_BF16) {
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(kLanes * kConvRows) void conv1d_kernel(ConvArgs a, 
         out[j] = SILU ? silu_f32(acc) : acc;
       }
       if (full) {
-        if (IO_BF16) {
+        if (IO_BF16 && !Y_F32) {
           *reinterpret_cast<uint4*>(y + t0) = make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
                                                          pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
         } else {
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(kLanes * kConvRows) void conv1d_kernel(ConvArgs a, 
       } else {
 #pragma unroll
         for (int j = 0; j < kConvRun; ++j)
-          if (t0 + j < a.len) IO::store(y, t0 + j, out[j]);
+          if (t0 + j < a.len) IOY::store(reinterpret_cast<typename IOY::T*>(y), t0 + j, out[j]);
       }
     }
   }
@@ -492,7 +494,15 @@ hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream) {
   // runs start at multiples of 8 tokens: 16-byte aligned when every row is
   const size_t esz = a.io_bf16 ? 2 : 4;
   const int vec = (size_t(a.len) * esz) % 16 == 0 && aligned16(a.x) && aligned16(a.y);
-  if (a.io_bf16) {
+  if (a.io_bf16 && a.y_f32) {
+    // bf16 x, float32 output (the backward's copy of u); float32 rows of 8-token
+    // runs are 16-byte aligned whenever the bf16 ones are
+    if (a.silu) {
+      hipLaunchKernelGGL((conv1d_kernel<true, true, true>), grid, block, 0, stream, a, vec);
+    } else {
+      hipLaunchKernelGGL((conv1d_kernel<true, false, true>), grid, block, 0, stream, a, vec);
+    }
+  } else if (a.io_bf16) {
     if (a.silu) {
       hipLaunchKernelGGL((conv1d_kernel<true, true>), grid, block, 0, stream, a, vec);
     } else {

@@ -36,11 +36,12 @@ CSRC = os.path.join(PKG, "csrc")
 COPY_BYTES = 512 << 20
 COPY_KERNEL = "neg_kernel"  # the calibration kernel (torch.neg), unique in the run
 KERNELS = {"stage_bc_kernel": "stage_bc", "scan_aggregate_kernel": "aggregate", "scan_carry_kernel": "carry",
-           "scan_output_dir_kernel": "output", "scan_output_bidir_kernel": "output"}
+           "scan_output_dir_kernel": "output", "scan_output_bidir_kernel": "output",
+           "scan_short_quad_kernel": "output"}
 
 
 # the files that define the forward scan's kernels (staging, aggregate, carry, output)
-FORWARD_SOURCES = ("sscan_device.h", "sscan_internal.h", "sscan_kernels.hip")
+FORWARD_SOURCES = ("sscan_device.h", "sscan_internal.h", "sscan_kernels.hip", "sscan_short.hip")
 
 
 def kernel_source_hash() -> str:

@@ -85,6 +85,18 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_validate_step.argtypes = [V, V, V, V, I, V, V, V, V, V, V, I64, I64, I64, I, I]
     lib.sscan_validate_step.restype = I
     CPP = ctypes.POINTER(ConvParams)
+    DGP = ctypes.POINTER(DirGrads)
+    lib.sscan_bwd_conv.argtypes = [V, CPP, V, V, I, V, V, V, V, V, V, V, V, DGP, V, V, I64, I64, I64, I64, I, V, I, I,
+                                   V, SZ]
+    lib.sscan_bwd_conv.restype = I
+    lib.sscan_bidir_bwd_conv.argtypes = [V, CPP, V, V, V, V, DP, DP, DGP, DGP, V, V, I, I64, I64, I64, I64, V, I, I, V,
+                                         SZ]
+    lib.sscan_bidir_bwd_conv.restype = I
+    lib.sscan_validate_bwd_conv.argtypes = [V, CPP, V, V, I, V, V, V, V, V, V, V, V, DGP, V, V, I64, I64, I64, I64, I,
+                                            I, I, V, SZ]
+    lib.sscan_validate_bwd_conv.restype = I
+    lib.sscan_bwd_conv_workspace_bytes.argtypes = [I64, I64, I64, I64, I, I]
+    lib.sscan_bwd_conv_workspace_bytes.restype = SZ
     lib.sscan_step_conv.argtypes = [V, V, V, CPP, V, V, I, V, V, V, V, V, V, I64, I64, I64, V, I, I]
     lib.sscan_step_conv.restype = I
     lib.sscan_validate_step_conv.argtypes = [V, V, V, CPP, V, V, I, V, V, V, V, V, V, I64, I64, I64, I, I]
@@ -762,6 +774,88 @@ def bidir_bwd(u, z, dout, fwd: dict, rev: dict, softplus: bool = True,
     if st != 0:
         raise SScanError(st, "sscan_bidir_bwd")
     return {"du": du, "dz": dz, "fwd": gf, "rev": gr}
+
+
+def bwd_conv_workspace_bytes(batch: int, dim: int, length: int, dstate: int = DSTATE, bidir: bool = False,
+                             io_dtype=torch.float32) -> int:
+    return int(load_library().sscan_bwd_conv_workspace_bytes(batch, dim, length, dstate, int(bool(bidir)),
+                                                             _DT_CODE[io_dtype]))
+
+
+def _conv_grads(conv: dict, dim: int, dev):
+    dw = torch.empty((dim, conv["weight"].shape[1]), dtype=torch.float32, device=dev)
+    db = torch.empty(dim, dtype=torch.float32, device=dev) if conv.get("bias") is not None else None
+    return dw, db
+
+
+def bwd_conv(x, conv: dict, delta, A, B, C, dout, D=None, z=None, delta_bias=None, softplus: bool = True,
+             reverse: bool = False, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Backward of ``fwd_conv`` (``sscan_bwd_conv``): the gradients of ``bwd`` with
+    dx in place of du, plus dconv_w [dim, width] and dconv_b [dim] (None without a
+    convolution bias)."""
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.bwd_conv needs CUDA (HIP) tensors")
+    if x.dtype not in _DT_CODE or B.dtype not in _DT_CODE:
+        raise TypeError("x/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = x.shape
+    _check(x, "x", dev)
+    _check(delta, "delta", dev, x.dtype, x.shape)
+    _check(z, "z", dev, x.dtype, x.shape)
+    _check(dout, "dout", dev, x.dtype, x.shape)
+    _check(A, "A", dev, torch.float32, (d, DSTATE))
+    _check(B, "B", dev, None, (b, DSTATE, L))
+    _check(C, "C", dev, B.dtype, (b, DSTATE, L))
+    _check(D, "D", dev, torch.float32, (d,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (d,))
+    cp = _conv_params(conv, d, dev)
+    g, gst = _grads_for(dict(delta=delta, A=A, B=B, C=C, D=D, delta_bias=delta_bias), x)
+    dx = torch.empty_like(x)
+    dz = torch.empty_like(x) if z is not None else None
+    dw, db = _conv_grads(conv, d, dev)
+    nbytes = bwd_conv_workspace_bytes(b, d, L, DSTATE, False, x.dtype)
+    ws, ws_bytes = _workspace(nbytes, dev, workspace)
+    st = lib.sscan_bwd_conv(_ptr(x), ctypes.byref(cp), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A),
+                            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dout), _ptr(dx), _ptr(dz), ctypes.byref(gst),
+                            _ptr(dw), _ptr(db), b, d, L, DSTATE, int(bool(reverse)), _stream(dev), _DT_CODE[x.dtype],
+                            _DT_CODE[B.dtype], _ptr(ws), ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_bwd_conv")
+    return dict(g, dx=dx, dz=dz, dconv_w=dw, dconv_b=db)
+
+
+def bidir_bwd_conv(x, conv: dict, z, dout, fwd: dict, rev: dict, softplus: bool = True,
+                   workspace: Optional[torch.Tensor] = None) -> dict:
+    """Backward of ``bidir_conv`` (``sscan_bidir_bwd_conv``): {"dx", "dz", "dconv_w",
+    "dconv_b", "fwd": {...}, "rev": {...}}."""
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.bidir_bwd_conv needs CUDA (HIP) tensors")
+    if x.dtype not in _DT_CODE or fwd["B"].dtype not in _DT_CODE:
+        raise TypeError("x/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = x.shape
+    _check(x, "x", dev)
+    _check(z, "z", dev, x.dtype, x.shape)
+    _check(dout, "dout", dev, x.dtype, x.shape)
+    pf = _dir(fwd, "fwd", dev, x, fwd["B"].dtype)
+    pr = _dir(rev, "rev", dev, x, fwd["B"].dtype)
+    cp = _conv_params(conv, d, dev)
+    gf, gfs = _grads_for(fwd, x)
+    gr, grs = _grads_for(rev, x)
+    dx = torch.empty_like(x)
+    dz = torch.empty_like(x) if z is not None else None
+    dw, db = _conv_grads(conv, d, dev)
+    nbytes = bwd_conv_workspace_bytes(b, d, L, DSTATE, True, x.dtype)
+    ws, ws_bytes = _workspace(nbytes, dev, workspace)
+    st = lib.sscan_bidir_bwd_conv(_ptr(x), ctypes.byref(cp), _ptr(z), _ptr(dout), _ptr(dx), _ptr(dz),
+                                  ctypes.byref(pf), ctypes.byref(pr), ctypes.byref(gfs), ctypes.byref(grs), _ptr(dw),
+                                  _ptr(db), int(bool(softplus)), b, d, L, DSTATE, _stream(dev), _DT_CODE[x.dtype],
+                                  _DT_CODE[fwd["B"].dtype], _ptr(ws), ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_bidir_bwd_conv")
+    return {"dx": dx, "dz": dz, "dconv_w": dw, "dconv_b": db, "fwd": gf, "rev": gr}
 
 
 def run_inputs(x, softplus: bool = True, out=None, workspace=None, events: Optional[HipEvents] = None) -> torch.Tensor:

@@ -308,6 +308,45 @@ def test_validate_step_conv(lib):
     assert st == ENULL  # rejected before any HIP call
 
 
+def test_validate_bwd_conv(lib):
+    """The backward through the convolution: the scan backward's checks with x and
+    dx in u's and du's places, the convolution's, its weight and bias gradients, and
+    the larger workspace."""
+    f = Fake()
+    f.next = 1 << 45
+    b, d, L = 2, 64, 300
+    ws_need = lib.sscan_bwd_conv_workspace_bytes(b, d, L, 16, 0, 0)
+    assert ws_need > lib.sscan_bwd_workspace_bytes(b, d, L, 16, 0)
+    a = fwd_args(b, d, L)
+    dout, dx, dz = f(b * d * L * 4), f(b * d * L * 4), f(b * d * L * 4)
+    gr = [f(b * d * L * 4), f(d * 4), f(d * 64), f(b * 16 * L * 4), f(b * 16 * L * 4), f(d * 4)]
+    gs = sscan.DirGrads(*gr)
+    wsp = f(ws_need)
+
+    def call(w=True, bias=True, width=4, same=0, dw="ok", db="ok", ws=wsp, ws_bytes=ws_need, xx=None):
+        cw = f(d * width * 4) if w else None
+        cb = f(d * 4) if bias else None
+        cp = sscan.ConvParams(cw, cb, width, same, 1)
+        dwp = f(d * width * 4) if dw == "ok" else dw
+        dbp = f(d * 4) if db == "ok" else db
+        return lib.sscan_validate_bwd_conv(a["u"] if xx is None else xx, ctypes.byref(cp), a["delta"], a["bias"], 1,
+                                           a["A"], a["B"], a["C"], a["D"], a["z"], dout, dx, dz, ctypes.byref(gs),
+                                           dwp, dbp, b, d, L, 16, 0, 0, 0, ws, ws_bytes)
+
+    assert call() == OK
+    assert call(bias=False, db=None) == OK       # no bias: no bias gradient
+    assert call(db=None) == ENULL                # a bias needs its gradient
+    assert call(dw=None) == ENULL
+    assert call(w=False) == ENULL
+    assert call(width=4, same=1) == EUNSUP
+    assert call(ws_bytes=ws_need - 256) == EWS
+    assert call(ws=None, ws_bytes=0) == EWS
+    assert call(dw=dx) == EALIAS                 # a conv gradient overlapping dx
+    assert call(dw=wsp + 1024 * 1024) == EALIAS  # ... or the workspace's back part
+    assert call(db=a["u"]) == EALIAS
+    assert call(xx=None) == OK
+
+
 # --- backward -------------------------------------------------------------------------------
 
 def bwd_call(lib, a, g, dout, du, dz):

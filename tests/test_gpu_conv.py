@@ -118,3 +118,67 @@ def test_fused_equals_conv_then_scan_f32(bidir):
     plain = sscan.run_inputs(xu)
     torch.cuda.synchronize()
     assert torch.equal(fused, plain)
+
+
+# --- backward through the convolution (sscan_bwd_conv, sscan_bidir_bwd_conv) ----------------------
+
+BWD_CONV_CASES = [
+    # name, batch, dim, len, bidir, io, bc, width, same, silu, reverse
+    ("bwd-w4-silu", 2, 64, 100, False, "f32", "f32", 4, False, True, False),
+    ("bwd-w3-rev", 2, 70, 77, False, "f32", "f32", 3, False, False, True),
+    ("bwd-segmented-bf16", 1, 128, 3000, False, "bf16", "f32", 4, False, True, False),
+    ("bwd-bidir-same3", 2, 64, 197, True, "f32", "f32", 3, True, False, False),
+    ("bwd-bidir-bf16", 1, 96, 1003, True, "bf16", "bf16", 4, False, True, False),
+    ("bwd-w1-same", 2, 40, 50, False, "f32", "f32", 1, True, True, False),
+]
+
+
+@pytest.mark.parametrize("name,b,d,L,bidir,io,bc,width,same,silu,reverse", BWD_CONV_CASES,
+                         ids=[c[0] for c in BWD_CONV_CASES])
+def test_bwd_conv_parity(name, b, d, L, bidir, io, bc, width, same, silu, reverse):
+    """Every gradient of the backward through the convolution against the oracle
+    (the scan's backward at u = conv(x), then the convolution's backward).  The
+    kernels recompute u in the I/O dtype, so a bf16 call is held to the bf16 bound
+    in all its gradients; float32 calls to 1e-4."""
+    seed = zlib.crc32(name.encode()) % 10000
+    x = I.make_inputs(b, d, L, bidir=bidir, io_dtype=io, bc_dtype=bc, seed=seed)
+    cp = conv_params(name, d, width, same, silu)
+    rng = np.random.default_rng(seed + 1)
+    dout = torch.from_numpy(rng.standard_normal((b, d, L), dtype=np.float32)).to(x.u.dtype)
+    xd = x.to(DEV)
+    c = dict(weight=cp["weight"].to(DEV), bias=cp["bias"].to(DEV), same=same, silu=silu)
+    mk = lambda p: dict(delta=xd.delta, delta_bias=p.delta_bias, A=p.A, B=p.B, C=p.C, D=p.D)
+    if bidir:
+        r = sscan.bidir_bwd_conv(xd.u, c, xd.z, dout.to(DEV), mk(xd.dirs[0]), mk(xd.dirs[1]))
+        got_dirs = [r["fwd"], r["rev"]]
+    else:
+        p = xd.dirs[0]
+        r = sscan.bwd_conv(xd.u, c, xd.delta, p.A, p.B, p.C, dout.to(DEV), D=p.D, z=xd.z, delta_bias=p.delta_bias,
+                           reverse=reverse)
+        got_dirs = [r]
+    torch.cuda.synchronize()
+    x64 = I.as_f64_dict(x)
+    dirs = [dict(delta=x64["delta"], A=q["A"], B=q["B"], C=q["C"], D=q["D"], delta_bias=q["delta_bias"])
+            for q in x64["dirs"]]
+    ref = oracle.sscan_bwd_conv(x64["u"], I.f64(cp["weight"]), I.f64(cp["bias"]), same, silu, x64["z"], I.f64(dout),
+                                dirs, reverse=reverse, nthreads=NTHREADS)
+    tol = TOL[io]
+    for k in ("dx", "dz", "dconv_w", "dconv_b"):
+        check(r[k], ref[k], tol, f"{name} {k}")
+    for k, (gd, rd) in enumerate(zip(got_dirs, ref["dirs"])):
+        for gname in ("ddelta", "ddelta_bias", "dA", "dB", "dC", "dD"):
+            check(gd[gname], rd[gname], tol, f"{name} dir{k} {gname}")
+
+
+def test_bwd_conv_deterministic():
+    x = I.make_inputs(2, 96, 700, io_dtype="bf16", bc_dtype="bf16", seed=71)
+    cp = conv_params("det", 96, 4, False, True)
+    xd = x.to(DEV)
+    c = dict(weight=cp["weight"].to(DEV), bias=cp["bias"].to(DEV), silu=True)
+    dout = torch.randn(x.u.shape, generator=torch.Generator().manual_seed(5)).to(x.u.dtype).to(DEV)
+    p = xd.dirs[0]
+    run = lambda: sscan.bwd_conv(xd.u, c, xd.delta, p.A, p.B, p.C, dout, D=p.D, z=xd.z, delta_bias=p.delta_bias)
+    a, b = run(), run()
+    torch.cuda.synchronize()
+    for k in ("dx", "dz", "dconv_w", "dconv_b", "dA", "dB"):
+        assert torch.equal(a[k], b[k]), k
