@@ -50,6 +50,8 @@ def _load():
         lib.oracle_sscan_bidir.restype = INT
         lib.oracle_sscan_bwd.argtypes = [P, P, P, P, P, INT, P, P, P, INT, I64, I64, I64, I64, INT]
         lib.oracle_sscan_bwd.restype = INT
+        lib.oracle_sscan_bwd_state.argtypes = [P, P, P, P, P, INT, P, P, P, INT, I64, I64, I64, I64, P, P, P, INT]
+        lib.oracle_sscan_bwd_state.restype = INT
         lib.oracle_conv1d.argtypes = [P, P, P, P, I64, I64, I64, I64, INT, INT]
         lib.oracle_conv1d.restype = INT
         lib.oracle_softplus_f64.argtypes = [ctypes.c_double]
@@ -132,12 +134,16 @@ def sscan_bidir(u, z, fwd: dict, rev: dict, softplus=True, nthreads: int = 1):
 GRAD_NAMES = ("ddelta", "ddelta_bias", "dA", "dB", "dC", "dD")
 
 
-def sscan_bwd(u, z, g, dirs, softplus=True, reverse=False, nthreads: int = 1):
+def sscan_bwd(u, z, g, dirs, softplus=True, reverse=False, nthreads: int = 1, h0=None, dh_last=None,
+              return_dh0=False):
     """Gradients of sum(g * out) for one direction (``dirs`` = [params], scanned
     in reverse if ``reverse``) or two (``dirs`` = [forward, reverse]).  Each params
     dict has delta, A, B, C and optional D, delta_bias.  Returns
     {"du", "dz" (None without z), "dirs": [{ddelta, ddelta_bias, dA, dB, dC, dD}]}
-    in float64; a gradient of an absent optional input is None."""
+    in float64; a gradient of an absent optional input is None.  One direction
+    only: ``h0`` [b, d, N] is the forward's entry state, ``dh_last`` [b, d, N] the
+    gradient reaching its final state, and with ``return_dh0`` the result also holds
+    "dh0", the gradient of the entry state."""
     u = _c64(u)
     b, d, L = u.shape
     z = _c64(z, (b, d, L))
@@ -164,11 +170,17 @@ def sscan_bwd(u, z, g, dirs, softplus=True, reverse=False, nthreads: int = 1):
     ins_a = (P * len(ins))(*[x.value if x is not None else None for x in ins])
     outs_a = (P * len(outs))(*[x.value if x is not None else None for x in outs])
     rev_a = (ctypes.c_int * ndir)(*rev)
-    st = _load().oracle_sscan_bwd(_p(u), _p(z), _p(g), _p(du), _p(dz), ndir, ins_a, rev_a, outs_a,
-                                  int(bool(softplus)), b, d, L, N, int(nthreads))
+    h0 = _c64(h0, (b, d, N))
+    dh_last = _c64(dh_last, (b, d, N))
+    dh0 = np.empty((b, d, N)) if return_dh0 else None
+    st = _load().oracle_sscan_bwd_state(_p(u), _p(z), _p(g), _p(du), _p(dz), ndir, ins_a, rev_a, outs_a,
+                                        int(bool(softplus)), b, d, L, N, _p(h0), _p(dh_last), _p(dh0), int(nthreads))
     if st != 0:
         raise RuntimeError(f"oracle_sscan_bwd failed with status {st}")
-    return {"du": du, "dz": dz, "dirs": res}
+    out = {"du": du, "dz": dz, "dirs": res}
+    if return_dh0:
+        out["dh0"] = dh0
+    return out
 
 
 def conv1d(x, w, bias=None, same=False, silu=False):

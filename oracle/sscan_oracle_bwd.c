@@ -26,6 +26,14 @@
  *   dbias   += ddelta_t                      mu_n = a_k,n lambda_n
  * Sums over tokens and batch rows (dA, dD, dbias) and over channels (dB, dC) are
  * accumulated per thread and added in thread order.
+ *
+ * State I/O (one direction; the forward of sscan_oracle.c with h0 and h_last): the
+ * forward sweep starts from h^-1 = h0 instead of 0, so the first token's previous
+ * state in dA and ddt is h0; the reverse sweep starts from mu = dLoss/dh_last (the
+ * gradient reaching the final state from outside, 0 when absent) instead of 0; and
+ * the gradient of the entry state is what the adjoint carries past the first token
+ * in scan order:  dh0_n = a_0,n lambda^0_n  (the mu left after the sweep; with no
+ * tokens at all, dh0 = dLoss/dh_last, as h_last = h0).
  */
 #include <math.h>
 #include <pthread.h>
@@ -61,6 +69,9 @@ typedef struct {
      * and dB, dC for the batch rows this thread touches [nb][N][len] */
     int64_t b_first, nb;
     double* acc;
+    const double* h0;       /* nullable, [batch, dim, dstate], one direction only */
+    const double* dh_last;  /* nullable, [batch, dim, dstate] */
+    double* dh0;            /* nullable, [batch, dim, dstate] */
     int status;
 } bwd_job;
 
@@ -108,7 +119,8 @@ static void* bwd_rows(void* arg) {
             double* dB = dbias + jb->dim + (b - jb->b_first) * N * L;
             double* dC = dB + jb->nb * N * L;
             /* forward sweep: states after every token (in scan order) and y */
-            for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+            const double* h0 = jb->h0 ? jb->h0 + r * N : NULL;
+            for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[n] : 0.0;
             for (int64_t s = 0; s < L; ++s) {
                 const int64_t t = jb->reverse[k] ? L - 1 - s : s;
                 const double x = dl[t] + bias;
@@ -122,7 +134,7 @@ static void* bwd_rows(void* arg) {
                 ysum[t] += yv;
             }
             /* reverse sweep */
-            for (int64_t n = 0; n < N; ++n) mu[n] = 0.0;
+            for (int64_t n = 0; n < N; ++n) mu[n] = jb->dh_last ? jb->dh_last[r * N + n] : 0.0;
             for (int64_t s = L - 1; s >= 0; --s) {
                 const int64_t t = jb->reverse[k] ? L - 1 - s : s;
                 const double x = dl[t] + bias;
@@ -131,7 +143,7 @@ static void* bwd_rows(void* arg) {
                 dD[d] += dy[t] * u[t];
                 for (int64_t n = 0; n < N; ++n) {
                     const double a = exp(dt * A[n]);
-                    const double hprev = s > 0 ? hist[(s - 1) * N + n] : 0.0;
+                    const double hprev = s > 0 ? hist[(s - 1) * N + n] : (h0 ? h0[n] : 0.0);
                     lam[n] = Cm[n * L + t] * dy[t] + mu[n];
                     dC[n * L + t] += dy[t] * hist[s * N + n];
                     dB[n * L + t] += lam[n] * dt * u[t];
@@ -145,6 +157,8 @@ static void* bwd_rows(void* arg) {
                 if (out[OUT_DDELTA]) out[OUT_DDELTA][r * L + t] = dd;
                 dbias[d] += dd;
             }
+            if (jb->dh0)
+                for (int64_t n = 0; n < N; ++n) jb->dh0[r * N + n] = mu[n];
         }
         if (z && jb->dz) {
             double* dz = jb->dz + r * L;
@@ -170,11 +184,16 @@ done:
  * len], dD [dim] (each nullable: not returned).  du is required, dz is written
  * only when z is given.  The directions' outputs are their own: when two
  * directions share one delta tensor, its gradient is the sum of the two ddelta. */
-int oracle_sscan_bwd(const double* u, const double* z, const double* g, double* du, double* dz, int ndir,
-                     const double* const* dir_in, const int* reverse, double* const* dir_out, int softplus,
-                     int64_t batch, int64_t dim, int64_t len, int64_t dstate, int nthreads) {
+int oracle_sscan_bwd_state(const double* u, const double* z, const double* g, double* du, double* dz, int ndir,
+                           const double* const* dir_in, const int* reverse, double* const* dir_out, int softplus,
+                           int64_t batch, int64_t dim, int64_t len, int64_t dstate, const double* h0,
+                           const double* dh_last, double* dh0, int nthreads) {
     if (batch < 0 || dim < 0 || len < 0 || dstate < 0 || ndir < 1 || ndir > 2) return -2;
+    if ((h0 || dh_last || dh0) && ndir != 1) return -3;
     const int64_t rows = batch * dim, N = dstate;
+    if (dh0 && len == 0) {
+        for (int64_t i = 0; i < rows * N; ++i) dh0[i] = dh_last ? dh_last[i] : 0.0;
+    }
     for (int k = 0; k < ndir; ++k) {
         double* const* out = dir_out + k * N_OUT;
         if (out[OUT_DBIAS]) memset(out[OUT_DBIAS], 0, sizeof(double) * (size_t)dim);
@@ -199,6 +218,7 @@ int oracle_sscan_bwd(const double* u, const double* z, const double* g, double* 
         jb->u = u; jb->z = z; jb->g = g; jb->du = du; jb->dz = dz; jb->ndir = ndir;
         jb->dir_in = dir_in; jb->reverse = reverse; jb->dir_out = dir_out; jb->softplus = softplus;
         jb->batch = batch; jb->dim = dim; jb->len = len; jb->dstate = dstate;
+        jb->h0 = h0; jb->dh_last = dh_last; jb->dh0 = dh0;
         jb->row_begin = rows * i / nthreads;
         jb->row_end = rows * (i + 1) / nthreads;
         if (jb->row_end > jb->row_begin) {
@@ -244,4 +264,12 @@ int oracle_sscan_bwd(const double* u, const double* z, const double* g, double* 
     free(jobs);
     free(th);
     return status;
+}
+
+/* Without state I/O: the entry state and the final state's gradient are zero. */
+int oracle_sscan_bwd(const double* u, const double* z, const double* g, double* du, double* dz, int ndir,
+                     const double* const* dir_in, const int* reverse, double* const* dir_out, int softplus,
+                     int64_t batch, int64_t dim, int64_t len, int64_t dstate, int nthreads) {
+    return oracle_sscan_bwd_state(u, z, g, du, dz, ndir, dir_in, reverse, dir_out, softplus, batch, dim, len, dstate,
+                                  NULL, NULL, NULL, nthreads);
 }

@@ -175,3 +175,119 @@ def test_optional_inputs_absent_and_thread_invariance():
     for k in ("ddelta", "dA", "dB", "dC"):
         np.testing.assert_allclose(one["dirs"][0][k], many["dirs"][0][k], rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(one["du"], many["du"], rtol=1e-13, atol=1e-14)
+
+
+# --- G4: state I/O (the backward of the forward with an entry state h0 and a final
+#         state h_last: Hand-written simplified Mamba2 page, section 5.2; a learned
+#         initial state, Samba page, section 3.2) ------------------------------------------------
+
+def _state_loss(u, z, g, p, h0, gh, reverse):
+    out, hl = oracle.sscan_fwd(u, p["delta"], p["A"], p["B"], p["C"], p["D"], z, p["delta_bias"], reverse=reverse,
+                               h0=h0, return_last_state=True)
+    return float(np.sum(g * out) + np.sum(gh * hl))
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_g4_state_gradients_match_central_differences(reverse):
+    """dh0 (and the gradients of u, delta, A, C with an entry state and a gradient on
+    the final state) against central differences of the forward oracle's
+    sum(g * out) + sum(gh * h_last)."""
+    b, d, L = 2, 3, 8
+    u, z, g, dirs = _inputs(700 + reverse, b, d, L, 1)
+    p = dirs[0]
+    rng = np.random.default_rng(701)
+    h0 = rng.normal(size=(b, d, 16))
+    gh = rng.normal(size=(b, d, 16))
+    got = oracle.sscan_bwd(u, z, g, [p], reverse=reverse, h0=h0, dh_last=gh, return_dh0=True)
+    h = 1e-5
+    checks = []
+    for idx in [(0, 0, 0), (1, 2, 15), (0, 1, 7), (1, 0, 3)]:
+        hp, hm = h0.copy(), h0.copy()
+        hp[idx] += h
+        hm[idx] -= h
+        ref = (_state_loss(u, z, g, p, hp, gh, reverse) - _state_loss(u, z, g, p, hm, gh, reverse)) / (2 * h)
+        checks.append(("dh0", got["dh0"][idx], ref))
+    for name, key, idx in [("du", None, (1, 1, 0)), ("ddelta", "delta", (0, 2, L - 1)), ("dA", "A", (1, 4)),
+                           ("dC", "C", (1, 9, 0))]:
+        def mut(e):
+            if key is None:
+                uu = u.copy()
+                uu[idx] += e
+                return uu, p
+            q = dict(p)
+            arr = q[key].copy()
+            arr[idx] += e
+            q[key] = arr
+            return u, q
+        (up, pp), (um, pm) = mut(h), mut(-h)
+        ref = (_state_loss(up, z, g, pp, h0, gh, reverse) - _state_loss(um, z, g, pm, h0, gh, reverse)) / (2 * h)
+        val = got["du"][idx] if key is None else got["dirs"][0]["d" + key][idx]
+        checks.append((name, val, ref))
+    for name, val, ref in checks:
+        assert abs(val - ref) <= 1e-6 * (1.0 + abs(ref)), (name, val, ref)
+
+
+def test_g4_state_gradients_match_autograd():
+    """PyTorch's reverse mode through the plain recurrence started from a leaf h0,
+    with a loss term on the final state."""
+    b, d, L = 2, 4, 11
+    u, z, g, dirs = _inputs(720, b, d, L, 1)
+    p = dirs[0]
+    rng = np.random.default_rng(721)
+    h0 = rng.normal(size=(b, d, 16))
+    gh = rng.normal(size=(b, d, 16))
+    got = oracle.sscan_bwd(u, z, g, [p], h0=h0, dh_last=gh, return_dh0=True)
+    T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    ut, h0t = T(u), T(h0)
+    pt = {k: T(v) for k, v in p.items()}
+    x = pt["delta"] + pt["delta_bias"][None, :, None]
+    dt = torch.nn.functional.softplus(x)
+    h = h0t
+    ys = []
+    for t in range(L):
+        h = torch.exp(dt[:, :, t, None] * pt["A"][None]) * h + (dt[:, :, t] * ut[:, :, t])[..., None] * pt["B"][:, None, :, t]
+        ys.append((h * pt["C"][:, None, :, t]).sum(-1) + pt["D"][None] * ut[:, :, t])
+    out = torch.stack(ys, -1) * torch.nn.functional.silu(torch.tensor(z))
+    ((out * torch.tensor(g)).sum() + (h * torch.tensor(gh)).sum()).backward()
+    np.testing.assert_allclose(got["dh0"], h0t.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["du"], ut.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["dirs"][0]["dA"], pt["A"].grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["dirs"][0]["ddelta"], pt["delta"].grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_g4_backward_of_pieces_equals_backward_of_the_whole(reverse):
+    """A sequence cut in two pieces, the state handed from the first to the second
+    (forward) and dh0 of the second handed back as dh_last of the first (backward):
+    the pieces' gradients, put together, are the whole sequence's."""
+    b, d, L, m = 2, 3, 17, 6
+    u, z, g, dirs = _inputs(740 + reverse, b, d, L, 1)
+    p = dirs[0]
+    whole = oracle.sscan_bwd(u, z, g, [p], reverse=reverse)
+    first, second = (slice(m, L), slice(0, m)) if reverse else (slice(0, m), slice(m, L))
+    cut = lambda a, s: np.ascontiguousarray(a[..., s])
+    pc = lambda s: dict(p, delta=cut(p["delta"], s), B=cut(p["B"], s), C=cut(p["C"], s))
+    _, hmid = oracle.sscan_fwd(cut(u, first), pc(first)["delta"], p["A"], pc(first)["B"], pc(first)["C"], p["D"],
+                               cut(z, first), p["delta_bias"], reverse=reverse, return_last_state=True)
+    g2 = oracle.sscan_bwd(cut(u, second), cut(z, second), cut(g, second), [pc(second)], reverse=reverse, h0=hmid,
+                          return_dh0=True)
+    g1 = oracle.sscan_bwd(cut(u, first), cut(z, first), cut(g, first), [pc(first)], reverse=reverse,
+                          dh_last=g2["dh0"])
+    join = lambda a1, a2: np.concatenate([a1, a2] if not reverse else [a2, a1], axis=-1)
+    np.testing.assert_allclose(join(g1["du"], g2["du"]), whole["du"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(join(g1["dz"], g2["dz"]), whole["dz"], rtol=1e-11, atol=1e-12)
+    for k in ("ddelta", "dB", "dC"):
+        np.testing.assert_allclose(join(g1["dirs"][0][k], g2["dirs"][0][k]), whole["dirs"][0][k], rtol=1e-11,
+                                   atol=1e-12, err_msg=k)
+    for k in ("dA", "dD", "ddelta_bias"):
+        np.testing.assert_allclose(g1["dirs"][0][k] + g2["dirs"][0][k], whole["dirs"][0][k], rtol=1e-11, atol=1e-12,
+                                   err_msg=k)
+
+
+def test_g4_empty_sequence_passes_the_state_gradient_through():
+    b, d = 2, 3
+    rng = np.random.default_rng(760)
+    gh = rng.normal(size=(b, d, 16))
+    u, z, g, dirs = _inputs(761, b, d, 0, 1)
+    got = oracle.sscan_bwd(u, z, g, dirs, dh_last=gh, h0=rng.normal(size=(b, d, 16)), return_dh0=True)
+    np.testing.assert_array_equal(got["dh0"], gh)
