@@ -257,6 +257,32 @@ SSCAN_API int sscan_bwd(const void* u, const void* delta, const float* delta_bia
               int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse, void* stream,
               int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
 
+/* Backward pass of sscan_fwd_state (one direction with state I/O): sscan_bwd's
+ * arguments and outputs, and
+ *   h0      [batch, dim, dstate] float32, optional: the forward call's entry state
+ *           (NULL = 0);
+ *   dh_last [batch, dim, dstate] float32, optional: dLoss/dh_last, the gradient
+ *           reaching the forward's final state from outside (NULL = 0);
+ *   dh0     [batch, dim, dstate] float32, optional output: dLoss/dh0, the gradient
+ *           of the entry state (NULL = not computed).
+ * The gradients are those of sum(dout * out) + sum(dh_last * h_last).  A learned
+ * initial state (Samba page, section 3.2) takes dh0; a stream trained in pieces
+ * (Hand-written simplified Mamba2 page, section 5.2) runs the pieces' backward in
+ * reverse order, each dh0 passed on as the previous piece's dh_last.  All three
+ * 16-byte aligned; dh0 overlaps nothing else, h0 and dh_last no output.  With
+ * len == 0, dh0 = dh_last.  Workspace: sscan_bwd_workspace_bytes(..., 0). */
+SSCAN_API int sscan_bwd_state(const void* u, const void* delta, const float* delta_bias, int softplus,
+                    const float* A, const void* B, const void* C, const float* D, const void* z, const void* dout,
+                    const float* h0, const float* dh_last, void* du, void* dz, const sscan_dir_grads* grads,
+                    float* dh0, int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse, void* stream,
+                    int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
+SSCAN_API int sscan_validate_bwd_state(const void* u, const void* delta, const float* delta_bias, int softplus,
+                             const float* A, const void* B, const void* C, const float* D, const void* z,
+                             const void* dout, const float* h0, const float* dh_last, const void* du,
+                             const void* dz, const sscan_dir_grads* grads, const float* dh0, int64_t batch,
+                             int64_t dim, int64_t len, int64_t dstate, int reverse, int io_dtype, int bc_dtype,
+                             const void* workspace, size_t workspace_bytes);
+
 /* Backward pass of sscan_bidir: du and dz of the shared u and z, and each
  * direction's parameter gradients in its own sscan_dir_grads (when both directions
  * read one delta tensor, its gradient is gfwd->ddelta + grev->ddelta).

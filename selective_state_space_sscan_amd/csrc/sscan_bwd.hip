@@ -282,8 +282,15 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           nx_s[q] = ch.s[q][chain_sum_index(dir, b, pred[q], d, f.batch, f.dim, nwin)];
         }
       }
+    } else {
+      // one window: the forward's entry state, and the gradient reaching its final state
+      nx_e[0] = f.h0 ? f.h0[(b * f.dim + d) * kDState + n] : 0.0f;
+      nx_e[1] = a.dh_last ? a.dh_last[(b * f.dim + d) * kDState + n] : 0.0f;
     }
   };
+  // the window holding the first token in scan order ends its adjoint sweep with the
+  // gradient of the forward's entry state
+  const bool writes_dh0 = a.dh0 != nullptr && k == (REV ? nwin - 1 : 0);
   if (g_begin < g_end) prefetch(g_begin);
 
   for (int64_t g = g_begin; g < g_end; ++g) {
@@ -344,6 +351,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
     const int slot_off = ((n >> 2) & 3) * kGroup + c;
     float hist[kWin];
     float dA_acc = 0.0f;
+    float mu_end = 0.0f;  // the adjoint past the window's first token in scan order
     auto sweeps = [&](auto full_tag) {
       constexpr bool kFull = decltype(full_tag)::value;
       // A chunk's row sums leave lane n holding token 4 * chunk + ((n >> 2) & 3) (the
@@ -403,6 +411,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
         }
         if (s % kSchedTokens == 0) __builtin_amdgcn_sched_barrier(0);
       }
+      mu_end = mu;
     };
     if (wl == kWin) {
       sweeps(std::integral_constant<bool, true>());
@@ -411,7 +420,10 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
     }
     {
       const int64_t d = g * kGroup + c;
-      if (d < f.dim) part[part_index(dir, b, k, n, d, f.batch, f.dim, nwin)] = dA_acc;
+      if (d < f.dim) {
+        part[part_index(dir, b, k, n, d, f.batch, f.dim, nwin)] = dA_acc;
+        if (writes_dh0) a.dh0[(b * f.dim + d) * kDState + n] = mu_end;
+      }
     }
     __syncthreads();
 
@@ -613,7 +625,10 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
     adj.u = a.dout;
     hipLaunchKernelGGL((bwd_chain_kernel<IO_BF16, SOFTPLUS, HAS_Z, true>), cgrid, dim3(kLanes), 0, stream, adj,
                        p.nwin, p.run_len, p.nrun, static_cast<const float*>(bc), pw[1], sw[1], rw[1], int(vec));
-    launch_carry(f, p.nrun, rw[1], ew[1], 1, stream);
+    // the adjoint chain enters from beyond the last token with the final state's gradient
+    ScanArgs adj_carry = f;
+    adj_carry.h0 = a.dh_last;
+    launch_carry(adj_carry, p.nrun, rw[1], ew[1], 1, stream);
     mark(3);
   }
   const dim3 wgrid(unsigned(f.batch * p.nwin * p.csplit));

@@ -307,18 +307,60 @@ int validate_bwd(const void* u, const void* z, const void* dout, const void* du,
   return SSCAN_OK;
 }
 
+// State I/O of a one-direction backward: h0 and dh_last (inputs) and dh0 (output),
+// [batch][dim][16] float32, 16-byte aligned; dh0 overlaps nothing else of the call.
+int check_bwd_state(const float* h0, const float* dh_last, const float* dh0, const void* u, const void* z,
+                    const void* dout, const void* du, const void* dz, const DirView& p, const sscan_dir_grads& g,
+                    int64_t batch, int64_t dim, int64_t len, int io_dtype, int bc_dtype, const void* workspace,
+                    size_t workspace_bytes) {
+  if (!aligned(h0, 16) || !aligned(dh_last, 16) || !aligned(dh0, 16)) return SSCAN_ERR_ALIGN;
+  Sizes sz{};
+  const int st = check_sizes(batch, dim, len, sscan::kDState, io_dtype, bc_dtype, &sz);
+  if (st != SSCAN_OK) return st;
+  const size_t sbytes = size_t(batch) * size_t(dim) * sscan::kDState * 4;
+  const size_t io = sz.io_elems * sz.io_esz, bcb = sz.bc_elems * sz.bc_esz, vec = size_t(dim) * 4;
+  const Range outr = range_of(dh0, dh0 ? sbytes : 0);
+  const Range others[] = {range_of(h0, h0 ? sbytes : 0), range_of(dh_last, dh_last ? sbytes : 0),
+                          range_of(u, io), range_of(z, z ? io : 0), range_of(dout, io), range_of(du, io),
+                          range_of(dz, dz ? io : 0), range_of(p.delta, io), range_of(p.B, bcb), range_of(p.C, bcb),
+                          range_of(p.A, vec * sscan::kDState), range_of(p.delta_bias, p.delta_bias ? vec : 0),
+                          range_of(p.D, p.D ? vec : 0), range_of(g.ddelta, io), range_of(g.dA, vec * sscan::kDState),
+                          range_of(g.dB, bcb), range_of(g.dC, bcb), range_of(g.ddelta_bias, g.ddelta_bias ? vec : 0),
+                          range_of(g.dD, g.dD ? vec : 0), range_of(workspace, workspace ? workspace_bytes : 0)};
+  for (const Range& r : others)
+    if (overlap(outr, r)) return SSCAN_ERR_ALIAS;
+  // the state inputs are read while the gradients are written
+  const Range outs[] = {range_of(du, io), range_of(dz, dz ? io : 0), range_of(g.ddelta, io),
+                        range_of(g.dA, vec * sscan::kDState), range_of(g.dB, bcb), range_of(g.dC, bcb),
+                        range_of(g.ddelta_bias, g.ddelta_bias ? vec : 0), range_of(g.dD, g.dD ? vec : 0),
+                        range_of(workspace, workspace ? workspace_bytes : 0)};
+  for (const Range& r : outs)
+    if (overlap(range_of(h0, h0 ? sbytes : 0), r) || overlap(range_of(dh_last, dh_last ? sbytes : 0), r))
+      return SSCAN_ERR_ALIAS;
+  return SSCAN_OK;
+}
+
 int run_bwd(const void* u, const void* z, const void* dout, void* du, void* dz, const DirView* dirs,
             const sscan_dir_grads* grads, int ndir, int reverse, int softplus, int64_t batch, int64_t dim,
             int64_t len, int64_t dstate, void* stream, int io_dtype, int bc_dtype, void* workspace,
-            size_t workspace_bytes, void* const* events = nullptr) {
+            size_t workspace_bytes, void* const* events = nullptr, const float* h0 = nullptr,
+            const float* dh_last = nullptr, float* dh0 = nullptr) {
   sscan::BwdPlan plan{};
   bool empty = false;
-  const int st = validate_bwd(u, z, dout, du, dz, dirs, grads, ndir, batch, dim, len, dstate, io_dtype, bc_dtype,
-                              workspace, workspace_bytes, &plan, &empty);
+  int st = validate_bwd(u, z, dout, du, dz, dirs, grads, ndir, batch, dim, len, dstate, io_dtype, bc_dtype,
+                        workspace, workspace_bytes, &plan, &empty);
   if (st != SSCAN_OK) return st;
+  if (h0 || dh_last || dh0) {
+    st = check_bwd_state(h0, dh_last, dh0, u, z, dout, du, dz, dirs[0], grads[0], batch, dim, len, io_dtype,
+                         bc_dtype, workspace, workspace_bytes);
+    if (st != SSCAN_OK) return st;
+  }
   sscan::BwdArgs a;
   std::memset(&a, 0, sizeof(a));
   a.fwd = make_args(u, z, nullptr, dirs, ndir, reverse, softplus, batch, dim, len, io_dtype, bc_dtype);
+  a.fwd.h0 = h0;
+  a.dh_last = dh_last;
+  a.dh0 = dh0;
   a.dout = dout;
   a.du = du;
   a.dz = dz;
@@ -328,9 +370,16 @@ int run_bwd(const void* u, const void* z, const void* dout, void* du, void* dz, 
   hipEvent_t ev[sscan::kBwdProfileEvents] = {};
   if (events)
     for (int i = 0; i < sscan::kBwdProfileEvents; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
-  const hipError_t e = empty ? sscan::launch_bwd_zero(a, static_cast<hipStream_t>(stream))
-                             : sscan::launch_bwd(a, plan, static_cast<float*>(workspace),
-                                                 static_cast<hipStream_t>(stream), events ? ev : nullptr);
+  hipError_t e = empty ? sscan::launch_bwd_zero(a, static_cast<hipStream_t>(stream))
+                       : sscan::launch_bwd(a, plan, static_cast<float*>(workspace), static_cast<hipStream_t>(stream),
+                                           events ? ev : nullptr);
+  if (e == hipSuccess && empty && dh0 && batch > 0 && dim > 0) {
+    // no tokens: the final state is the entry state, so dh0 = dh_last (or zeros)
+    sscan::ScanArgs pass = a.fwd;
+    pass.h0 = dh_last;
+    pass.h_last = dh0;
+    e = sscan::launch_state_passthrough(pass, static_cast<hipStream_t>(stream));
+  }
   return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
 }
 
@@ -706,6 +755,36 @@ int sscan_bwd(const void* u, const void* delta, const float* delta_bias, int sof
   const DirView d{delta, delta_bias, A, B, C, D};
   return run_bwd(u, z, dout, du, dz, &d, grads, 1, reverse, softplus, batch, dim, len, dstate, stream, io_dtype,
                  bc_dtype, workspace, workspace_bytes);
+}
+
+int sscan_bwd_state(const void* u, const void* delta, const float* delta_bias, int softplus, const float* A,
+                    const void* B, const void* C, const float* D, const void* z, const void* dout, const float* h0,
+                    const float* dh_last, void* du, void* dz, const sscan_dir_grads* grads, float* dh0,
+                    int64_t batch, int64_t dim, int64_t len, int64_t dstate, int reverse, void* stream, int io_dtype,
+                    int bc_dtype, void* workspace, size_t workspace_bytes) {
+  if (!grads) return SSCAN_ERR_NULL;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  return run_bwd(u, z, dout, du, dz, &d, grads, 1, reverse, softplus, batch, dim, len, dstate, stream, io_dtype,
+                 bc_dtype, workspace, workspace_bytes, nullptr, h0, dh_last, dh0);
+}
+
+int sscan_validate_bwd_state(const void* u, const void* delta, const float* delta_bias, int softplus,
+                             const float* A, const void* B, const void* C, const float* D, const void* z,
+                             const void* dout, const float* h0, const float* dh_last, const void* du, const void* dz,
+                             const sscan_dir_grads* grads, const float* dh0, int64_t batch, int64_t dim, int64_t len,
+                             int64_t dstate, int reverse, int io_dtype, int bc_dtype, const void* workspace,
+                             size_t workspace_bytes) {
+  (void)softplus;
+  (void)reverse;
+  if (!grads) return SSCAN_ERR_NULL;
+  const DirView d{delta, delta_bias, A, B, C, D};
+  sscan::BwdPlan plan{};
+  bool empty = false;
+  const int st = validate_bwd(u, z, dout, du, dz, &d, grads, 1, batch, dim, len, dstate, io_dtype, bc_dtype,
+                              workspace, workspace_bytes, &plan, &empty);
+  if (st != SSCAN_OK) return st;
+  return check_bwd_state(h0, dh_last, dh0, u, z, dout, du, dz, d, *grads, batch, dim, len, io_dtype, bc_dtype,
+                         workspace, workspace_bytes);
 }
 
 int sscan_bidir_bwd(const void* u, const void* z, const void* dout, void* du, void* dz, const sscan_dir_params* fwd,

@@ -155,6 +155,11 @@ struct BwdArgs {
   // float32, as the fused forward computes it.  The state chain recomputes it from
   // x itself; the window pass reads it here.
   const float* u32;
+  // State I/O (one direction): the forward's entry state is fwd.h0; dh_last
+  // (nullable, [batch][dim][16]) is the gradient reaching its final state, and dh0
+  // (nullable) receives the gradient of the entry state.
+  const float* dh_last;
+  float* dh0;
 };
 
 // Backward split into 32-token windows, and its workspace (float offsets):

@@ -110,6 +110,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_validate_bwd.restype = I
     lib.sscan_validate_bidir_bwd.argtypes = [V, V, V, V, V, DP, DP, DG, DG, I, I64, I64, I64, I64, I, I, V, SZ]
     lib.sscan_validate_bidir_bwd.restype = I
+    lib.sscan_bwd_state.argtypes = [V, V, V, I, V, V, V, V, V, V, V, V, V, V, DG, V, I64, I64, I64, I64, I, V, I, I,
+                                    V, SZ]
+    lib.sscan_bwd_state.restype = I
+    lib.sscan_validate_bwd_state.argtypes = [V, V, V, I, V, V, V, V, V, V, V, V, V, V, DG, V, I64, I64, I64, I64, I,
+                                             I, I, V, SZ]
+    lib.sscan_validate_bwd_state.restype = I
     lib.sscan_bwd_profiled.argtypes = lib.sscan_bwd.argtypes + [V]
     lib.sscan_bwd_profiled.restype = I
     lib.sscan_bidir_bwd_profiled.argtypes = lib.sscan_bidir_bwd.argtypes + [V]
@@ -743,6 +749,43 @@ def bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, softplus: bool
     if st != 0:
         raise SScanError(st, "sscan_bwd")
     return dict(g, du=du, dz=dz)
+
+
+def bwd_state(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, h0=None, dh_last=None,
+              softplus: bool = True, reverse: bool = False, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Backward pass of ``fwd_state`` (``sscan_bwd_state``): the gradients of
+    sum(dout * out) + sum(dh_last * h_last) given the forward's entry state ``h0``;
+    returns ``bwd``'s dict plus "dh0" [batch, dim, 16] f32."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.bwd_state needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or B.dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = u.shape
+    _check(u, "u", dev)
+    _check(delta, "delta", dev, u.dtype, u.shape)
+    _check(z, "z", dev, u.dtype, u.shape)
+    _check(dout, "dout", dev, u.dtype, u.shape)
+    _check(A, "A", dev, torch.float32, (d, DSTATE))
+    _check(B, "B", dev, None, (b, DSTATE, L))
+    _check(C, "C", dev, B.dtype, (b, DSTATE, L))
+    _check(D, "D", dev, torch.float32, (d,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (d,))
+    _check(h0, "h0", dev, torch.float32, (b, d, DSTATE))
+    _check(dh_last, "dh_last", dev, torch.float32, (b, d, DSTATE))
+    g, gst = _grads_for(dict(delta=delta, A=A, B=B, C=C, D=D, delta_bias=delta_bias), u)
+    du = torch.empty_like(u)
+    dz = torch.empty_like(u) if z is not None else None
+    dh0 = torch.empty((b, d, DSTATE), dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(bwd_workspace_bytes(b, d, L, DSTATE, False), dev, workspace)
+    st = lib.sscan_bwd_state(_ptr(u), _ptr(delta), _ptr(delta_bias), int(bool(softplus)), _ptr(A), _ptr(B), _ptr(C),
+                             _ptr(D), _ptr(z), _ptr(dout), _ptr(h0), _ptr(dh_last), _ptr(du), _ptr(dz),
+                             ctypes.byref(gst), _ptr(dh0), b, d, L, DSTATE, int(bool(reverse)), _stream(dev),
+                             _DT_CODE[u.dtype], _DT_CODE[B.dtype], _ptr(ws), ws_bytes)
+    if st != 0:
+        raise SScanError(st, "sscan_bwd_state")
+    return dict(g, du=du, dz=dz, dh0=dh0)
 
 
 def bidir_bwd(u, z, dout, fwd: dict, rev: dict, softplus: bool = True,

@@ -308,6 +308,36 @@ def test_validate_step_conv(lib):
     assert st == ENULL  # rejected before any HIP call
 
 
+def test_validate_bwd_state(lib):
+    """The state backward: the backward's checks plus h0, dh_last (inputs) and dh0
+    (output), 16-byte aligned [batch, dim, 16] float32."""
+    f = Fake()
+    f.next = 1 << 44
+    b, d, L = 2, 64, 300
+    a = fwd_args(b, d, L)
+    dout, du, dz = f(b * d * L * 4), f(b * d * L * 4), f(b * d * L * 4)
+    gs = sscan.DirGrads(f(b * d * L * 4), f(d * 4), f(d * 64), f(b * 16 * L * 4), f(b * 16 * L * 4), f(d * 4))
+    h0, dhl, dh0 = f(b * d * 64), f(b * d * 64), f(b * d * 64)
+    ws = lib.sscan_bwd_workspace_bytes(b, d, L, 16, 0)
+    wsp = f(ws)
+
+    def call(h0=h0, dhl=dhl, dh0=dh0):
+        return lib.sscan_validate_bwd_state(a["u"], a["delta"], a["bias"], 1, a["A"], a["B"], a["C"], a["D"], a["z"],
+                                            dout, h0, dhl, du, dz, ctypes.byref(gs), dh0, b, d, L, 16, 0, 0, 0, wsp,
+                                            ws)
+
+    assert call() == OK
+    assert call(h0=None, dhl=None, dh0=None) == OK
+    assert call(h0=h0 + 4) == EALIGN
+    assert call(dh0=dh0 + 8) == EALIGN
+    assert call(dh0=du) == EALIAS            # dh0 over an output
+    assert call(dh0=h0) == EALIAS            # ... or over the entry state
+    assert call(h0=gs.dB) == EALIAS          # an input under an output
+    assert call(dhl=wsp) == EALIAS
+    assert lib.sscan_validate_bwd_state(a["u"], a["delta"], a["bias"], 1, a["A"], a["B"], a["C"], a["D"], a["z"], dout,
+                                        h0, dhl, du, dz, None, dh0, b, d, L, 16, 0, 0, 0, wsp, ws) == ENULL
+
+
 def test_validate_bwd_conv(lib):
     """The backward through the convolution: the scan backward's checks with x and
     dx in u's and du's places, the convolution's, its weight and bias gradients, and

@@ -186,3 +186,80 @@ def test_bwd_empty_sequence_zeroes_parameter_grads():
     for k in ("dA", "dD", "ddelta_bias"):
         assert torch.count_nonzero(r[k]).item() == 0, k
     assert r["du"].numel() == 0 and r["dB"].numel() == 0
+
+
+# --- state I/O: sscan_bwd_state (entry state h0, gradient of the final state, dh0) ------------
+
+STATE_CASES = [
+    # name, batch, dim, len, io, bc, reverse
+    ("state-one-window", 2, 64, 30, "f32", "f32", False),
+    ("state-many-windows", 2, 96, 1000, "f32", "f32", False),
+    ("state-many-windows-rev", 1, 130, 777, "f32", "f32", True),
+    ("state-bf16", 2, 64, 2000, "bf16", "f32", False),
+    ("state-long-runs", 1, 64, 40000, "f32", "f32", True),
+]
+
+
+def _state_draw(name, b, d, L, io, bc):
+    seed = zlib.crc32(name.encode()) % 10000
+    x = I.make_inputs(b, d, L, io_dtype=io, bc_dtype=bc, seed=seed)
+    rng = np.random.default_rng(seed + 5)
+    h0 = torch.from_numpy(rng.normal(0.0, 1.0, (b, d, 16))).float()
+    dhl = torch.from_numpy(rng.normal(0.0, 1.0, (b, d, 16))).float()
+    return x, make_dout(x, seed + 1), h0, dhl
+
+
+@pytest.mark.parametrize("name,b,d,L,io,bc,reverse", STATE_CASES, ids=[c[0] for c in STATE_CASES])
+def test_bwd_state_parity(name, b, d, L, io, bc, reverse):
+    x, dout, h0, dhl = _state_draw(name, b, d, L, io, bc)
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    r = sscan.bwd_state(xd.u, xd.delta, p.A, p.B, p.C, dout.to(DEV), D=p.D, z=xd.z, delta_bias=p.delta_bias,
+                        h0=h0.to(DEV), dh_last=dhl.to(DEV), reverse=reverse)
+    torch.cuda.synchronize()
+    x64 = I.as_f64_dict(x)
+    q = x64["dirs"][0]
+    ref = oracle.sscan_bwd(x64["u"], x64["z"], I.f64(dout), [dict(delta=x64["delta"], A=q["A"], B=q["B"], C=q["C"],
+                                                                  D=q["D"], delta_bias=q["delta_bias"])],
+                           reverse=reverse, nthreads=NTHREADS, h0=h0.double().numpy(), dh_last=dhl.double().numpy(),
+                           return_dh0=True)
+    check(r["dh0"], ref["dh0"], f"{name} dh0")
+    compare({"du": r["du"], "dz": r["dz"], "dirs": [{k: r[k] for k in GRADS}]}, ref, name)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_bwd_state_pieces_equal_the_whole(reverse):
+    """A sequence trained in two pieces: forward piece by piece with the state handed
+    on, backward piece by piece in reverse order with dh0 handed back as dh_last;
+    the joined gradients match the oracle's gradients of the whole sequence."""
+    b, d, L, m = 2, 96, 1500, 700
+    x, dout, _, _ = _state_draw(f"pieces-{reverse}", b, d, L, "f32", "f32")
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    g = dout.to(DEV)
+    first, second = (slice(m, L), slice(0, m)) if reverse else (slice(0, m), slice(m, L))
+    cut = lambda t, s: t[..., s].contiguous()
+    _, hmid = sscan.fwd_state(cut(xd.u, first), cut(xd.delta, first), p.A, cut(p.B, first), cut(p.C, first), p.D,
+                              cut(xd.z, first), p.delta_bias, reverse=reverse)
+    g2 = sscan.bwd_state(cut(xd.u, second), cut(xd.delta, second), p.A, cut(p.B, second), cut(p.C, second),
+                         cut(g, second), D=p.D, z=cut(xd.z, second), delta_bias=p.delta_bias, h0=hmid, reverse=reverse)
+    g1 = sscan.bwd_state(cut(xd.u, first), cut(xd.delta, first), p.A, cut(p.B, first), cut(p.C, first), cut(g, first),
+                         D=p.D, z=cut(xd.z, first), delta_bias=p.delta_bias, dh_last=g2["dh0"], reverse=reverse)
+    torch.cuda.synchronize()
+    join = lambda a1, a2: torch.cat([a1, a2] if not reverse else [a2, a1], dim=-1)
+    got = {"du": join(g1["du"], g2["du"]), "dz": join(g1["dz"], g2["dz"]),
+           "dirs": [{"ddelta": join(g1["ddelta"], g2["ddelta"]), "dB": join(g1["dB"], g2["dB"]),
+                     "dC": join(g1["dC"], g2["dC"]), "dA": g1["dA"] + g2["dA"], "dD": g1["dD"] + g2["dD"],
+                     "ddelta_bias": g1["ddelta_bias"] + g2["ddelta_bias"]}]}
+    compare(got, oracle_grads(x, dout, reverse=reverse), f"pieces reverse={reverse}")
+
+
+def test_bwd_state_empty_sequence_passes_dh_last():
+    b, d = 2, 70
+    x, _, h0, dhl = _state_draw("state-empty", b, d, 0, "f32", "f32")
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    r = sscan.bwd_state(xd.u, xd.delta, p.A, p.B, p.C, torch.empty_like(xd.u), D=p.D, z=xd.z,
+                        delta_bias=p.delta_bias, h0=h0.to(DEV), dh_last=dhl.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(r["dh0"].cpu(), dhl)
