@@ -730,6 +730,20 @@ BwdPlan make_bwd_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   return p;
 }
 
+bool bwd_plan_fits_grid(const BwdPlan& p, int64_t batch, int64_t dim, int64_t len, int ndir) {
+  constexpr int64_t kMax = (int64_t(1) << 32) - 1;
+  auto fits = [](int64_t blocks, int64_t threads) { return blocks <= kMax / threads; };
+  const int64_t ngroups64 = (dim + 63) / 64;
+  bool ok = fits(int64_t(ndir) * batch * ((len + 63) / 64), 256);     // B/C staging
+  ok = ok && fits(batch * p.nwin * p.csplit, kLanes);                 // window pass
+  if (p.nwin > 1) {
+    ok = ok && fits(batch * p.nrun * ngroups64, kLanes);              // chain passes (blockIdx.y: direction)
+    ok = ok && fits(int64_t(ndir) * batch * kDState * ngroups64, int64_t(kLanes) * carry_parts(p.nrun));
+  }
+  ok = ok && fits((len + 255) / 256, 256);                            // dB/dC sums
+  return ok;
+}
+
 hipError_t launch_bwd_zero(const BwdArgs& a, hipStream_t stream) {
   const ScanArgs& f = a.fwd;
   const int64_t bc_esz = f.bc_bf16 ? 2 : 4;

@@ -122,6 +122,7 @@ int validate(const void* u, const void* z, const void* y, const DirView* dirs, i
   st = check_conv(conv, dim, yr);
   if (st != SSCAN_OK) return st;
   *plan = sscan::make_plan(batch, dim, len, ndir);
+  if (!sscan::plan_fits_grid(*plan, batch, dim, len, ndir)) return SSCAN_ERR_SHAPE;
   if (plan->workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan->workspace_bytes) return SSCAN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return SSCAN_ERR_ALIGN;
@@ -294,6 +295,7 @@ int validate_bwd(const void* u, const void* z, const void* dout, const void* du,
   }
   if (!*empty) {
     *plan = sscan::make_bwd_plan(batch, dim, len, ndir);
+    if (!sscan::bwd_plan_fits_grid(*plan, batch, dim, len, ndir)) return SSCAN_ERR_SHAPE;
     if (!workspace || workspace_bytes < plan->workspace_bytes) return SSCAN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return SSCAN_ERR_ALIGN;
     out.add(workspace, plan->workspace_bytes);
@@ -971,6 +973,10 @@ int validate_multi(const void* u, const void* z, const void* y, const sscan_dir_
   }
   *plan = sscan::make_multi_plan(batch, dim, height, width, kinds, ndirs, io_dtype == SSCAN_BF16,
                                  bc_dtype == SSCAN_BF16);
+  // each family's scan runs one or two directions over the whole map
+  for (int n = 1; n <= 2; ++n)
+    if (!sscan::plan_fits_grid(sscan::make_plan(batch, dim, height * width, n), batch, dim, height * width, n))
+      return SSCAN_ERR_SHAPE;
   if (!workspace || workspace_bytes < plan->workspace_bytes) return SSCAN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return SSCAN_ERR_ALIGN;
   if (overlap(yr, range_of(workspace, plan->workspace_bytes))) return SSCAN_ERR_ALIAS;

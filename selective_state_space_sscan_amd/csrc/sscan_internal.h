@@ -223,6 +223,11 @@ struct Plan {
 
 Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir);
 
+// A dispatch covers fewer than 2^32 work-items per grid dimension (blocks x block
+// size): true when every kernel a call of this plan launches stays below that.
+bool plan_fits_grid(const Plan& p, int64_t batch, int64_t dim, int64_t len, int ndir);
+bool bwd_plan_fits_grid(const BwdPlan& p, int64_t batch, int64_t dim, int64_t len, int ndir);
+
 // Boundaries of the steps of one call: before staging, after staging, after the
 // segment aggregates, after the carry chain, after the output pass.
 constexpr int kProfileEvents = 5;

@@ -447,8 +447,9 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
       seg_len = (len + target_segs - 1) / target_segs;
       seg_len = std::max<int64_t>(kSegAlign, (seg_len + kTile - 1) / kTile * kTile);
     }
-    // keep the block count within a 1-D grid
-    while ((len + seg_len - 1) / seg_len > 1 && batch * ((len + seg_len - 1) / seg_len) * ngroups > (int64_t(1) << 30))
+    // keep the output pass's grid (two-wave blocks) under 2^32 work-items
+    while ((len + seg_len - 1) / seg_len > 1 &&
+           batch * ((len + seg_len - 1) / seg_len) * ngroups * 2 * kLanes >= (int64_t(1) << 32))
       seg_len *= 2;
     p.seg_len = seg_len;
     p.nseg = (len + seg_len - 1) / seg_len;
@@ -478,6 +479,23 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t len, int ndir) {
   p.workspace_bytes =
       (p.bc_floats + p.p_floats + p.s_floats + p.r_floats + p.e_floats + p.park_floats) * sizeof(float);
   return p;
+}
+
+namespace {
+constexpr int64_t kMaxItems = (int64_t(1) << 32) - 1;  // work-items of one grid dimension
+bool fits(int64_t blocks, int64_t threads) { return blocks <= kMaxItems / threads; }
+}  // namespace
+
+bool plan_fits_grid(const Plan& p, int64_t batch, int64_t dim, int64_t len, int ndir) {
+  const int64_t ngroups = (dim + kLanes - 1) / kLanes;
+  bool ok = fits(int64_t(ndir) * batch * ((len + 63) / 64), 256);  // B/C staging
+  if (p.quad) ok = ok && fits(batch * ((dim + 15) / 16), int64_t(ndir) * kLanes);
+  ok = ok && fits(batch * p.nseg * ngroups, int64_t(ndir) * kLanes);  // output pass (also the fallback for a quad plan)
+  if (p.nseg > 1) {
+    ok = ok && fits(batch * p.nrun * ngroups, kLanes);  // aggregate (blockIdx.y: direction)
+    ok = ok && fits(int64_t(ndir) * batch * kDState * ngroups, int64_t(kLanes) * carry_parts(p.nrun));
+  }
+  return ok;
 }
 
 hipError_t launch_scan(const ScanArgs& a, const Plan& p, float* ws, hipStream_t stream, hipEvent_t const* events) {

@@ -114,6 +114,18 @@ def test_validate_fwd_aliasing(lib):
     assert call_validate_fwd(lib, dict(a, y=a["B"])) == EALIAS
 
 
+def test_grids_stay_under_2_32_work_items(lib):
+    """A dispatch covers fewer than 2^32 work-items per grid dimension: a call whose
+    kernels would need more is refused before any launch (SSCAN_ERR_SHAPE), a call
+    just inside is accepted.  B/C staging runs 256 threads per 64 tokens of each
+    batch row: batch 2^26 x len 1 needs 2^34; batch 2^23 needs 2^31."""
+    for batch, expect in ((1 << 26, ESHAPE), (1 << 23, OK)):
+        a = fwd_args(batch, 64, 1, io=1, bc=1)
+        assert call_validate_fwd(lib, dict(a, ws=1 << 60, ws_bytes=1 << 62)) == expect, batch
+    # the same bound through batch x len: 2^16 rows of 2^16 tokens
+    assert call_validate_fwd(lib, dict(fwd_args(1 << 16, 64, 1 << 16), ws=1 << 60, ws_bytes=1 << 62)) == ESHAPE
+
+
 def test_empty_call_is_ok_even_without_pointers(lib):
     a = fwd_args(0, 64, 32, u=None, y=None, delta=None)
     assert call_validate_fwd(lib, a) == OK
