@@ -89,3 +89,50 @@ def scan_multi(u, z, dirs, kinds, h, w, index=None, softplus=True, nthreads=1):
         zz = np.asarray(z, np.float64)
         total = total * (zz / (1.0 + np.exp(-zz)))
     return total
+
+
+def scan_multi_bwd(u, z, g, dirs, kinds, h, w, index=None, softplus=True, nthreads=1):
+    """Gradients of sum(g * scan_multi(u, z, dirs, kinds, h, w, index)) (fp64).
+
+    The chain rule through the sum and the gate: with s the sum of the directions'
+    outputs, out = s * silu(z), so ds = g * silu(z) reaches every direction's output
+    and dz = g * s * silu'(z).  Each direction's gradients are the one-direction
+    backward (oracle.sscan_bwd, no gate) of its inputs gathered into its visiting
+    order, with ds gathered the same way; they are put back at the tokens'
+    positions (the gather's transpose: a permutation, so position o[i] receives
+    visit step i).  du sums over the directions; the parameter gradients are per
+    direction.  ``index`` must be a permutation of the tokens.  Returns
+    {"du", "dz" (None without z), "dirs": [{ddelta, ddelta_bias, dA, dB, dC, dD}]}."""
+    u = np.asarray(u, np.float64)
+    b, d, L = u.shape
+    if L != h * w:
+        raise ValueError("len must be height * width")
+    g = np.asarray(g, np.float64)
+    dz = None
+    if z is not None:
+        zz = np.asarray(z, np.float64)
+        sig = 1.0 / (1.0 + np.exp(-zz))
+        s = scan_multi(u, None, dirs, kinds, h, w, index, softplus=softplus, nthreads=nthreads)
+        dz = g * s * (sig * (1.0 + zz * (1.0 - sig)))
+        ds = g * (zz * sig)
+    else:
+        ds = g
+    du = np.zeros((b, d, L))
+    grads = []
+    for p, kind in zip(dirs, kinds):
+        o = visit_order(kind, h, w, index)
+        if not np.array_equal(np.sort(o), np.arange(L)):
+            raise ValueError("the index order must be a permutation of the tokens")
+        gat = lambda a: np.ascontiguousarray(np.asarray(a, np.float64)[..., o])
+        q = dict(delta=gat(p["delta"]), A=p["A"], B=gat(p["B"]), C=gat(p["C"]), D=p.get("D"),
+                 delta_bias=p.get("delta_bias"))
+        r = oracle.sscan_bwd(gat(u), None, gat(ds), [q], softplus=softplus, nthreads=nthreads)
+        du[..., o] += r["du"]
+        gd = r["dirs"][0]
+        out = dict(gd)
+        for name in ("ddelta", "dB", "dC"):
+            back = np.empty_like(gd[name])
+            back[..., o] = gd[name]
+            out[name] = back
+        grads.append(out)
+    return {"du": du, "dz": dz, "dirs": grads}

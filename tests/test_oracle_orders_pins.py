@@ -104,3 +104,119 @@ def test_clockwise_first_moves():
     o = orders.spiral_order(5, 5)
     rc = [(t // 5, t % 5) for t in o[:4]]
     assert rc == [(2, 2), (2, 3), (3, 3), (3, 2)]
+
+
+# --- backward along several orders ---------------------------------------------------------------
+
+def _torch_multi(u, z, dirs, kinds, h, w, index, softplus=True):
+    """The forward definition in fp64 torch ops: every direction walks its visiting
+    order token by token (its own recurrence, no gathered copies), writes each
+    output at the token it visits, the outputs are summed and gated."""
+    import torch
+    b, d, L = u.shape
+    total = torch.zeros_like(u)
+    for p, kind in zip(dirs, kinds):
+        if kind in (orders.ROW, orders.ROW_REV):
+            steps = [t for t in range(L)]
+        elif kind in (orders.COL, orders.COL_REV):
+            steps = [r * w + c for c in range(w) for r in range(h)]
+        else:
+            steps = [int(t) for t in index]
+        if kind % 2 == 1:
+            steps = steps[::-1]
+        x = p["delta"] + p["delta_bias"][None, :, None]
+        dt = torch.nn.functional.softplus(x) if softplus else x
+        hs = torch.zeros(b, d, p["A"].shape[1], dtype=torch.float64)
+        cols = [None] * L
+        for t in steps:
+            hs = torch.exp(dt[:, :, t, None] * p["A"][None]) * hs + (dt[:, :, t] * u[:, :, t])[..., None] * \
+                p["B"][:, None, :, t]
+            cols[t] = (hs * p["C"][:, None, :, t]).sum(-1) + p["D"][None] * u[:, :, t]
+        total = total + torch.stack(cols, -1)
+    return total * torch.nn.functional.silu(z) if z is not None else total
+
+
+@pytest.mark.parametrize("kinds,gate", [
+    ((orders.ROW, orders.ROW_REV, orders.COL, orders.COL_REV, orders.INDEX, orders.INDEX_REV), True),
+    ((orders.COL, orders.INDEX_REV), False),
+    ((orders.COL_REV,), True),
+])
+def test_multi_bwd_matches_autograd(kinds, gate):
+    """Every gradient of the multi-order backward against PyTorch's reverse-mode
+    differentiation of the token-by-token definition above (a library routine that
+    shares nothing with the gather/put-back of the oracle): a wrong put-back index,
+    a transposed column order or a gate applied per direction fails here."""
+    import torch
+    rng = np.random.default_rng(50 + len(kinds))
+    b, d, h, w = 2, 3, 3, 5
+    L = h * w
+    perm = np.asarray(orders.spiral_order(h, w))
+    u, z, g = (rng.normal(size=(b, d, L)) for _ in range(3))
+    dirs = [_params(rng, b, d, L) for _ in kinds]
+    got = orders.scan_multi_bwd(u, z if gate else None, g, dirs, list(kinds), h, w, index=perm)
+    T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    ut, zt = T(u), T(z)
+    dts = [{k: T(v) for k, v in p.items()} for p in dirs]
+    out = _torch_multi(ut, zt if gate else None, dts, kinds, h, w, perm)
+    (out * torch.tensor(g)).sum().backward()
+    np.testing.assert_allclose(got["du"], ut.grad.numpy(), rtol=1e-10, atol=1e-12)
+    if gate:
+        np.testing.assert_allclose(got["dz"], zt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    else:
+        assert got["dz"] is None
+    keys = {"ddelta": "delta", "ddelta_bias": "delta_bias", "dA": "A", "dB": "B", "dC": "C", "dD": "D"}
+    for k in range(len(kinds)):
+        for gname, pname in keys.items():
+            ref = dts[k][pname].grad.numpy()
+            np.testing.assert_allclose(got["dirs"][k][gname], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max(),
+                                       err_msg=f"dir{k}.{gname}")
+
+
+def test_multi_bwd_matches_central_differences():
+    """A sample of entries against central differences of the forward oracle
+    scan_multi (pinned above), four directions with a gate."""
+    rng = np.random.default_rng(61)
+    b, d, h, w = 1, 2, 4, 3
+    L = h * w
+    kinds = [orders.ROW_REV, orders.COL, orders.INDEX, orders.INDEX_REV]
+    perm = rng.permutation(L)
+    u, z, g = (rng.normal(size=(b, d, L)) for _ in range(3))
+    dirs = [_params(rng, b, d, L) for _ in kinds]
+    got = orders.scan_multi_bwd(u, z, g, dirs, kinds, h, w, index=perm)
+    loss = lambda uu, zz, dd: float(np.sum(g * orders.scan_multi(uu, zz, dd, kinds, h, w, index=perm)))
+    e = 1e-5
+    for idx in ((0, 0, 0), (0, 1, 7), (0, 1, 11)):
+        for name, arr in (("du", u), ("dz", z)):
+            hi, lo = arr.copy(), arr.copy()
+            hi[idx] += e
+            lo[idx] -= e
+            args = lambda a: (a, z, dirs) if name == "du" else (u, a, dirs)
+            ref = (loss(*args(hi)) - loss(*args(lo))) / (2 * e)
+            assert abs(got[name][idx] - ref) <= 1e-6 * (1 + abs(ref)), (name, idx)
+    for k in range(len(kinds)):
+        for gname, pname, idx in (("ddelta", "delta", (0, 1, 5)), ("dB", "B", (0, 3, 9)), ("dC", "C", (0, 15, 2)),
+                                  ("dA", "A", (1, 4)), ("dD", "D", (0,)), ("ddelta_bias", "delta_bias", (1,))):
+            def mut(sign, k=k, pname=pname, idx=idx):
+                nd = [dict(p) for p in dirs]
+                arr = nd[k][pname].copy()
+                arr[idx] += sign * e
+                nd[k][pname] = arr
+                return loss(u, z, nd)
+            ref = (mut(1) - mut(-1)) / (2 * e)
+            assert abs(got["dirs"][k][gname][idx] - ref) <= 1e-6 * (1 + abs(ref)), (k, gname, idx)
+
+
+def test_multi_bwd_rows_are_the_bidirectional_backward():
+    """Rows forward + reverse: the gated bidirectional backward of the C oracle."""
+    rng = np.random.default_rng(62)
+    b, d, h, w = 2, 2, 3, 4
+    L = h * w
+    u, z, g = (rng.normal(size=(b, d, L)) for _ in range(3))
+    dirs = [_params(rng, b, d, L) for _ in range(2)]
+    got = orders.scan_multi_bwd(u, z, g, dirs, [orders.ROW, orders.ROW_REV], h, w)
+    ref = oracle.sscan_bwd(u, z, g, dirs)
+    for name in ("du", "dz"):
+        np.testing.assert_allclose(got[name], ref[name], rtol=1e-12, atol=1e-13)
+    for k in range(2):
+        for gname in ("ddelta", "ddelta_bias", "dA", "dB", "dC", "dD"):
+            np.testing.assert_allclose(got["dirs"][k][gname], ref["dirs"][k][gname], rtol=1e-12, atol=1e-12)
