@@ -293,6 +293,37 @@ SSCAN_API int sscan_bidir_bwd(const void* u, const void* z, const void* dout, vo
                     int64_t batch, int64_t dim, int64_t len, int64_t dstate, void* stream,
                     int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes);
 
+/* Backward pass of sscan_multi (Mamba in the YOLO26 backbone page, sections 1.2,
+ * 2.2 and 4.4, and Samba page, section 3.1, for the orders; Reproducing Vision
+ * Mamba page, section 1.3: the scan block is trained with hand-written gradients).
+ * Given dout [batch, dim, height*width] io_dtype for the output of sscan_multi with
+ * the same inputs, writes du (required) and dz (required when z is given) in the
+ * token layout, and for every direction k its own grads[k] (sscan_dir_grads;
+ * ddelta, dB, dC in the token layout): the exact gradients of sum(dout * out) up to
+ * float32 rounding.  Through the single gate, dout * silu(z) reaches every
+ * direction's output and dz = dout * (sum_k scan_k) * silu'(z); each direction's
+ * gradients are those of its own scan along its order; du sums them over the
+ * directions in float32 and is rounded once.  index must be a permutation of the
+ * tokens (the gradients of any other index are unspecified).  When two directions
+ * read one tensor (a shared delta), its gradient is the sum of theirs.  Results
+ * are bitwise reproducible.  Workspace: sscan_multi_bwd_workspace_bytes(...) bytes,
+ * 256-byte aligned.  Outputs must not overlap each other, any input or the
+ * workspace.  An empty call writes zeros to the parameter gradients that have
+ * elements. */
+SSCAN_API int sscan_multi_bwd(const void* u, const void* z, const void* dout, void* du, void* dz,
+                    const sscan_dir_params* dirs, const sscan_dir_grads* grads, const int* kinds, int ndirs,
+                    const int32_t* index, int softplus, int64_t batch, int64_t dim, int64_t height,
+                    int64_t width, int64_t dstate, void* stream, int io_dtype, int bc_dtype, void* workspace,
+                    size_t workspace_bytes);
+SSCAN_API int sscan_validate_multi_bwd(const void* u, const void* z, const void* dout, const void* du,
+                             const void* dz, const sscan_dir_params* dirs, const sscan_dir_grads* grads,
+                             const int* kinds, int ndirs, const int32_t* index, int softplus, int64_t batch,
+                             int64_t dim, int64_t height, int64_t width, int64_t dstate, int io_dtype,
+                             int bc_dtype, const void* workspace, size_t workspace_bytes);
+SSCAN_API size_t sscan_multi_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width,
+                                       int64_t dstate, const int* kinds, int ndirs, int io_dtype,
+                                       int bc_dtype);
+
 /* Backward of sscan_fwd_conv / sscan_bidir_conv: the scan's gradients taken at
  * u = conv(x), and du carried back through the convolution (Reproducing Vision
  * Mamba page, section 1.3: the block is trained with hand-written gradients;

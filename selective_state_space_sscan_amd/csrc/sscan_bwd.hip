@@ -451,7 +451,13 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
               } else {
                 IO::store(static_cast<T*>(a.du), row + i, du);
               }
-              if (HAS_Z) IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * y);
+              if (HAS_Z) {
+                if (a.dz_f32) {
+                  static_cast<float*>(a.dz)[row + i] = sTok[QDZ][i][cc] * y;
+                } else {
+                  IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * y);
+                }
+              }
             } else if (OUT == kFirst) {
               acc_du[row + i] = du;
               if (HAS_Z) acc_y[row + i] = y;
@@ -461,8 +467,13 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
               } else {
                 IO::store(static_cast<T*>(a.du), row + i, du + acc_du[row + i]);
               }
-              if (HAS_Z)
-                IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (y + acc_y[row + i]));
+              if (HAS_Z) {
+                if (a.dz_f32) {
+                  static_cast<float*>(a.dz)[row + i] = sTok[QDZ][i][cc] * (y + acc_y[row + i]);
+                } else {
+                  IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (y + acc_y[row + i]));
+                }
+              }
             }
           }
         }

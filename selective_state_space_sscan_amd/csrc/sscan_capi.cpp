@@ -242,6 +242,45 @@ struct RangeSet {
   }
 };
 
+// One direction of a backward call: alignment of its parameters and gradients,
+// and their ranges (gradients as outputs, parameters as inputs when not empty).
+int add_bwd_dir(const DirView& p, const sscan_dir_grads& g, const Sizes& sz, int64_t dim, bool empty, RangeSet* in,
+                RangeSet* out) {
+  const size_t io = sz.io_elems * sz.io_esz, bcb = sz.bc_elems * sz.bc_esz, vec = size_t(dim) * 4;
+  if (!aligned(p.A, 4) || !aligned(p.delta_bias, 4) || !aligned(p.D, 4) || !aligned(g.dA, 4) ||
+      !aligned(g.ddelta_bias, 4) || !aligned(g.dD, 4) || !aligned(g.dB, sz.bc_esz) || !aligned(g.dC, sz.bc_esz))
+    return SSCAN_ERR_ALIGN;
+  out->add(g.dA, vec * sscan::kDState);
+  out->add(g.ddelta_bias, vec);
+  out->add(g.dD, vec);
+  out->add(g.dB, bcb);
+  out->add(g.dC, bcb);
+  if (!empty) {
+    if (!aligned(p.delta, sz.io_esz) || !aligned(p.B, sz.bc_esz) || !aligned(p.C, sz.bc_esz) ||
+        !aligned(g.ddelta, sz.io_esz))
+      return SSCAN_ERR_ALIGN;
+    in->add(p.delta, io);
+    in->add(p.B, bcb);
+    in->add(p.C, bcb);
+    in->add(p.A, vec * sscan::kDState);
+    in->add(p.delta_bias, vec);
+    in->add(p.D, vec);
+    out->add(g.ddelta, io);
+  }
+  return SSCAN_OK;
+}
+
+// Outputs overlap neither each other nor any input.
+int disjoint(const RangeSet& in, const RangeSet& out) {
+  for (int i = 0; i < out.n; ++i) {
+    for (int j = 0; j < in.n; ++j)
+      if (overlap(out.r[i], in.r[j])) return SSCAN_ERR_ALIAS;
+    for (int j = i + 1; j < out.n; ++j)
+      if (overlap(out.r[i], out.r[j])) return SSCAN_ERR_ALIAS;
+  }
+  return SSCAN_OK;
+}
+
 // Checks a backward call; on success fills *plan and *empty.
 int validate_bwd(const void* u, const void* z, const void* dout, const void* du, const void* dz, const DirView* dirs,
                  const sscan_dir_grads* grads, int ndir, int64_t batch, int64_t dim, int64_t len, int64_t dstate,
@@ -254,7 +293,7 @@ int validate_bwd(const void* u, const void* z, const void* dout, const void* du,
   for (int k = 0; k < ndir; ++k)
     if ((dim > 0 && !grads[k].dA) || (sz.bc_elems > 0 && (!grads[k].dB || !grads[k].dC))) return SSCAN_ERR_NULL;
   *empty = (batch == 0 || dim == 0 || len == 0);
-  const size_t io = sz.io_elems * sz.io_esz, bcb = sz.bc_elems * sz.bc_esz, vec = size_t(dim) * 4;
+  const size_t io = sz.io_elems * sz.io_esz;
   RangeSet in, out;
   if (!*empty) {
     if (!u || !dout || !du || (z && !dz)) return SSCAN_ERR_NULL;
@@ -270,28 +309,8 @@ int validate_bwd(const void* u, const void* z, const void* dout, const void* du,
     if (z) out.add(dz, io);
   }
   for (int k = 0; k < ndir; ++k) {
-    const DirView& p = dirs[k];
-    const sscan_dir_grads& g = grads[k];
-    if (!aligned(p.A, 4) || !aligned(p.delta_bias, 4) || !aligned(p.D, 4) || !aligned(g.dA, 4) ||
-        !aligned(g.ddelta_bias, 4) || !aligned(g.dD, 4) || !aligned(g.dB, sz.bc_esz) || !aligned(g.dC, sz.bc_esz))
-      return SSCAN_ERR_ALIGN;
-    out.add(g.dA, vec * sscan::kDState);
-    out.add(g.ddelta_bias, vec);
-    out.add(g.dD, vec);
-    out.add(g.dB, bcb);
-    out.add(g.dC, bcb);
-    if (!*empty) {
-      if (!aligned(p.delta, sz.io_esz) || !aligned(p.B, sz.bc_esz) || !aligned(p.C, sz.bc_esz) ||
-          !aligned(g.ddelta, sz.io_esz))
-        return SSCAN_ERR_ALIGN;
-      in.add(p.delta, io);
-      in.add(p.B, bcb);
-      in.add(p.C, bcb);
-      in.add(p.A, vec * sscan::kDState);
-      in.add(p.delta_bias, vec);
-      in.add(p.D, vec);
-      out.add(g.ddelta, io);
-    }
+    st = add_bwd_dir(dirs[k], grads[k], sz, dim, *empty, &in, &out);
+    if (st != SSCAN_OK) return st;
   }
   if (!*empty) {
     *plan = sscan::make_bwd_plan(batch, dim, len, ndir);
@@ -300,13 +319,7 @@ int validate_bwd(const void* u, const void* z, const void* dout, const void* du,
     if (!aligned(workspace, 16)) return SSCAN_ERR_ALIGN;
     out.add(workspace, plan->workspace_bytes);
   }
-  for (int i = 0; i < out.n; ++i) {
-    for (int j = 0; j < in.n; ++j)
-      if (overlap(out.r[i], in.r[j])) return SSCAN_ERR_ALIAS;
-    for (int j = i + 1; j < out.n; ++j)
-      if (overlap(out.r[i], out.r[j])) return SSCAN_ERR_ALIAS;
-  }
-  return SSCAN_OK;
+  return disjoint(in, out);
 }
 
 // State I/O of a one-direction backward: h0 and dh_last (inputs) and dh0 (output),
@@ -1038,6 +1051,144 @@ size_t sscan_multi_workspace_bytes(int64_t batch, int64_t dim, int64_t height, i
   if (batch == 0 || dim == 0 || height * width == 0) return 0;
   return sscan::make_multi_plan(batch, dim, height, width, kinds, ndirs, io_dtype == SSCAN_BF16,
                                 bc_dtype == SSCAN_BF16)
+      .workspace_bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// A multi-order backward call: the forward's sizes, kinds and parameters, the
+// backward's gradient buffers (every direction's, per direction), and the
+// workspace.  Outputs overlap nothing else; inputs may overlap each other.
+int validate_multi_bwd(const void* u, const void* z, const void* dout, const void* du, const void* dz,
+                       const sscan_dir_params* dirs, const sscan_dir_grads* grads, const int* kinds, int ndirs,
+                       const int32_t* index, int64_t batch, int64_t dim, int64_t height, int64_t width,
+                       int64_t dstate, int io_dtype, int bc_dtype, const void* workspace, size_t workspace_bytes,
+                       sscan::MultiBwdPlan* plan, bool* empty) {
+  if (height < 0 || width < 0) return SSCAN_ERR_SHAPE;
+  if (height > 0 && width > (int64_t(1) << 40) / height) return SSCAN_ERR_SHAPE;
+  const int64_t len = height * width;
+  Sizes sz{};
+  int st = check_sizes(batch, dim, len, dstate, io_dtype, bc_dtype, &sz);
+  if (st != SSCAN_OK) return st;
+  st = check_kinds(kinds, ndirs, index);
+  if (st != SSCAN_OK) return st;
+  if (!dirs || !grads) return SSCAN_ERR_NULL;
+  for (int k = 0; k < ndirs; ++k)
+    if ((dim > 0 && !grads[k].dA) || (sz.bc_elems > 0 && (!grads[k].dB || !grads[k].dC))) return SSCAN_ERR_NULL;
+  *empty = (batch == 0 || dim == 0 || len == 0);
+  const size_t io = sz.io_elems * sz.io_esz;
+  RangeSet in, out;
+  if (!*empty) {
+    if (!u || !dout || !du || (z && !dz)) return SSCAN_ERR_NULL;
+    for (int k = 0; k < ndirs; ++k)
+      if (!dirs[k].delta || !dirs[k].A || !dirs[k].B || !dirs[k].C || !grads[k].ddelta) return SSCAN_ERR_NULL;
+    const void* io_ptrs[] = {u, z, dout, du, dz};
+    for (const void* q : io_ptrs)
+      if (!aligned(q, sz.io_esz)) return SSCAN_ERR_ALIGN;
+    if (!aligned(index, 4)) return SSCAN_ERR_ALIGN;
+    in.add(u, io);
+    in.add(z, io);
+    in.add(dout, io);
+    in.add(index, size_t(len) * 4);
+    out.add(du, io);
+    if (z) out.add(dz, io);
+  }
+  for (int k = 0; k < ndirs; ++k) {
+    st = add_bwd_dir(view_of(&dirs[k]), grads[k], sz, dim, *empty, &in, &out);
+    if (st != SSCAN_OK) return st;
+  }
+  if (!*empty) {
+    // each family's backward runs one or two directions over the whole map
+    for (int n = 1; n <= 2; ++n)
+      if (!sscan::bwd_plan_fits_grid(sscan::make_bwd_plan(batch, dim, len, n), batch, dim, len, n))
+        return SSCAN_ERR_SHAPE;
+    *plan = sscan::make_multi_bwd_plan(batch, dim, height, width, kinds, ndirs, io_dtype == SSCAN_BF16,
+                                       bc_dtype == SSCAN_BF16);
+    if (!workspace || workspace_bytes < plan->workspace_bytes) return SSCAN_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SSCAN_ERR_ALIGN;
+    out.add(workspace, plan->workspace_bytes);
+  }
+  return disjoint(in, out);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sscan_validate_multi_bwd(const void* u, const void* z, const void* dout, const void* du, const void* dz,
+                             const sscan_dir_params* dirs, const sscan_dir_grads* grads, const int* kinds, int ndirs,
+                             const int32_t* index, int softplus, int64_t batch, int64_t dim, int64_t height,
+                             int64_t width, int64_t dstate, int io_dtype, int bc_dtype, const void* workspace,
+                             size_t workspace_bytes) {
+  (void)softplus;
+  sscan::MultiBwdPlan plan{};
+  bool empty = false;
+  return validate_multi_bwd(u, z, dout, du, dz, dirs, grads, kinds, ndirs, index, batch, dim, height, width, dstate,
+                            io_dtype, bc_dtype, workspace, workspace_bytes, &plan, &empty);
+}
+
+int sscan_multi_bwd(const void* u, const void* z, const void* dout, void* du, void* dz, const sscan_dir_params* dirs,
+                    const sscan_dir_grads* grads, const int* kinds, int ndirs, const int32_t* index, int softplus,
+                    int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate, void* stream,
+                    int io_dtype, int bc_dtype, void* workspace, size_t workspace_bytes) {
+  sscan::MultiBwdPlan plan{};
+  bool empty = false;
+  const int st = validate_multi_bwd(u, z, dout, du, dz, dirs, grads, kinds, ndirs, index, batch, dim, height, width,
+                                    dstate, io_dtype, bc_dtype, workspace, workspace_bytes, &plan, &empty);
+  if (st != SSCAN_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (empty) {
+    // no tokens or no channels: the parameter gradients that have elements are zero
+    for (int k = 0; k < ndirs; ++k) {
+      sscan::BwdArgs b;
+      std::memset(&b, 0, sizeof(b));
+      b.fwd = make_args(u, z, nullptr, nullptr, 0, 0, softplus, batch, dim, height * width, io_dtype, bc_dtype);
+      b.fwd.ndir = 1;
+      b.grads[0] = sscan::DirGrads{grads[k].ddelta, grads[k].ddelta_bias, grads[k].dA, grads[k].dB, grads[k].dC,
+                                   grads[k].dD};
+      if (sscan::launch_bwd_zero(b, s) != hipSuccess) return SSCAN_ERR_HIP;
+    }
+    return SSCAN_OK;
+  }
+  sscan::MultiBwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  sscan::MultiArgs& m = a.fwd;
+  m.u = u;
+  m.z = z;
+  for (int k = 0; k < ndirs; ++k) {
+    const sscan_dir_params& p = dirs[k];
+    m.dir[k] = sscan::DirArgs{p.delta, p.delta_bias, p.A, p.B, p.C, p.D};
+    m.kind[k] = kinds[k];
+    a.grads[k] = sscan::DirGrads{grads[k].ddelta, grads[k].ddelta_bias, grads[k].dA, grads[k].dB, grads[k].dC,
+                                 grads[k].dD};
+  }
+  m.ndir = ndirs;
+  m.index = index;
+  m.softplus = softplus ? 1 : 0;
+  m.io_bf16 = io_dtype == SSCAN_BF16;
+  m.bc_bf16 = bc_dtype == SSCAN_BF16;
+  m.batch = batch;
+  m.dim = dim;
+  m.height = height;
+  m.width = width;
+  a.dout = dout;
+  a.du = du;
+  a.dz = dz;
+  const hipError_t e = sscan::launch_multi_bwd(a, plan, static_cast<char*>(workspace), s);
+  return e == hipSuccess ? SSCAN_OK : SSCAN_ERR_HIP;
+}
+
+size_t sscan_multi_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate,
+                                       const int* kinds, int ndirs, int io_dtype, int bc_dtype) {
+  if (height < 0 || width < 0 || (height > 0 && width > (int64_t(1) << 40) / height)) return 0;
+  Sizes sz{};
+  if (check_sizes(batch, dim, height * width, dstate, io_dtype, bc_dtype, &sz) != SSCAN_OK) return 0;
+  if (check_kinds(kinds, ndirs, reinterpret_cast<const int32_t*>(1)) != SSCAN_OK) return 0;
+  if (batch == 0 || dim == 0 || height * width == 0) return 0;
+  return sscan::make_multi_bwd_plan(batch, dim, height, width, kinds, ndirs, io_dtype == SSCAN_BF16,
+                                    bc_dtype == SSCAN_BF16)
       .workspace_bytes;
 }
 

@@ -151,6 +151,7 @@ struct BwdArgs {
   void* dz;                 // written when fwd.z is set
   DirGrads grads[2];
   int du_f32;               // du stored in float32 whatever the io dtype (for the convolution's backward)
+  int dz_f32;               // dz stored in float32 likewise (a partial summed with other orders' before rounding)
   // With the convolution in front (fwd.conv_w set, fwd.u holding x): u = conv(x) in
   // float32, as the fused forward computes it.  The state chain recomputes it from
   // x itself; the window pass reads it here.
@@ -198,6 +199,36 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, float* workspace, hipS
 // Gradients of an empty call: the parameter gradients (dA, dD, delta_bias, dB, dC)
 // that have elements are zero.
 hipError_t launch_bwd_zero(const BwdArgs& a, hipStream_t stream);
+
+// Backward of the scans along several orders: each family's backward runs on its
+// gathered inputs (gated, du and dz in fp32); du and dz are put back and summed
+// over the families in the fixed family order, ddelta/dB/dC put back per
+// direction.  Workspace (byte offsets, 256-aligned):
+//   acc_du, acc_dz  [batch][dim][len] f32   sums over the families (two or more)
+//   vdu, vdz        [batch][dim][len] f32   a gathered family's du, dz (visit order)
+//   u, z, dout      io dtype                gathered
+//   delta[2]        io dtype, B[2], C[2]    gathered per direction slot
+//   dd[2]           io dtype, dB[2], dC[2]  gradients in visit order
+//   inv             [len] int32             inverse of the index order
+//   bwd             the backward's own workspace (largest family)
+struct MultiBwdArgs {
+  MultiArgs fwd;            // fwd.y unused
+  const void* dout;
+  void* du;
+  void* dz;                 // written when fwd.z is set
+  DirGrads grads[kMaxMultiDirs];
+};
+
+struct MultiBwdPlan {
+  size_t off_acc_du, off_acc_dz, off_vdu, off_vdz, off_u, off_z, off_g;
+  size_t off_delta[2], off_B[2], off_C[2], off_dd[2], off_dB[2], off_dC[2];
+  size_t off_inv, off_bwd;
+  size_t workspace_bytes;
+};
+
+MultiBwdPlan make_multi_bwd_plan(int64_t batch, int64_t dim, int64_t height, int64_t width, const int* kinds,
+                                 int ndir, bool io_bf16, bool bc_bf16);
+hipError_t launch_multi_bwd(const MultiBwdArgs& a, const MultiBwdPlan& p, char* workspace, hipStream_t stream);
 
 // How a call is split along the sequence, and the workspace it needs (floats,
 // in this order):

@@ -386,6 +386,30 @@ void put_family(int family, const float* yf, float* acc, const int32_t* inv, con
   }
 }
 
+// Puts a tensor in a family's visiting order back at the token positions (the
+// gather's inverse): the column order's [w][h] map is transposed back onto [h][w];
+// the index order is read through its inverse (out[t] = vis[inv[t]]).
+void scatter_family(int family, bool bf16, const void* vis, void* out, const int32_t* inv, int64_t rows, int64_t h,
+                    int64_t w, hipStream_t s) {
+  if (family == kFamilyCol) {
+    gather_family(kFamilyCol, bf16, vis, out, nullptr, rows, w, h, s);
+  } else {
+    gather_family(kFamilyIndex, bf16, vis, out, inv, rows, h, w, s);
+  }
+}
+
+// The families present among kinds[0..ndir), in the fixed order rows, columns, index.
+int families_of(const int* kinds, int ndir, int* fams) {
+  int nf = 0;
+  for (int f = 0; f < kFamilies; ++f)
+    for (int k = 0; k < ndir; ++k)
+      if (kinds[k] / 2 == f) {
+        fams[nf++] = f;
+        break;
+      }
+  return nf;
+}
+
 }  // namespace
 
 MultiPlan make_multi_plan(int64_t batch, int64_t dim, int64_t height, int64_t width, const int* kinds, int ndir,
@@ -429,13 +453,8 @@ hipError_t launch_multi(const MultiArgs& a, const MultiPlan& p, char* ws, hipStr
   const int64_t len = a.height * a.width;
   const int64_t rows = a.batch * a.dim, bc_rows = a.batch * kDState;
   float* acc = reinterpret_cast<float*>(ws + p.off_acc);
-  int fams[kFamilies], nf = 0;
-  for (int f = 0; f < kFamilies; ++f)
-    for (int k = 0; k < a.ndir; ++k)
-      if (a.kind[k] / 2 == f) {
-        fams[nf++] = f;
-        break;
-      }
+  int fams[kFamilies];
+  const int nf = families_of(a.kind, a.ndir, fams);
   for (int fi = 0; fi < nf; ++fi) {
     const int f = fams[fi];
     const bool first = fi == 0, last = fi == nf - 1;
@@ -506,6 +525,164 @@ hipError_t launch_multi(const MultiArgs& a, const MultiPlan& p, char* ws, hipStr
       } else {
         put_family<float>(f, yf, acc, inv, a.z, a.y, rows, a.height, a.width, first, last, stream);
       }
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sscan
+
+namespace sscan {
+
+MultiBwdPlan make_multi_bwd_plan(int64_t batch, int64_t dim, int64_t height, int64_t width, const int* kinds,
+                                 int ndir, bool io_bf16, bool bc_bf16) {
+  MultiBwdPlan p{};
+  const int64_t len = height * width;
+  const size_t io = io_bf16 ? 2 : 4, bc = bc_bf16 ? 2 : 4;
+  const size_t n = size_t(batch) * size_t(dim) * size_t(len), nbc = size_t(batch) * kDState * size_t(len);
+  int nfam = 0, slots = 0;  // families present; direction slots of the gathered families
+  bool has_index = false;
+  size_t bwd = 0;
+  for (int f = 0; f < kFamilies; ++f) {
+    int nd = 0;
+    for (int k = 0; k < ndir; ++k) nd += kinds[k] / 2 == f;
+    if (nd == 0) continue;
+    ++nfam;
+    bwd = std::max(bwd, make_bwd_plan(batch, dim, len, nd).workspace_bytes);
+    if (f != kFamilyRow) slots = std::max(slots, nd);
+    has_index = has_index || f == kFamilyIndex;
+  }
+  size_t off = 0;
+  auto take = [&off](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  const size_t acc = nfam > 1 ? n * 4 : 0;
+  p.off_acc_du = take(acc);
+  p.off_acc_dz = take(acc);
+  const size_t gat = slots > 0 ? 1 : 0;
+  p.off_vdu = take(gat * n * 4);
+  p.off_vdz = take(gat * n * 4);
+  p.off_u = take(gat * n * io);
+  p.off_z = take(gat * n * io);
+  p.off_g = take(gat * n * io);
+  for (int j = 0; j < 2; ++j) {
+    const size_t on = j < slots ? 1 : 0;
+    p.off_delta[j] = take(on * n * io);
+    p.off_B[j] = take(on * nbc * bc);
+    p.off_C[j] = take(on * nbc * bc);
+    p.off_dd[j] = take(on * n * io);
+    p.off_dB[j] = take(on * nbc * bc);
+    p.off_dC[j] = take(on * nbc * bc);
+  }
+  p.off_inv = take(has_index ? size_t(len) * 4 : 0);
+  p.off_bwd = take(bwd);
+  p.workspace_bytes = off;
+  return p;
+}
+
+hipError_t launch_multi_bwd(const MultiBwdArgs& a, const MultiBwdPlan& p, char* ws, hipStream_t stream) {
+  const MultiArgs& m = a.fwd;
+  const int64_t len = m.height * m.width;
+  const int64_t rows = m.batch * m.dim, bc_rows = m.batch * kDState;
+  float* acc_du = reinterpret_cast<float*>(ws + p.off_acc_du);
+  float* acc_dz = reinterpret_cast<float*>(ws + p.off_acc_dz);
+  float* vdu = reinterpret_cast<float*>(ws + p.off_vdu);
+  float* vdz = reinterpret_cast<float*>(ws + p.off_vdz);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + p.off_inv);
+  int fams[kFamilies];
+  const int nf = families_of(m.kind, m.ndir, fams);
+  for (int fi = 0; fi < nf; ++fi) {
+    const int f = fams[fi];
+    const bool first = fi == 0, last = fi == nf - 1, gathered = f != kFamilyRow;
+    int idx[2] = {-1, -1};  // forward, reverse direction of this family
+    for (int k = 0; k < m.ndir; ++k)
+      if (m.kind[k] / 2 == f) idx[m.kind[k] % 2] = k;
+    BwdArgs b;
+    std::memset(&b, 0, sizeof(b));
+    ScanArgs& s = b.fwd;
+    s.softplus = m.softplus;
+    s.io_bf16 = m.io_bf16;
+    s.bc_bf16 = m.bc_bf16;
+    s.batch = m.batch;
+    s.dim = m.dim;
+    s.len = len;
+    if (!gathered) {
+      s.u = m.u;
+      s.z = m.z;
+      b.dout = a.dout;
+      if (last) {
+        // rows alone: the plain (gated) backward
+        b.du = a.du;
+        b.dz = a.dz;
+      } else {
+        // rows come first: du and dz straight into the sums
+        b.du = acc_du;
+        b.dz = acc_dz;
+        b.du_f32 = b.dz_f32 = 1;
+      }
+    } else {
+      gather_family(f, m.io_bf16, m.u, ws + p.off_u, m.index, rows, m.height, m.width, stream);
+      gather_family(f, m.io_bf16, a.dout, ws + p.off_g, m.index, rows, m.height, m.width, stream);
+      if (m.z) gather_family(f, m.io_bf16, m.z, ws + p.off_z, m.index, rows, m.height, m.width, stream);
+      s.u = ws + p.off_u;
+      s.z = m.z ? ws + p.off_z : nullptr;
+      b.dout = ws + p.off_g;
+      b.du = vdu;
+      b.dz = vdz;
+      b.du_f32 = b.dz_f32 = 1;  // summed with the other families' before any rounding
+    }
+    int slot = 0, dir_of[2] = {-1, -1};
+    const void* gathered_delta = nullptr;  // a delta shared by the family's two directions is gathered once
+    for (int j = 0; j < 2; ++j) {
+      if (idx[j] < 0) continue;
+      DirArgs d = m.dir[idx[j]];
+      DirGrads g = a.grads[idx[j]];
+      if (gathered) {
+        if (slot == 1 && d.delta == m.dir[idx[0]].delta && gathered_delta) {
+          d.delta = gathered_delta;
+        } else {
+          gather_family(f, m.io_bf16, d.delta, ws + p.off_delta[slot], m.index, rows, m.height, m.width, stream);
+          d.delta = ws + p.off_delta[slot];
+        }
+        if (slot == 0) gathered_delta = d.delta;
+        gather_family(f, m.bc_bf16, d.B, ws + p.off_B[slot], m.index, bc_rows, m.height, m.width, stream);
+        gather_family(f, m.bc_bf16, d.C, ws + p.off_C[slot], m.index, bc_rows, m.height, m.width, stream);
+        d.B = ws + p.off_B[slot];
+        d.C = ws + p.off_C[slot];
+        // the sequence-shaped gradients land in visit order first
+        g.ddelta = ws + p.off_dd[slot];
+        g.dB = ws + p.off_dB[slot];
+        g.dC = ws + p.off_dC[slot];
+      }
+      s.dir[slot] = d;
+      b.grads[slot] = g;
+      dir_of[slot++] = idx[j];
+    }
+    s.ndir = slot;
+    s.reverse = (slot == 1 && idx[1] >= 0) ? 1 : 0;  // a lone reverse direction
+    const BwdPlan bp = make_bwd_plan(m.batch, m.dim, len, slot);
+    hipError_t e = launch_bwd(b, bp, reinterpret_cast<float*>(ws + p.off_bwd), stream);
+    if (e != hipSuccess) return e;
+    if (!gathered) continue;
+    if (f == kFamilyIndex) {
+      hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(len)), dim3(256), 0, stream, inv, len, -1);
+      hipLaunchKernelGGL(invert_kernel, dim3(blocks_for(len)), dim3(256), 0, stream, m.index, inv, len);
+    }
+    // du, dz: summed over the families in fp32, rounded once by the last put-back
+    if (m.io_bf16) {
+      put_family<uint16_t>(f, vdu, acc_du, inv, nullptr, a.du, rows, m.height, m.width, first, last, stream);
+      if (m.z) put_family<uint16_t>(f, vdz, acc_dz, inv, nullptr, a.dz, rows, m.height, m.width, first, last, stream);
+    } else {
+      put_family<float>(f, vdu, acc_du, inv, nullptr, a.du, rows, m.height, m.width, first, last, stream);
+      if (m.z) put_family<float>(f, vdz, acc_dz, inv, nullptr, a.dz, rows, m.height, m.width, first, last, stream);
+    }
+    for (int j = 0; j < slot; ++j) {
+      const DirGrads& g = a.grads[dir_of[j]];
+      scatter_family(f, m.io_bf16, ws + p.off_dd[j], g.ddelta, inv, rows, m.height, m.width, stream);
+      scatter_family(f, m.bc_bf16, ws + p.off_dB[j], g.dB, inv, bc_rows, m.height, m.width, stream);
+      scatter_family(f, m.bc_bf16, ws + p.off_dC[j], g.dC, inv, bc_rows, m.height, m.width, stream);
     }
   }
   return hipGetLastError();

@@ -142,6 +142,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sscan_validate_multi.restype = I
     lib.sscan_multi_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, IP, I, I, I]
     lib.sscan_multi_workspace_bytes.restype = SZ
+    lib.sscan_multi_bwd.argtypes = [V, V, V, V, V, DP, DG, IP, I, V, I, I64, I64, I64, I64, I64, V, I, I, V, SZ]
+    lib.sscan_multi_bwd.restype = I
+    lib.sscan_validate_multi_bwd.argtypes = [V, V, V, V, V, DP, DG, IP, I, V, I, I64, I64, I64, I64, I64, I, I, V,
+                                             SZ]
+    lib.sscan_validate_multi_bwd.restype = I
+    lib.sscan_multi_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, IP, I, I, I]
+    lib.sscan_multi_bwd_workspace_bytes.restype = SZ
     lib.sscan_spiral_order.argtypes = [I64, I64, V]
     lib.sscan_spiral_order.restype = I
     lib.sscan_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
@@ -687,6 +694,53 @@ def multi(u, z, dirs, kinds, height: int, width: int, index: Optional[torch.Tens
     if st != 0:
         raise SScanError(st, "sscan_multi")
     return out
+
+
+def multi_bwd_workspace_bytes(batch, dim, height, width, kinds, io_dtype=torch.float32,
+                              bc_dtype=torch.float32) -> int:
+    k = (ctypes.c_int * len(kinds))(*kinds)
+    return int(load_library().sscan_multi_bwd_workspace_bytes(batch, dim, height, width, DSTATE, k, len(kinds),
+                                                              _DT_CODE[io_dtype], _DT_CODE[bc_dtype]))
+
+
+def multi_bwd(u, z, dout, dirs, kinds, height: int, width: int, index: Optional[torch.Tensor] = None,
+              softplus: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Backward pass of ``multi`` (``sscan_multi_bwd``): gradients of
+    sum(dout * out).  Returns {"du", "dz" (None without z), "dirs": [one dict per
+    direction with ddelta, ddelta_bias, dA, dB, dC, dD as in ``bwd``]}."""
+    lib = load_library()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("sscan.multi_bwd needs CUDA (HIP) tensors")
+    if u.dtype not in _DT_CODE or dirs[0]["B"].dtype not in _DT_CODE:
+        raise TypeError("u/delta/z and B/C must be float32 or bfloat16")
+    b, d, L = u.shape
+    if L != height * width:
+        raise ValueError("u's last axis must be height * width")
+    if len(dirs) != len(kinds):
+        raise ValueError("one parameter dict per order")
+    _check(u, "u", dev)
+    _check(z, "z", dev, u.dtype, u.shape)
+    _check(dout, "dout", dev, u.dtype, u.shape)
+    _check(index, "index", dev, torch.int32, (L,))
+    bdt = dirs[0]["B"].dtype
+    ps = [_dir(p, f"dirs[{k}]", dev, u, bdt) for k, p in enumerate(dirs)]
+    gs = [_grads_for(p, u) for p in dirs]
+    arr = (DirParams * len(ps))(*ps)
+    garr = (DirGrads * len(gs))(*[g[1] for g in gs])
+    kk = (ctypes.c_int * len(kinds))(*kinds)
+    du = torch.empty_like(u)
+    dz = torch.empty_like(u) if z is not None else None
+    nbytes = multi_bwd_workspace_bytes(b, d, height, width, kinds, u.dtype, bdt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", dev)
+    st = lib.sscan_multi_bwd(_ptr(u), _ptr(z), _ptr(dout), _ptr(du), _ptr(dz), arr, garr, kk, len(kinds), _ptr(index),
+                             int(bool(softplus)), b, d, height, width, DSTATE, _stream(dev), _DT_CODE[u.dtype],
+                             _DT_CODE[bdt], _ptr(workspace), workspace.numel())
+    if st != 0:
+        raise SScanError(st, "sscan_multi_bwd")
+    return {"du": du, "dz": dz, "dirs": [g[0] for g in gs]}
 
 
 def bwd_workspace_bytes(batch: int, dim: int, length: int, dstate: int = DSTATE, bidir: bool = False) -> int:

@@ -495,6 +495,60 @@ def test_validate_multi(lib):
     assert V(kinds, 4, y=u) == EALIAS
     assert V(kinds, 4, h=-1) == ESHAPE
 
+
+def test_validate_multi_bwd(lib):
+    f = Fake()
+    f.next = 1 << 46
+    b, d, h, w = 2, 64, 8, 12
+    L = h * w
+    io, bc = b * d * L * 4, b * 16 * L * 4
+    u, z, dout, du, dz, index = f(io), f(io), f(io), f(io), f(io), f(L * 4)
+    mk = lambda: sscan.DirParams(f(io), f(d * 4), f(d * 64), f(bc), f(bc), f(d * 4))
+    mg = lambda: [f(io), f(d * 4), f(d * 64), f(bc), f(bc), f(d * 4)]
+    dirs = (sscan.DirParams * 4)(*[mk() for _ in range(4)])
+    grads = [mg() for _ in range(4)]
+    G = lambda gs: (sscan.DirGrads * len(gs))(*[sscan.DirGrads(*g) for g in gs])
+    K = lambda *k: (ctypes.c_int * len(k))(*k)
+    kinds = K(0, 1, 2, 3)
+    ws = lib.sscan_multi_bwd_workspace_bytes(b, d, h, w, 16, kinds, 4, 0, 0)
+    assert ws > lib.sscan_multi_workspace_bytes(b, d, h, w, 16, kinds, 4, 0, 0)
+    wsp = f(ws)
+
+    def V(kk, n, gs=grads, **kw):
+        return lib.sscan_validate_multi_bwd(kw.get("u", u), kw.get("z", z), kw.get("dout", dout), kw.get("du", du),
+                                            kw.get("dz", dz), dirs, G(gs), kk, n, kw.get("index", None), 1,
+                                            kw.get("b", b), d, kw.get("h", h), w, 16, 0, 0, kw.get("ws", wsp),
+                                            kw.get("ws_bytes", ws))
+
+    assert V(kinds, 4) == OK
+    assert V(kinds, 4, z=None, dz=None) == OK
+    assert V(kinds, 4, dz=None) == ENULL                           # z given: dz required
+    assert V(kinds, 4, dout=None) == ENULL
+    assert V(K(4), 1) == ENULL                                     # the index orders need the index
+    ws4 = lib.sscan_multi_bwd_workspace_bytes(b, d, h, w, 16, K(4), 1, 0, 0)
+    assert V(K(4), 1, index=index, ws_bytes=ws4) == OK
+    assert V(K(4), 1, index=index, du=index, ws_bytes=ws4) == EALIAS  # an output over the index
+    assert V(K(0, 0), 2) == EUNSUP
+    bad = [list(g) for g in grads]
+    bad[2][0] = None                                               # a direction's ddelta
+    assert V(kinds, 4, bad) == ENULL
+    bad = [list(g) for g in grads]
+    bad[3][4] = grads[1][4]                                        # two directions' dC in one buffer
+    assert V(kinds, 4, bad) == EALIAS
+    bad = [list(g) for g in grads]
+    bad[1][3] = dirs[0].B                                          # a gradient over an input
+    assert V(kinds, 4, bad) == EALIAS
+    assert V(kinds, 4, du=dz) == EALIAS
+    assert V(kinds, 4, ws_bytes=ws - 1) == EWS
+    assert V(kinds, 4, ws=wsp + 16) == EALIGN
+    assert V(kinds, 4, dout=dout + 2) == EALIGN
+    assert V(kinds, 4, h=-1) == ESHAPE
+    # an empty map: only the parameter gradients with elements are needed
+    assert V(kinds, 4, [[None, g[1], g[2], None, None, g[5]] for g in grads], h=0, u=None, z=None, dout=None,
+             du=None, dz=None, ws=None, ws_bytes=0) == OK
+    assert lib.sscan_multi_bwd_workspace_bytes(b, d, 0, w, 16, kinds, 4, 0, 0) == 0
+
+
 def test_bwd_plan_splits():
     """How backward calls are split: a window's channel groups go to about 32768
     blocks per launch (one direction per launch) with at least 16 groups per block,
