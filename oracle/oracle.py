@@ -21,6 +21,7 @@ SRC = os.path.join(HERE, "sscan_oracle.c")
 SRC_BWD = os.path.join(HERE, "sscan_oracle_bwd.c")
 SRC_CONV = os.path.join(HERE, "sscan_oracle_conv.c")
 LIB = os.path.join(HERE, "liboracle_sscan.so")
+SOURCES = (SRC, SRC_BWD, SRC_CONV)
 
 _lib = None
 
@@ -38,9 +39,11 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        if not os.environ.get("SSCAN_ORACLE_LIB") and not os.path.exists(LIB):
             build(force=True)
-        lib = ctypes.CDLL(LIB)
+        # SSCAN_ORACLE_LIB: another build of the same sources (the sanitizer build of
+        # the tests) to load instead
+        lib = ctypes.CDLL(os.environ.get("SSCAN_ORACLE_LIB") or LIB)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         INT = ctypes.c_int

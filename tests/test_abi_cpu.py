@@ -21,6 +21,11 @@ MB = 1 << 20
 
 @pytest.fixture(scope="module")
 def lib():
+    # SSCAN_TEST_LIBRARY: another build of the same library to run these checks on
+    # (the sanitizer build of test_asan_host.py)
+    other = os.environ.get("SSCAN_TEST_LIBRARY")
+    if other:
+        return sscan.load_library(other)
     if not os.path.exists(sscan.LIB_PATH):
         from selective_state_space_sscan_amd import build
         build.build()
