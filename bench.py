@@ -7,7 +7,7 @@ resident in HBM).  One step = one sscan_fwd call (all its kernels).  Prints ONE
 JSON line on stdout.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                 [--pass fwd|bwd|conv|fwd-conv|cross4|spiral]
+                 [--pass fwd|bwd|bwd-conv|conv|fwd-conv|cross4|spiral|cross4-bwd]
                  [--no-cpu] [--copy-calibration]
 
 Timing: K plain calls between two HIP events give ms_per_step (for a workload
@@ -222,11 +222,21 @@ def bench_bwd(args, torch, I, sscan, cfg, ci):
     xd = x.to(dev)
     g = torch.from_numpy(np.random.default_rng(4242).standard_normal(tuple(x.u.shape), dtype=np.float32))
     g = g.to(x.u.dtype).to(dev)
-    ws = torch.empty(max(1, sscan.bwd_workspace_bytes(cfg.batch, cfg.dim, cfg.len, cfg.dstate, cfg.bidir)),
-                     dtype=torch.uint8, device=dev)
+    conv = args.pass_ == "bwd-conv"
+    nws = (sscan.bwd_conv_workspace_bytes(cfg.batch, cfg.dim, cfg.len, cfg.dstate, cfg.bidir, x.u.dtype) if conv
+           else sscan.bwd_workspace_bytes(cfg.batch, cfg.dim, cfg.len, cfg.dstate, cfg.bidir))
+    ws = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
     mk = lambda p: dict(delta=xd.delta, delta_bias=p.delta_bias, A=p.A, B=p.B, C=p.C, D=p.D)
+    cp = conv_params(torch, cfg.dim, dev) if conv else None
 
     def step(events=None):
+        if conv:
+            # u holds x: the backward through the front-end convolution (no events)
+            if cfg.ndir == 1:
+                p = xd.dirs[0]
+                return sscan.bwd_conv(xd.u, cp, xd.delta, p.A, p.B, p.C, g, D=p.D, z=xd.z, delta_bias=p.delta_bias,
+                                      workspace=ws)
+            return sscan.bidir_bwd_conv(xd.u, cp, xd.z, g, mk(xd.dirs[0]), mk(xd.dirs[1]), workspace=ws)
         if cfg.ndir == 1:
             p = xd.dirs[0]
             return sscan.bwd(xd.u, xd.delta, p.A, p.B, p.C, g, D=p.D, z=xd.z, delta_bias=p.delta_bias,
@@ -244,13 +254,28 @@ def bench_bwd(args, torch, I, sscan, cfg, ci):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    nbytes = bwd_alg_bytes(cfg)
+    if conv:
+        # the convolution's weights and bias read, their gradients written
+        nbytes += 2 * cfg.dim * (CONV["width"] + 1) * 4
+        return {
+            "metric": METRIC, "value": cfg.elems / (ms * 1e-3) / 1e6, "unit": "Melem/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded numpy PCG64, shapes of the pages' workloads)",
+            "config": {"workload": cfg.name, "pass": "bwd-conv", "batch": cfg.batch, "dim": cfg.dim, "len": cfg.len,
+                       "dstate": cfg.dstate, "directions": cfg.ndir, "io_dtype": cfg.io_dtype,
+                       "bc_dtype": cfg.bc_dtype, "conv": CONV},
+            # the whole call: x, z, dout, delta read; dx, dz, ddelta written; B/C and their
+            # gradients; the scan's and the convolution's parameters
+            "roofline": hbm_roofline("whole call", nbytes, ms),
+            "workspace_bytes": ws.numel()}
     evsets = [sscan.HipEvents(sscan.BWD_PROFILE_STEPS) for _ in range(args.steps)]
     for ev in evsets:
         step(ev)
     torch.cuda.synchronize()
     kernel_ms = {k: sum(ev.step_ms()[k] for ev in evsets) / args.steps for k in sscan.BWD_PROFILE_STEPS}
     per_call = [ev.total_ms() for ev in evsets]
-    nbytes = bwd_alg_bytes(cfg)
     out = {
         "metric": METRIC, "value": cfg.elems / (ms * 1e-3) / 1e6, "unit": "Melem/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -438,15 +463,25 @@ def bench_multi(args, torch, I, sscan, cfg, ci):
     dirs = [dict(delta=xd.delta, delta_bias=p.delta_bias.to(dev), A=p.A.to(dev), B=p.B.to(dev), C=p.C.to(dev),
                  D=p.D.to(dev)) for p in x1.dirs + x2.dirs]
     index = None
-    if args.pass_ == "cross4":
+    if args.pass_ in ("cross4", "cross4-bwd"):
         kinds = [sscan.ORDER_ROW, sscan.ORDER_ROW_REV, sscan.ORDER_COL, sscan.ORDER_COL_REV]
     else:
         kinds = [sscan.ORDER_INDEX, sscan.ORDER_INDEX_REV, sscan.ORDER_ROW, sscan.ORDER_ROW_REV]
         index = sscan.spiral_order(side, side).to(dev)
     y = torch.empty_like(xd.u)
-    ws = torch.empty(sscan.multi_workspace_bytes(cfg.batch, cfg.dim, side, side, kinds, xd.u.dtype,
-                                                 dirs[0]["B"].dtype), dtype=torch.uint8, device=dev)
-    step = lambda: sscan.multi(xd.u, xd.z, dirs, kinds, side, side, index=index, out=y, workspace=ws)
+    bwd = args.pass_ == "cross4-bwd"
+    if bwd:
+        import numpy as np
+
+        g = torch.from_numpy(np.random.default_rng(4243).standard_normal(tuple(xd.u.shape), dtype=np.float32))
+        g = g.to(xd.u.dtype).to(dev)
+        ws = torch.empty(sscan.multi_bwd_workspace_bytes(cfg.batch, cfg.dim, side, side, kinds, xd.u.dtype,
+                                                         dirs[0]["B"].dtype), dtype=torch.uint8, device=dev)
+        step = lambda: sscan.multi_bwd(xd.u, xd.z, g, dirs, kinds, side, side, index=index, workspace=ws)
+    else:
+        ws = torch.empty(sscan.multi_workspace_bytes(cfg.batch, cfg.dim, side, side, kinds, xd.u.dtype,
+                                                     dirs[0]["B"].dtype), dtype=torch.uint8, device=dev)
+        step = lambda: sscan.multi(xd.u, xd.z, dirs, kinds, side, side, index=index, out=y, workspace=ws)
     for _ in range(args.warmup):
         step()
     stream = torch.cuda.current_stream(dev)
@@ -461,9 +496,15 @@ def bench_multi(args, torch, I, sscan, cfg, ci):
     io = 2 if cfg.io_dtype == "bf16" else 4
     bc = 2 if cfg.bc_dtype == "bf16" else 4
     # u, the shared raw delta and z read once, y written once; per direction its
-    # B, C and parameters
-    nbytes = 4 * cfg.elems * io + len(kinds) * (2 * cfg.batch * cfg.dstate * cfg.len * bc +
-                                                cfg.dim * (cfg.dstate + 2) * 4)
+    # B, C and parameters.  Backward: u, delta, z, dout read, du and dz written, per
+    # direction its ddelta written, B, C read, dB, dC written, parameters read and
+    # their gradients written.
+    if bwd:
+        nbytes = (6 + len(kinds)) * cfg.elems * io + len(kinds) * (4 * cfg.batch * cfg.dstate * cfg.len * bc +
+                                                                   2 * cfg.dim * (cfg.dstate + 2) * 4)
+    else:
+        nbytes = 4 * cfg.elems * io + len(kinds) * (2 * cfg.batch * cfg.dstate * cfg.len * bc +
+                                                    cfg.dim * (cfg.dstate + 2) * 4)
     return {"metric": METRIC, "value": cfg.elems / (ms * 1e-3) / 1e6, "unit": "Melem/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -568,11 +609,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long-seq-fwd",
                     help="a scan workload of selective_state_space_sscan_amd.inputs.CONFIGS, or decode-step")
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "conv", "fwd-conv", "cross4", "spiral"),
+    ap.add_argument("--pass", dest="pass_",
+                    choices=("fwd", "bwd", "bwd-conv", "conv", "fwd-conv", "cross4", "spiral", "cross4-bwd"),
                     default="fwd",
-                    help="the forward call (default), its backward pass, the front-end convolution alone, "
-                         "the scan with the convolution fused in, or a square map scanned in four "
-                         "directions (rows and columns both ways) or along the spiral")
+                    help="the forward call (default), its backward pass, the backward through the front-end "
+                         "convolution, the convolution alone, the scan with the convolution fused in, a square "
+                         "map scanned in four directions (rows and columns both ways) or along the spiral, or "
+                         "the backward of the four-direction scan")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with a 512 MiB negation kernel (counter calibration for rocprofv3 --pmc runs)")
@@ -593,10 +636,10 @@ def main():
     names = [c.name for c in I.CONFIGS]
     ci = names.index(args.workload)
     cfg = I.CONFIGS[ci]
-    if args.pass_ == "bwd":
+    if args.pass_ in ("bwd", "bwd-conv"):
         print(json.dumps(bench_bwd(args, torch, I, sscan, cfg, ci)), flush=True)
         return
-    if args.pass_ in ("cross4", "spiral"):
+    if args.pass_ in ("cross4", "spiral", "cross4-bwd"):
         print(json.dumps(bench_multi(args, torch, I, sscan, cfg, ci)), flush=True)
         return
     if args.pass_ in ("conv", "fwd-conv"):

@@ -189,7 +189,7 @@ struct TokIn {
   float bias, D;
 };
 
-template <bool IO_BF16, bool HAS_Z>
+template <bool IO_BF16, bool HAS_Z, bool EXT>
 __device__ __forceinline__ void load_tok(TokIn<IO_BF16, HAS_Z>& r, const BwdArgs& a, const DirArgs& pd, int64_t b,
                                          int64_t g, int64_t t0, int wl) {
   using IO = Io<IO_BF16>;
@@ -202,7 +202,7 @@ __device__ __forceinline__ void load_tok(TokIn<IO_BF16, HAS_Z>& r, const BwdArgs
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int i = i0 + e < wl ? i0 + e : wl - 1;  // a valid token for the ragged tail
-    r.u[e] = a.u32 ? a.u32[row + i] : IO::load(static_cast<const T*>(a.fwd.u), row + i);
+    r.u[e] = (EXT && a.u32) ? a.u32[row + i] : IO::load(static_cast<const T*>(a.fwd.u), row + i);
     r.draw[e] = IO::load(static_cast<const T*>(pd.delta), row + i);
     r.g[e] = IO::load(static_cast<const T*>(a.dout), row + i);
     r.z[e] = HAS_Z ? IO::load(static_cast<const T*>(a.fwd.z), row + i) : 0.0f;
@@ -210,8 +210,12 @@ __device__ __forceinline__ void load_tok(TokIn<IO_BF16, HAS_Z>& r, const BwdArgs
 }
 
 // The window pass for one direction.  Grid: batch * nwin * csplit one-wave blocks;
-// block j of a window covers channel groups [j*gps, (j+1)*gps).
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, bool REV, int OUT>
+// block j of a window covers channel groups [j*gps, (j+1)*gps).  EXT compiles in
+// the extensions (fp32 u from the convolution, du / dz stored in fp32, the entry
+// state, the final state's gradient and dh0): the plain backward keeps a kernel
+// without them (their live values had spilled registers in the sweeps: window pass
+// 7.09 -> 8.61 ms on the long workload).
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, bool REV, int OUT, bool EXT>
 __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, int64_t nwin, int csplit, int64_t gps,
                                                            const float* __restrict__ bc, WinChains ch,
                                                            float* __restrict__ part, float* __restrict__ pbc,
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
   TokIn<IO_BF16, HAS_Z> nx;
   float nx_A = 0.0f, nx_e[2] = {0.0f, 0.0f}, nx_p[2] = {0.0f, 0.0f}, nx_s[2] = {0.0f, 0.0f};
   auto prefetch = [&](int64_t g) {
-    load_tok(nx, a, pd, b, g, t0, wl);
+    load_tok<IO_BF16, HAS_Z, EXT>(nx, a, pd, b, g, t0, wl);
     const int64_t d = min64(g * kGroup + c, f.dim - 1);
     nx_A = pd.A[d * kDState + n];
     if (nwin > 1) {
@@ -282,7 +286,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           nx_s[q] = ch.s[q][chain_sum_index(dir, b, pred[q], d, f.batch, f.dim, nwin)];
         }
       }
-    } else {
+    } else if constexpr (EXT) {
       // one window: the forward's entry state, and the gradient reaching its final state
       nx_e[0] = f.h0 ? f.h0[(b * f.dim + d) * kDState + n] : 0.0f;
       nx_e[1] = a.dh_last ? a.dh_last[(b * f.dim + d) * kDState + n] : 0.0f;
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
   };
   // the window holding the first token in scan order ends its adjoint sweep with the
   // gradient of the forward's entry state
-  const bool writes_dh0 = a.dh0 != nullptr && k == (REV ? nwin - 1 : 0);
+  const bool writes_dh0 = EXT && a.dh0 != nullptr && k == (REV ? nwin - 1 : 0);
   if (g_begin < g_end) prefetch(g_begin);
 
   for (int64_t g = g_begin; g < g_end; ++g) {
@@ -422,7 +426,9 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
       const int64_t d = g * kGroup + c;
       if (d < f.dim) {
         part[part_index(dir, b, k, n, d, f.batch, f.dim, nwin)] = dA_acc;
-        if (writes_dh0) a.dh0[(b * f.dim + d) * kDState + n] = mu_end;
+        if constexpr (EXT) {
+          if (writes_dh0) a.dh0[(b * f.dim + d) * kDState + n] = mu_end;
+        }
       }
     }
     __syncthreads();
@@ -446,13 +452,13 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           if (act) {
             IO::store(static_cast<T*>(gd.ddelta), row + i, ddl);
             if (OUT == kSingle) {
-              if (a.du_f32) {
+              if (EXT && a.du_f32) {
                 static_cast<float*>(a.du)[row + i] = du;
               } else {
                 IO::store(static_cast<T*>(a.du), row + i, du);
               }
               if (HAS_Z) {
-                if (a.dz_f32) {
+                if (EXT && a.dz_f32) {
                   static_cast<float*>(a.dz)[row + i] = sTok[QDZ][i][cc] * y;
                 } else {
                   IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * y);
@@ -462,13 +468,13 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
               acc_du[row + i] = du;
               if (HAS_Z) acc_y[row + i] = y;
             } else {
-              if (a.du_f32) {
+              if (EXT && a.du_f32) {
                 static_cast<float*>(a.du)[row + i] = du + acc_du[row + i];
               } else {
                 IO::store(static_cast<T*>(a.du), row + i, du + acc_du[row + i]);
               }
               if (HAS_Z) {
-                if (a.dz_f32) {
+                if (EXT && a.dz_f32) {
                   static_cast<float*>(a.dz)[row + i] = sTok[QDZ][i][cc] * (y + acc_y[row + i]);
                 } else {
                   IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (y + acc_y[row + i]));
@@ -644,19 +650,28 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
   }
   const dim3 wgrid(unsigned(f.batch * p.nwin * p.csplit));
   const int64_t nw = p.nwin;
-  if (f.ndir == 1) {
-    if (f.reverse) {
-      hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSingle>), wgrid, dim3(kLanes), 0, stream,
-                         a, 0, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
+  const bool ext = a.u32 || a.du_f32 || a.dz_f32 || f.h0 || a.dh_last || a.dh0;
+  auto windows = [&](auto ext_tag) {
+    constexpr bool E = decltype(ext_tag)::value;
+    if (f.ndir == 1) {
+      if (f.reverse) {
+        hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSingle, E>), wgrid, dim3(kLanes), 0,
+                           stream, a, 0, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
+      } else {
+        hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, false, kSingle, E>), wgrid, dim3(kLanes), 0,
+                           stream, a, 0, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
+      }
     } else {
-      hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, false, kSingle>), wgrid, dim3(kLanes), 0,
+      hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, false, kFirst, E>), wgrid, dim3(kLanes), 0,
                          stream, a, 0, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
+      hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSecond, E>), wgrid, dim3(kLanes), 0,
+                         stream, a, 1, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
     }
+  };
+  if (ext) {
+    windows(std::integral_constant<bool, true>());
   } else {
-    hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, false, kFirst>), wgrid, dim3(kLanes), 0, stream, a,
-                       0, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
-    hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSecond>), wgrid, dim3(kLanes), 0, stream,
-                       a, 1, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
+    windows(std::integral_constant<bool, false>());
   }
   mark(4);
   hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned((f.dim + kLanes - 1) / kLanes), unsigned(f.ndir * kPartRows)),
