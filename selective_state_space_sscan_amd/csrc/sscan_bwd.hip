@@ -189,7 +189,11 @@ struct TokIn {
   float bias, D;
 };
 
-template <bool IO_BF16, bool HAS_Z, bool EXT>
+// What a window-pass instance compiles in beyond the plain backward (bit mask).
+constexpr int kExtIO = 1;     // u read in fp32 (the convolution's output), du / dz stored in fp32
+constexpr int kExtState = 2;  // the entry state, the final state's gradient, dh0
+
+template <bool IO_BF16, bool HAS_Z, int EXT>
 __device__ __forceinline__ void load_tok(TokIn<IO_BF16, HAS_Z>& r, const BwdArgs& a, const DirArgs& pd, int64_t b,
                                          int64_t g, int64_t t0, int wl) {
   using IO = Io<IO_BF16>;
@@ -202,7 +206,7 @@ __device__ __forceinline__ void load_tok(TokIn<IO_BF16, HAS_Z>& r, const BwdArgs
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int i = i0 + e < wl ? i0 + e : wl - 1;  // a valid token for the ragged tail
-    r.u[e] = (EXT && a.u32) ? a.u32[row + i] : IO::load(static_cast<const T*>(a.fwd.u), row + i);
+    r.u[e] = ((EXT & kExtIO) && a.u32) ? a.u32[row + i] : IO::load(static_cast<const T*>(a.fwd.u), row + i);
     r.draw[e] = IO::load(static_cast<const T*>(pd.delta), row + i);
     r.g[e] = IO::load(static_cast<const T*>(a.dout), row + i);
     r.z[e] = HAS_Z ? IO::load(static_cast<const T*>(a.fwd.z), row + i) : 0.0f;
@@ -210,12 +214,11 @@ __device__ __forceinline__ void load_tok(TokIn<IO_BF16, HAS_Z>& r, const BwdArgs
 }
 
 // The window pass for one direction.  Grid: batch * nwin * csplit one-wave blocks;
-// block j of a window covers channel groups [j*gps, (j+1)*gps).  EXT compiles in
-// the extensions (fp32 u from the convolution, du / dz stored in fp32, the entry
-// state, the final state's gradient and dh0): the plain backward keeps a kernel
+// block j of a window covers channel groups [j*gps, (j+1)*gps).  EXT selects the
+// extensions compiled in (kExtIO, kExtState): the plain backward keeps a kernel
 // without them (their live values had spilled registers in the sweeps: window pass
-// 7.09 -> 8.61 ms on the long workload).
-template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, bool REV, int OUT, bool EXT>
+// 7.09 -> 8.61 ms on the long workload), and each extension is an instance of its own.
+template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, bool REV, int OUT, int EXT>
 __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, int64_t nwin, int csplit, int64_t gps,
                                                            const float* __restrict__ bc, WinChains ch,
                                                            float* __restrict__ part, float* __restrict__ pbc,
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           nx_s[q] = ch.s[q][chain_sum_index(dir, b, pred[q], d, f.batch, f.dim, nwin)];
         }
       }
-    } else if constexpr (EXT) {
+    } else if constexpr ((EXT & kExtState) != 0) {
       // one window: the forward's entry state, and the gradient reaching its final state
       nx_e[0] = f.h0 ? f.h0[(b * f.dim + d) * kDState + n] : 0.0f;
       nx_e[1] = a.dh_last ? a.dh_last[(b * f.dim + d) * kDState + n] : 0.0f;
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
   };
   // the window holding the first token in scan order ends its adjoint sweep with the
   // gradient of the forward's entry state
-  const bool writes_dh0 = EXT && a.dh0 != nullptr && k == (REV ? nwin - 1 : 0);
+  const bool writes_dh0 = (EXT & kExtState) && a.dh0 != nullptr && k == (REV ? nwin - 1 : 0);
   if (g_begin < g_end) prefetch(g_begin);
 
   for (int64_t g = g_begin; g < g_end; ++g) {
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
       const int64_t d = g * kGroup + c;
       if (d < f.dim) {
         part[part_index(dir, b, k, n, d, f.batch, f.dim, nwin)] = dA_acc;
-        if constexpr (EXT) {
+        if constexpr ((EXT & kExtState) != 0) {
           if (writes_dh0) a.dh0[(b * f.dim + d) * kDState + n] = mu_end;
         }
       }
@@ -452,13 +455,13 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           if (act) {
             IO::store(static_cast<T*>(gd.ddelta), row + i, ddl);
             if (OUT == kSingle) {
-              if (EXT && a.du_f32) {
+              if ((EXT & kExtIO) && a.du_f32) {
                 static_cast<float*>(a.du)[row + i] = du;
               } else {
                 IO::store(static_cast<T*>(a.du), row + i, du);
               }
               if (HAS_Z) {
-                if (EXT && a.dz_f32) {
+                if ((EXT & kExtIO) && a.dz_f32) {
                   static_cast<float*>(a.dz)[row + i] = sTok[QDZ][i][cc] * y;
                 } else {
                   IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * y);
@@ -468,13 +471,13 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
               acc_du[row + i] = du;
               if (HAS_Z) acc_y[row + i] = y;
             } else {
-              if (EXT && a.du_f32) {
+              if ((EXT & kExtIO) && a.du_f32) {
                 static_cast<float*>(a.du)[row + i] = du + acc_du[row + i];
               } else {
                 IO::store(static_cast<T*>(a.du), row + i, du + acc_du[row + i]);
               }
               if (HAS_Z) {
-                if (EXT && a.dz_f32) {
+                if ((EXT & kExtIO) && a.dz_f32) {
                   static_cast<float*>(a.dz)[row + i] = sTok[QDZ][i][cc] * (y + acc_y[row + i]);
                 } else {
                   IO::store(static_cast<T*>(a.dz), row + i, sTok[QDZ][i][cc] * (y + acc_y[row + i]));
@@ -650,9 +653,9 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
   }
   const dim3 wgrid(unsigned(f.batch * p.nwin * p.csplit));
   const int64_t nw = p.nwin;
-  const bool ext = a.u32 || a.du_f32 || a.dz_f32 || f.h0 || a.dh_last || a.dh0;
+  const int ext = ((a.u32 || a.du_f32 || a.dz_f32) ? kExtIO : 0) | ((f.h0 || a.dh_last || a.dh0) ? kExtState : 0);
   auto windows = [&](auto ext_tag) {
-    constexpr bool E = decltype(ext_tag)::value;
+    constexpr int E = decltype(ext_tag)::value;
     if (f.ndir == 1) {
       if (f.reverse) {
         hipLaunchKernelGGL((bwd_window_kernel<IO_BF16, SOFTPLUS, HAS_Z, true, kSingle, E>), wgrid, dim3(kLanes), 0,
@@ -668,10 +671,15 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdPlan& p, float* w, hipStr
                          stream, a, 1, nw, p.csplit, p.gps, bc, ch, part, pbc, acc_du, acc_y);
     }
   };
-  if (ext) {
-    windows(std::integral_constant<bool, true>());
+  // no entry point combines state I/O with the fp32 paths of the convolution or the
+  // multi-order scan, so no instance has both
+  if (ext == (kExtState | kExtIO)) return hipErrorInvalidValue;
+  if (ext & kExtState) {
+    windows(std::integral_constant<int, kExtState>());
+  } else if (ext & kExtIO) {
+    windows(std::integral_constant<int, kExtIO>());
   } else {
-    windows(std::integral_constant<bool, false>());
+    windows(std::integral_constant<int, 0>());
   }
   mark(4);
   hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned((f.dim + kLanes - 1) / kLanes), unsigned(f.ndir * kPartRows)),
