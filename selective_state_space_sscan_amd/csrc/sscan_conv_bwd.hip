@@ -8,16 +8,18 @@
 //   dbias   = sum over batch rows and t of g[t]
 // The taps sit in the same fixed five-token window as the forward's (x[t-3 .. t+1],
 // zeros where the kernel has no tap), so every index below is a compile-time one.
-// dx is written per run of eight tokens; the weight and bias sums are reduced over
-// the wave's 64 runs with a fixed butterfly, stored per (run chunk, batch row,
-// channel), and summed in a fixed order by a second kernel: results are bitwise
-// reproducible (no atomics).
+// dx is written per run of eight tokens; a thread takes four runs (each pass of the
+// wave covers 64 consecutive runs) and keeps its weight and bias sums in registers,
+// which are then reduced over the wave with a fixed butterfly, stored per (run
+// chunk, batch row, channel), and summed in a fixed order by a second kernel:
+// results are bitwise reproducible (no atomics).
 #include "sscan_device.h"
 
 namespace sscan {
 namespace {
 
-constexpr int kRun = 8;                      // tokens per thread
+constexpr int kRun = 8;                      // tokens per thread and pass
+constexpr int kReps = 4;                     // passes per thread before the weight sums leave registers
 constexpr int kRows = 4;                     // channels per block (one wave each)
 constexpr int kParts = kConvTaps + 1;        // five window taps + bias per partial
 constexpr int kXSpan = kRun + 8;             // x[t0 - 4 .. t0 + 12)
@@ -31,12 +33,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 template <bool IO_BF16, bool SILU>
-__global__ __launch_bounds__(kLanes * kRows) void conv1d_bwd_kernel(ConvBwdArgs a, float* __restrict__ part, int vec) {
+__global__ __launch_bounds__(kLanes * kRows) void conv1d_bwd_kernel(ConvBwdArgs a, float* __restrict__ part, int vec,
+                                                                    int duvec) {
   using IO = Io<IO_BF16>;
   using T = typename IO::T;
   const int64_t chunk = blockIdx.x;
-  const int64_t t0 = (chunk * kLanes + threadIdx.x) * kRun;  // may be past the row's end (zeros)
-  const bool full = vec && t0 + kRun <= a.len;
   for (int64_t d = int64_t(blockIdx.y) * kRows + threadIdx.y; d < a.dim; d += int64_t(gridDim.y) * kRows) {
     // tap k of the window multiplies x[t - 3 + k]: tap j of the kernel sits at k = 3 - left + j
     float cw[kConvTaps];
@@ -52,6 +53,16 @@ __global__ __launch_bounds__(kLanes * kRows) void conv1d_bwd_kernel(ConvBwdArgs 
       const float* du = a.du + row;
       auto ld = [&](const T* p, int64_t t) { return (t >= 0 && t < a.len) ? IO::load(p, t) : 0.0f; };
       auto ldu = [&](int64_t t) { return (t >= 0 && t < a.len) ? du[t] : 0.0f; };
+      // the weight and bias sums of this thread's kReps runs (each pass of the wave
+      // covers 64 consecutive runs)
+      float ps[kParts];
+#pragma unroll
+      for (int k = 0; k < kParts; ++k) ps[k] = 0.0f;
+      for (int rep = 0; rep < kReps; ++rep) {
+      const int64_t pass0 = (chunk * kReps + rep) * kLanes * kRun;  // first token of this pass
+      if (pass0 >= a.len) break;                                      // wave-uniform
+      const int64_t t0 = pass0 + int64_t(threadIdx.x) * kRun;       // may be past the row's end (zeros)
+      const bool full = vec && t0 + kRun <= a.len;
       float xs[kXSpan];  // x[t0 - 4 + i]
       float gs[kGSpan];  // g[t0 - 1 + i]
       if (full) {
@@ -79,10 +90,25 @@ __global__ __launch_bounds__(kLanes * kRows) void conv1d_bwd_kernel(ConvBwdArgs 
         xs[k] = ld(x, t0 - 4 + k);
         xs[kRun + 4 + k] = ld(x, t0 + kRun + k);
       }
+      // du over t0 - 1 .. t0 + 10: the run's own eight as two 16-byte loads where the
+      // rows allow, the halo as single loads
+      float dus[kGSpan];
+      if (full && duvec) {
+        const float4* q = reinterpret_cast<const float4*>(du + t0);
+        const float4 v0 = q[0], v1 = q[1];
+        dus[1] = v0.x, dus[2] = v0.y, dus[3] = v0.z, dus[4] = v0.w;
+        dus[5] = v1.x, dus[6] = v1.y, dus[7] = v1.z, dus[8] = v1.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) dus[1 + k] = ldu(t0 + k);
+      }
+      dus[0] = ldu(t0 - 1);
+#pragma unroll
+      for (int k = 0; k < kGSpan - 1 - kRun; ++k) dus[1 + kRun + k] = ldu(t0 + kRun + k);
       // g over t = t0 - 1 + i: pre from the window x[t - 3 .. t + 1] = xs[i .. i + 4]
 #pragma unroll
       for (int i = 0; i < kGSpan; ++i) {
-        const float d_u = ldu(t0 - 1 + i);
+        const float d_u = dus[i];
         if (SILU) {
           float pre = cb;
 #pragma unroll
@@ -119,9 +145,6 @@ __global__ __launch_bounds__(kLanes * kRows) void conv1d_bwd_kernel(ConvBwdArgs 
       }
       // this run's share of the weight and bias sums: t = t0 + m inside the row (g is
       // zero outside it), window x[t - 3 + k] = xs[m + 1 + k]
-      float ps[kParts];
-#pragma unroll
-      for (int k = 0; k < kParts; ++k) ps[k] = 0.0f;
 #pragma unroll
       for (int m = 0; m < kRun; ++m) {
         const float g = gs[m + 1];
@@ -129,6 +152,7 @@ __global__ __launch_bounds__(kLanes * kRows) void conv1d_bwd_kernel(ConvBwdArgs 
         for (int k = 0; k < kConvTaps; ++k) ps[k] = fmaf(g, xs[m + 1 + k], ps[k]);
         ps[kConvTaps] += g;
       }
+      }  // passes
 #pragma unroll
       for (int k = 0; k < kParts; ++k) ps[k] = wave_sum(ps[k]);
       if (threadIdx.x < kParts) {
@@ -173,7 +197,7 @@ bool aligned16_c(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) 
 
 int64_t conv_bwd_chunks(int64_t len) {
   const int64_t runs = (len + kRun - 1) / kRun;
-  return std::max<int64_t>(1, (runs + kLanes - 1) / kLanes);
+  return std::max<int64_t>(1, (runs + kLanes * kReps - 1) / (kLanes * kReps));
 }
 
 size_t conv_bwd_partial_floats(int64_t batch, int64_t dim, int64_t len) {
@@ -194,17 +218,18 @@ hipError_t launch_conv1d_bwd(const ConvBwdArgs& a, float* part, hipStream_t stre
   const dim3 block(kLanes, kRows);
   const size_t esz = a.io_bf16 ? 2 : 4;
   const int vec = (size_t(a.len) * esz) % 16 == 0 && aligned16_c(a.x) && aligned16_c(a.dx);
+  const int duvec = vec && a.len % 4 == 0 && aligned16_c(a.du);
   if (a.io_bf16) {
     if (a.silu) {
-      hipLaunchKernelGGL((conv1d_bwd_kernel<true, true>), grid, block, 0, stream, a, part, vec);
+      hipLaunchKernelGGL((conv1d_bwd_kernel<true, true>), grid, block, 0, stream, a, part, vec, duvec);
     } else {
-      hipLaunchKernelGGL((conv1d_bwd_kernel<true, false>), grid, block, 0, stream, a, part, vec);
+      hipLaunchKernelGGL((conv1d_bwd_kernel<true, false>), grid, block, 0, stream, a, part, vec, duvec);
     }
   } else {
     if (a.silu) {
-      hipLaunchKernelGGL((conv1d_bwd_kernel<false, true>), grid, block, 0, stream, a, part, vec);
+      hipLaunchKernelGGL((conv1d_bwd_kernel<false, true>), grid, block, 0, stream, a, part, vec, duvec);
     } else {
-      hipLaunchKernelGGL((conv1d_bwd_kernel<false, false>), grid, block, 0, stream, a, part, vec);
+      hipLaunchKernelGGL((conv1d_bwd_kernel<false, false>), grid, block, 0, stream, a, part, vec, duvec);
     }
   }
   hipLaunchKernelGGL(conv1d_bwd_reduce_kernel, dim3(unsigned((a.dim * kParts + 255) / 256)), dim3(256), 0, stream, a,
