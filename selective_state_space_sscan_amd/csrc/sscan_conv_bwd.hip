@@ -59,100 +59,100 @@ __global__ __launch_bounds__(kLanes * kRows) void conv1d_bwd_kernel(ConvBwdArgs 
 #pragma unroll
       for (int k = 0; k < kParts; ++k) ps[k] = 0.0f;
       for (int rep = 0; rep < kReps; ++rep) {
-      const int64_t pass0 = (chunk * kReps + rep) * kLanes * kRun;  // first token of this pass
-      if (pass0 >= a.len) break;                                      // wave-uniform
-      const int64_t t0 = pass0 + int64_t(threadIdx.x) * kRun;       // may be past the row's end (zeros)
-      const bool full = vec && t0 + kRun <= a.len;
-      float xs[kXSpan];  // x[t0 - 4 + i]
-      float gs[kGSpan];  // g[t0 - 1 + i]
-      if (full) {
-        if (IO_BF16) {
-          const uint4 v = *reinterpret_cast<const uint4*>(x + t0);
-          const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+        const int64_t pass0 = (chunk * kReps + rep) * kLanes * kRun;  // first token of this pass
+        if (pass0 >= a.len) break;                                      // wave-uniform
+        const int64_t t0 = pass0 + int64_t(threadIdx.x) * kRun;       // may be past the row's end (zeros)
+        const bool full = vec && t0 + kRun <= a.len;
+        float xs[kXSpan];  // x[t0 - 4 + i]
+        float gs[kGSpan];  // g[t0 - 1 + i]
+        if (full) {
+          if (IO_BF16) {
+            const uint4 v = *reinterpret_cast<const uint4*>(x + t0);
+            const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            xs[4 + 2 * k] = bf16_lo(ws[k]);
-            xs[5 + 2 * k] = bf16_hi(ws[k]);
+            for (int k = 0; k < 4; ++k) {
+              xs[4 + 2 * k] = bf16_lo(ws[k]);
+              xs[5 + 2 * k] = bf16_hi(ws[k]);
+            }
+          } else {
+            const float4* p = reinterpret_cast<const float4*>(x + t0);
+            const float4 v0 = p[0], v1 = p[1];
+            const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) xs[4 + k] = f[k];
           }
         } else {
-          const float4* p = reinterpret_cast<const float4*>(x + t0);
-          const float4 v0 = p[0], v1 = p[1];
-          const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-          for (int k = 0; k < 8; ++k) xs[4 + k] = f[k];
+          for (int k = 0; k < kRun; ++k) xs[4 + k] = ld(x, t0 + k);
         }
-      } else {
 #pragma unroll
-        for (int k = 0; k < kRun; ++k) xs[4 + k] = ld(x, t0 + k);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        xs[k] = ld(x, t0 - 4 + k);
-        xs[kRun + 4 + k] = ld(x, t0 + kRun + k);
-      }
-      // du over t0 - 1 .. t0 + 10: the run's own eight as two 16-byte loads where the
-      // rows allow, the halo as single loads
-      float dus[kGSpan];
-      if (full && duvec) {
-        const float4* q = reinterpret_cast<const float4*>(du + t0);
-        const float4 v0 = q[0], v1 = q[1];
-        dus[1] = v0.x, dus[2] = v0.y, dus[3] = v0.z, dus[4] = v0.w;
-        dus[5] = v1.x, dus[6] = v1.y, dus[7] = v1.z, dus[8] = v1.w;
-      } else {
-#pragma unroll
-        for (int k = 0; k < kRun; ++k) dus[1 + k] = ldu(t0 + k);
-      }
-      dus[0] = ldu(t0 - 1);
-#pragma unroll
-      for (int k = 0; k < kGSpan - 1 - kRun; ++k) dus[1 + kRun + k] = ldu(t0 + kRun + k);
-      // g over t = t0 - 1 + i: pre from the window x[t - 3 .. t + 1] = xs[i .. i + 4]
-#pragma unroll
-      for (int i = 0; i < kGSpan; ++i) {
-        const float d_u = dus[i];
-        if (SILU) {
-          float pre = cb;
-#pragma unroll
-          for (int k = 0; k < kConvTaps; ++k) pre = fmaf(cw[k], xs[i + k], pre);
-          const float s = rcp_hw(1.0f + exp2_hw(-pre * kLog2e));
-          gs[i] = d_u * (s * fmaf(pre, 1.0f - s, 1.0f));
+        for (int k = 0; k < 4; ++k) {
+          xs[k] = ld(x, t0 - 4 + k);
+          xs[kRun + 4 + k] = ld(x, t0 + kRun + k);
+        }
+        // du over t0 - 1 .. t0 + 10: the run's own eight as two 16-byte loads where the
+        // rows allow, the halo as single loads
+        float dus[kGSpan];
+        if (full && duvec) {
+          const float4* q = reinterpret_cast<const float4*>(du + t0);
+          const float4 v0 = q[0], v1 = q[1];
+          dus[1] = v0.x, dus[2] = v0.y, dus[3] = v0.z, dus[4] = v0.w;
+          dus[5] = v1.x, dus[6] = v1.y, dus[7] = v1.z, dus[8] = v1.w;
         } else {
-          gs[i] = d_u;
+#pragma unroll
+          for (int k = 0; k < kRun; ++k) dus[1 + k] = ldu(t0 + k);
         }
-      }
-      // dx[t0 + m] = sum_k cw[k] g[t0 + m + 3 - k] = sum_k cw[k] gs[m + 4 - k]
-      float dxo[kRun];
+        dus[0] = ldu(t0 - 1);
 #pragma unroll
-      for (int m = 0; m < kRun; ++m) {
-        float acc = 0.0f;
+        for (int k = 0; k < kGSpan - 1 - kRun; ++k) dus[1 + kRun + k] = ldu(t0 + kRun + k);
+        // g over t = t0 - 1 + i: pre from the window x[t - 3 .. t + 1] = xs[i .. i + 4]
 #pragma unroll
-        for (int k = 0; k < kConvTaps; ++k) acc = fmaf(cw[k], gs[m + 4 - k], acc);
-        dxo[m] = acc;
-      }
-      T* dx = static_cast<T*>(a.dx) + row;
-      if (full) {
-        if (IO_BF16) {
-          *reinterpret_cast<uint4*>(dx + t0) = make_uint4(pack_bf16x2(dxo[0], dxo[1]), pack_bf16x2(dxo[2], dxo[3]),
-                                                          pack_bf16x2(dxo[4], dxo[5]), pack_bf16x2(dxo[6], dxo[7]));
+        for (int i = 0; i < kGSpan; ++i) {
+          const float d_u = dus[i];
+          if (SILU) {
+            float pre = cb;
+#pragma unroll
+            for (int k = 0; k < kConvTaps; ++k) pre = fmaf(cw[k], xs[i + k], pre);
+            const float s = rcp_hw(1.0f + exp2_hw(-pre * kLog2e));
+            gs[i] = d_u * (s * fmaf(pre, 1.0f - s, 1.0f));
+          } else {
+            gs[i] = d_u;
+          }
+        }
+        // dx[t0 + m] = sum_k cw[k] g[t0 + m + 3 - k] = sum_k cw[k] gs[m + 4 - k]
+        float dxo[kRun];
+#pragma unroll
+        for (int m = 0; m < kRun; ++m) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < kConvTaps; ++k) acc = fmaf(cw[k], gs[m + 4 - k], acc);
+          dxo[m] = acc;
+        }
+        T* dx = static_cast<T*>(a.dx) + row;
+        if (full) {
+          if (IO_BF16) {
+            *reinterpret_cast<uint4*>(dx + t0) = make_uint4(pack_bf16x2(dxo[0], dxo[1]), pack_bf16x2(dxo[2], dxo[3]),
+                                                            pack_bf16x2(dxo[4], dxo[5]), pack_bf16x2(dxo[6], dxo[7]));
+          } else {
+            float4* p = reinterpret_cast<float4*>(dx + t0);
+            p[0] = make_float4(dxo[0], dxo[1], dxo[2], dxo[3]);
+            p[1] = make_float4(dxo[4], dxo[5], dxo[6], dxo[7]);
+          }
         } else {
-          float4* p = reinterpret_cast<float4*>(dx + t0);
-          p[0] = make_float4(dxo[0], dxo[1], dxo[2], dxo[3]);
-          p[1] = make_float4(dxo[4], dxo[5], dxo[6], dxo[7]);
+#pragma unroll
+          for (int m = 0; m < kRun; ++m)
+            if (t0 + m < a.len) IO::store(dx, t0 + m, dxo[m]);
         }
-      } else {
+        // this run's share of the weight and bias sums: t = t0 + m inside the row (g is
+        // zero outside it), window x[t - 3 + k] = xs[m + 1 + k]
 #pragma unroll
-        for (int m = 0; m < kRun; ++m)
-          if (t0 + m < a.len) IO::store(dx, t0 + m, dxo[m]);
+        for (int m = 0; m < kRun; ++m) {
+          const float g = gs[m + 1];
+#pragma unroll
+          for (int k = 0; k < kConvTaps; ++k) ps[k] = fmaf(g, xs[m + 1 + k], ps[k]);
+          ps[kConvTaps] += g;
+        }
       }
-      // this run's share of the weight and bias sums: t = t0 + m inside the row (g is
-      // zero outside it), window x[t - 3 + k] = xs[m + 1 + k]
-#pragma unroll
-      for (int m = 0; m < kRun; ++m) {
-        const float g = gs[m + 1];
-#pragma unroll
-        for (int k = 0; k < kConvTaps; ++k) ps[k] = fmaf(g, xs[m + 1 + k], ps[k]);
-        ps[kConvTaps] += g;
-      }
-      }  // passes
 #pragma unroll
       for (int k = 0; k < kParts; ++k) ps[k] = wave_sum(ps[k]);
       if (threadIdx.x < kParts) {
