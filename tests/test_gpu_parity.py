@@ -243,3 +243,33 @@ def test_step_size_softplus_accuracy():
     rel = np.abs(got - ref) / np.abs(ref)
     print(f"softplus max rel err {rel.max():.3e} at x={x[np.argmax(rel)]:.4g}", flush=True)
     assert rel.max() <= 2e-6
+
+
+DEGENERATE = [
+    # A = 0: no decay, the state is the running sum of dt u B (Mamba2 page section
+    # 2.2 with exp(0) = 1); several segments, so the carry chains plain sums
+    ("A-zero", dict(A=0.0)),
+    # dt -> 0 (softplus of a very negative input): the state never moves and the
+    # output is D u alone, gated
+    ("dt-to-zero", dict(delta=-60.0)),
+    # very large steps (dt = 40): exp(dt A) is at most about 4e-7, so each token all
+    # but forgets everything before it and y_t is close to dt_t u_t (C_t . B_t) + D u_t
+    ("dt-large", dict(delta=40.0)),
+]
+
+
+@pytest.mark.parametrize("name,mod", DEGENERATE, ids=[d[0] for d in DEGENERATE])
+@pytest.mark.parametrize("bidir", [False, True])
+def test_degenerate_regimes(name, mod, bidir):
+    """The method's degenerate regimes over segmented sequences (the aggregate and
+    carry steps run): A = 0, dt -> 0, dt -> infinity."""
+    x = I.make_inputs(2, 96, 3000, bidir=bidir, io_dtype="f32", bc_dtype="f32",
+                      seed=zlib.crc32(name.encode()) % 10000 + int(bidir))
+    if "A" in mod:
+        for p in x.dirs:
+            p.A.fill_(mod["A"])
+    if "delta" in mod:
+        x.delta.fill_(mod["delta"])
+        for p in x.dirs:
+            p.delta_bias.zero_()
+    check(gpu_run(x), oracle_run(x), "f32", f"{name} bidir={bidir}")
