@@ -964,3 +964,61 @@ def run_inputs(x, softplus: bool = True, out=None, workspace=None, events: Optio
     f, r = x.dirs
     mk = lambda p: dict(delta=x.delta, delta_bias=p.delta_bias, A=p.A, B=p.B, C=p.C, D=p.D)
     return bidir(x.u, x.z, mk(f), mk(r), softplus=softplus, out=out, workspace=workspace, events=events)
+
+
+# ---- autograd ---------------------------------------------------------------------
+# torch.autograd.Function wrappers: the forward call, and in backward the matching
+# backward entry point (the forward states are recomputed there, nothing beyond the
+# inputs is kept).  Argument marshalling only, like the functions above.
+
+class _ScanFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, u, delta, A, B, C, D, z, delta_bias, softplus, reverse):
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias)
+        ctx.softplus, ctx.reverse = softplus, reverse
+        return fwd(u, delta, A, B, C, D, z, delta_bias, softplus=softplus, reverse=reverse)
+
+    @staticmethod
+    def backward(ctx, dout):
+        u, delta, A, B, C, D, z, delta_bias = ctx.saved_tensors
+        g = bwd(u, delta, A, B, C, dout.contiguous(), D=D, z=z, delta_bias=delta_bias, softplus=ctx.softplus,
+                reverse=ctx.reverse)
+        return (g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"], g["ddelta_bias"], None, None)
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                   reverse: bool = False) -> torch.Tensor:
+    """``fwd`` with gradients: differentiable in every tensor argument (``sscan_bwd``
+    in the backward pass)."""
+    return _ScanFn.apply(u, delta, A, B, C, D, z, delta_bias, softplus, reverse)
+
+
+class _BidirFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, u, z, d_f, A_f, B_f, C_f, D_f, bias_f, d_r, A_r, B_r, C_r, D_r, bias_r, softplus):
+        ctx.save_for_backward(u, z, d_f, A_f, B_f, C_f, D_f, bias_f, d_r, A_r, B_r, C_r, D_r, bias_r)
+        ctx.softplus = softplus
+        pf = dict(delta=d_f, A=A_f, B=B_f, C=C_f, D=D_f, delta_bias=bias_f)
+        pr = dict(delta=d_r, A=A_r, B=B_r, C=C_r, D=D_r, delta_bias=bias_r)
+        return bidir(u, z, pf, pr, softplus=softplus)
+
+    @staticmethod
+    def backward(ctx, dout):
+        u, z, d_f, A_f, B_f, C_f, D_f, bias_f, d_r, A_r, B_r, C_r, D_r, bias_r = ctx.saved_tensors
+        pf = dict(delta=d_f, A=A_f, B=B_f, C=C_f, D=D_f, delta_bias=bias_f)
+        pr = dict(delta=d_r, A=A_r, B=B_r, C=C_r, D=D_r, delta_bias=bias_r)
+        g = bidir_bwd(u, z, dout.contiguous(), pf, pr, softplus=ctx.softplus)
+        gf, gr = g["fwd"], g["rev"]
+        # a delta tensor shared by the two directions appears twice in the inputs, and
+        # autograd adds the two gradients it receives for it
+        return (g["du"], g["dz"],
+                gf["ddelta"], gf["dA"], gf["dB"], gf["dC"], gf["dD"], gf["ddelta_bias"],
+                gr["ddelta"], gr["dA"], gr["dB"], gr["dC"], gr["dD"], gr["ddelta_bias"], None)
+
+
+def selective_scan_bidir(u, z, fwd_params: dict, rev_params: dict, softplus: bool = True) -> torch.Tensor:
+    """``bidir`` with gradients (``sscan_bidir_bwd`` in the backward pass); each
+    parameter dict holds delta, A, B, C and optional D, delta_bias."""
+    f, r = fwd_params, rev_params
+    return _BidirFn.apply(u, z, f["delta"], f["A"], f["B"], f["C"], f.get("D"), f.get("delta_bias"),
+                          r["delta"], r["A"], r["B"], r["C"], r.get("D"), r.get("delta_bias"), softplus)
