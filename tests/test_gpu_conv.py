@@ -138,8 +138,9 @@ BWD_CONV_CASES = [
 def test_bwd_conv_parity(name, b, d, L, bidir, io, bc, width, same, silu, reverse):
     """Every gradient of the backward through the convolution against the oracle
     (the scan's backward at u = conv(x), then the convolution's backward).  The
-    kernels recompute u in the I/O dtype, so a bf16 call is held to the bf16 bound
-    in all its gradients; float32 calls to 1e-4."""
+    kernels recompute u in fp32 as the fused forward computes it; a bf16 call is
+    held to the bf16 bound in all its gradients (its inputs and stored gradients
+    are bf16), float32 calls to 1e-4."""
     seed = zlib.crc32(name.encode()) % 10000
     x = I.make_inputs(b, d, L, bidir=bidir, io_dtype=io, bc_dtype=bc, seed=seed)
     cp = conv_params(name, d, width, same, silu)
