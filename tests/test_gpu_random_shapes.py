@@ -243,3 +243,58 @@ def test_random_conv_forward_and_backward(c):
         tol = TOL["bf16" if (a.dtype == torch.bfloat16 or c["io"] == "bf16") else "f32"]
         m = metrics(I.f64(a.cpu()), b)
         assert m["floored_max"] <= tol, (conv_name(c), what, m)
+
+
+# ---- state I/O: forward with an entry state and the final state, and its backward
+
+def draw_states(seed, n):
+    rng = np.random.default_rng(seed)
+    return [dict(b=int(rng.integers(1, 4)), d=int(rng.choice([3, 64, 65, 130])),
+                 L=int(rng.choice([0, 1, 17, 200, 600, 1500])), reverse=bool(rng.integers(0, 2)),
+                 io=str(rng.choice(["f32", "bf16"])), bc=str(rng.choice(["f32", "bf16"])),
+                 h0=bool(rng.integers(0, 4) > 0), dh_last=bool(rng.integers(0, 4) > 0),
+                 seed=int(rng.integers(0, 1 << 30))) for _ in range(n)]
+
+
+STATES = draw_states(2028, 10)
+
+
+def state_name(c):
+    return (f"b{c['b']}-d{c['d']}-L{c['L']}-{'rev' if c['reverse'] else 'fwd'}-{c['io']}-{c['bc']}"
+            f"{'-h0' if c['h0'] else ''}{'-dhl' if c['dh_last'] else ''}")
+
+
+@pytest.mark.parametrize("c", STATES, ids=[state_name(c) for c in STATES])
+def test_random_state_io_forward_and_backward(c):
+    rng = np.random.default_rng(c["seed"])
+    x = I.make_inputs(c["b"], c["d"], c["L"], io_dtype=c["io"], bc_dtype=c["bc"], seed=c["seed"])
+    h0 = torch.from_numpy(rng.standard_normal((c["b"], c["d"], 16), dtype=np.float32)) if c["h0"] else None
+    dhl = torch.from_numpy(rng.standard_normal((c["b"], c["d"], 16), dtype=np.float32)) if c["dh_last"] else None
+    g = torch.from_numpy(rng.standard_normal((c["b"], c["d"], c["L"]), dtype=np.float32)).to(x.u.dtype)
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    dv = lambda t: None if t is None else t.to(DEV)
+    y, hl = sscan.fwd_state(xd.u, xd.delta, p.A, p.B, p.C, p.D, xd.z, p.delta_bias, h0=dv(h0),
+                            reverse=c["reverse"])
+    r = sscan.bwd_state(xd.u, xd.delta, p.A, p.B, p.C, g.to(DEV), D=p.D, z=xd.z, delta_bias=p.delta_bias,
+                        h0=dv(h0), dh_last=dv(dhl), reverse=c["reverse"])
+    torch.cuda.synchronize()
+    x64 = I.as_f64_dict(x)
+    q = x64["dirs"][0]
+    h064 = I.f64(h0) if c["h0"] else None
+    ref_y, ref_h = oracle.sscan_fwd(x64["u"], x64["delta"], q["A"], q["B"], q["C"], q["D"], x64["z"],
+                                    q["delta_bias"], reverse=c["reverse"], h0=h064, return_last_state=True,
+                                    nthreads=NTHREADS)
+    ref = oracle.sscan_bwd(x64["u"], x64["z"], I.f64(g), [dict(delta=x64["delta"], **q)], reverse=c["reverse"],
+                           h0=h064, dh_last=I.f64(dhl) if c["dh_last"] else None, return_dh0=True,
+                           nthreads=NTHREADS)
+    pairs = [("y", y, ref_y), ("h_last", hl, ref_h), ("du", r["du"], ref["du"]), ("dz", r["dz"], ref["dz"]),
+             ("dh0", r["dh0"], ref["dh0"])]
+    pairs += [(n, r[n], ref["dirs"][0][n]) for n in ("ddelta", "ddelta_bias", "dA", "dB", "dC", "dD")]
+    for what, a, b in pairs:
+        if b is None or np.asarray(b).size == 0:
+            continue
+        # the bound of the stored dtype (the oracle reads the same bf16 input values)
+        tol = TOL["bf16" if a.dtype == torch.bfloat16 else "f32"]
+        m = metrics(I.f64(a.cpu()), b)
+        assert m["floored_max"] <= tol, (state_name(c), what, m)
