@@ -123,7 +123,8 @@ static void* run_rows(void* arg) {
 static int run(job proto, int nthreads) {
     const int64_t rows = proto.batch * proto.dim;
     if (proto.batch < 0 || proto.dim < 0 || proto.len < 0 || proto.dstate < 0) return -2;
-    if (rows == 0 || proto.len == 0) return 0;
+    /* with no tokens the rows still run: each copies its entry state to h_last */
+    if (rows == 0) return 0;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > rows) nthreads = (int)rows;
     job* jobs = (job*)calloc((size_t)nthreads, sizeof(job));

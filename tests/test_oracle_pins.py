@@ -361,6 +361,22 @@ def test_p12_len1_step_closed_form(oracle_lib):
     np.testing.assert_allclose(out[:, :, 0], ref, rtol=1e-13, atol=1e-14)
 
 
+@pytest.mark.parametrize("reverse", [False, True])
+def test_p12_no_tokens_hand_the_state_through(oracle_lib, reverse):
+    """A piece of a stream with no tokens applies the recurrence zero times, so the
+    final state is the entry state (zeros without one) and the output is empty.
+    Catches a final state left unwritten when the sequence is empty."""
+    rng = np.random.default_rng(123)
+    b, d, N = 2, 5, 16
+    u, z, p = _case(rng, b, d, 0, N)
+    h0 = rng.normal(size=(b, d, N))
+    out, hl = _fwd(oracle_lib, u, p, z=z, reverse=reverse, h0=h0, return_last_state=True)
+    assert out.shape == (b, d, 0)
+    np.testing.assert_array_equal(hl, h0)
+    _, hl0 = _fwd(oracle_lib, u, p, z=z, reverse=reverse, return_last_state=True)
+    np.testing.assert_array_equal(hl0, np.zeros((b, d, N)))
+
+
 # --- scalar helpers and special values ------------------------------------------------------------
 
 @pytest.mark.parametrize("x", [-700.0, -60.0, -20.0, -9.2, -3.0, -1e-8, 0.0, 1e-8, 2.5, 20.0, 60.0, 700.0])
