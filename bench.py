@@ -55,9 +55,12 @@ def valu_view(valu_doc, kernel: str, kernel_ms: float):
     if not k.get("valu_insts_per_wave"):
         return None
     floor_ms = k["valu_insts_per_wave"] * k["waves_per_launch"] * CYCLES_PER_VALU_INST / (SIMDS * CLOCK_HZ) * 1e3
-    return {"kernel": kernel, "busy_pct": k["valu_busy_pct"], "insts_per_wave": k["valu_insts_per_wave"],
+    view = {"kernel": kernel, "busy_pct": k["valu_busy_pct"], "insts_per_wave": k["valu_insts_per_wave"],
             "waves_per_launch": k["waves_per_launch"], "trans_share": k["trans_share"],
             "issue_floor_ms": floor_ms, "frac_of_issue_floor": floor_ms / kernel_ms if kernel_ms else None}
+    if "mean_occupancy_per_cu" in k:
+        view["mean_occupancy_per_cu"] = k["mean_occupancy_per_cu"]
+    return view
 
 
 def hbm_roofline(kernel: str, nbytes: int, kernel_ms: float, traffic=None) -> dict:
@@ -682,6 +685,11 @@ def main():
             per_kernel[name].append(v)
         per_call.append(ev.total_ms())
     kernel_ms = {name: sum(v) / len(v) for name, v in per_kernel.items()}
+    if sscan.scan_plan(cfg.batch, cfg.dim, cfg.len, cfg.dstate, bidir=cfg.ndir == 2)["nseg"] == 1:
+        # one segment per row: no aggregate or carry kernel runs, and the interval
+        # between their events is only the events' own cost
+        for name in ("aggregate", "carry"):
+            kernel_ms.pop(name)
     dominant = max(kernel_ms, key=kernel_ms.get)
     footprint = ws_bytes + sum(t.numel() * t.element_size() for t in xd.tensors()) + y.numel() * y.element_size()
     warm = None

@@ -14,12 +14,14 @@ FETCH_DIR / WRITE_DIR are the rocprofv3 output directories (containing
 *counter_collection.csv) of ``bench.py --copy-calibration`` runs.
 
 VALU issue of the same kernels, from one ``rocprofv3 --pmc VALUBusy SQ_WAVES
-SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32`` run of bench.py:
+SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32`` run of bench.py (MeanOccupancyPerCU may be
+added to the same pass):
 
   python -m selective_state_space_sscan_amd.profiling valu SQ_DIR OUT.json
 
 gives per kernel the VALUBusy percentage, the VALU instructions per wave (and the
-share of transcendentals) and the waves per launch, keyed by the same source hash.
+share of transcendentals), the waves per launch and, when counted, the mean number
+of resident waves per compute unit, keyed by the same source hash.
 """
 from __future__ import annotations
 
@@ -99,7 +101,7 @@ def summarize(fetch_dir: str, write_dir: str) -> dict:
             "copy_bytes": COPY_BYTES, "per_launch": steps}
 
 
-VALU_COUNTERS = ("VALUBusy", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32")
+VALU_COUNTERS = ("VALUBusy", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "MeanOccupancyPerCU")
 
 
 def summarize_valu(sq_dir: str) -> dict:
@@ -107,11 +109,13 @@ def summarize_valu(sq_dir: str) -> dict:
     transcendental instructions per wave, over the launches of one counter run."""
     vals = collections.defaultdict(lambda: collections.defaultdict(float))
     disp = collections.defaultdict(set)
+    seen = collections.defaultdict(set)  # counters present per kernel
     for f, r in _rows(sq_dir):
         key = next((v for k, v in KERNELS.items() if k in r["Kernel_Name"]), None)
         if key is None or r["Counter_Name"] not in VALU_COUNTERS:
             continue
         vals[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        seen[key].add(r["Counter_Name"])
         disp[key].add((f, r["Dispatch_Id"]))
     out = {}
     for k, v in vals.items():
@@ -121,6 +125,8 @@ def summarize_valu(sq_dir: str) -> dict:
                   "valu_insts_per_wave": v["SQ_INSTS_VALU"] / v["SQ_WAVES"] if v["SQ_WAVES"] else None,
                   "trans_share": v["SQ_INSTS_VALU_TRANS_F32"] / v["SQ_INSTS_VALU"] if v["SQ_INSTS_VALU"] else None,
                   "launches": n}
+        if "MeanOccupancyPerCU" in seen[k]:
+            out[k]["mean_occupancy_per_cu"] = v["MeanOccupancyPerCU"] / n
     return {"kernel_source_sha256": kernel_source_hash(), "per_launch": out}
 
 
