@@ -90,6 +90,49 @@ def test_random_permutation_order():
     run_both("perm", 1, 64, 20, 20, [X], index=perm)
 
 
+@pytest.mark.parametrize("h,w", [(20, 20), (256, 256)])
+def test_index_entries_outside_the_map_read_as_zero(h, w):
+    """The index order with entries outside [0, h*w): such a visit step reads u, delta,
+    B and C as 0 (the state still decays by exp(softplus(bias) A) there) and its
+    output goes nowhere, and a token no entry names gets nothing from the index
+    directions -- the documented behaviour of sscan_multi for a non-permutation.
+    Expected values: the fp64 oracle on the inputs gathered that way, put back at the
+    named tokens.  256 x 256 takes the flat-order gather, 20 x 20 the row groups."""
+    L = h * w
+    rng = np.random.default_rng(h)
+    index = rng.permutation(L).astype(np.int64)
+    bad = rng.choice(L, size=max(3, L // 50), replace=False)
+    index[bad] = rng.choice([-1, -1000, L, L + 17], size=bad.size)
+    x, dirs = draw(f"bad-index-{h}", 1, 64, h, w, 2, "f32", "f32")
+    xd = x.to(DEV)
+    gd = [dict(delta=xd.delta, delta_bias=p.delta_bias.to(DEV), A=p.A.to(DEV), B=p.B.to(DEV), C=p.C.to(DEV),
+               D=p.D.to(DEV)) for p in dirs]
+    got = sscan.multi(xd.u, xd.z, gd, [X, XR], h, w, index=torch.as_tensor(index, dtype=torch.int32).to(DEV))
+    torch.cuda.synchronize()
+    x64 = I.as_f64_dict(x)
+    valid = (index >= 0) & (index < L)
+    safe = np.where(valid, index, 0)
+
+    def gat(a):
+        a = np.asarray(a, np.float64)
+        return np.ascontiguousarray(np.where(valid, a[..., safe], 0.0))
+
+    total = np.zeros(x64["u"].shape)
+    for p, rev in zip(dirs, (False, True)):
+        y = oracle.sscan_fwd(gat(x64["u"]), gat(x64["delta"]), I.f64(p.A), gat(I.f64(p.B)), gat(I.f64(p.C)),
+                             I.f64(p.D), None, I.f64(p.delta_bias), reverse=rev, nthreads=NTHREADS)
+        total[..., index[valid]] += y[..., valid]
+    zz = x64["z"]
+    ref = total * (zz / (1.0 + np.exp(-zz)))
+    unnamed = np.setdiff1d(np.arange(L), index[valid])
+    assert unnamed.size == bad.size
+    g = I.f64(got.cpu())
+    assert np.all(g[..., unnamed] == 0.0)
+    m = metrics(g, ref)
+    print(f"bad index {h}x{w}: floored {m['floored_max']:.3e}", flush=True)
+    assert m["floored_max"] <= TOL["f32"], m
+
+
 def test_yolo_stage1_map_cross4():
     """The Mamba-YOLO stage-1 map (128 x 128 tokens, 192 channels, bf16) in the
     four-direction cross order (two batch rows)."""
