@@ -6,7 +6,7 @@ a child process with the matching sanitizer runtime preloaded:
 * the C ABI's argument checks (sscan_capi.cpp) compiled with the host sanitizers
   and linked with the library's other objects; test_abi_cpu.py then drives every
   validate entry point, the workspace-size and plan queries and the spiral order
-  through it (no kernel is launched);
+  through it, and test_abi_fuzz_cpu.py its randomised calls (no kernel is launched);
 * the fp64 oracle's C sources built by gcc with the same sanitizers; the oracle
   pin tests then run on it.
 
@@ -60,7 +60,8 @@ def test_c_abi_checks_under_asan_ubsan(tmp_path):
                    check=True, capture_output=True)
     subprocess.run([B.hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + san + ["-o", lib, capi] + objs,
                    check=True, capture_output=True)
-    _run_tests(["tests/test_abi_cpu.py"], {"SSCAN_TEST_LIBRARY": lib, "LD_PRELOAD": rts[0]}, tmp_path)
+    _run_tests(["tests/test_abi_cpu.py", "tests/test_abi_fuzz_cpu.py"], {"SSCAN_TEST_LIBRARY": lib, "LD_PRELOAD": rts[0]},
+               tmp_path)
 
 
 def test_oracle_under_asan_ubsan(tmp_path):
