@@ -561,7 +561,9 @@ def test_bwd_plan_splits():
     plan = sscan.bwd_plan
     assert plan(1, 1536, 262144) == dict(nwin=8192, csplit=4, gps=96, run_len=24, nrun=342)
     assert plan(8, 192, 16384, bidir=True) == dict(nwin=512, csplit=3, gps=16, run_len=3, nrun=171)
-    assert plan(128, 768, 197, bidir=True) == dict(nwin=7, csplit=12, gps=16, run_len=2, nrun=4)
+    # a short sequence whose whole-sequence runs still give 3,072 chain waves is one run
+    assert plan(128, 768, 197, bidir=True) == dict(nwin=7, csplit=12, gps=16, run_len=7, nrun=1)
+    assert plan(64, 384, 197, bidir=True)["run_len"] == 1
     p = plan(64, 384, 197, bidir=True)
     assert (p["csplit"], p["gps"]) == (6, 16)
     # fewer than 32 groups: one block per window
