@@ -716,7 +716,9 @@ hipError_t launch_bwd_io(const BwdArgs& a, const BwdPlan& p, float* w, hipStream
 // long sequence (8192 windows, 384 groups) 1: 7.61, 2: 7.33, 3: 7.44, 4: 7.11,
 // 8: 7.24, 16: 7.48; Mamba-YOLO map rows (8 x 512 windows per direction, 48 groups)
 // 1: 1.18, 2: 1.09, 3: 1.06, 4: 1.08, 8: 1.14; Vim-small (128 x 7 windows per
-// direction, 192 groups) 3: 1.00, 8: 0.96, 16: 0.93.
+// direction, 192 groups) 3: 1.00, 8: 0.96, 16: 0.93.  The minimum of groups per
+// block, 8 / 12 / 16 / 32 / 48: Vim-small 1.01 / 0.98 / 0.98 / 1.02 / 1.18, Vim-tiny
+// 0.28 / 0.31 / 0.27 / 0.38 / 0.49, Mamba-YOLO rows 1.17 / 1.14 / 1.12 / - / -.
 constexpr int64_t kBwdBlockTarget = 32768;
 constexpr int64_t kMinGroupsPerBlock = 16;
 // Chain passes: blocks per pass the run length aims for (about eight waves per
