@@ -40,6 +40,12 @@ namespace {
 
 constexpr int kWin = 32;           // tokens per backward window
 constexpr int kGroup = 4;          // channels per wavefront in the window pass
+// LDS floats per token of the window pass's per-token tables.  In steps 1 and 4 a
+// lane handles two tokens of one channel, so with 4 floats per token the 16 lanes of
+// a channel hit addresses 8 floats apart: four banks, four-way conflicts.  With 5,
+// each 32-lane half of a wave reaches 32 different banks.  Window pass on the long
+// sequence 7.13 -> 6.95 ms, Mamba-YOLO rows 1.12 -> 1.09 ms.
+constexpr int kTokPad = kGroup + 1;
 constexpr int kPartRows = kDState + 2;  // per-window partials: dA[16], dD, delta_bias
 #ifndef SSCAN_BWD_SCHED_TOKENS
 #define SSCAN_BWD_SCHED_TOKENS 4
@@ -226,9 +232,9 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
   using IO = Io<IO_BF16>;
   using T = typename IO::T;
   __shared__ float sBC[kWin][kBC];
-  __shared__ float sTok[kTokQ][kWin][kGroup];
-  __shared__ float sOutF[kOutQ * kWin * kGroup];  // [q][i][c]
-  auto sOut = [&](int q, int i, int cc) -> float { return sOutF[(q * kWin + i) * kGroup + cc]; };
+  __shared__ float sTok[kTokQ][kWin][kTokPad];
+  __shared__ float sOutF[kOutQ * kWin * kTokPad];  // [q][i][c]
+  auto sOut = [&](int q, int i, int cc) -> float { return sOutF[(q * kWin + i) * kTokPad + cc]; };
   const ScanArgs& f = a.fwd;
   const int lane = threadIdx.x;
   const int c = lane >> 4, n = lane & 15;
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
     // channel rows (dB, dC) are taken a chunk of four tokens at a time,
     // reduce-scattered over the lanes; the state sums go to LDS for step 4.
     const bool hi8 = (n & 8) != 0, hi4 = (n & 4) != 0;
-    const int slot_off = ((n >> 2) & 3) * kGroup + c;
+    const int slot_off = ((n >> 2) & 3) * kTokPad + c;
     float hist[kWin];
     float dA_acc = 0.0f;
     float mu_end = 0.0f;  // the adjoint past the window's first token in scan order
@@ -363,7 +369,7 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
       constexpr bool kFull = decltype(full_tag)::value;
       // A chunk's row sums leave lane n holding token 4 * chunk + ((n >> 2) & 3) (the
       // four lanes of a quad store the same value to the same word).
-      auto out_slot = [&](int q, int i) { return (q * kWin + (i & ~(kGroup - 1))) * kGroup + slot_off; };
+      auto out_slot = [&](int q, int i) { return (q * kWin + (i & ~(kGroup - 1))) * kTokPad + slot_off; };
       // a chunk of four tokens is complete at its last token in sweep order
       constexpr int kFwdLast = REV ? 0 : kGroup - 1, kRevLast = REV ? kGroup - 1 : 0;
       float h = h_in;
