@@ -177,6 +177,19 @@ __device__ __forceinline__ void store_tile(typename Io<BF16>::T* row, int64_t t,
 }
 
 typedef __attribute__((address_space(3))) float lds_float;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_uint4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+// A bf16 tile is half of a 128-byte line, and by the time a lane reaches the
+// line's other half it has left L2, so it would be fetched twice.  Where rows are
+// 128-byte aligned the one-direction output and aggregate passes load each line of
+// u and delta once: the half scanned first into registers, the other half with
+// gfx950's direct-to-LDS loads (each lane's 16 bytes land at base + lane * 16) into
+// a per-wave slot, read back when that tile comes up.  Slot: [u, delta][4][64
+// lanes] x 16 bytes = 8 KB per wave.
+constexpr int kLineSlot = 2 * 4 * 64;
 
 // What a scan pass does with each token's output.
 enum Mode : int {
@@ -230,6 +243,41 @@ struct Lane {
   int lane;
   bool vec;       // 16-byte vector access is valid for full tiles
   bool active;    // lane maps to a real channel (stores enabled)
+  bool line;      // rows are 128-byte aligned and lbuf is this wave's line slot
+  lds_uint4* lbuf;
+
+  // The one-direction output and aggregate passes with bf16 I/O load whole lines.
+  template <int MODE>
+  static constexpr bool kLinePairs = IO_BF16 && CONV == kNoConv && !GPARK && (MODE == kStore || MODE == kAggregate);
+
+  // Issues the direct-to-LDS loads of the tile of u and delta at t (the other half
+  // of a line whose first half is being loaded into registers).
+  __device__ __forceinline__ void park_half(int64_t t) const {
+    const uint4* pu = reinterpret_cast<const uint4*>(u + t);
+    const uint4* pd = reinterpret_cast<const uint4*>(delta + t);
+#pragma unroll
+    for (int i = 0; i < kWords / 4; ++i) {
+      __builtin_amdgcn_global_load_lds((global_void*)(pu + i), (lds_void*)(lbuf + i * kLanes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(pd + i), (lds_void*)(lbuf + (kWords / 4 + i) * kLanes), 16, 0, 0);
+    }
+  }
+
+  // Reads the parked tile back (the compiler waits for the loads that wrote it).
+  __device__ __forceinline__ void unpark_half(uint32_t (&wu)[kWords], uint32_t (&wd)[kWords]) const {
+#pragma unroll
+    for (int i = 0; i < kWords / 4; ++i) {
+      const u32x4 a = lbuf[i * kLanes + lane];
+      const u32x4 b = lbuf[(kWords / 4 + i) * kLanes + lane];
+      wu[4 * i] = a.x;
+      wu[4 * i + 1] = a.y;
+      wu[4 * i + 2] = a.z;
+      wu[4 * i + 3] = a.w;
+      wd[4 * i] = b.x;
+      wd[4 * i + 1] = b.y;
+      wd[4 * i + 2] = b.z;
+      wd[4 * i + 3] = b.w;
+    }
+  }
 
   __device__ __forceinline__ float step_size(float draw) const {
     const float x = draw + bias;
@@ -338,9 +386,13 @@ struct Lane {
     constexpr bool kAhead =
         !(IO_BF16 && CONV == kNoConv && (MODE == kStore || ((MODE == kPark || MODE == kMeet) && !GPARK)));
     int64_t t = REV ? tb - kTok : ta;
+    // Tiles in pairs that fill a 128-byte line: the first visited of a pair (even i)
+    // is loaded into registers and its partner (the next tile) parked in LDS.
+    const bool pairs = kLinePairs<MODE> && line && (ta % (2 * kTok)) == 0 && (tb % (2 * kTok)) == 0;
     if (kAhead) {
       load_tile<IO_BF16>(cu, u, t, vec);
       load_tile<IO_BF16>(cd, delta, t, vec);
+      if (pairs) park_half(REV ? t - kTok : t + kTok);
     }
     // convolution halo of the tile: the three tokens before it and the one after.
     // Inside a run of tiles it comes from the neighbouring tiles' registers (the one
@@ -358,11 +410,26 @@ struct Lane {
       const int64_t tn = REV ? t - kTok : t + kTok;
       const bool more = i + 1 < ntiles;
       if (!kAhead) {
-        load_tile<IO_BF16>(cu, u, t, vec);
-        load_tile<IO_BF16>(cd, delta, t, vec);
+        if (pairs && (i & 1)) {
+          unpark_half(cu, cd);
+        } else {
+          load_tile<IO_BF16>(cu, u, t, vec);
+          load_tile<IO_BF16>(cd, delta, t, vec);
+          if (pairs) park_half(tn);
+        }
       } else if (more) {
-        load_tile<IO_BF16>(nu, u, tn, vec);
-        load_tile<IO_BF16>(nd, delta, tn, vec);
+        if (pairs && !(i & 1)) {
+          unpark_half(nu, nd);
+        } else {
+          load_tile<IO_BF16>(nu, u, tn, vec);
+          load_tile<IO_BF16>(nd, delta, tn, vec);
+          if (pairs) {
+            // the slot still holds the tile read back one tile ago, whose registers
+            // this tile is about to use: let that read finish before it is overwritten
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            park_half(REV ? tn - kTok : tn + kTok);
+          }
+        }
       }
       if (CONV != kNoConv) {
         if (REV) {
@@ -397,8 +464,8 @@ struct Lane {
                                       const float (&xl)[kConvBack], float xr) {
     constexpr bool kOut = (MODE == kStore || MODE == kMeet);
     uint32_t wz[kWords];
-    // z is needed only for the gate at the end of the tile: its load latency hides
-    // behind the tile's tokens (the adjoint reads it at every token)
+    // z is needed only for the gate at the end of the tile (the adjoint reads it at
+    // every token)
     if ((kOut || MODE == kAdjoint) && HAS_Z) load_tile<IO_BF16>(wz, z, t, vec);
     float yt[kTok];
     BC cur, nxt;
@@ -570,6 +637,7 @@ __device__ __forceinline__ void init_lane(LaneT& L, const ScanArgs& a, int dir, 
   }
   L.lane = lane;
   L.vec = vec;
+  L.line = false;
 #pragma unroll
   for (int n = 0; n < kDState; ++n) L.h[n] = 0.0f;
 }
@@ -708,10 +776,16 @@ __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_aggregate_kernel(
   const int reverse = a.ndir == 2 ? dir : a.reverse;
   const int64_t last = reverse ? 0 : nseg - 1;
   Lane<IO_BF16, SOFTPLUS, false, CONV> L;
+  constexpr bool kLines = IO_BF16 && CONV == kNoConv;
+  __shared__ uint4 lslot[kLines ? kLineSlot : 1];
   const int64_t d = s.g * kLanes + threadIdx.x;
   if (!RUNS) {
     if (s.seg == last) return;
-    init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
+    init_lane(L, a, dir, s.b, s.g, bc, (vec & 1) != 0);
+    if (kLines) {
+      L.line = (vec & 2) != 0;
+      L.lbuf = (lds_uint4*)lslot;
+    }
     const int64_t t0 = s.seg * seg_len;
     const int64_t t1 = min64(a.len, t0 + seg_len);
     if (reverse) {
@@ -722,7 +796,11 @@ __global__ __launch_bounds__(kLanes) SSCAN_OCCUPANCY void scan_aggregate_kernel(
   } else {
     const int64_t k_lo = s.seg * ch.run_len, k_hi = min64(nseg, k_lo + ch.run_len);
     if (k_hi - k_lo == 1 && k_lo == last) return;
-    init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
+    init_lane(L, a, dir, s.b, s.g, bc, (vec & 1) != 0);
+    if (kLines) {
+      L.line = (vec & 2) != 0;
+      L.lbuf = (lds_uint4*)lslot;
+    }
     for (int64_t i = k_lo; i < k_hi; ++i) {
       const int64_t k = reverse ? k_lo + k_hi - 1 - i : i;
       if (k == last) break;

@@ -45,7 +45,13 @@ __global__ __launch_bounds__(kLanes) SSCAN_OUT_OCCUPANCY(IO_BF16 && CONV == kNoC
   const int64_t ngroups = (a.dim + kLanes - 1) / kLanes;
   const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
   Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32> L;
-  init_lane(L, a, 0, s.b, s.g, bc, vec != 0);
+  constexpr bool kLines = IO_BF16 && CONV == kNoConv;
+  __shared__ uint4 lslot[kLines ? kLineSlot : 1];
+  init_lane(L, a, 0, s.b, s.g, bc, (vec & 1) != 0);
+  if (kLines) {
+    L.line = (vec & 2) != 0;
+    L.lbuf = (lds_uint4*)lslot;
+  }
   load_entry(L, a, 0, s.b, s.seg, s.g, nseg, ch);
   const int64_t t0 = s.seg * seg_len;
   const int64_t t1 = min64(a.len, t0 + seg_len);
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(2 * kLanes) SSCAN_OUT_OCCUPANCY(IO_BF16 && CONV == 
   const SegIndex s = decode_block(blockIdx.x, ngroups, nseg);
   const int dir = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kLanes);  // wave-uniform
   Lane<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32, GPARK> L;
-  init_lane(L, a, dir, s.b, s.g, bc, vec != 0);
+  init_lane(L, a, dir, s.b, s.g, bc, (vec & 1) != 0);
   load_entry(L, a, dir, s.b, s.seg, s.g, nseg, ch);
   const int64_t t0 = s.seg * seg_len;
   const int64_t t1 = min64(a.len, t0 + seg_len);
@@ -211,6 +217,7 @@ __global__ __launch_bounds__(2 * kLanes) SSCAN_OUT_OCCUPANCY(IO_BF16 && CONV == 
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned128(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 127u) == 0; }
 
 template <bool IO_BF16, bool SOFTPLUS, bool HAS_Z, int CONV, bool Y_F32 = false>
 hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t stream, hipEvent_t const* ev) {
@@ -222,6 +229,11 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   const size_t esz = IO_BF16 ? 2 : 4;
   bool vec = (size_t(a.len) * esz) % 16 == 0 && aligned16(a.u) && aligned16(a.y) && (!a.z || aligned16(a.z));
   for (int k = 0; k < a.ndir; ++k) vec = vec && aligned16(a.dir[k].delta);
+  // whole 128-byte lines of u and delta (bf16): rows and segments start on a line
+  bool line = IO_BF16 && vec && (size_t(a.len) * esz) % 128 == 0 && (p.nseg <= 1 || (size_t(p.seg_len) * esz) % 128 == 0) &&
+              aligned128(a.u);
+  for (int k = 0; k < a.ndir; ++k) line = line && aligned128(a.dir[k].delta);
+  const int flags = int(vec) | (int(line) << 1);
   float* bc = w;
   SegChain ch{};
   ch.run_len = p.run_len;
@@ -254,11 +266,11 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
     if (p.run_len > 1) {
       hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS, CONV, true>),
                          dim3(unsigned(agg_blocks), unsigned(a.ndir)), dim3(kLanes), 0, stream, a, p.seg_len, p.nseg,
-                         ch, static_cast<const float*>(bc), int(vec));
+                         ch, static_cast<const float*>(bc), flags);
     } else {
       hipLaunchKernelGGL((scan_aggregate_kernel<IO_BF16, SOFTPLUS, CONV, false>),
                          dim3(unsigned(agg_blocks), unsigned(a.ndir)), dim3(kLanes), 0, stream, a, p.seg_len, p.nseg,
-                         ch, static_cast<const float*>(bc), int(vec));
+                         ch, static_cast<const float*>(bc), flags);
     }
     mark(2);
     launch_carry(a, p.nrun, ch.r, ch.e, 0, stream);
@@ -267,7 +279,7 @@ hipError_t launch_typed(const ScanArgs& a, const Plan& p, float* w, hipStream_t 
   mark(3);
   if (a.ndir == 1) {
     hipLaunchKernelGGL((scan_output_dir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32>), dim3(unsigned(nblocks)), dim3(kLanes), 0,
-                       stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), ch, int(vec));
+                       stream, a, p.seg_len, p.nseg, static_cast<const float*>(bc), ch, flags);
   } else if (p.park_floats) {
     float* gpark = w + p.bc_floats + p.p_floats + p.s_floats + p.r_floats + p.e_floats;
     hipLaunchKernelGGL((scan_output_bidir_kernel<IO_BF16, SOFTPLUS, HAS_Z, CONV, Y_F32, true>), dim3(unsigned(nblocks)),
