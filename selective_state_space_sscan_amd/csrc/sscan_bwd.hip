@@ -87,22 +87,66 @@ __device__ __forceinline__ float row_sum16(float v) {
 // Sums over the 16 states of a channel for a chunk of four tokens v[0..3] (slot =
 // token % 4), reduce-scattered over the row: lane n of the row receives the sum
 // for slot (n >> 2) & 3.  Round one pairs lanes n and n^8 (row_ror:8): the lower
-// half keeps slots 0, 1 and passes on 2, 3, the upper half the other way round;
-// round two pairs n and n^7 (row_half_mirror), which keeps bit 3 and flips bit 2:
-// the lane keeps the first or second of its two slots by bit 2; the last two
-// rounds add over the quad (quad_perm xor 1, xor 2), the lanes n..n^3 whose
-// partial sums together cover the whole row.  11 VALU operations for four tokens,
-// where four all-lane sums take 16.
-__device__ __forceinline__ float row_scatter4(const float (&v)[kGroup], bool hi8, bool hi4) {
-  float k0 = hi8 ? v[2] : v[0], k1 = hi8 ? v[3] : v[1];
-  const float s0 = hi8 ? v[0] : v[2], s1 = hi8 ? v[1] : v[3];
-  k0 += dpp_mov<0x128>(s0);  // row_ror:8
-  k1 += dpp_mov<0x128>(s1);
-  float k = hi4 ? k1 : k0;
-  k += dpp_mov<0x141>(hi4 ? k0 : k1);  // row_half_mirror
-  k += dpp_mov<0xB1>(k);
-  k += dpp_mov<0x4E>(k);
-  return k;
+// half keeps slots 0, 1 (the sums with the lanes 8 apart), the upper half slots 2,
+// 3; round two pairs n and n^7 (row_half_mirror), which keeps bit 3 and flips bit
+// 2: lanes with bit 2 clear keep the first of their two slots, the others the
+// second; the last two rounds add over the quad (quad_perm xor 1, xor 2), the
+// lanes n..n^3 whose partial sums together cover the whole row.  Where lanes keep
+// different slots, two DPP adds with complementary bank masks (bank = four lanes
+// of a row) write one register, each for its own lanes, so no lane has to select
+// what it sends or keeps: 8 VALU operations for four tokens, where four all-lane
+// sums take 16 (and selecting operands, 11).  The DPP reads of registers written
+// by the VALU just before take two wait states (s_nop 1), which the compiler does
+// not insert for an asm block.
+// a = (a of the lane 8 apart) + a on banks LO (lanes of the row's lower or mirror
+// half as the control says), b's sum on the other banks: two DPP adds, each writing
+// its own lanes of one register.  The first reads only lanes the second writes, and
+// the second does not read a, so a can be updated in place.
+#define SSCAN_DPP_PAIR(CTRL, LO, HI)                                                  \
+  "s_nop 1\n\t"                                                                     \
+  "v_add_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:" LO "\n\t"             \
+  "v_add_f32_dpp %0, %1, %1 " CTRL " row_mask:0xf bank_mask:" HI
+__device__ __forceinline__ float row_scatter4(const float (&v)[kGroup], bool, bool) {
+  float k0 = v[0], k1 = v[1];
+  asm(SSCAN_DPP_PAIR("row_ror:8", "0x3", "0xc") : "+v"(k0) : "v"(v[2]));
+  asm(SSCAN_DPP_PAIR("row_ror:8", "0x3", "0xc") : "+v"(k1) : "v"(v[3]));
+  asm(SSCAN_DPP_PAIR("row_half_mirror", "0x5", "0xa") : "+v"(k0) : "v"(k1));
+  k0 += dpp_mov<0xB1>(k0);
+  k0 += dpp_mov<0x4E>(k0);
+  return k0;
+}
+#undef SSCAN_DPP_PAIR
+
+// row_scatter4 of two chunks at once (the reverse sweep's P and Q terms), their
+// rounds interleaved so that each DPP add reads registers written at least two
+// instructions earlier (the wait states the hardware needs) with four s_nop wait
+// states in all instead of about twenty.
+__device__ __forceinline__ void row_scatter4x2(const float (&v)[kGroup], const float (&w)[kGroup], float& rv,
+                                               float& rw) {
+  float a0 = v[0], a1 = v[1], b0 = w[0], b1 = w[1];
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %4, %4 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %2, %6, %6 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %3, %3, %3 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %3, %7, %7 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %2, %3, %3 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32_dpp %2, %2, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32_dpp %2, %2, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1)
+      : "v"(v[2]), "v"(v[3]), "v"(w[2]), "v"(w[3]));
+  rv = a0;
+  rw = b0;
 }
 
 // x + (x of the lane 32 apart) on lanes 0..31, y + (y of the lane 32 apart) on lanes
@@ -417,8 +461,10 @@ __global__ __launch_bounds__(kLanes) void bwd_window_kernel(BwdArgs a, int dir, 
           mu = at * lam;
         }
         if (i % kGroup == kRevLast) {
-          sOutF[out_slot(OP, i)] = row_scatter4(tP, hi8, hi4);
-          sOutF[out_slot(OQ, i)] = row_scatter4(tQ, hi8, hi4);
+          float sP, sQ;
+          row_scatter4x2(tP, tQ, sP, sQ);
+          sOutF[out_slot(OP, i)] = sP;
+          sOutF[out_slot(OQ, i)] = sQ;
           accB[i / kGroup] += chunk_sum(tB);
           accC[i / kGroup] += chunk_sum(tC);
         }

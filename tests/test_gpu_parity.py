@@ -273,3 +273,47 @@ def test_degenerate_regimes(name, mod, bidir):
         for p in x.dirs:
             p.delta_bias.zero_()
     check(gpu_run(x), oracle_run(x), "f32", f"{name} bidir={bidir}")
+
+
+# Whole-line loads.  Where bf16 rows and segments start on 128-byte lines, the
+# one-direction output pass and the aggregate pass read u and delta a whole line
+# (two tiles) at a time, the second tile by way of LDS.  The same inputs placed 16
+# bytes past a line (16-byte vectors still, lines no longer) take the tile-at-a-time
+# path.  Both runs are compared with the oracle, and with each other: the arithmetic
+# is the same, so they agree bitwise.
+LINE_CASES = [
+    # name, batch, dim, len, kwargs
+    ("fwd-segments", 2, 128, 4096, {}),
+    ("rev-segments", 2, 128, 4096, dict(reverse=True)),
+    ("no-gate", 1, 192, 2048, dict(gate=False)),
+    ("one-segment", 4, 64, 192, {}),
+    ("one-pair", 3, 64, 64, dict(reverse=True)),
+    ("not-on-lines", 2, 64, 4096 + 32, {}),  # rows 64 bytes off a line: no pairs
+]
+
+
+def offset_copy(t, elems):
+    """t copied into a buffer that starts `elems` elements past an allocation."""
+    buf = torch.empty(t.numel() + elems, dtype=t.dtype, device=t.device)
+    v = buf[elems:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("name,b,d,L,kw", LINE_CASES, ids=[c[0] for c in LINE_CASES])
+def test_whole_line_loads(name, b, d, L, kw):
+    x = I.make_inputs(b, d, L, io_dtype="bf16", bc_dtype="f32", seed=zlib.crc32(name.encode()) % 10000,
+                      a_init="random")
+    xd = x.to(DEV)
+    p = xd.dirs[0]
+    z = xd.z if kw.get("gate", True) else None
+    rev = kw.get("reverse", False)
+    assert xd.u.data_ptr() % 128 == 0 and xd.delta.data_ptr() % 128 == 0
+    y_line = sscan.fwd(xd.u, xd.delta, p.A, p.B, p.C, p.D, z, p.delta_bias, reverse=rev)
+    u8, d8 = offset_copy(xd.u, 8), offset_copy(xd.delta, 8)
+    assert u8.data_ptr() % 128 == 16
+    y_tile = sscan.fwd(u8, d8, p.A, p.B, p.C, p.D, z, p.delta_bias, reverse=rev)
+    torch.cuda.synchronize()
+    assert torch.equal(y_line, y_tile), f"{name}: whole-line and tile paths differ"
+    ref = oracle_run(x, gate=kw.get("gate", True), reverse=rev)
+    check(y_line, ref, "bf16", f"whole lines {name}")
