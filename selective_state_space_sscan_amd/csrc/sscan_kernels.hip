@@ -318,17 +318,20 @@ hipError_t launch_io(const ScanArgs& a, const Plan& p, float* w, hipStream_t str
                      : launch_conv_mode<IO_BF16, kConvLin>(a, p, w, stream, ev);
 }
 
-// Standalone depthwise convolution: each thread produces kConvRun consecutive outputs
-// of one row.  The run itself moves as 16-byte vectors when rows are 16-byte aligned.
+// Standalone depthwise convolution: each thread produces kConvReps runs of kConvRun
+// consecutive outputs of one row, the runs 64 x kConvRun tokens apart.  A run moves
+// as 16-byte vectors when rows are 16-byte aligned, and all of a thread's runs are
+// loaded before any is computed, so each wave keeps kConvReps KB in flight.
 // Block (64 runs, 4 channels): a wavefront holds 64 consecutive runs of one row, so
 // the halo -- three tokens before the run, one after -- is the neighbouring lanes'
 // data, moved across lanes; only the wave's first and last lanes read theirs from
 // memory.  Grid (run chunks, channel quads, batch rows -- striding above the grid
-// limit), so every thread knows its run and channel without dividing and loads its
+// limit), so every thread knows its runs and channel without dividing and loads its
 // channel's taps once.  Lanes past the row's end stay active (zeros) for the
 // cross-lane moves.
 constexpr int kConvRun = 8;
 constexpr int kConvRows = 4;
+constexpr int kConvReps = 4;
 
 template <bool IO_BF16, bool SILU, bool Y_F32 = false>
 __global__ __launch_bounds__(kLanes * kConvRows) void conv1d_kernel(ConvArgs a, int vec) {
@@ -336,9 +339,6 @@ __global__ __launch_bounds__(kLanes * kConvRows) void conv1d_kernel(ConvArgs a, 
   using T = typename IO::T;
   using TY = typename std::conditional<Y_F32, float, T>::type;
   using IOY = Io<!Y_F32 && IO_BF16>;
-  const int64_t r = int64_t(blockIdx.x) * kLanes + threadIdx.x;
-  const int64_t t0 = r * kConvRun;  // may be past the row's end: the lane loads and stores nothing
-  const bool full = vec && t0 + kConvRun <= a.len;
   constexpr int kSpan = kConvBack + kConvRun + 1;
   for (int64_t d = int64_t(blockIdx.y) * kConvRows + threadIdx.y; d < a.dim; d += int64_t(gridDim.y) * kConvRows) {
     float cw[kConvTaps];
@@ -352,60 +352,105 @@ __global__ __launch_bounds__(kLanes * kConvRows) void conv1d_kernel(ConvArgs a, 
       const int64_t row = b * a.dim + d;
       const T* x = static_cast<const T*>(a.x) + row * a.len;
       TY* y = static_cast<TY*>(a.y) + row * a.len;
-      float xs[kSpan];  // x[t0 - 3 .. t0 + kConvRun], zero outside the row
-      if (full) {
-        if (IO_BF16) {
-          const uint4 v = *reinterpret_cast<const uint4*>(x + t0);
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      // x[t0 - 3 .. t0 + kConvRun] of each run, zero outside the row; a run may start
+      // past the row's end: the lane loads and stores nothing for it.  The runs' words
+      // are only loaded here (unpacked below), so no load waits for another.
+      constexpr int kRaw = IO_BF16 ? 4 : 8;
+      uint32_t raw[kConvReps][kRaw];
+      uint32_t hraw[kConvReps][kConvBack + 1];
+      // one element's bits (zero-extended for bf16), t clamped into the row
+      auto raw_at = [&](int64_t t) -> uint32_t {
+        t = t < 0 ? 0 : (t >= a.len ? a.len - 1 : t);
+        if (IO_BF16) return uint32_t(reinterpret_cast<const uint16_t*>(x)[t]);
+        return __float_as_uint(reinterpret_cast<const float*>(x)[t]);
+      };
+      auto widen = [](uint32_t r) -> float { return IO_BF16 ? __uint_as_float(r << 16) : __uint_as_float(r); };
+      float xs[kConvReps][kSpan];
+      int64_t t0[kConvReps];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            xs[kConvBack + 2 * k] = bf16_lo(w[k]);
-            xs[kConvBack + 2 * k + 1] = bf16_hi(w[k]);
+      for (int q = 0; q < kConvReps; ++q) {
+        t0[q] = ((int64_t(blockIdx.x) * kConvReps + q) * kLanes + threadIdx.x) * kConvRun;
+        const bool full = vec && t0[q] + kConvRun <= a.len;
+        if (full) {
+          const uint4* p = reinterpret_cast<const uint4*>(x + t0[q]);
+          const uint4 v = p[0];
+          raw[q][0] = v.x;
+          raw[q][1] = v.y;
+          raw[q][2] = v.z;
+          raw[q][3] = v.w;
+          if (!IO_BF16) {
+            const uint4 v1 = p[1];
+            raw[q][4 % kRaw] = v1.x;
+            raw[q][5 % kRaw] = v1.y;
+            raw[q][6 % kRaw] = v1.z;
+            raw[q][7 % kRaw] = v1.w;
           }
         } else {
-          const float4* p = reinterpret_cast<const float4*>(x + t0);
-          const float4 v0 = p[0], v1 = p[1];
-          const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-          for (int k = 0; k < 8; ++k) xs[kConvBack + k] = f[k];
+          for (int k = 0; k < kConvRun; ++k) {
+            const uint32_t e = t0[q] + k < a.len ? __float_as_uint(IO::load(x, t0[q] + k)) : 0u;
+            if (IO_BF16) {
+              // the widened value's upper half is the bf16 bit pattern
+              raw[q][k / 2] = (k & 1) ? ((raw[q][k / 2] & 0xffffu) | (e & 0xffff0000u)) : (e >> 16);
+            } else {
+              raw[q][k % kRaw] = e;
+            }
+          }
         }
-      } else {
+        // the halo tokens, raw, at indices clamped into the row (zeroed outside it below):
+        // loaded by every lane, with no branch for a wait to land in, though only the
+        // wave's end lanes use theirs (the others' come across lanes; all are in lines
+        // the wave reads anyway)
 #pragma unroll
-        for (int k = 0; k < kConvRun; ++k) xs[kConvBack + k] = t0 + k < a.len ? IO::load(x, t0 + k) : 0.0f;
+        for (int k = 0; k < kConvBack; ++k) hraw[q][k] = raw_at(t0[q] - kConvBack + k);
+        hraw[q][kConvBack] = raw_at(t0[q] + kConvRun);
       }
-      // the halo: the previous lane's last three tokens, the next lane's first
 #pragma unroll
-      for (int k = 0; k < kConvBack; ++k) xs[k] = __shfl_up(xs[kConvRun + k], 1);
-      xs[kSpan - 1] = __shfl_down(xs[kConvBack], 1);
-      if (threadIdx.x == 0) {
+      for (int q = 0; q < kConvReps; ++q) {
+#pragma unroll
+        for (int k = 0; k < kConvRun; ++k)
+          xs[q][kConvBack + k] = IO_BF16 ? ((k & 1) ? bf16_hi(raw[q][k / 2]) : bf16_lo(raw[q][k / 2]))
+                                         : __uint_as_float(raw[q][k % kRaw]);
 #pragma unroll
         for (int k = 0; k < kConvBack; ++k) {
-          const int64_t t = t0 - kConvBack + k;
-          xs[k] = (t >= 0 && t < a.len) ? IO::load(x, t) : 0.0f;
+          const int64_t t = t0[q] - kConvBack + k;
+          xs[q][k] = (t >= 0 && t < a.len) ? widen(hraw[q][k]) : 0.0f;
         }
-      }
-      if (threadIdx.x == kLanes - 1) xs[kSpan - 1] = t0 + kConvRun < a.len ? IO::load(x, t0 + kConvRun) : 0.0f;
-      float out[kConvRun];
+        xs[q][kSpan - 1] = t0[q] + kConvRun < a.len ? widen(hraw[q][kConvBack]) : 0.0f;
+        // the halo: the previous lane's last three tokens, the next lane's first (the
+        // wave's end lanes keep what they loaded)
 #pragma unroll
-      for (int j = 0; j < kConvRun; ++j) {
-        float acc = cb;
+        for (int k = 0; k < kConvBack; ++k) {
+          const float v = __shfl_up(xs[q][kConvRun + k], 1);
+          if (threadIdx.x != 0) xs[q][k] = v;
+        }
+        {
+          const float v = __shfl_down(xs[q][kConvBack], 1);
+          if (threadIdx.x != kLanes - 1) xs[q][kSpan - 1] = v;
+        }
+        float out[kConvRun];
 #pragma unroll
-        for (int k = 0; k < kConvTaps; ++k) acc = fmaf(cw[k], xs[j + k], acc);
-        out[j] = SILU ? silu_f32(acc) : acc;
-      }
-      if (full) {
-        if (IO_BF16 && !Y_F32) {
-          *reinterpret_cast<uint4*>(y + t0) = make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
-                                                         pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
+        for (int j = 0; j < kConvRun; ++j) {
+          float acc = cb;
+#pragma unroll
+          for (int k = 0; k < kConvTaps; ++k) acc = fmaf(cw[k], xs[q][j + k], acc);
+          out[j] = SILU ? silu_f32(acc) : acc;
+        }
+        const bool full = vec && t0[q] + kConvRun <= a.len;
+        if (full) {
+          if (IO_BF16 && !Y_F32) {
+            *reinterpret_cast<uint4*>(y + t0[q]) = make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
+                                                              pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
+          } else {
+            float4* p = reinterpret_cast<float4*>(y + t0[q]);
+            p[0] = make_float4(out[0], out[1], out[2], out[3]);
+            p[1] = make_float4(out[4], out[5], out[6], out[7]);
+          }
         } else {
-          float4* p = reinterpret_cast<float4*>(y + t0);
-          p[0] = make_float4(out[0], out[1], out[2], out[3]);
-          p[1] = make_float4(out[4], out[5], out[6], out[7]);
-        }
-      } else {
 #pragma unroll
-        for (int j = 0; j < kConvRun; ++j)
-          if (t0 + j < a.len) IOY::store(reinterpret_cast<typename IOY::T*>(y), t0 + j, out[j]);
+          for (int j = 0; j < kConvRun; ++j)
+            if (t0[q] + j < a.len) IOY::store(reinterpret_cast<typename IOY::T*>(y), t0[q] + j, out[j]);
+        }
       }
     }
   }
@@ -518,7 +563,8 @@ hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream) {
   constexpr int64_t kMaxGridYZ = 65535;
   const int64_t runs = (a.len + kConvRun - 1) / kConvRun;
   const int64_t quads = (a.dim + kConvRows - 1) / kConvRows;
-  const dim3 grid(unsigned((runs + kLanes - 1) / kLanes), unsigned(std::min(quads, kMaxGridYZ)),
+  const int64_t per_block = int64_t(kLanes) * kConvReps;
+  const dim3 grid(unsigned((runs + per_block - 1) / per_block), unsigned(std::min(quads, kMaxGridYZ)),
                   unsigned(std::min(a.batch, kMaxGridYZ)));
   const dim3 block(kLanes, kConvRows);
   // runs start at multiples of 8 tokens: 16-byte aligned when every row is
